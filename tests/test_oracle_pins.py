@@ -1,0 +1,291 @@
+"""Pins for the CPU oracle, checked against things other than the oracle.
+
+Each test pins one oracle function to hand-worked values, closed forms,
+invariants, an independent library routine (numpy BLAS / int64 einsum) or an
+exact rational computation, so that a dropped term, a wrong sign, a
+transposed operand or a different rounding rule fails at least one of them.
+CPU only.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import tern_synth as ts
+from tests import exact
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+@pytest.fixture(scope="module")
+def hand():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def bf16(a) -> np.ndarray:
+    return ts.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def f16(a) -> np.ndarray:
+    return np.asarray(a, np.float64).astype(np.float16).view(np.uint16)
+
+
+# ------------------------------------------------------------ hand-worked
+
+
+def test_hand_linear_bf16(hand):
+    c = hand["linear_bf16"]
+    x = bf16(c["x"])
+    assert np.array_equal(ts.bf16_bits_to_f32(x), np.asarray(c["x"], np.float32))
+    y = oracle.linear_bf16(x, np.asarray(c["w"], np.int8), f16(c["s"]))
+    assert np.array_equal(y, np.asarray(c["y"], np.float64))
+
+
+def test_hand_quant_s8(hand):
+    for c in hand["quant_s8"]:
+        x = bf16([c["x"]])
+        q, sc = oracle.quant_s8(x)
+        assert exact.f32_bits(float(sc[0])) == int(c["scale_bits"], 16), c["derivation"]
+        assert q[0].tolist() == c["q"], c["derivation"]
+
+
+def test_hand_s8_acc_and_linear(hand):
+    c = hand["s8_linear"]
+    q = np.asarray([c["q"]], np.int8)
+    w = np.asarray(c["w"], np.int8)
+    acc = oracle.s8_acc(q, w, c["G"])
+    assert acc[0].tolist() == c["acc"]
+    y = oracle.linear_s8(q, np.asarray([c["scale"]], np.float32), w, f16(c["s"]))
+    assert y[0].tolist() == c["y"]
+
+
+def test_hand_layout_reader(hand):
+    c = hand["layout_v1"]
+    N, K, G = c["N"], c["K"], c["G"]
+    sp = np.zeros(N * (K // G), np.uint16)
+    for case in c["cases"]:
+        codes = np.zeros(N * K // 4, np.uint8)
+        codes[case["byte"]] = int(case["value"], 16)
+        w, _ = oracle.unpack_layout_v1(codes, sp, N, K, G)
+        nz = np.argwhere(w != 0)
+        assert nz.tolist() == [[case["n"], case["k"]]], case["derivation"]
+        assert w[case["n"], case["k"]] == case["w"], case["derivation"]
+    codes = np.zeros(N * K // 4, np.uint8)
+    for sc in c["scale_cases"]:
+        sp = np.zeros(N * (K // G), np.uint16)
+        sp[sc["index"]] = 0x3C00  # fp16 1.0
+        _, s = oracle.unpack_layout_v1(codes, sp, N, K, G)
+        assert np.argwhere(s != 0).tolist() == [[sc["n"], sc["g"]]], sc["derivation"]
+
+
+def test_layout_reader_rejects_code_10():
+    codes = np.zeros(16 * 256 // 4, np.uint8)
+    codes[3] = 0x80  # bits 31:30 of lane 0 word 0 = 10
+    with pytest.raises(ValueError):
+        oracle.unpack_layout_v1(codes, np.zeros(16 * 2, np.uint16), 16, 256, 128)
+
+
+# ------------------------------------------------------- closed forms
+
+
+def _small_case(seed=7, T=3, N=16, K=256, G=64):
+    rng = np.random.default_rng(seed)
+    w = ts.draw_weights(rng, N, K, 1.0 / 3.0)
+    s = ts.draw_scales(rng, N, K, G)
+    x = bf16(rng.standard_normal((T, K)).astype(np.float32) * 3)
+    return x, w, s
+
+
+def test_zero_weights_give_zero():
+    x, w, s = _small_case()
+    y = oracle.linear_bf16(x, np.zeros_like(w), s)
+    assert np.all(y == 0.0)
+    q, sc = oracle.quant_s8(x)
+    assert np.all(oracle.linear_s8(q, sc, np.zeros_like(w), s) == 0.0)
+    assert np.all(oracle.s8_acc(q, np.zeros_like(w), 64) == 0)
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_all_same_sign_weights_give_group_sums(sign):
+    # Integer x and power-of-two scales make every sum exact, so the closed
+    # form y = sign * sum_g s[n, g] * (sum of x over group g) holds bit for bit.
+    T, N, K, G = 2, 16, 256, 64
+    x = ts.integer_activations(K, T, seed=11)
+    s = ts.pow2_scales(N, K, G, seed=12)
+    w = np.full((N, K), sign, np.int8)
+    y = oracle.linear_bf16(x, w, s)
+    xs = ts.bf16_bits_to_f32(x).astype(np.float64).reshape(T, K // G, G).sum(-1)  # [T, NG]
+    sv = s.view(np.float16).astype(np.float64)  # [N, NG]
+    expect = sign * (xs @ sv.T)
+    assert np.array_equal(y, expect)
+
+
+def test_single_nonzero_weight_picks_one_product():
+    x, w, s = _small_case(T=2)
+    w = np.zeros_like(w)
+    w[5, 77] = -1
+    y = oracle.linear_bf16(x, w, s)
+    xf = ts.bf16_bits_to_f32(x).astype(np.float64)
+    sv = s.view(np.float16).astype(np.float64)
+    expect = np.zeros_like(y)
+    expect[:, 5] = -sv[5, 77 // 64] * xf[:, 77]
+    assert np.array_equal(y, expect)
+
+
+# ---------------------------------------------------------- invariants
+
+
+def test_linear_bf16_is_linear_in_x():
+    T, N, K, G = 3, 32, 512, 128
+    rng = np.random.default_rng(5)
+    w = ts.draw_weights(rng, N, K, 0.4)
+    s = ts.pow2_scales(N, K, G, seed=6)
+    xi = rng.integers(-50, 51, size=(T, K)).astype(np.float32)
+    x = bf16(xi)
+    y = oracle.linear_bf16(x, w, s)
+    assert np.array_equal(oracle.linear_bf16(bf16(2 * xi), w, s), 2 * y)
+    assert np.array_equal(oracle.linear_bf16(bf16(-xi), w, s), -y)
+    mask = rng.random(K) < 0.5  # disjoint supports: x1 + x2 is exact
+    x1 = np.where(mask, xi, 0).astype(np.float32)
+    x2 = np.where(mask, 0, xi).astype(np.float32)
+    y12 = oracle.linear_bf16(bf16(x1), w, s) + oracle.linear_bf16(bf16(x2), w, s)
+    assert np.array_equal(y12, y)
+
+
+def test_quant_s8_invariances():
+    x, _, _ = _small_case(T=4, K=512)
+    xf = ts.bf16_bits_to_f32(x)
+    q, sc = oracle.quant_s8(x)
+    q2, sc2 = oracle.quant_s8(bf16(2 * xf))
+    assert np.array_equal(q2, q) and np.array_equal(sc2, 2 * sc)
+    qn, scn = oracle.quant_s8(bf16(-xf))
+    assert np.array_equal(qn, -q) and np.array_equal(scn, sc)
+    assert q.min() >= -127 and q.max() <= 127
+    # the absmax element maps to +-127 exactly
+    am = np.abs(xf).argmax(axis=1)
+    assert np.array_equal(np.abs(q[np.arange(4), am]), np.full(4, 127, np.int8))
+
+
+def test_linear_s8_sign_symmetry_bitwise():
+    x, w, s = _small_case(T=3, N=32, K=512, G=128)
+    q, sc = oracle.quant_s8(x)
+    y = oracle.linear_s8(q, sc, w, s)
+    yn = oracle.linear_s8(-q, sc, w, s)
+    assert np.array_equal(yn.view(np.uint32), (-y).view(np.uint32))
+
+
+def test_batch_invariance():
+    x, w, s = _small_case(T=5)
+    y = oracle.linear_bf16(x, w, s)
+    q, sc = oracle.quant_s8(x)
+    ys8 = oracle.linear_s8(q, sc, w, s)
+    for t in range(5):
+        assert np.array_equal(oracle.linear_bf16(x[t:t + 1], w, s)[0], y[t])
+        qt, st = oracle.quant_s8(x[t:t + 1])
+        assert np.array_equal(qt[0], q[t]) and st[0] == sc[t]
+        assert np.array_equal(oracle.linear_s8(qt, st, w, s)[0].view(np.uint32),
+                              ys8[t].view(np.uint32))
+
+
+# ------------------------------------------------- library routines
+
+
+def test_linear_bf16_matches_numpy_blas_on_dequantised_matrix():
+    x, w, s = _small_case(T=4, N=64, K=1024, G=128)
+    y = oracle.linear_bf16(x, w, s)
+    xf = ts.bf16_bits_to_f32(x).astype(np.float64)
+    W = w.astype(np.float64) * np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+    y_np = xf @ W.T
+    bound = 1e-13 * (np.abs(xf) @ np.abs(W).T)
+    assert np.all(np.abs(y - y_np) <= bound)
+    # a transposed/misaligned scale would be visibly off
+    W_bad = w.astype(np.float64) * np.tile(s.view(np.float16).astype(np.float64), (1, 128))
+    assert not np.allclose(xf @ W_bad.T, y)
+
+
+def test_s8_acc_matches_int64_einsum():
+    x, w, s = _small_case(T=4, N=48, K=512, G=64)
+    q, _ = oracle.quant_s8(x)
+    acc = oracle.s8_acc(q, w, 64)
+    ref = np.einsum("tgk,ngk->tng", q.astype(np.int64).reshape(4, 8, 64),
+                    w.astype(np.int64).reshape(48, 8, 64))
+    assert np.array_equal(acc, ref)
+
+
+# --------------------------------------------------- exact rationals
+
+
+def test_linear_s8_is_exactly_rounded():
+    x, w, s = _small_case(T=3, N=24, K=512, G=128)
+    q, sc = oracle.quant_s8(x)
+    y = oracle.linear_s8(q, sc, w, s)
+    acc = oracle.s8_acc(q, w, 128)
+    for t in range(3):
+        st = exact.f32_to_fraction(float(sc[t]))
+        for n in range(24):
+            tot = sum(exact.half_bits_to_fraction(int(s[n, g])) * int(acc[t, n, g])
+                      for g in range(4))
+            assert exact.f32_bits(float(y[t, n])) == exact.fraction_to_f32_bits(st * tot)
+
+
+def test_linear_s8_within_gate_of_fp32_order():
+    # The fixed fp32-order diagnostic differs from the exactly rounded value
+    # by accumulated fp32 rounding only (far below the 1e-6 relative gate).
+    x, w, s = _small_case(T=4, N=64, K=2048, G=128)
+    q, sc = oracle.quant_s8(x)
+    y = oracle.linear_s8(q, sc, w, s).astype(np.float64)
+    yo = oracle.linear_s8_fp32_ordered(q, sc, w, s).astype(np.float64)
+    assert np.linalg.norm(yo - y) / np.linalg.norm(y) < 1e-6
+
+
+def _all_positive_bf16_upto(a: float) -> np.ndarray:
+    b = np.arange(1, 0x7F80, dtype=np.uint32).astype(np.uint16)  # positive finite
+    v = ts.bf16_bits_to_f32(b)
+    return b[v <= a]
+
+
+@pytest.mark.parametrize("absmax", [1.0, 3.0, 7.5, 20.0, 37.25, 51.5, 100.0, 126.0, 254.0,
+                                    0.1875, 1e-3, 6.0e4])
+def test_quant_code_rule_brute_force(absmax):
+    """Every positive finite bf16 <= absmax (and its negation) against the
+    exactly computed double rounding fl32(x / fl32(absmax / 127)) -> nearest
+    even integer -> clamp."""
+    a_bits = int(bf16([absmax])[0])
+    a = exact.bf16_bits_to_fraction(a_bits)
+    vals = _all_positive_bf16_upto(float(exact.bits_f32(a_bits << 16)))
+    row = np.concatenate([[a_bits], vals, vals | 0x8000]).astype(np.uint16)[None, :]
+    q, sc = oracle.quant_s8(row)
+    sbits = exact.f32_bits(float(sc[0]))
+    assert sbits == exact.quant_scale_exact(a)
+    # the exact rule for every element
+    cache = {}
+    for i, b in enumerate(row[0].tolist()):
+        key = b & 0x7FFF
+        if key not in cache:
+            cache[key] = exact.quant_code_exact(exact.bf16_bits_to_fraction(key), sbits)
+        expect = cache[key] if not (b & 0x8000) else -cache[key]
+        assert q[0, i] == expect, (hex(b), q[0, i], expect)
+
+
+def test_quant_double_rounding_differs_from_single_rounding_somewhere():
+    """The spec rounds twice (quotient to fp32, then to an integer). Over a
+    range of scales this must differ from rounding the exact quotient once in
+    at least one case; otherwise the brute-force test above could not tell
+    the two rules apart."""
+    diffs = 0
+    for absmax in [3.0, 7.5, 20.0, 37.25, 51.5, 100.0]:
+        a_bits = int(bf16([absmax])[0])
+        sbits = exact.quant_scale_exact(exact.bf16_bits_to_fraction(a_bits))
+        sc = exact.f32_to_fraction(exact.bits_f32(sbits))
+        for b in _all_positive_bf16_upto(absmax).tolist():
+            xv = exact.bf16_bits_to_fraction(b)
+            once = max(-127, min(127, exact.rne_to_int(xv / sc)))
+            if once != exact.quant_code_exact(xv, sbits):
+                diffs += 1
+    assert diffs > 0
