@@ -1,0 +1,210 @@
+/*
+ * tern.h -- C ABI of the MI355X (gfx950) ternary-weight linear layer.
+ *
+ * The operation (sources cited by page title and section):
+ *   y[t][n] = sum_g s[n][g] * sum_{k in group g} w[n][k] * x[t][k]
+ * with ternary weights w in {-1, 0, +1} and one fp16 scale s per group of G
+ * consecutive weights along the input dimension K ("NInfer sm_89 fork"
+ * article, section 9 item 2, which uses G = 128; G = 64 is also accepted),
+ * applied to T activation rows x (bf16). The layer picks one of four
+ * "rungs" by T ("NINFER ternary perf-tuning" notes, section 2, rung map):
+ *   gemv           T = 1 (decode)
+ *   small_t        T = 2..8 (draft-verify batches)
+ *   small_t_tiled  T = 9..16
+ *   s8             T >= 17: activations quantised per token to int8 and the
+ *                  product run as an integer contraction (article, sections
+ *                  7 and 9 item 2); the only rung that changes numerics
+ *                  (notes, section 4).
+ *
+ * Conventions for every entry point:
+ *  - Plain pointers and sizes. "host" pointers are CPU memory; "device"
+ *    pointers are HIP device memory on the current device. The caller owns
+ *    every buffer; the library allocates no device memory and keeps no
+ *    device state.
+ *  - Matrices are row-major: x [T][K] bf16 bit patterns (uint16), y [T][N]
+ *    float32, w [N][K] int8, scales [N][K/G] fp16 bit patterns (uint16).
+ *  - stream is a hipStream_t (NULL = the default stream). Device work is
+ *    enqueued asynchronously and the call returns without synchronising;
+ *    a kernel fault surfaces at the caller's next synchronisation.
+ *  - Every argument is validated on the host before any HIP call. On error
+ *    nothing is enqueued, a tern_status other than TERN_OK is returned and
+ *    tern_last_error() describes it (thread-local). There is no silent
+ *    fallback: a forced rung either runs or returns an error.
+ *  - Environment knobs (read once, at the first call that needs them,
+ *    validated and then frozen for the life of the process; an invalid value
+ *    makes every later tern_linear call fail with TERN_ERR_CONFIG):
+ *      TERN_RUNG=auto|gemv|small_t|small_t_tiled|s8   rung for TERN_RUNG_AUTO calls
+ *      TERN_S8=0|1                 0 sends T >= TERN_S8_MIN_T to small_t_tiled
+ *      TERN_S8_MIN_T=<int>=1..>    first T of the s8 rung (default 17)
+ *      TERN_SMALL_T_MAX=<int>      last T of small_t (default 8, at most 16)
+ *      TERN_SMALL_T_TILED_MAX=<int> last T of small_t_tiled before s8 (default 16)
+ *      TERN_DEBUG=0|1, TERN_DEBUG_MIN_T=<int>, TERN_DEBUG_BUDGET=<int>
+ *                                  print "rung=<name> T= N= K= G=" lines to
+ *                                  stderr for calls with T >= MIN_T, at most
+ *                                  BUDGET lines (default 1000)
+ *    The rung map, the env-switchable thresholds and the probe follow the
+ *    perf-tuning notes, section 2 (every branch must report itself) and
+ *    section 7 (decode choices frozen per process).
+ */
+#ifndef TERN_H
+#define TERN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Tag of packed weight layout v1 (stored in tern_weights.layout). */
+#define TERN_LAYOUT_V1 0x54524e31u /* "TRN1" */
+
+typedef enum {
+  TERN_RUNG_AUTO = 0,
+  TERN_RUNG_GEMV = 1,
+  TERN_RUNG_SMALL_T = 2,
+  TERN_RUNG_SMALL_T_TILED = 3,
+  TERN_RUNG_S8 = 4,
+  TERN_RUNG_COUNT = 5
+} tern_rung;
+
+typedef enum {
+  TERN_OK = 0,
+  TERN_ERR_NULL = 1,      /* a required pointer is NULL */
+  TERN_ERR_SHAPE = 2,     /* T < 1, N % 16, K % 256, K % G, G not 64/128, size overflow */
+  TERN_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
+  TERN_ERR_VALUE = 4,     /* a weight outside {-1,0,+1}, a code 10 in packed data */
+  TERN_ERR_RUNG = 5,      /* unknown rung, or a forced rung that cannot take this T */
+  TERN_ERR_WORKSPACE = 6, /* workspace missing or smaller than tern_workspace_bytes() */
+  TERN_ERR_CONFIG = 7,    /* invalid TERN_* environment value */
+  TERN_ERR_HIP = 8,       /* a HIP runtime call failed (launch error) */
+  TERN_ERR_LAYOUT = 9     /* tern_weights.layout is not TERN_LAYOUT_V1 */
+} tern_status;
+
+/*
+ * Packed weight layout v1 (this library's own format; the pages pack base-3,
+ * five weights per byte, and pre-lay weights out for their kernels at load
+ * time -- "pwwt" engine overview, section 3, weight loader).
+ *
+ *  - N % 16 == 0, K % 256 == 0, G in {64, 128}.
+ *  - 2-bit code per weight: 00 -> 0, 01 -> +1, 11 -> -1; 10 is never written
+ *    and is rejected by tern_unpack.
+ *  - Strip s = rows [16s, 16s+16); k-tile kt = columns [256kt, 256kt+256).
+ *    Tile (s, kt) is 1024 bytes at byte offset (s*KT + kt)*1024, KT = K/256,
+ *    so one strip's k-tiles are contiguous (KT KiB per strip).
+ *  - Inside a tile, lane L in [0, 64) owns bytes [16L, 16L+16), read as four
+ *    little-endian 32-bit words P[0..3].
+ *  - Weight (row 16s + r, column 256kt + kk) with kk = 32m + 8g + 2d + h,
+ *    m in [0,8), g in [0,4), d in [0,4), h in {0,1}: lane L = 16g + r, word
+ *    P[m >> 1], j = 4*(m & 1) + d, and the code occupies bits [b+1 : b] with
+ *    b = (h ? 30 : 14) - 2j.
+ *    (Shifting P left by 2j and masking 0xC000C000 leaves the two codes of a
+ *    bf16 pair at bits 15:14 and 31:30: 0x4000 = +2.0, 0xC000 = -2.0, 0 = 0.)
+ *  - Scales are re-laid as [s][kt][r][gi], gi in [0, 256/G): element
+ *    ((s*KT + kt)*16 + r)*(256/G) + gi holds scale[16s + r][kt*(256/G) + gi].
+ *  - Sizes: N*K/4 bytes of codes, N*(K/G)*2 bytes of scales.
+ */
+typedef struct {
+  const void* codes;      /* device, N*K/4 bytes, layout v1, 16-byte aligned */
+  const uint16_t* scales; /* device, N*(K/G) fp16 in the re-laid order, 16-byte aligned */
+  int32_t n;              /* output features N */
+  int32_t k;              /* input features K */
+  int32_t group;          /* G: 64 or 128 */
+  uint32_t layout;        /* must be TERN_LAYOUT_V1 */
+} tern_weights;
+
+/* Bytes of packed codes for an N x K matrix (N*K/4), 0 if the shape is invalid. */
+size_t tern_packed_code_bytes(int n, int k);
+/* Number of fp16 scales (N*(K/G)), 0 if the shape is invalid. */
+size_t tern_scale_count(int n, int k, int group);
+
+/*
+ * Offline relayout (host, synchronous): int8 weights w [N][K] (host) and fp16
+ * scales [N][K/G] (host, bit patterns) -> packed codes (host, N*K/4 bytes)
+ * and re-laid scales (host, N*(K/G) uint16). Copy both to the device and
+ * describe them with a tern_weights. Errors: TERN_ERR_NULL, TERN_ERR_SHAPE,
+ * TERN_ERR_VALUE (a weight outside {-1,0,+1}; outputs are then undefined).
+ */
+tern_status tern_pack(const int8_t* w, const uint16_t* scales_f16, int n, int k, int group,
+                      void* codes_out, uint16_t* scales_out);
+
+/* Inverse of tern_pack (host, synchronous). scales_packed and scales_out may be
+ * NULL to skip the scales. TERN_ERR_VALUE if a code 10 is found. */
+tern_status tern_unpack(const void* codes, const uint16_t* scales_packed, int n, int k,
+                        int group, int8_t* w_out, uint16_t* scales_out);
+
+/*
+ * Per-token symmetric int8 activation quantisation (device, async), the first
+ * step of the s8 rung ("NInfer sm_89 fork" article, section 7 and section 9
+ * item 2):
+ *   a_t = max_k |x[t][k]|;  scale_t = fl32(a_t / 127) (IEEE division);
+ *   q[t][k] = clamp(round-half-even(fl32(x[t][k] / scale_t)), -127, 127);
+ *   a_t == 0 gives scale_t = 0 and q[t][:] = 0.
+ * x: device bf16 [T][K]; q: device int8 [T][K]; act_scale: device float [T].
+ * K % 8 == 0; x and q 16-byte aligned.
+ */
+tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float* act_scale,
+                              void* stream);
+
+/*
+ * Device workspace tern_linear needs for this call (bytes, 0 if none). The s8
+ * rung keeps the int8 activations and their scales there. Every scratch
+ * buffer of every rung is counted here; a call given less fails with
+ * TERN_ERR_WORKSPACE ("NINFER ternary perf-tuning" notes, section 5 item 8:
+ * the workspace capacity declaration must cover every scratch).
+ * rung may be TERN_RUNG_AUTO (resolved the way tern_linear resolves it).
+ * Returns (size_t)-1 for an invalid shape, rung or configuration.
+ */
+size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung);
+
+/*
+ * y = ternary_linear(x) (device, async).
+ *  x:  device bf16 [T][K], 16-byte aligned
+ *  W:  host struct describing device codes and scales (layout v1)
+ *  y:  device float [T][N], 16-byte aligned; fully overwritten
+ *  rung: TERN_RUNG_AUTO picks by T (after TERN_RUNG); any other value forces
+ *        that rung. small_t takes T <= 16 (one 16-token tile); gemv runs
+ *        one token per grid row (T <= 65535); small_t_tiled (16-token tiles
+ *        in grid y) and s8 take any T >= 1.
+ *  ws, ws_bytes: device workspace (16-byte aligned) of at least
+ *        tern_workspace_bytes(T, N, K, G, rung) bytes (may be NULL/0 if that is 0)
+ * Output numerics: the bf16-activation rungs (gemv, small_t, small_t_tiled)
+ * accumulate exact bf16 x {-1,0,+1} products in fp32; s8 computes exact int32
+ * group accumulators and y = scale_t * sum_g s[n][g] * acc in fp32, groups in
+ * ascending order.
+ */
+tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float* y,
+                        tern_rung rung, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Debug export of the s8 rung's integer group accumulators (device, async):
+ * acc[t][n][g] = sum_{k in group g} q[t][k] * w[n][k], int32 [T][N][K/G].
+ * Runs the s8 contraction kernel with its epilogue replaced by a store of the
+ * accumulators, so the integer path can be checked bit for bit.
+ */
+tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int32_t* acc_out,
+                              void* stream);
+
+/* Rung probe: number of kernel launches per rung since the last reset,
+ * counted at the launch site of the kernel that actually ran. */
+void tern_probe_snapshot(uint64_t out[TERN_RUNG_COUNT]);
+void tern_probe_reset(void);
+/* Rung of the most recent successful tern_linear call on any thread
+ * (TERN_RUNG_AUTO if none yet). */
+tern_rung tern_last_rung(void);
+/* The rung tern_linear would run for (T, rung) under the frozen
+ * configuration, or minus the tern_status it would fail with (with
+ * tern_last_error set). */
+int tern_resolve_rung(int T, tern_rung rung);
+/* Name of a rung ("gemv", "small_t", "small_t_tiled", "s8", "auto"). */
+const char* tern_rung_name(tern_rung rung);
+/* Message of the last error on this thread ("" if none). */
+const char* tern_last_error(void);
+/* ABI version of this library (currently 1). */
+int tern_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERN_H */

@@ -1,0 +1,274 @@
+"""Python binding of ``libtern.so``, the MI355X ternary-weight linear layer.
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels (gfx950). PyTorch provides device memory and the current stream.
+The binding fails loudly if the library has not been built; there is no CPU
+fallback.
+
+Entry points mirror the C ABI in ``include/tern.h``:
+
+* ``pack`` / ``unpack``        -- offline relayout to packed layout v1 (host)
+* ``TernaryWeights``           -- packed codes + scales resident on the GPU
+* ``quant_act_s8``             -- per-token int8 activation quantisation
+* ``linear``                   -- ``y = ternary_linear(x)`` with rung dispatch
+* ``debug_s8_acc``             -- the s8 rung's int32 group accumulators
+* ``probe_snapshot`` / ``probe_reset`` / ``last_rung`` / ``resolve_rung``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtern.so")
+
+RUNGS = ("auto", "gemv", "small_t", "small_t_tiled", "s8")
+RUNG_ID = {name: i for i, name in enumerate(RUNGS)}
+LAYOUT_V1 = 0x54524E31
+
+STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_ALIGN",
+          4: "TERN_ERR_VALUE", 5: "TERN_ERR_RUNG", 6: "TERN_ERR_WORKSPACE", 7: "TERN_ERR_CONFIG",
+          8: "TERN_ERR_HIP", 9: "TERN_ERR_LAYOUT"}
+
+# Symbols declared in include/tern.h (checked by the host tests).
+EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpack",
+           "tern_quant_act_s8", "tern_workspace_bytes", "tern_linear", "tern_debug_s8_acc",
+           "tern_probe_snapshot", "tern_probe_reset", "tern_last_rung", "tern_resolve_rung",
+           "tern_rung_name", "tern_last_error", "tern_abi_version")
+
+
+class TernError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("n", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("group", ctypes.c_int32), ("layout", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtern.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m ternary_weight_linear_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i, sz, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "tern_packed_code_bytes": (sz, [i, i]),
+        "tern_scale_count": (sz, [i, i, i]),
+        "tern_pack": (st, [p, p, i, i, i, p, p]),
+        "tern_unpack": (st, [p, p, i, i, i, p, p]),
+        "tern_quant_act_s8": (st, [p, i, i, p, p, p]),
+        "tern_workspace_bytes": (sz, [i, i, i, i, i]),
+        "tern_linear": (st, [p, i, ctypes.POINTER(_Weights), p, i, p, sz, p]),
+        "tern_debug_s8_acc": (st, [p, i, ctypes.POINTER(_Weights), p, p]),
+        "tern_probe_snapshot": (None, [p]),
+        "tern_probe_reset": (None, []),
+        "tern_last_rung": (i, []),
+        "tern_resolve_rung": (i, [i, i]),
+        "tern_rung_name": (ctypes.c_char_p, [i]),
+        "tern_last_error": (ctypes.c_char_p, []),
+        "tern_abi_version": (i, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise TernError(status, lib().tern_last_error().decode())
+
+
+def _rung(r) -> int:
+    if isinstance(r, str):
+        if r not in RUNG_ID:
+            raise ValueError(f"unknown rung {r!r}; expected one of {RUNGS}")
+        return RUNG_ID[r]
+    return int(r)
+
+
+# ------------------------------------------------------------------- host
+
+
+def pack(w: np.ndarray, scales: np.ndarray):
+    """Relayout int8 weights [N, K] and fp16 scales [N, K/G] (uint16 bits or
+    float16) to packed layout v1. Returns (codes uint8 [N*K/4], scales uint16 [N*K/G])."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    scales = np.ascontiguousarray(scales)
+    if scales.dtype == np.float16:
+        scales = scales.view(np.uint16)
+    if scales.dtype != np.uint16:
+        raise TypeError("scales must be float16 or uint16 bit patterns")
+    n, k = w.shape
+    if scales.ndim != 2 or scales.shape[0] != n or scales.shape[1] == 0 or k % scales.shape[1]:
+        raise ValueError(f"scales shape {scales.shape} does not match w {w.shape}")
+    group = k // scales.shape[1]
+    nbytes = lib().tern_packed_code_bytes(n, k)
+    codes = np.empty(max(nbytes, 1), np.uint8)
+    sp = np.empty(scales.size, np.uint16)
+    _check(lib().tern_pack(w.ctypes.data, scales.ctypes.data, n, k, group, codes.ctypes.data,
+                           sp.ctypes.data))
+    return codes[:nbytes], sp
+
+
+def unpack(codes: np.ndarray, scales_packed, n: int, k: int, group: int):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    w = np.empty((n, k), np.int8)
+    if scales_packed is None:
+        _check(lib().tern_unpack(codes.ctypes.data, None, n, k, group, w.ctypes.data, None))
+        return w, None
+    sp = np.ascontiguousarray(scales_packed, dtype=np.uint16)
+    s = np.empty((n, k // group), np.uint16)
+    _check(lib().tern_unpack(codes.ctypes.data, sp.ctypes.data, n, k, group, w.ctypes.data,
+                             s.ctypes.data))
+    return w, s
+
+
+def workspace_bytes(T: int, n: int, k: int, group: int, rung="auto") -> int:
+    v = lib().tern_workspace_bytes(T, n, k, group, _rung(rung))
+    if v == ctypes.c_size_t(-1).value:
+        raise TernError(5, lib().tern_last_error().decode())
+    return v
+
+
+def resolve_rung(T: int, rung="auto") -> str:
+    r = lib().tern_resolve_rung(T, _rung(rung))
+    if r < 0:
+        raise TernError(-r, lib().tern_last_error().decode())
+    return RUNGS[r]
+
+
+def probe_snapshot() -> dict:
+    arr = (ctypes.c_uint64 * len(RUNGS))()
+    lib().tern_probe_snapshot(arr)
+    return {RUNGS[i]: int(arr[i]) for i in range(1, len(RUNGS))}
+
+
+def probe_reset() -> None:
+    lib().tern_probe_reset()
+
+
+def last_rung() -> str:
+    return RUNGS[lib().tern_last_rung()]
+
+
+# ----------------------------------------------------------------- device
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+class TernaryWeights:
+    """Packed ternary weights resident on the GPU (layout v1)."""
+
+    def __init__(self, codes, scales, n: int, k: int, group: int):
+        torch = _torch()
+        self.codes = _dev(codes, torch.uint8, "codes")
+        self.scales = _dev(scales, torch.int16, "scales")
+        self.n, self.k, self.group = int(n), int(k), int(group)
+        self._struct = _Weights(self.codes.data_ptr(), self.scales.data_ptr(), self.n, self.k,
+                                self.group, LAYOUT_V1)
+
+    @classmethod
+    def from_host(cls, w: np.ndarray, scales: np.ndarray, device="cuda"):
+        torch = _torch()
+        codes, sp = pack(w, scales)
+        n, k = w.shape
+        group = k // scales.shape[1]
+        return cls(torch.from_numpy(codes).to(device), torch.from_numpy(sp.view(np.int16)).to(device),
+                   n, k, group)
+
+    @property
+    def nbytes(self) -> int:
+        return self.codes.numel() + 2 * self.scales.numel()
+
+    def ref(self):
+        return ctypes.byref(self._struct)
+
+
+def quant_act_s8(x, q=None, scale=None, stream=None):
+    """Per-token int8 quantisation of bf16 activations x [T, K] (device)."""
+    torch = _torch()
+    _dev(x, torch.bfloat16, "x")
+    T, K = x.shape
+    if q is None:
+        q = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _dev(q, torch.int8, "q")
+    _dev(scale, torch.float32, "scale")
+    _check(lib().tern_quant_act_s8(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
+                                   _stream(stream)))
+    return q, scale
+
+
+def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=None):
+    """y [T, N] float32 = ternary_linear(x [T, K] bf16) on the GPU."""
+    torch = _torch()
+    _dev(x, torch.bfloat16, "x")
+    T, K = x.shape
+    if K != W.k:
+        raise ValueError(f"x has K={K}, weights have K={W.k}")
+    if y is None:
+        y = torch.empty((T, W.n), dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    r = _rung(rung)
+    need = lib().tern_workspace_bytes(T, W.n, W.k, W.group, r)
+    if need == ctypes.c_size_t(-1).value:
+        raise TernError(5, lib().tern_last_error().decode())
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().tern_linear(x.data_ptr(), T, W.ref(), y.data_ptr(), r, ws_ptr, ws_bytes,
+                             _stream(stream)))
+    return y
+
+
+def debug_s8_acc(q, W: TernaryWeights, acc=None, stream=None):
+    """int32 [T, N, K/G] group accumulators of the s8 contraction."""
+    torch = _torch()
+    _dev(q, torch.int8, "q")
+    T = q.shape[0]
+    if acc is None:
+        acc = torch.empty((T, W.n, W.k // W.group), dtype=torch.int32, device=q.device)
+    _dev(acc, torch.int32, "acc")
+    _check(lib().tern_debug_s8_acc(q.data_ptr(), T, W.ref(), acc.data_ptr(), _stream(stream)))
+    return acc

@@ -1,0 +1,54 @@
+"""Build libtern.so (gfx950 kernels + host C ABI) in-tree with hipcc.
+
+Usage: ``python -m ternary_weight_linear_amd.build`` (or ``build()``). Always
+recompiles. The result is ``ternary_weight_linear_amd/libtern.so``.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libtern.so")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Device code: MI355X only. Packed-fp32 VALU ops are disabled; fp32 division
+# is the correctly rounded IEEE one (the s8 quantisation relies on it);
+# fp32 denormals are kept.
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-ffp-contract=off", "-Wall",
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    k_obj = os.path.join(BUILD, "tern_kernels.o")
+    h_obj = os.path.join(BUILD, "tern_host.o")
+    _run([HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+          os.path.join(CSRC, "tern_kernels.hip"), "-o", k_obj])
+    _run(["g++", *HOST_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+          os.path.join(CSRC, "tern_host.cpp"), "-o", h_obj])
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, k_obj, h_obj])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,461 @@
+// tern_host.cpp -- host side of the C ABI declared in include/tern.h:
+// argument validation, the offline weight relayout (tern_pack / tern_unpack),
+// the T-based rung dispatcher with its environment knobs and probe counters,
+// and the launches of the gfx950 kernels (tern_kernels.hip).
+//
+// Dispatcher: rung map, env-switchable thresholds, one probe per branch and
+// env read once per process follow the "NINFER ternary perf-tuning" notes,
+// section 2 (rung map and probe), section 5 items 1 and 8 (no silent
+// fallback; every scratch counted in the declared workspace) and section 7
+// (one launch signature; decode choices frozen per process).
+#include <algorithm>
+#include <atomic>
+#include <cerrno>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/tern.h"
+#include "tern_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tern_status fail(tern_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tern_status ok() {
+  g_last_error.clear();
+  return TERN_OK;
+}
+
+const char* const kRungNames[TERN_RUNG_COUNT] = {"auto", "gemv", "small_t", "small_t_tiled", "s8"};
+
+// ------------------------------------------------------------ configuration
+
+struct Config {
+  bool valid = true;
+  std::string error;
+  tern_rung forced = TERN_RUNG_AUTO;  // TERN_RUNG
+  bool s8_enabled = true;             // TERN_S8
+  int s8_min_t = 17;                  // TERN_S8_MIN_T
+  int small_t_max = 8;                // TERN_SMALL_T_MAX
+  bool debug = false;                 // TERN_DEBUG
+  int debug_min_t = 1;                // TERN_DEBUG_MIN_T
+  long debug_budget = 1000;           // TERN_DEBUG_BUDGET
+  int tune_strips = 0;                // TERN_TUNE_STRIPS (0 = heuristic)
+  int tune_waves = 0;                 // TERN_TUNE_WAVES (0 = heuristic)
+  int tune_s8_bm = 0;                 // TERN_TUNE_S8_BM (0 = heuristic)
+};
+
+bool parse_int(const char* s, long lo, long hi, long* out) {
+  if (!s || !*s) return false;
+  errno = 0;
+  char* end = nullptr;
+  long v = strtol(s, &end, 10);
+  if (errno || *end != '\0' || v < lo || v > hi) return false;
+  *out = v;
+  return true;
+}
+
+Config read_config() {
+  Config c;
+  auto bad = [&](const char* name, const char* val) {
+    if (c.valid) {
+      c.valid = false;
+      c.error = std::string("invalid ") + name + "='" + val + "'";
+    }
+  };
+  long v;
+  if (const char* s = getenv("TERN_RUNG")) {
+    int found = -1;
+    for (int i = 0; i < TERN_RUNG_COUNT; ++i)
+      if (strcmp(s, kRungNames[i]) == 0) found = i;
+    if (found < 0)
+      bad("TERN_RUNG", s);
+    else
+      c.forced = (tern_rung)found;
+  }
+  if (const char* s = getenv("TERN_S8")) {
+    if (parse_int(s, 0, 1, &v))
+      c.s8_enabled = v != 0;
+    else
+      bad("TERN_S8", s);
+  }
+  if (const char* s = getenv("TERN_S8_MIN_T")) {
+    if (parse_int(s, 1, 1L << 30, &v))
+      c.s8_min_t = (int)v;
+    else
+      bad("TERN_S8_MIN_T", s);
+  }
+  if (const char* s = getenv("TERN_SMALL_T_MAX")) {
+    if (parse_int(s, 1, 16, &v))
+      c.small_t_max = (int)v;
+    else
+      bad("TERN_SMALL_T_MAX", s);
+  }
+  if (const char* s = getenv("TERN_DEBUG")) {
+    if (parse_int(s, 0, 1, &v))
+      c.debug = v != 0;
+    else
+      bad("TERN_DEBUG", s);
+  }
+  if (const char* s = getenv("TERN_DEBUG_MIN_T")) {
+    if (parse_int(s, 1, 1L << 30, &v))
+      c.debug_min_t = (int)v;
+    else
+      bad("TERN_DEBUG_MIN_T", s);
+  }
+  if (const char* s = getenv("TERN_DEBUG_BUDGET")) {
+    if (parse_int(s, 0, 1L << 40, &v))
+      c.debug_budget = v;
+    else
+      bad("TERN_DEBUG_BUDGET", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_STRIPS")) {
+    if (parse_int(s, 0, 4, &v) && v != 3)
+      c.tune_strips = (int)v;
+    else
+      bad("TERN_TUNE_STRIPS", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_WAVES")) {
+    if (parse_int(s, 0, 16, &v))
+      c.tune_waves = (int)v;
+    else
+      bad("TERN_TUNE_WAVES", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_S8_BM")) {
+    if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 64 || v == 128))
+      c.tune_s8_bm = (int)v;
+    else
+      bad("TERN_TUNE_S8_BM", s);
+  }
+  return c;
+}
+
+const Config& config() {
+  static std::once_flag once;
+  static Config cfg;
+  std::call_once(once, [] { cfg = read_config(); });
+  return cfg;
+}
+
+// ------------------------------------------------------------------- probe
+
+std::atomic<uint64_t> g_probe[TERN_RUNG_COUNT];
+std::atomic<int> g_last_rung{TERN_RUNG_AUTO};
+std::atomic<long> g_debug_lines{0};
+
+void probe_hit(tern_rung r, int T, int n, int k, int group) {
+  g_probe[r].fetch_add(1, std::memory_order_relaxed);
+  g_last_rung.store(r, std::memory_order_relaxed);
+  const Config& c = config();
+  if (c.debug && T >= c.debug_min_t) {
+    long i = g_debug_lines.fetch_add(1, std::memory_order_relaxed);
+    if (i < c.debug_budget)
+      fprintf(stderr, "rung=%s T=%d N=%d K=%d G=%d\n", kRungNames[r], T, n, k, group);
+  }
+}
+
+// -------------------------------------------------------------- validation
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+tern_status check_shape(int n, int k, int group) {
+  if (n < 16 || n % 16 != 0)
+    return fail(TERN_ERR_SHAPE, "N=%d must be a positive multiple of 16", n);
+  if (k < 256 || k % 256 != 0)
+    return fail(TERN_ERR_SHAPE, "K=%d must be a positive multiple of 256", k);
+  if (group != 64 && group != 128) return fail(TERN_ERR_SHAPE, "G=%d must be 64 or 128", group);
+  if ((uint64_t)n * (uint64_t)k > (1ull << 40))
+    return fail(TERN_ERR_SHAPE, "N*K=%llu too large", (unsigned long long)n * k);
+  return TERN_OK;
+}
+
+constexpr int kMaxTokens = 1 << 19;  // keeps every grid y dimension below 65536
+
+// Resolve the rung for a call. Returns TERN_OK and sets *out, or an error.
+tern_status resolve(int T, tern_rung req, tern_rung* out) {
+  const Config& c = config();
+  if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
+  if ((int)req < 0 || (int)req >= TERN_RUNG_COUNT)
+    return fail(TERN_ERR_RUNG, "unknown rung %d", (int)req);
+  if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range [1, %d]", T, kMaxTokens);
+  tern_rung r = req;
+  if (r == TERN_RUNG_AUTO) r = c.forced;
+  if (r == TERN_RUNG_AUTO) {
+    if (c.s8_enabled && T >= c.s8_min_t)
+      r = TERN_RUNG_S8;
+    else if (T == 1)
+      r = TERN_RUNG_GEMV;
+    else if (T <= c.small_t_max)
+      r = TERN_RUNG_SMALL_T;
+    else
+      r = TERN_RUNG_SMALL_T_TILED;
+  }
+  if (r == TERN_RUNG_GEMV && T > 65535)
+    return fail(TERN_ERR_RUNG, "rung gemv runs one token per grid row: T=%d > 65535", T);
+  if (r == TERN_RUNG_SMALL_T && T > 16)
+    return fail(TERN_ERR_RUNG, "rung small_t takes one 16-token tile: T=%d > 16", T);
+  *out = r;
+  return TERN_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t workspace_for(int T, int k, tern_rung r) {
+  if (r == TERN_RUNG_S8) return align256((size_t)T * k) + align256((size_t)T * sizeof(float));
+  return 0;
+}
+
+tern::SmallTPlan plan_small_t(int T, int n, int k, tern_rung r) {
+  const Config& c = config();
+  tern::SmallTPlan p;
+  const int NS = n / 16, KT = k / 256;
+  p.tokens_per_tile = (r == TERN_RUNG_GEMV) ? 1 : 16;
+  p.token_tiles = (r == TERN_RUNG_GEMV) ? T : (T + 15) / 16;
+  int S = NS >= 1024 ? 2 : 1;
+  if (c.tune_strips) S = c.tune_strips;
+  const int nsb = (NS + S - 1) / S;
+  int W = (int)((4096.0 * 1.0) / (double)(nsb * (long)std::max(1, p.token_tiles)) + 0.5);
+  W = std::max(1, std::min(W, std::min(16, KT)));
+  if (c.tune_waves) W = std::min(c.tune_waves, KT);
+  p.strips_per_wave = S;
+  p.waves = W;
+  return p;
+}
+
+tern::S8Plan plan_s8(int T) {
+  const Config& c = config();
+  tern::S8Plan p;
+  int bm = T >= 128 ? 128 : (T >= 48 ? 64 : 32);
+  if (c.tune_s8_bm) bm = c.tune_s8_bm;
+  p.bm = bm;
+  p.bn = bm == 128 ? 128 : 64;
+  return p;
+}
+
+tern_status hip_fail(int err, const char* what) {
+  return fail(TERN_ERR_HIP, "%s: %s", what, tern::hip_error_string(err));
+}
+
+tern_status check_weights(const tern_weights* W) {
+  if (!W) return fail(TERN_ERR_NULL, "W is NULL");
+  if (!W->codes || !W->scales) return fail(TERN_ERR_NULL, "W->codes or W->scales is NULL");
+  if (W->layout != TERN_LAYOUT_V1)
+    return fail(TERN_ERR_LAYOUT, "W->layout=0x%08x is not TERN_LAYOUT_V1", W->layout);
+  tern_status st = check_shape(W->n, W->k, W->group);
+  if (st != TERN_OK) return st;
+  if (!aligned16(W->codes) || !aligned16(W->scales))
+    return fail(TERN_ERR_ALIGN, "W->codes / W->scales must be 16-byte aligned");
+  return TERN_OK;
+}
+
+inline uint32_t encode(int8_t v) { return v == 0 ? 0u : (v == 1 ? 1u : 3u); }
+
+}  // namespace
+
+extern "C" {
+
+int tern_abi_version(void) { return 1; }
+
+const char* tern_last_error(void) { return g_last_error.c_str(); }
+
+const char* tern_rung_name(tern_rung rung) {
+  if ((int)rung < 0 || (int)rung >= TERN_RUNG_COUNT) return "invalid";
+  return kRungNames[rung];
+}
+
+size_t tern_packed_code_bytes(int n, int k) {
+  if (n < 16 || n % 16 || k < 256 || k % 256) return 0;
+  return (size_t)n * (size_t)k / 4;
+}
+
+size_t tern_scale_count(int n, int k, int group) {
+  if (check_shape(n, k, group) != TERN_OK) return 0;
+  return (size_t)n * (size_t)(k / group);
+}
+
+tern_status tern_pack(const int8_t* w, const uint16_t* scales_f16, int n, int k, int group,
+                      void* codes_out, uint16_t* scales_out) {
+  if (!w || !scales_f16 || !codes_out || !scales_out)
+    return fail(TERN_ERR_NULL, "tern_pack: NULL pointer");
+  tern_status st = check_shape(n, k, group);
+  if (st != TERN_OK) return st;
+  const size_t NS = (size_t)n / 16, KT = (size_t)k / 256, GPT = 256 / (size_t)group;
+  const size_t NG = (size_t)k / group;
+  uint32_t* out = (uint32_t*)codes_out;
+  for (size_t s = 0; s < NS; ++s)
+    for (size_t kt = 0; kt < KT; ++kt) {
+      uint32_t* tile = out + (s * KT + kt) * 256;
+      for (int L = 0; L < 64; ++L) {
+        const int r = L & 15, g = L >> 4;
+        const int8_t* wrow = w + (s * 16 + r) * (size_t)k + kt * 256;
+        for (int qw = 0; qw < 4; ++qw) {
+          uint32_t P = 0;
+          for (int half = 0; half < 2; ++half) {  // m = 2qw + half
+            const int m = 2 * qw + half;
+            for (int d = 0; d < 4; ++d)
+              for (int h = 0; h < 2; ++h) {
+                const int kk = 32 * m + 8 * g + 2 * d + h;
+                const int8_t v = wrow[kk];
+                if (v < -1 || v > 1)
+                  return fail(TERN_ERR_VALUE, "tern_pack: w[%zu][%zu]=%d not in {-1,0,1}",
+                              s * 16 + r, kt * 256 + kk, (int)v);
+                const int j = 4 * half + d;
+                const int b = (h ? 30 : 14) - 2 * j;
+                P |= encode(v) << b;
+              }
+          }
+          tile[L * 4 + qw] = P;
+        }
+      }
+      for (int r = 0; r < 16; ++r)
+        for (size_t gi = 0; gi < GPT; ++gi)
+          scales_out[((s * KT + kt) * 16 + r) * GPT + gi] =
+              scales_f16[(s * 16 + r) * NG + kt * GPT + gi];
+    }
+  return ok();
+}
+
+tern_status tern_unpack(const void* codes, const uint16_t* scales_packed, int n, int k, int group,
+                        int8_t* w_out, uint16_t* scales_out) {
+  if (!codes || !w_out) return fail(TERN_ERR_NULL, "tern_unpack: NULL pointer");
+  if ((scales_packed == nullptr) != (scales_out == nullptr))
+    return fail(TERN_ERR_NULL, "tern_unpack: give both scale pointers or neither");
+  tern_status st = check_shape(n, k, group);
+  if (st != TERN_OK) return st;
+  const size_t NS = (size_t)n / 16, KT = (size_t)k / 256, GPT = 256 / (size_t)group;
+  const size_t NG = (size_t)k / group;
+  const uint32_t* in = (const uint32_t*)codes;
+  for (size_t s = 0; s < NS; ++s)
+    for (size_t kt = 0; kt < KT; ++kt) {
+      const uint32_t* tile = in + (s * KT + kt) * 256;
+      for (int L = 0; L < 64; ++L) {
+        const int r = L & 15, g = L >> 4;
+        int8_t* wrow = w_out + (s * 16 + r) * (size_t)k + kt * 256;
+        for (int qw = 0; qw < 4; ++qw) {
+          const uint32_t P = tile[L * 4 + qw];
+          for (int half = 0; half < 2; ++half) {
+            const int m = 2 * qw + half;
+            for (int d = 0; d < 4; ++d)
+              for (int h = 0; h < 2; ++h) {
+                const int j = 4 * half + d;
+                const int b = (h ? 30 : 14) - 2 * j;
+                const uint32_t c = (P >> b) & 3u;
+                if (c == 2u)
+                  return fail(TERN_ERR_VALUE, "tern_unpack: invalid code 10 in tile (%zu,%zu)", s,
+                              kt);
+                wrow[32 * m + 8 * g + 2 * d + h] = c == 0 ? 0 : (c == 1 ? 1 : -1);
+              }
+          }
+        }
+      }
+      if (scales_out)
+        for (int r = 0; r < 16; ++r)
+          for (size_t gi = 0; gi < GPT; ++gi)
+            scales_out[(s * 16 + r) * NG + kt * GPT + gi] =
+                scales_packed[((s * KT + kt) * 16 + r) * GPT + gi];
+    }
+  return ok();
+}
+
+size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung) {
+  if (check_shape(n, k, group) != TERN_OK) return (size_t)-1;
+  tern_rung r;
+  if (resolve(T, rung, &r) != TERN_OK) return (size_t)-1;
+  return workspace_for(T, k, r);
+}
+
+int tern_resolve_rung(int T, tern_rung rung) {
+  tern_rung r;
+  const tern_status st = resolve(T, rung, &r);
+  if (st != TERN_OK) return -(int)st;
+  return (int)r;
+}
+
+tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float* act_scale,
+                              void* stream) {
+  if (!x_bf16 || !q || !act_scale) return fail(TERN_ERR_NULL, "tern_quant_act_s8: NULL pointer");
+  if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
+  if (k < 8 || k % 8 != 0) return fail(TERN_ERR_SHAPE, "K=%d must be a positive multiple of 8", k);
+  if (!aligned16(x_bf16) || !aligned16(q))
+    return fail(TERN_ERR_ALIGN, "x and q must be 16-byte aligned");
+  int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, act_scale, stream);
+  if (err) return hip_fail(err, "quant_s8 launch");
+  return ok();
+}
+
+tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float* y,
+                        tern_rung rung, void* ws, size_t ws_bytes, void* stream) {
+  if (!x_bf16 || !y) return fail(TERN_ERR_NULL, "tern_linear: x or y is NULL");
+  tern_status st = check_weights(W);
+  if (st != TERN_OK) return st;
+  if (!aligned16(x_bf16) || !aligned16(y))
+    return fail(TERN_ERR_ALIGN, "x and y must be 16-byte aligned");
+  tern_rung r;
+  st = resolve(T, rung, &r);
+  if (st != TERN_OK) return st;
+  const size_t need = workspace_for(T, W->k, r);
+  if (need) {
+    if (!ws || ws_bytes < need)
+      return fail(TERN_ERR_WORKSPACE, "rung %s needs %zu bytes of workspace, got %zu%s",
+                  kRungNames[r], need, ws ? ws_bytes : (size_t)0, ws ? "" : " (NULL)");
+    if (!aligned16(ws)) return fail(TERN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  const int n = W->n, k = W->k, G = W->group;
+  if (r == TERN_RUNG_S8) {
+    int8_t* q = (int8_t*)ws;
+    float* sc = (float*)((char*)ws + align256((size_t)T * k));
+    int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, stream);
+    if (err) return hip_fail(err, "quant_s8 launch");
+    tern::S8Args a{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr};
+    err = tern::launch_s8(a, plan_s8(T), stream);
+    if (err) return hip_fail(err, "s8 launch");
+  } else {
+    tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
+    int err = tern::launch_small_t(a, plan_small_t(T, n, k, r), stream);
+    if (err) return hip_fail(err, "small_t launch");
+  }
+  probe_hit(r, T, n, k, G);
+  return ok();
+}
+
+tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int32_t* acc_out,
+                              void* stream) {
+  if (!q || !acc_out) return fail(TERN_ERR_NULL, "tern_debug_s8_acc: NULL pointer");
+  tern_status st = check_weights(W);
+  if (st != TERN_OK) return st;
+  if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
+  if (!aligned16(q)) return fail(TERN_ERR_ALIGN, "q must be 16-byte aligned");
+  const Config& c = config();
+  if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
+  tern::S8Args a{q, nullptr, T, W->k, W->n, W->group, W->codes, W->scales, nullptr, acc_out};
+  int err = tern::launch_s8(a, plan_s8(T), stream);
+  if (err) return hip_fail(err, "s8 debug launch");
+  return ok();
+}
+
+void tern_probe_snapshot(uint64_t out[TERN_RUNG_COUNT]) {
+  for (int i = 0; i < TERN_RUNG_COUNT; ++i) out[i] = g_probe[i].load(std::memory_order_relaxed);
+}
+
+void tern_probe_reset(void) {
+  for (int i = 0; i < TERN_RUNG_COUNT; ++i) g_probe[i].store(0, std::memory_order_relaxed);
+  g_last_rung.store(TERN_RUNG_AUTO, std::memory_order_relaxed);
+}
+
+tern_rung tern_last_rung(void) { return (tern_rung)g_last_rung.load(std::memory_order_relaxed); }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// tern_internal.h -- interface between the host ABI layer (tern_host.cpp) and
+// the gfx950 kernels (tern_kernels.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tern {
+
+// Launch shape of the bf16-activation MFMA kernel (gemv / small_t / small_t_tiled).
+struct SmallTPlan {
+  int tokens_per_tile;  // 1 (gemv: one token per grid row) or 16
+  int strips_per_wave;  // S: 16-row strips each wave streams (1, 2 or 4)
+  int waves;            // W: waves per workgroup, each takes a contiguous K range (1..16)
+  int token_tiles;      // grid.y
+};
+
+struct SmallTArgs {
+  const uint16_t* x;  // bf16 [T][K]
+  int T, K, N, G;
+  const void* codes;
+  const uint16_t* scales;
+  float* y;  // [T][N]
+};
+
+// Launch shape of the s8 integer MFMA kernel.
+struct S8Plan {
+  int bm;  // tokens per workgroup tile
+  int bn;  // outputs per workgroup tile
+};
+
+struct S8Args {
+  const int8_t* q;         // int8 [T][K]
+  const float* act_scale;  // [T]
+  int T, K, N, G;
+  const void* codes;
+  const uint16_t* scales;
+  float* y;          // [T][N] (nullptr in debug-acc mode)
+  int32_t* acc_out;  // [T][N][K/G] (debug-acc mode only)
+};
+
+// All launchers return 0 on success or a hipError_t value.
+int launch_small_t(const SmallTArgs& a, const SmallTPlan& p, void* stream);
+int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, void* stream);
+int launch_s8(const S8Args& a, const S8Plan& p, void* stream);
+const char* hip_error_string(int err);
+
+}  // namespace tern

@@ -1,0 +1,289 @@
+"""GPU parity: every rung of the HIP library against the CPU oracle.
+
+Gates: bf16-activation rungs (gemv, small_t, small_t_tiled) within 2e-3
+relative L2 of the fp64 oracle; s8 int8 codes, scales and int32 group
+accumulators bit-exact; s8 fp32 output within 1e-6 relative L2 of the exactly
+rounded oracle. Integer-valued inputs with power-of-two scales make every
+fp32 step exact, so there the bf16 rungs must match bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import tern_synth as ts
+
+pytestmark = pytest.mark.gpu
+
+BF16_GATE = 2e-3
+S8_GATE = 1e-6
+RUNGS = ("gemv", "small_t", "small_t_tiled", "s8")
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def tl(torch):
+    import ternary_weight_linear_amd as tl
+    tl.lib()
+    return tl
+
+
+def rel_l2(y, ref):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(y - ref) / (den if den > 0 else 1.0)
+
+
+def to_dev_bf16(torch, xbits):
+    return torch.from_numpy(xbits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def rung_ok(rung, T):
+    return not (rung == "small_t" and T > 16)
+
+
+def run(tl, torch, x_dev, W, rung):
+    tl.probe_reset()
+    y = tl.linear(x_dev, W, rung=rung)
+    torch.cuda.synchronize()
+    snap = tl.probe_snapshot()
+    expect = rung if rung != "auto" else tl.resolve_rung(x_dev.shape[0])
+    assert snap[expect] == 1 and sum(snap.values()) == 1, snap
+    assert tl.last_rung() == expect
+    return y.cpu().numpy()
+
+
+def check_s8(tl, torch, xbits, x_dev, W, w, s, y, rows=None):
+    """q/scale bit-exact, acc bit-exact, y within 1e-6 (and bit-exact to the
+    fixed fp32 order the kernel documents)."""
+    q_ref, sc_ref = oracle.quant_s8(xbits)
+    q, sc = tl.quant_act_s8(x_dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), sc_ref.view(np.uint32))
+    ws, ss = (w, s) if rows is None else (w[rows], s[rows])
+    ycols = y if rows is None else y[:, rows]
+    ref = oracle.linear_s8(q_ref, sc_ref, ws, ss)
+    assert rel_l2(ycols, ref) <= S8_GATE
+    ordered = oracle.linear_s8_fp32_ordered(q_ref, sc_ref, ws, ss)
+    assert np.array_equal(ycols.view(np.uint32), ordered.view(np.uint32))
+
+
+# ---------------------------------------------------------- small shape
+
+
+@pytest.fixture(scope="module")
+def small(tl, torch):
+    wts = ts.weights(ts.SMALL)
+    W = tl.TernaryWeights.from_host(wts.w, wts.s)
+    return wts, W
+
+
+@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("rung", RUNGS + ("auto",))
+def test_small_case_every_rung(tl, torch, small, T, rung):
+    wts, W = small
+    xbits = ts.activations(wts, T)
+    y = run(tl, torch, to_dev_bf16(torch, xbits), W, rung)
+    effective = rung if rung != "auto" else tl.resolve_rung(T)
+    if effective == "s8":
+        check_s8(tl, torch, xbits, to_dev_bf16(torch, xbits), W, wts.w, wts.s, y)
+    else:
+        ref = oracle.linear_bf16(xbits, wts.w, wts.s)
+        assert rel_l2(y, ref) <= BF16_GATE
+        assert rel_l2(y, ref) <= 1e-6  # fp32 accumulation of exact products
+
+
+def test_small_case_s8_accumulators_bit_exact(tl, torch, small):
+    wts, W = small
+    xbits = ts.activations(wts, 4)
+    q_ref, _ = oracle.quant_s8(xbits)
+    acc = tl.debug_s8_acc(torch.from_numpy(q_ref).cuda(), W)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), oracle.s8_acc(q_ref, wts.w, 64))
+
+
+# ------------------------------------------------ exact (integer) inputs
+
+
+@pytest.mark.parametrize("n,k,G", [(64, 512, 128), (128, 256, 64), (48, 1280, 128)])
+@pytest.mark.parametrize("T", [1, 3, 8, 13, 16, 21])
+def test_integer_inputs_bit_exact(tl, torch, n, k, G, T):
+    rng = np.random.default_rng(n + k + T)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.pow2_scales(n, k, G, seed=n * 7 + T)
+    xbits = ts.integer_activations(k, T, seed=k + T)
+    W = tl.TernaryWeights.from_host(w, s)
+    ref = oracle.linear_bf16(xbits, w, s)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)  # exact in fp32
+    x_dev = to_dev_bf16(torch, xbits)
+    for rung in ("gemv", "small_t", "small_t_tiled"):
+        if not rung_ok(rung, T):
+            continue
+        y = run(tl, torch, x_dev, W, rung)
+        assert np.array_equal(y.astype(np.float64), ref), rung
+
+
+@pytest.mark.parametrize("rung", RUNGS)
+def test_single_nonzero_weight(tl, torch, rung):
+    n, k, G, T = 64, 768, 128, 5
+    w = np.zeros((n, k), np.int8)
+    w[37, 517] = -1
+    rng = np.random.default_rng(1)
+    s = ts.draw_scales(rng, n, k, G)
+    xbits = ts.f32_to_bf16_bits(rng.standard_normal((T, k)).astype(np.float32))
+    W = tl.TernaryWeights.from_host(w, s)
+    x_dev = to_dev_bf16(torch, xbits)
+    y = run(tl, torch, x_dev, W, rung)
+    expect = np.zeros((T, n), np.float32)
+    if rung == "s8":
+        q, sc = oracle.quant_s8(xbits)
+        expect[:, 37] = oracle.linear_s8(q, sc, w[37:38], s[37:38])[:, 0]
+    else:
+        sv = ts.f16_bits_to_f32(s[37, 517 // G])
+        expect[:, 37] = -(sv * ts.bf16_bits_to_f32(xbits[:, 517]))
+    assert np.array_equal(y.view(np.uint32), expect.view(np.uint32))
+
+
+# ------------------------------------------------------------ edge cases
+
+
+@pytest.fixture(scope="module")
+def mid(tl, torch):
+    shape = ts.Shape("mid_1024x256", 1024, 256, 128, 0.4, True, 301)
+    wts = ts.weights(shape)
+    return wts, tl.TernaryWeights.from_host(wts.w, wts.s)
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 9, 15, 16, 17, 31, 33, 63, 65, 100, 129])
+def test_ragged_token_counts(tl, torch, mid, T):
+    wts, W = mid
+    xbits = ts.activations(wts, T)
+    x_dev = to_dev_bf16(torch, xbits)
+    ref = oracle.linear_bf16(xbits, wts.w, wts.s)
+    for rung in ("auto",) + RUNGS:
+        if not rung_ok(rung, T):
+            continue
+        y = run(tl, torch, x_dev, W, rung)
+        eff = rung if rung != "auto" else tl.resolve_rung(T)
+        if eff == "s8":
+            check_s8(tl, torch, xbits, x_dev, W, wts.w, wts.s, y)
+        else:
+            assert rel_l2(y, ref) <= BF16_GATE, rung
+
+
+def test_zero_activation_rows(tl, torch, mid):
+    wts, W = mid
+    xbits = ts.activations(wts, 40)
+    xbits[[0, 5, 39]] = 0
+    xbits[7] = 0x8000  # -0.0
+    x_dev = to_dev_bf16(torch, xbits)
+    for rung in ("small_t_tiled", "s8"):
+        y = run(tl, torch, x_dev, W, rung)
+        assert np.all(y[[0, 5, 7, 39]] == 0)
+    q, sc = tl.quant_act_s8(x_dev)
+    assert np.all(sc.cpu().numpy()[[0, 5, 7, 39]] == 0)
+    assert np.all(q.cpu().numpy()[[0, 5, 7, 39]] == 0)
+    check_s8(tl, torch, xbits, x_dev, W, wts.w, wts.s, tl.linear(x_dev, W, rung="s8").cpu().numpy())
+
+
+def test_output_guard_bands_and_determinism(tl, torch, mid):
+    wts, W = mid
+    T, N = 12, W.n
+    xbits = ts.activations(wts, T)
+    x_dev = to_dev_bf16(torch, xbits)
+    for rung in RUNGS:
+        buf = torch.full((T * N + 64,), float("nan"), device="cuda")
+        y = buf[:T * N].view(T, N)
+        tl.linear(x_dev, W, rung=rung, y=y)
+        y2 = tl.linear(x_dev, W, rung=rung)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[T * N:]).all(), rung
+        assert not torch.isnan(y).any(), rung
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32)), rung
+
+
+def test_batch_invariance(tl, torch, mid):
+    wts, W = mid
+    xbits = ts.activations(wts, 24)
+    x_dev = to_dev_bf16(torch, xbits)
+    for rung in ("small_t_tiled", "s8"):
+        y = tl.linear(x_dev, W, rung=rung).cpu()
+        for t in (0, 11, 23):
+            yt = tl.linear(x_dev[t:t + 1].contiguous(), W, rung=rung).cpu()
+            assert torch.equal(yt[0].view(torch.int32), y[t].view(torch.int32)), (rung, t)
+
+
+# ------------------------------------------------------ full layer shapes
+
+
+@pytest.fixture(scope="module")
+def big(tl, torch):
+    cache = {}
+
+    def get(shape):
+        if shape.name not in cache:
+            wts = ts.weights(shape)
+            cache[shape.name] = (wts, tl.TernaryWeights.from_host(wts.w, wts.s))
+        return cache[shape.name]
+
+    return get
+
+
+def sample_rows(N, seed, n=64):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(N, n, replace=False), [0, 15, 16, N - 1]]))
+    return rows
+
+
+@pytest.mark.parametrize("shape", [ts.GATE_UP, ts.DOWN])
+def test_decode_T1_full_rows(tl, torch, big, shape):
+    """Decode at T=1 on the 27B-class shapes: every output checked."""
+    wts, W = big(shape)
+    xbits = ts.activations(wts, 1)
+    x_dev = to_dev_bf16(torch, xbits)
+    ref = oracle.linear_bf16(xbits, wts.w, wts.s)
+    for rung in ("auto", "gemv", "small_t"):
+        y = run(tl, torch, x_dev, W, rung)
+        assert rel_l2(y, ref) <= BF16_GATE, rung
+        assert rel_l2(y, ref) <= 1e-6, rung
+
+
+@pytest.mark.parametrize("shape", [ts.GATE_UP, ts.DOWN, ts.OUT_PROJ])
+@pytest.mark.parametrize("T", [2, 4, 8, 12, 16])
+def test_small_T_batches_sampled(tl, torch, big, shape, T):
+    wts, W = big(shape)
+    xbits = ts.activations(wts, T)
+    x_dev = to_dev_bf16(torch, xbits)
+    rows = sample_rows(W.n, T)
+    ref = oracle.linear_bf16(xbits, wts.w[rows], wts.s[rows])
+    for rung in ("auto", "small_t", "small_t_tiled"):
+        y = run(tl, torch, x_dev, W, rung)
+        assert rel_l2(y[:, rows], ref) <= BF16_GATE, rung
+
+
+@pytest.mark.parametrize("shape", [ts.GATE_UP, ts.DOWN])
+@pytest.mark.parametrize("T", [17, 36, 508, 2048])
+def test_prefill_s8_sampled(tl, torch, big, shape, T):
+    wts, W = big(shape)
+    xbits = ts.activations(wts, T)
+    x_dev = to_dev_bf16(torch, xbits)
+    rows = sample_rows(W.n, T)
+    y = run(tl, torch, x_dev, W, "auto")
+    assert tl.resolve_rung(T) == "s8"
+    check_s8(tl, torch, xbits, x_dev, W, wts.w, wts.s, y, rows=rows)
+    if T <= 36:
+        q_ref, _ = oracle.quant_s8(xbits)
+        acc = tl.debug_s8_acc(torch.from_numpy(q_ref).cuda(), W)
+        torch.cuda.synchronize()
+        acc = acc.cpu().numpy()
+        assert np.array_equal(acc[:, rows], oracle.s8_acc(q_ref, wts.w[rows], 128))
