@@ -1,0 +1,243 @@
+"""Benchmark of the ternary-weight linear layer on one MI355X.
+
+One step = one decode pass (T = 1) through the two 27B-class layer shapes,
+gate/up (K=5120 -> N=34816) and down (K=17408 -> N=5120), with weights
+rotated over enough device copies (> 512 MB) that every step streams them
+from HBM rather than from the 256 MiB Infinity Cache. The headline value is
+the whole step's algorithmic bytes per second (GB/s = 1e9 B/s). The same
+line reports the s8 prefill rung at T = 2048 on the same two shapes in int8
+TOPS, the roofline fraction of the dominant kernel of each, and the CPU
+oracle timed on the host as a baseline.
+
+Timing: the K timed steps are captured once into a HIP graph (PyTorch's
+CUDAGraph on ROCm) and replayed between HIP events recorded on the same
+stream, so host launch overhead does not enter the measurement.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8.0 TB/s
+I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POPS
+MALL_BYTES = 256 * 2**20
+ROTATE_BYTES = 600e6  # > 2x the Infinity Cache
+METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
+KERNEL_SRC = os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", "tern_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(T, n, k, group):
+    """Codes (2 bits/weight) + fp16 scales + bf16 activations + fp32 outputs."""
+    return n * k // 4 + 2 * n * (k // group) + 2 * T * k + 4 * T * n
+
+
+def kernel_source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel_key):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    v = d.get("kernels", {}).get(kernel_key)
+    return None if v is None else v.get("bytes_per_launch")
+
+
+def graph_time(torch, fn, steps, warmup):
+    """Capture `steps` calls of fn(i) into one graph; return seconds per replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(max(1, warmup)):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()  # untimed warm replay
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    g.replay()
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3
+
+
+def cpu_baseline(wts_list, x_list, budget_s=12.0):
+    import oracle
+    nthreads = 1  # oracle.c is single-threaded plain C
+    step_bytes = sum(algorithmic_bytes(1, w.shape.n, w.shape.k, w.shape.group) for w in wts_list)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for w, x in zip(wts_list, x_list):
+            oracle.linear_bf16(x, w.w, w.s)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 30:
+            break
+    return {"value": round(reps * step_bytes / el / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{reps} full T=1 decode steps (gate_up 5120->34816 + down 17408->5120) "
+                      f"through oracle_linear_bf16 (fp64, single thread), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--s8-steps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-s8", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the layer is not sharded across "
+              "GPUs); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tern_synth as ts
+    import ternary_weight_linear_amd as tl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tl.lib()
+
+    shapes = (ts.GATE_UP, ts.DOWN)
+    log("drawing weights")
+    wts = [ts.weights(s) for s in shapes]
+    base = [tl.TernaryWeights.from_host(w.w, w.s, device=dev) for w in wts]
+    step_bytes = sum(algorithmic_bytes(1, s.n, s.k, s.group) for s in shapes)
+    nsets = max(2, math.ceil(ROTATE_BYTES / step_bytes))
+    sets = [base]
+    for _ in range(nsets - 1):
+        sets.append([tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group)
+                     for b in base])
+    torch.cuda.synchronize()
+    log(f"{nsets} rotation sets x {step_bytes / 1e6:.2f} MB")
+
+    xb = [ts.activations(w, 1) for w in wts]
+    x1 = [torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16) for b in xb]
+    y1 = [torch.empty((1, s.n), dtype=torch.float32, device=dev) for s in shapes]
+    assert tl.resolve_rung(1) == "gemv"
+
+    def decode_step(i):
+        ws = sets[i % nsets]
+        tl.linear(x1[0], ws[0], y=y1[0])
+        tl.linear(x1[1], ws[1], y=y1[1])
+
+    K, Wm = args.steps, args.warmup
+    el = graph_time(torch, decode_step, K, Wm)
+    value = K * step_bytes / el / 1e9
+    ms_per_step = el / K * 1e3
+    log(f"decode step {ms_per_step * 1e3:.2f} us, {value:.1f} GB/s")
+
+    per_shape = {}
+    for j, s in enumerate(shapes):
+        def one(i, j=j):
+            tl.linear(x1[j], sets[i % nsets][j], y=y1[j])
+        t = graph_time(torch, one, K, Wm) / K
+        b = algorithmic_bytes(1, s.n, s.k, s.group)
+        per_shape[s.name] = {"rung": "gemv", "us_per_launch": round(t * 1e6, 3),
+                             "bytes": b, "GB/s": round(b / t / 1e9, 1)}
+        log(f"  {s.name}: {t * 1e6:.2f} us/launch, {b / t / 1e9:.1f} GB/s")
+    dom = shapes[0].name
+    achieved = per_shape[dom]["GB/s"]
+    traffic = stored_traffic(f"gemv:{dom}")
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": f"tern_small_t_kernel (gemv rung, T=1) on {dom}",
+                "algorithmic_bytes_per_launch": per_shape[dom]["bytes"],
+                "us_per_launch": per_shape[dom]["us_per_launch"]}
+
+    s8 = None
+    if not args.no_s8:
+        T = 2048
+        xs = [torch.from_numpy(ts.activations(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
+              for w in wts]
+        ys = [torch.empty((T, s.n), dtype=torch.float32, device=dev) for s in shapes]
+        wsz = max(tl.workspace_bytes(T, s.n, s.k, s.group) for s in shapes)
+        wsp = torch.empty((wsz,), dtype=torch.uint8, device=dev)
+        qs = [tl.quant_act_s8(x) for x in xs]
+        assert tl.resolve_rung(T) == "s8"
+        ops = sum(2 * T * s.n * s.k for s in shapes)
+        K8 = args.s8_steps
+
+        def prefill_step(i):
+            for j in range(2):
+                tl.linear(xs[j], sets[i % nsets][j], y=ys[j], workspace=wsp)
+
+        el8 = graph_time(torch, prefill_step, K8, 2)
+        tops = K8 * ops / el8 / 1e12
+        gemm = {}
+        for j, s in enumerate(shapes):
+            def g1(i, j=j):
+                tl.linear_s8_q(qs[j][0], qs[j][1], sets[i % nsets][j], y=ys[j])
+            t = graph_time(torch, g1, K8, 2) / K8
+            def q1(i, j=j):
+                tl.quant_act_s8(xs[j], q=qs[j][0], scale=qs[j][1])
+            tq = graph_time(torch, q1, K8, 2) / K8
+            o = 2 * T * s.n * s.k
+            gemm[s.name] = {"us_s8_kernel": round(t * 1e6, 2), "TOPS_s8_kernel": round(o / t / 1e12, 1),
+                            "us_quant_kernel": round(tq * 1e6, 2)}
+            log(f"  s8 {s.name}: gemm {t * 1e6:.1f} us ({o / t / 1e12:.0f} TOPS), quant {tq * 1e6:.1f} us")
+        ach = gemm[dom]["TOPS_s8_kernel"]
+        s8 = {"metric": "int8 TOPS at T=2048 (quant + s8 contraction, both shapes)",
+              "value": round(tops, 1), "unit": "TOPS", "ms_per_step": round(el8 / K8 * 1e3, 4),
+              "steps": K8, "dtype": "i8", "per_shape": gemm,
+              "roofline": {"bound": "mfma", "achieved": ach, "peak": I8_PEAK_TOPS, "unit": "TOPS",
+                           "frac": round(ach / I8_PEAK_TOPS, 4),
+                           "traffic": stored_traffic(f"s8:{dom}"),
+                           "kernel": f"tern_s8_kernel on {dom}, T={T}"}}
+        log(f"s8 prefill step {el8 / K8 * 1e3:.3f} ms, {tops:.1f} TOPS")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(wts, xb)
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+           "warmup": Wm, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "decode T=1 through gate_up 5120->34816 and down 17408->5120, "
+                                  "ternary weights (2-bit packed), fp16 scale per 128, bf16 x",
+                      "T": 1, "rotation_sets": nsets, "bytes_per_step": step_bytes,
+                      "per_shape": per_shape, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+           "roofline": roofline, "s8_prefill": s8, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

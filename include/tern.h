@@ -177,6 +177,18 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
                         tern_rung rung, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The s8 rung's contraction on activations already quantised by
+ * tern_quant_act_s8 (device, async): y[t][n] = scale_t * sum_g s[n][g] *
+ * acc[t][n][g] in fp32, groups ascending -- the same kernel and numerics as
+ * tern_linear(..., TERN_RUNG_S8, ...) after its quantisation step. Lets a
+ * caller quantise one activation once and apply several projections to it.
+ * q: device int8 [T][K] (16-byte aligned); act_scale: device float [T];
+ * y: device float [T][N] (16-byte aligned). Counts as an s8 launch in the probe.
+ */
+tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
+                             const tern_weights* W, float* y, void* stream);
+
+/*
  * Debug export of the s8 rung's integer group accumulators (device, async):
  * acc[t][n][g] = sum_{k in group g} q[t][k] * w[n][k], int32 [T][N][K/G].
  * Runs the s8 contraction kernel with its epilogue replaced by a store of the

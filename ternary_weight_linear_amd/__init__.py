@@ -11,6 +11,7 @@ Entry points mirror the C ABI in ``include/tern.h``:
 * ``TernaryWeights``           -- packed codes + scales resident on the GPU
 * ``quant_act_s8``             -- per-token int8 activation quantisation
 * ``linear``                   -- ``y = ternary_linear(x)`` with rung dispatch
+* ``linear_s8_q``              -- the s8 contraction on pre-quantised activations
 * ``debug_s8_acc``             -- the s8 rung's int32 group accumulators
 * ``probe_snapshot`` / ``probe_reset`` / ``last_rung`` / ``resolve_rung``
 """
@@ -34,7 +35,8 @@ STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_AL
 
 # Symbols declared in include/tern.h (checked by the host tests).
 EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpack",
-           "tern_quant_act_s8", "tern_workspace_bytes", "tern_linear", "tern_debug_s8_acc",
+           "tern_quant_act_s8", "tern_workspace_bytes", "tern_linear", "tern_linear_s8_q",
+           "tern_debug_s8_acc",
            "tern_probe_snapshot", "tern_probe_reset", "tern_last_rung", "tern_resolve_rung",
            "tern_rung_name", "tern_last_error", "tern_abi_version")
 
@@ -72,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "tern_quant_act_s8": (st, [p, i, i, p, p, p]),
         "tern_workspace_bytes": (sz, [i, i, i, i, i]),
         "tern_linear": (st, [p, i, ctypes.POINTER(_Weights), p, i, p, sz, p]),
+        "tern_linear_s8_q": (st, [p, p, i, ctypes.POINTER(_Weights), p, p]),
         "tern_debug_s8_acc": (st, [p, i, ctypes.POINTER(_Weights), p, p]),
         "tern_probe_snapshot": (None, [p]),
         "tern_probe_reset": (None, []),
@@ -259,6 +262,22 @@ def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=Non
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().tern_linear(x.data_ptr(), T, W.ref(), y.data_ptr(), r, ws_ptr, ws_bytes,
                              _stream(stream)))
+    return y
+
+
+def linear_s8_q(q, scale, W: TernaryWeights, y=None, stream=None):
+    """s8 contraction on pre-quantised activations (q int8 [T, K], scale float32 [T])."""
+    torch = _torch()
+    _dev(q, torch.int8, "q")
+    _dev(scale, torch.float32, "scale")
+    T, K = q.shape
+    if K != W.k:
+        raise ValueError(f"q has K={K}, weights have K={W.k}")
+    if y is None:
+        y = torch.empty((T, W.n), dtype=torch.float32, device=q.device)
+    _dev(y, torch.float32, "y")
+    _check(lib().tern_linear_s8_q(q.data_ptr(), scale.data_ptr(), T, W.ref(), y.data_ptr(),
+                                  _stream(stream)))
     return y
 
 

@@ -219,18 +219,23 @@ size_t workspace_for(int T, int k, tern_rung r) {
   return 0;
 }
 
-tern::SmallTPlan plan_small_t(int T, int n, int k, tern_rung r) {
+tern::SmallTPlan plan_small_t(int T, int n, int k, int group, tern_rung r) {
+  (void)group;
   const Config& c = config();
   tern::SmallTPlan p;
   const int NS = n / 16, KT = k / 256;
-  p.tokens_per_tile = (r == TERN_RUNG_GEMV) ? 1 : 16;
-  p.token_tiles = (r == TERN_RUNG_GEMV) ? T : (T + 15) / 16;
   int S = NS >= 1024 ? 2 : 1;
   if (c.tune_strips) S = c.tune_strips;
+  // gemv stages the token row in LDS; rows too long for that take the
+  // 16-token kernel (its absent rows read as zeros).
+  const bool row_in_lds = r == TERN_RUNG_GEMV && tern::small_t_max_waves(1, S, k) >= 1;
+  p.tokens_per_tile = row_in_lds ? 1 : 16;
+  p.token_tiles = row_in_lds ? T : (T + 15) / 16;
   const int nsb = (NS + S - 1) / S;
-  int W = (int)((4096.0 * 1.0) / (double)(nsb * (long)std::max(1, p.token_tiles)) + 0.5);
-  W = std::max(1, std::min(W, std::min(16, KT)));
-  if (c.tune_waves) W = std::min(c.tune_waves, KT);
+  int W = (int)(4096.0 / (double)(nsb * (long)std::max(1, p.token_tiles)) + 0.5);
+  const int wmax = std::max(1, tern::small_t_max_waves(p.tokens_per_tile, S, k));
+  W = std::max(1, std::min(W, std::min(wmax, KT)));
+  if (c.tune_waves) W = std::max(1, std::min(std::min(c.tune_waves, wmax), KT));
   p.strips_per_wave = S;
   p.waves = W;
   return p;
@@ -425,10 +430,26 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
     if (err) return hip_fail(err, "s8 launch");
   } else {
     tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
-    int err = tern::launch_small_t(a, plan_small_t(T, n, k, r), stream);
+    int err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
     if (err) return hip_fail(err, "small_t launch");
   }
   probe_hit(r, T, n, k, G);
+  return ok();
+}
+
+tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
+                             const tern_weights* W, float* y, void* stream) {
+  if (!q || !act_scale || !y) return fail(TERN_ERR_NULL, "tern_linear_s8_q: NULL pointer");
+  tern_status st = check_weights(W);
+  if (st != TERN_OK) return st;
+  if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
+  if (!aligned16(q) || !aligned16(y)) return fail(TERN_ERR_ALIGN, "q and y must be 16-byte aligned");
+  const Config& c = config();
+  if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
+  tern::S8Args a{q, act_scale, T, W->k, W->n, W->group, W->codes, W->scales, y, nullptr};
+  int err = tern::launch_s8(a, plan_s8(T), stream);
+  if (err) return hip_fail(err, "s8 launch");
+  probe_hit(TERN_RUNG_S8, T, W->n, W->k, W->group);
   return ok();
 }
 

@@ -41,6 +41,10 @@ struct S8Args {
 
 // All launchers return 0 on success or a hipError_t value.
 int launch_small_t(const SmallTArgs& a, const SmallTPlan& p, void* stream);
+// Largest waves-per-block the bf16 kernel accepts for this variant (LDS and
+// register limits; 0 if none fits).
+int small_t_max_waves(int tokens_per_tile, int strips, int K);
+int small_t_lds_bytes(int tokens_per_tile, int strips, int waves, int K);
 int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, void* stream);
 int launch_s8(const S8Args& a, const S8Plan& p, void* stream);
 const char* hip_error_string(int err);

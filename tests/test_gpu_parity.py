@@ -76,6 +76,10 @@ def check_s8(tl, torch, xbits, x_dev, W, w, s, y, rows=None):
     assert rel_l2(ycols, ref) <= S8_GATE
     ordered = oracle.linear_s8_fp32_ordered(q_ref, sc_ref, ws, ss)
     assert np.array_equal(ycols.view(np.uint32), ordered.view(np.uint32))
+    # the same contraction on the pre-quantised activations
+    y2 = tl.linear_s8_q(q, sc, W)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().numpy().view(np.uint32), y.view(np.uint32))
 
 
 # ---------------------------------------------------------- small shape
@@ -287,3 +291,45 @@ def test_prefill_s8_sampled(tl, torch, big, shape, T):
         torch.cuda.synchronize()
         acc = acc.cpu().numpy()
         assert np.array_equal(acc[:, rows], oracle.s8_acc(q_ref, wts.w[rows], 128))
+
+
+# ------------------------------------------------ launch-shape variants
+
+_TUNE_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import oracle, tern_synth as ts, ternary_weight_linear_amd as tl
+shape = ts.Shape("tune_4096x96", 4096, 96, int(sys.argv[2]), 0.4, True, 401)
+wts = ts.weights(shape)
+W = tl.TernaryWeights.from_host(wts.w, wts.s)
+worst = 0.0
+for T in (1, 5, 16, 23):
+    xb = ts.activations(wts, T)
+    x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    ref = oracle.linear_bf16(xb, wts.w, wts.s)
+    for rung in ("gemv", "small_t", "small_t_tiled"):
+        if rung == "small_t" and T > 16:
+            continue
+        y = tl.linear(x, W, rung=rung).cpu().numpy().astype(np.float64)
+        err = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+        worst = max(worst, err)
+print("WORST", worst)
+"""
+
+
+@pytest.mark.parametrize("strips,waves,G", [(1, 1, 128), (2, 1, 64), (4, 1, 128), (4, 3, 64),
+                                            (1, 16, 128), (2, 8, 128)])
+def test_launch_shapes_keep_parity(strips, waves, G):
+    """Every (strips per wave, waves per block) launch shape the tuning knobs
+    can select, including multi-chunk k-ranges (16 k-tiles on one wave) and
+    partial strip blocks (6 strips with 4 per block), stays within the gate."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, TERN_TUNE_STRIPS=str(strips), TERN_TUNE_WAVES=str(waves))
+    r = subprocess.run([sys.executable, "-c", _TUNE_CHILD, root, str(G)], env=env,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    worst = float(r.stdout.split("WORST")[1])
+    assert worst <= 1e-6, worst
