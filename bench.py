@@ -190,7 +190,7 @@ def main():
         ys = [torch.empty((T, s.n), dtype=torch.float32, device=dev) for s in shapes]
         wsz = max(tl.workspace_bytes(T, s.n, s.k, s.group) for s in shapes)
         wsp = torch.empty((wsz,), dtype=torch.uint8, device=dev)
-        qs = [tl.quant_act_s8(x) for x in xs]
+        qs = [tl.quant_act_s8(x, layout="operand_order") for x in xs]
         assert tl.resolve_rung(T) == "s8"
         ops = sum(2 * T * s.n * s.k for s in shapes)
         K8 = args.s8_steps
@@ -204,10 +204,11 @@ def main():
         gemm = {}
         for j, s in enumerate(shapes):
             def g1(i, j=j):
-                tl.linear_s8_q(qs[j][0], qs[j][1], sets[i % nsets][j], y=ys[j])
+                tl.linear_s8_q(qs[j][0], qs[j][1], sets[i % nsets][j], y=ys[j],
+                               layout="operand_order")
             t = graph_time(torch, g1, K8, 2) / K8
             def q1(i, j=j):
-                tl.quant_act_s8(xs[j], q=qs[j][0], scale=qs[j][1])
+                tl.quant_act_s8(xs[j], q=qs[j][0], scale=qs[j][1], layout="operand_order")
             tq = graph_time(torch, q1, K8, 2) / K8
             o = 2 * T * s.n * s.k
             gemm[s.name] = {"us_s8_kernel": round(t * 1e6, 2), "TOPS_s8_kernel": round(o / t / 1e12, 1),

@@ -133,6 +133,14 @@ tern_status tern_pack(const int8_t* w, const uint16_t* scales_f16, int n, int k,
 tern_status tern_unpack(const void* codes, const uint16_t* scales_packed, int n, int k,
                         int group, int8_t* w_out, uint16_t* scales_out);
 
+/* Layouts of int8 activations q [T][K]. */
+typedef enum {
+  TERN_Q_ROW_MAJOR = 0,     /* q[t][k] at byte t*K + k */
+  TERN_Q_OPERAND_ORDER = 1  /* K % 64 == 0; inside row t, the byte at 64b + 16g + 4i + e holds
+                               k = 64b + 8g + m(i, e), m(i, .) = {32+2i, 2i, 33+2i, 2i+1}: the
+                               order in which the s8 contraction consumes a 64-wide k-block */
+} tern_q_layout;
+
 /*
  * Per-token symmetric int8 activation quantisation (device, async), the first
  * step of the s8 rung ("NInfer sm_89 fork" article, section 7 and section 9
@@ -140,11 +148,12 @@ tern_status tern_unpack(const void* codes, const uint16_t* scales_packed, int n,
  *   a_t = max_k |x[t][k]|;  scale_t = fl32(a_t / 127) (IEEE division);
  *   q[t][k] = clamp(round-half-even(fl32(x[t][k] / scale_t)), -127, 127);
  *   a_t == 0 gives scale_t = 0 and q[t][:] = 0.
- * x: device bf16 [T][K]; q: device int8 [T][K]; act_scale: device float [T].
- * K % 8 == 0; x and q 16-byte aligned.
+ * x: device bf16 [T][K]; q: device int8 [T][K] in `layout`; act_scale: device
+ * float [T]. K % 8 == 0 (K % 64 == 0 for TERN_Q_OPERAND_ORDER); x and q
+ * 16-byte aligned.
  */
 tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float* act_scale,
-                              void* stream);
+                              tern_q_layout layout, void* stream);
 
 /*
  * Device workspace tern_linear needs for this call (bytes, 0 if none). The s8
@@ -180,13 +189,14 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
  * The s8 rung's contraction on activations already quantised by
  * tern_quant_act_s8 (device, async): y[t][n] = scale_t * sum_g s[n][g] *
  * acc[t][n][g] in fp32, groups ascending -- the same kernel and numerics as
- * tern_linear(..., TERN_RUNG_S8, ...) after its quantisation step. Lets a
- * caller quantise one activation once and apply several projections to it.
- * q: device int8 [T][K] (16-byte aligned); act_scale: device float [T];
- * y: device float [T][N] (16-byte aligned). Counts as an s8 launch in the probe.
+ * tern_linear(..., TERN_RUNG_S8, ...) after its quantisation step (which uses
+ * TERN_Q_OPERAND_ORDER). Lets a caller quantise one activation once and apply
+ * several projections to it. q: device int8 [T][K] in `layout` (16-byte
+ * aligned); act_scale: device float [T]; y: device float [T][N] (16-byte
+ * aligned). Counts as an s8 launch in the probe.
  */
 tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
-                             const tern_weights* W, float* y, void* stream);
+                             const tern_weights* W, float* y, tern_q_layout layout, void* stream);
 
 /*
  * Debug export of the s8 rung's integer group accumulators (device, async):
@@ -195,7 +205,7 @@ tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
  * accumulators, so the integer path can be checked bit for bit.
  */
 tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int32_t* acc_out,
-                              void* stream);
+                              void* stream); /* q row-major */
 
 /* Rung probe: number of kernel launches per rung since the last reset,
  * counted at the launch site of the kernel that actually ran. */

@@ -71,10 +71,10 @@ def lib() -> ctypes.CDLL:
         "tern_scale_count": (sz, [i, i, i]),
         "tern_pack": (st, [p, p, i, i, i, p, p]),
         "tern_unpack": (st, [p, p, i, i, i, p, p]),
-        "tern_quant_act_s8": (st, [p, i, i, p, p, p]),
+        "tern_quant_act_s8": (st, [p, i, i, p, p, i, p]),
         "tern_workspace_bytes": (sz, [i, i, i, i, i]),
         "tern_linear": (st, [p, i, ctypes.POINTER(_Weights), p, i, p, sz, p]),
-        "tern_linear_s8_q": (st, [p, p, i, ctypes.POINTER(_Weights), p, p]),
+        "tern_linear_s8_q": (st, [p, p, i, ctypes.POINTER(_Weights), p, i, p]),
         "tern_debug_s8_acc": (st, [p, i, ctypes.POINTER(_Weights), p, p]),
         "tern_probe_snapshot": (None, [p]),
         "tern_probe_reset": (None, []),
@@ -226,8 +226,12 @@ class TernaryWeights:
         return ctypes.byref(self._struct)
 
 
-def quant_act_s8(x, q=None, scale=None, stream=None):
-    """Per-token int8 quantisation of bf16 activations x [T, K] (device)."""
+Q_LAYOUTS = {"row_major": 0, "operand_order": 1}
+
+
+def quant_act_s8(x, q=None, scale=None, stream=None, layout="row_major"):
+    """Per-token int8 quantisation of bf16 activations x [T, K] (device).
+    layout: "row_major" or "operand_order" (the s8 contraction's byte order)."""
     torch = _torch()
     _dev(x, torch.bfloat16, "x")
     T, K = x.shape
@@ -238,7 +242,7 @@ def quant_act_s8(x, q=None, scale=None, stream=None):
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
     _check(lib().tern_quant_act_s8(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
-                                   _stream(stream)))
+                                   Q_LAYOUTS[layout], _stream(stream)))
     return q, scale
 
 
@@ -265,8 +269,9 @@ def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=Non
     return y
 
 
-def linear_s8_q(q, scale, W: TernaryWeights, y=None, stream=None):
-    """s8 contraction on pre-quantised activations (q int8 [T, K], scale float32 [T])."""
+def linear_s8_q(q, scale, W: TernaryWeights, y=None, stream=None, layout="row_major"):
+    """s8 contraction on pre-quantised activations (q int8 [T, K] in `layout`,
+    scale float32 [T])."""
     torch = _torch()
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
@@ -277,7 +282,7 @@ def linear_s8_q(q, scale, W: TernaryWeights, y=None, stream=None):
         y = torch.empty((T, W.n), dtype=torch.float32, device=q.device)
     _dev(y, torch.float32, "y")
     _check(lib().tern_linear_s8_q(q.data_ptr(), scale.data_ptr(), T, W.ref(), y.data_ptr(),
-                                  _stream(stream)))
+                                  Q_LAYOUTS[layout], _stream(stream)))
     return y
 
 

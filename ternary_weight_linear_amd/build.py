@@ -35,16 +35,22 @@ def _run(cmd):
     subprocess.check_call(cmd)
 
 
+# The s8 contraction reads every MFMA accumulator in its fp32 epilogue: keep
+# MFMA results in VGPRs (no accumulator-register round trips).
+S8_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
     k_obj = os.path.join(BUILD, "tern_kernels.o")
+    s8_obj = os.path.join(BUILD, "tern_s8.o")
     h_obj = os.path.join(BUILD, "tern_host.o")
-    _run([HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
-          os.path.join(CSRC, "tern_kernels.hip"), "-o", k_obj])
-    _run(["g++", *HOST_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
-          os.path.join(CSRC, "tern_host.cpp"), "-o", h_obj])
+    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_kernels.hip"), "-o", k_obj])
+    _run([HIPCC, *HIP_FLAGS, *S8_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_s8.hip"), "-o", s8_obj])
+    _run(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_host.cpp"), "-o", h_obj])
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, k_obj, h_obj])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, k_obj, s8_obj, h_obj])
     os.replace(tmp, LIB)
     return LIB
 

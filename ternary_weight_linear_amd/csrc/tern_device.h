@@ -1,0 +1,53 @@
+// tern_device.h -- device-side helpers shared by the gfx950 kernels of this
+// library (tern_kernels.hip, tern_s8.hip). Internal, not installed.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tern {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Bf16 pair j (0..7) of a code word: codes at bits 15:14 and 31:30 after the
+// shift; 0x4000 = +2.0, 0xC000 = -2.0 (scales are halved to compensate).
+__device__ __forceinline__ uint32_t code_pair(uint32_t P, int j) {
+  return (P << (2 * j)) & 0xC000C000u;
+}
+
+// B operand of MFMA m (0..7) of a 256-wide k-tile from the lane's 4 code words.
+__device__ __forceinline__ bf16x8 weights_operand(const uint4& P, int m) {
+  const uint32_t word = (m >> 1) == 0 ? P.x : (m >> 1) == 1 ? P.y : (m >> 1) == 2 ? P.z : P.w;
+  const int j0 = 4 * (m & 1);
+  uint4 b;
+  b.x = code_pair(word, j0 + 0);
+  b.y = code_pair(word, j0 + 1);
+  b.z = code_pair(word, j0 + 2);
+  b.w = code_pair(word, j0 + 3);
+  return __builtin_bit_cast(bf16x8, b);
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [p, p + bytes): loads past the end return zero,
+// which is how absent tokens and rows read as zeros without branches.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // The descriptor lives in scalar registers: state that its inputs are
+  // wave-uniform so the compiler never needs a per-lane loop to build it.
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                           0x00020000);
+}
+constexpr int kAuxNontemporal = 2;  // "nt": streamed once, do not keep in cache
+}  // namespace dev
+}  // namespace tern

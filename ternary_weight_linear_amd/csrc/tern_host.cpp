@@ -224,7 +224,8 @@ tern::SmallTPlan plan_small_t(int T, int n, int k, int group, tern_rung r) {
   const Config& c = config();
   tern::SmallTPlan p;
   const int NS = n / 16, KT = k / 256;
-  int S = NS >= 1024 ? 2 : 1;
+  int S = 2;
+  if (T > 1 && r != TERN_RUNG_GEMV && NS >= 1024) S = 4;
   if (c.tune_strips) S = c.tune_strips;
   // gemv stages the token row in LDS; rows too long for that take the
   // 16-token kernel (its absent rows read as zeros).
@@ -232,7 +233,12 @@ tern::SmallTPlan plan_small_t(int T, int n, int k, int group, tern_rung r) {
   p.tokens_per_tile = row_in_lds ? 1 : 16;
   p.token_tiles = row_in_lds ? T : (T + 15) / 16;
   const int nsb = (NS + S - 1) / S;
-  int W = (int)(4096.0 / (double)(nsb * (long)std::max(1, p.token_tiles)) + 0.5);
+  // About 4.3k waves in flight (4 per SIMD) fill the chip in one round for
+  // every layer shape measured; the sweep over (S, W) on MI355X picked S = 2
+  // everywhere except wide 16-token tiles (S = 4, which share the activation
+  // fragments across more strips).
+  int W = (int)(4352.0 / (double)(nsb * (long)std::max(1, p.token_tiles)) + 0.5);
+  if (p.tokens_per_tile == 16 && NS >= 1024 && !c.tune_strips) W = 4;
   const int wmax = std::max(1, tern::small_t_max_waves(p.tokens_per_tile, S, k));
   W = std::max(1, std::min(W, std::min(wmax, KT)));
   if (c.tune_waves) W = std::max(1, std::min(std::min(c.tune_waves, wmax), KT));
@@ -391,13 +397,18 @@ int tern_resolve_rung(int T, tern_rung rung) {
 }
 
 tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float* act_scale,
-                              void* stream) {
+                              tern_q_layout layout, void* stream) {
   if (!x_bf16 || !q || !act_scale) return fail(TERN_ERR_NULL, "tern_quant_act_s8: NULL pointer");
   if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
-  if (k < 8 || k % 8 != 0) return fail(TERN_ERR_SHAPE, "K=%d must be a positive multiple of 8", k);
+  if (layout != TERN_Q_ROW_MAJOR && layout != TERN_Q_OPERAND_ORDER)
+    return fail(TERN_ERR_VALUE, "unknown q layout %d", (int)layout);
+  const int mult = layout == TERN_Q_OPERAND_ORDER ? 64 : 8;
+  if (k < mult || k % mult != 0)
+    return fail(TERN_ERR_SHAPE, "K=%d must be a positive multiple of %d", k, mult);
   if (!aligned16(x_bf16) || !aligned16(q))
     return fail(TERN_ERR_ALIGN, "x and q must be 16-byte aligned");
-  int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, act_scale, stream);
+  int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, act_scale,
+                                  layout == TERN_Q_OPERAND_ORDER, stream);
   if (err) return hip_fail(err, "quant_s8 launch");
   return ok();
 }
@@ -423,9 +434,9 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
   if (r == TERN_RUNG_S8) {
     int8_t* q = (int8_t*)ws;
     float* sc = (float*)((char*)ws + align256((size_t)T * k));
-    int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, stream);
+    int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, true, stream);
     if (err) return hip_fail(err, "quant_s8 launch");
-    tern::S8Args a{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr};
+    tern::S8Args a{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr, true};
     err = tern::launch_s8(a, plan_s8(T), stream);
     if (err) return hip_fail(err, "s8 launch");
   } else {
@@ -438,15 +449,18 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
 }
 
 tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
-                             const tern_weights* W, float* y, void* stream) {
+                             const tern_weights* W, float* y, tern_q_layout layout, void* stream) {
   if (!q || !act_scale || !y) return fail(TERN_ERR_NULL, "tern_linear_s8_q: NULL pointer");
   tern_status st = check_weights(W);
   if (st != TERN_OK) return st;
   if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
+  if (layout != TERN_Q_ROW_MAJOR && layout != TERN_Q_OPERAND_ORDER)
+    return fail(TERN_ERR_VALUE, "unknown q layout %d", (int)layout);
   if (!aligned16(q) || !aligned16(y)) return fail(TERN_ERR_ALIGN, "q and y must be 16-byte aligned");
   const Config& c = config();
   if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
-  tern::S8Args a{q, act_scale, T, W->k, W->n, W->group, W->codes, W->scales, y, nullptr};
+  tern::S8Args a{q,       act_scale, T,       W->k,    W->n, W->group, W->codes,
+                 W->scales, y,       nullptr, layout == TERN_Q_OPERAND_ORDER};
   int err = tern::launch_s8(a, plan_s8(T), stream);
   if (err) return hip_fail(err, "s8 launch");
   probe_hit(TERN_RUNG_S8, T, W->n, W->k, W->group);
@@ -462,7 +476,7 @@ tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int
   if (!aligned16(q)) return fail(TERN_ERR_ALIGN, "q must be 16-byte aligned");
   const Config& c = config();
   if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
-  tern::S8Args a{q, nullptr, T, W->k, W->n, W->group, W->codes, W->scales, nullptr, acc_out};
+  tern::S8Args a{q, nullptr, T, W->k, W->n, W->group, W->codes, W->scales, nullptr, acc_out, false};
   int err = tern::launch_s8(a, plan_s8(T), stream);
   if (err) return hip_fail(err, "s8 debug launch");
   return ok();

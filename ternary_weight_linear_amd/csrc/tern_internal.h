@@ -37,6 +37,7 @@ struct S8Args {
   const uint16_t* scales;
   float* y;          // [T][N] (nullptr in debug-acc mode)
   int32_t* acc_out;  // [T][N][K/G] (debug-acc mode only)
+  bool q_operand_order;  // q is in the s8 operand order (from launch_quant_s8(..., true, ...))
 };
 
 // All launchers return 0 on success or a hipError_t value.
@@ -45,7 +46,10 @@ int launch_small_t(const SmallTArgs& a, const SmallTPlan& p, void* stream);
 // register limits; 0 if none fits).
 int small_t_max_waves(int tokens_per_tile, int strips, int K);
 int small_t_lds_bytes(int tokens_per_tile, int strips, int waves, int K);
-int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, void* stream);
+// operand_order: write q in the s8 kernel's operand order (K % 64 == 0)
+// instead of row-major.
+int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
+                    void* stream);
 int launch_s8(const S8Args& a, const S8Plan& p, void* stream);
 const char* hip_error_string(int err);
 

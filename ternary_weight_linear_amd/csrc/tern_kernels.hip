@@ -27,56 +27,12 @@
 
 #include <type_traits>
 
+#include "tern_device.h"
 #include "tern_internal.h"
 
 namespace tern {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
-typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
-
-__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
-}
-
-// Bf16 pair j (0..7) of a code word: codes at bits 15:14 and 31:30 after the
-// shift; 0x4000 = +2.0, 0xC000 = -2.0 (scales are halved to compensate).
-__device__ __forceinline__ uint32_t code_pair(uint32_t P, int j) {
-  return (P << (2 * j)) & 0xC000C000u;
-}
-
-// B operand of MFMA m (0..7) of a 256-wide k-tile from the lane's 4 code words.
-__device__ __forceinline__ bf16x8 weights_operand(const uint4& P, int m) {
-  const uint32_t word = (m >> 1) == 0 ? P.x : (m >> 1) == 1 ? P.y : (m >> 1) == 2 ? P.z : P.w;
-  const int j0 = 4 * (m & 1);
-  uint4 b;
-  b.x = code_pair(word, j0 + 0);
-  b.y = code_pair(word, j0 + 1);
-  b.z = code_pair(word, j0 + 2);
-  b.w = code_pair(word, j0 + 3);
-  return __builtin_bit_cast(bf16x8, b);
-}
-
-template <int GPT>
-struct ScaleWords;
-template <>
-struct ScaleWords<2> {  // G = 128: two fp16 per (row, k-tile)
-  uint32_t v;
-  __device__ __forceinline__ void load(const uint16_t* p) { v = *(const uint32_t*)p; }
-  __device__ __forceinline__ float get(int gi) const {
-    return half_bits_to_float((uint16_t)(gi == 0 ? (v & 0xffffu) : (v >> 16)));
-  }
-};
-template <>
-struct ScaleWords<4> {  // G = 64: four fp16 per (row, k-tile)
-  uint2 v;
-  __device__ __forceinline__ void load(const uint16_t* p) { v = *(const uint2*)p; }
-  __device__ __forceinline__ float get(int gi) const {
-    const uint32_t w = gi < 2 ? v.x : v.y;
-    return half_bits_to_float((uint16_t)((gi & 1) ? (w >> 16) : (w & 0xffffu)));
-  }
-};
+using namespace dev;
 
 // --------------------------------------------------------------------------
 // bf16-activation kernel (gemv: TT = 1, small_t / small_t_tiled: TT = 16)
@@ -89,16 +45,6 @@ struct ScaleWords<4> {  // G = 64: four fp16 per (row, k-tile)
 // stages, so every wave keeps 2*S KiB of weights in flight.
 // Dynamic LDS: W * S * (TT == 16 ? 256 : 16) floats for the reduction.
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer resource over [p, p + bytes): loads past the end return zero,
-// which is how absent tokens and rows read as zeros without branches.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                           0x00020000);
-}
-constexpr int kAuxNontemporal = 2;  // "nt": streamed once, do not keep in cache
 
 // One register stage: the codes of S strips for one k-tile, their scales
 // and, at TT = 16, the activation fragments of the k-tile's 8 MFMAs.
@@ -326,224 +272,6 @@ __global__ void __launch_bounds__(small_t_max_threads<S>()) tern_small_t_kernel(
   }
 }
 
-// --------------------------------------------------------------------------
-// per-token int8 activation quantisation
-// --------------------------------------------------------------------------
-
-// Max over the 64 lanes of a wavefront of non-negative float bit patterns
-// (integer order equals float order for them). DPP inside each row of 16
-// lanes, then the four row results through readlane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(a, b), max(c, d));
-}
-
-__device__ __forceinline__ uint32_t quant_byte(uint32_t xbits, float sc) {
-  const float r = rintf(__uint_as_float(xbits) / sc);  // IEEE division, ties-to-even rounding
-  const float c = fminf(fmaxf(r, -127.f), 127.f);
-  return (uint32_t)((int)c) & 0xffu;
-}
-
-__global__ void __launch_bounds__(256) tern_quant_s8_kernel(const uint16_t* __restrict__ x, int K,
-                                                            int8_t* __restrict__ q,
-                                                            float* __restrict__ scale) {
-  __shared__ uint32_t wmax[4];
-  const int t = blockIdx.x;
-  const uint4* xr = (const uint4*)(x + (size_t)t * K);
-  const int nchunk = K >> 3;
-  uint32_t m = 0;
-  for (int c = threadIdx.x; c < nchunk; c += 256) {
-    const uint4 v = xr[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m = max(m, (w[i] << 16) & 0x7fff0000u);
-      m = max(m, w[i] & 0x7fff0000u);
-    }
-  }
-  m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  const uint32_t am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  const float a = __uint_as_float(am);
-  const float sc = a / 127.0f;  // IEEE single division
-  if (threadIdx.x == 0) scale[t] = am == 0 ? 0.0f : sc;
-  uint2* qr = (uint2*)(q + (size_t)t * K);
-  for (int c = threadIdx.x; c < nchunk; c += 256) {
-    uint2 out = uint2{0u, 0u};
-    if (am != 0) {
-      const uint4 v = xr[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t b[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        b[2 * i] = quant_byte(w[i] << 16, sc);
-        b[2 * i + 1] = quant_byte(w[i] & 0xffff0000u, sc);
-      }
-      out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-      out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-    }
-    qr[c] = out;
-  }
-}
-
-// --------------------------------------------------------------------------
-// s8 kernel: int8 activations x ternary weights on the i8 matrix cores
-// --------------------------------------------------------------------------
-//
-// Workgroup tile BM tokens x BN outputs, (BM/WM) x (BN/WN) waves, each wave a
-// WM x WN block of 16x16 MFMA tiles. Per 256-wide k-tile the workgroup copies
-// the int8 activation tile to LDS and decodes the BN/16 packed weight tiles
-// to int8 rows in LDS ([row][k], padded rows of 272 bytes so that 16 rows
-// read 16 bytes each without bank conflicts). An i8 MFMA operand slot
-// (l >> 4, i) of lane l holds k = 64*kb + 16*(l >> 4) + i for both operands.
-
-constexpr int kS8Pitch = 256 + 16;
-
-// Sign-extend the 2-bit code at bit b of P to an int8 byte.
-__device__ __forceinline__ uint32_t code_byte(uint32_t P, int b) {
-  return (uint32_t)(((int32_t)(P << (30 - b))) >> 30) & 0xffu;
-}
-
-template <int BM, int BN, int WM, int WN, int GPT, bool DEBUG_ACC>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-    tern_s8_kernel(const int8_t* __restrict__ q, const float* __restrict__ act_scale, int T, int K,
-                   const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                   float* __restrict__ y, int32_t* __restrict__ acc_out, int N) {
-  constexpr int NWN = BN / WN;
-  constexpr int NTHR = (BM / WM) * NWN * 64;
-  constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
-  __shared__ __attribute__((aligned(16))) int8_t As[BM * kS8Pitch];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[BN * kS8Pitch];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / NWN, wn = wave % NWN;
-  const int t0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
-  const int NS = N >> 4;
-  const int KT = K >> 8;
-  const int NG = K / (256 / GPT);
-  const int r = lane & 15;
-  const int g = lane >> 4;
-
-  f32x4 tot[TM][TN];
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int b = 0; b < TN; ++b) tot[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kt = 0; kt < KT; ++kt) {
-    // Activation tile: BM rows x 256 bytes.
-    for (int c = tid; c < BM * 16; c += NTHR) {
-      const int row = c >> 4, col = (c & 15) * 16;
-      uint4 v = uint4{0u, 0u, 0u, 0u};
-      if (t0 + row < T) v = *(const uint4*)(q + (size_t)(t0 + row) * K + kt * 256 + col);
-      *(uint4*)(As + row * kS8Pitch + col) = v;
-    }
-    // Weight tiles: BN/16 strips x 256 code words, decoded to int8 rows.
-    for (int c = tid; c < (BN / 16) * 256; c += NTHR) {
-      const int sl = c >> 8;
-      const int win = c & 255;
-      const int L = win >> 2, qw = win & 3;
-      const int st = (n0 >> 4) + sl;
-      const uint32_t P = st < NS ? codes[((size_t)st * KT + kt) * 256 + win] : 0u;
-      // word qw holds MFMAs m = 2qw (k = 64qw + 8g' + e) and m = 2qw+1
-      // (k = 64qw + 32 + 8g' + e), e = 2d + h at bit (h ? 30 : 14) - 2d (- 8).
-      uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = e >> 1, h = e & 1;
-        const int b = (h ? 30 : 14) - 2 * d;
-        lo0 |= code_byte(P, b) << (8 * e);
-        hi0 |= code_byte(P, b - 8) << (8 * e);
-        const int b2 = (h ? 30 : 14) - 2 * (d + 2);
-        lo1 |= code_byte(P, b2) << (8 * e);
-        hi1 |= code_byte(P, b2 - 8) << (8 * e);
-      }
-      int8_t* rowp = Bs + (sl * 16 + (L & 15)) * kS8Pitch + 64 * qw + 8 * (L >> 4);
-      *(uint2*)(rowp) = uint2{lo0, lo1};
-      *(uint2*)(rowp + 32) = uint2{hi0, hi1};
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int gi = 0; gi < GPT; ++gi) {
-      i32x4 acc[TM][TN];
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b) acc[a][b] = i32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int kk = 0; kk < KBPG; ++kk) {
-        const int kb = gi * KBPG + kk;
-        i32x4 af[TM], bf[TN];
-#pragma unroll
-        for (int a = 0; a < TM; ++a)
-          af[a] = *(const i32x4*)(As + (wm * WM + a * 16 + r) * kS8Pitch + kb * 64 + 16 * g);
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-          bf[b] = *(const i32x4*)(Bs + (wn * WN + b * 16 + r) * kS8Pitch + kb * 64 + 16 * g);
-#pragma unroll
-        for (int a = 0; a < TM; ++a)
-#pragma unroll
-          for (int b = 0; b < TN; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
-      }
-      const int gidx = kt * GPT + gi;
-#pragma unroll
-      for (int b = 0; b < TN; ++b) {
-        const int n = n0 + wn * WN + b * 16 + r;  // accumulator column of this lane
-        const int st = n >> 4;
-        if (DEBUG_ACC) {
-#pragma unroll
-          for (int a = 0; a < TM; ++a)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = t0 + wm * WM + a * 16 + 4 * g + i;
-              if (t < T && st < NS) acc_out[((size_t)t * N + n) * NG + gidx] = acc[a][b][i];
-            }
-        } else {
-          const float sv =
-              st < NS ? half_bits_to_float(scales[(((size_t)st * KT + kt) * 16 + r) * GPT + gi])
-                      : 0.f;
-#pragma unroll
-          for (int a = 0; a < TM; ++a)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              tot[a][b][i] = __builtin_fmaf((float)acc[a][b][i], sv, tot[a][b][i]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  if (!DEBUG_ACC) {
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + wm * WM + a * 16 + 4 * g + i;
-        if (t >= T) continue;
-        const float as = act_scale[t];
-#pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int n = n0 + wn * WN + b * 16 + r;
-          if ((n >> 4) < NS) y[(size_t)t * N + n] = tot[a][b][i] * as;
-        }
-      }
-  }
-}
-
 template <int TT, int S>
 hipError_t launch_small_t_s(const SmallTArgs& a, const SmallTPlan& p, hipStream_t st) {
   const int NS = a.N / 16;
@@ -570,33 +298,6 @@ hipError_t launch_small_t_tt(const SmallTArgs& a, const SmallTPlan& p, hipStream
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_s8_tile(const S8Args& a, hipStream_t st) {
-  dim3 grid((a.N + BN - 1) / BN, (a.T + BM - 1) / BM);
-  dim3 block((BM / WM) * (BN / WN) * 64);
-  const bool dbg = a.acc_out != nullptr;
-  if (a.G == 128) {
-    if (dbg)
-      hipLaunchKernelGGL((tern_s8_kernel<BM, BN, WM, WN, 2, true>), grid, block, 0, st, a.q,
-                         a.act_scale, a.T, a.K, (const uint32_t*)a.codes, a.scales, a.y,
-                         a.acc_out, a.N);
-    else
-      hipLaunchKernelGGL((tern_s8_kernel<BM, BN, WM, WN, 2, false>), grid, block, 0, st, a.q,
-                         a.act_scale, a.T, a.K, (const uint32_t*)a.codes, a.scales, a.y,
-                         a.acc_out, a.N);
-  } else {
-    if (dbg)
-      hipLaunchKernelGGL((tern_s8_kernel<BM, BN, WM, WN, 4, true>), grid, block, 0, st, a.q,
-                         a.act_scale, a.T, a.K, (const uint32_t*)a.codes, a.scales, a.y,
-                         a.acc_out, a.N);
-    else
-      hipLaunchKernelGGL((tern_s8_kernel<BM, BN, WM, WN, 4, false>), grid, block, 0, st, a.q,
-                         a.act_scale, a.T, a.K, (const uint32_t*)a.codes, a.scales, a.y,
-                         a.acc_out, a.N);
-  }
-  return hipGetLastError();
-}
-
 }  // namespace
 
 int small_t_lds_bytes(int tokens_per_tile, int strips, int waves, int K) {
@@ -616,21 +317,6 @@ int launch_small_t(const SmallTArgs& a, const SmallTPlan& p, void* stream) {
     return (int)hipErrorInvalidValue;
   if (p.tokens_per_tile == 1) return (int)launch_small_t_tt<1>(a, p, st);
   if (p.tokens_per_tile == 16) return (int)launch_small_t_tt<16>(a, p, st);
-  return (int)hipErrorInvalidValue;
-}
-
-int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, void* stream) {
-  if (T <= 0) return 0;
-  hipLaunchKernelGGL(tern_quant_s8_kernel, dim3(T), dim3(256), 0, (hipStream_t)stream, x, K, q,
-                     scale);
-  return (int)hipGetLastError();
-}
-
-int launch_s8(const S8Args& a, const S8Plan& p, void* stream) {
-  hipStream_t st = (hipStream_t)stream;
-  if (p.bm == 128 && p.bn == 128) return (int)launch_s8_tile<128, 128, 64, 64>(a, st);
-  if (p.bm == 64 && p.bn == 64) return (int)launch_s8_tile<64, 64, 32, 32>(a, st);
-  if (p.bm == 32 && p.bn == 64) return (int)launch_s8_tile<32, 64, 16, 32>(a, st);
   return (int)hipErrorInvalidValue;
 }
 

@@ -1,0 +1,374 @@
+// tern_s8.hip -- gfx950 kernels of the s8 rung: per-token int8 activation
+// quantisation and the int8 x ternary contraction on the i8 matrix cores.
+// Built with the MFMA results kept in VGPRs (the fp32 scale epilogue reads
+// every accumulator), see build.py.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tern_device.h"
+#include "tern_internal.h"
+
+namespace tern {
+namespace {
+using namespace dev;
+
+// --------------------------------------------------------------------------
+// per-token int8 activation quantisation
+// --------------------------------------------------------------------------
+
+// Max over the 64 lanes of a wavefront of non-negative float bit patterns
+// (integer order equals float order for them). DPP inside each row of 16
+// lanes, then the four row results through readlane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ uint32_t quant_byte(uint32_t xbits, float sc) {
+  const float r = rintf(__uint_as_float(xbits) / sc);  // IEEE division, ties-to-even rounding
+  const float c = fminf(fmaxf(r, -127.f), 127.f);
+  return (uint32_t)((int)c) & 0xffu;
+}
+
+// The s8 kernel's operand order inside every 64-byte k-block kb: byte
+// 16g + 4i + beta holds k = 64kb + 8g + kmap(i, beta) with
+// kmap(i, .) = {32 + 2i, 2i, 33 + 2i, 2i + 1}. It is the order in which
+// (word << 2i) & 0xC0C0C0C0 lays out the codes of a packed weight word (see
+// weights_operand_i8), so activations stored this way feed the MFMA as is.
+// From the natural order (lo = bytes 8g..8g+7, hi = bytes 32+8g..32+8g+7 of
+// the block) each dword is one byte permute.
+__device__ __forceinline__ u32x4 s8_operand_order(uint32_t L0, uint32_t L1, uint32_t H0,
+                                                  uint32_t H1) {
+  return u32x4{__builtin_amdgcn_perm(H0, L0, 0x01050004u), __builtin_amdgcn_perm(H0, L0, 0x03070206u),
+               __builtin_amdgcn_perm(H1, L1, 0x01050004u), __builtin_amdgcn_perm(H1, L1, 0x03070206u)};
+}
+
+// Per-token quantisation. One block per token: absmax (DPP wave reduction,
+// then across the 4 waves), scale = absmax / 127, then the codes. PERM writes
+// them in the s8 operand order (K % 64 == 0), otherwise row-major.
+template <bool PERM>
+__global__ void __launch_bounds__(256) tern_quant_s8_kernel(const uint16_t* __restrict__ x, int K,
+                                                            int8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+  __shared__ uint32_t wmax[4];
+  const int t = blockIdx.x;
+  const uint4* xr = (const uint4*)(x + (size_t)t * K);
+  const int nchunk = K >> 3;
+  uint32_t m = 0;
+  for (int c = threadIdx.x; c < nchunk; c += 256) {
+    const uint4 v = xr[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = max(m, (w[i] << 16) & 0x7fff0000u);
+      m = max(m, w[i] & 0x7fff0000u);
+    }
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const uint32_t am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float a = __uint_as_float(am);
+  const float sc = a / 127.0f;  // IEEE single division
+  if (threadIdx.x == 0) scale[t] = am == 0 ? 0.0f : sc;
+  auto codes8 = [&](const uint4 v, uint32_t& lo, uint32_t& hi) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b[2 * i] = quant_byte(w[i] << 16, sc);
+      b[2 * i + 1] = quant_byte(w[i] & 0xffff0000u, sc);
+    }
+    lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  };
+  if (!PERM) {
+    uint2* qr = (uint2*)(q + (size_t)t * K);
+    for (int c = threadIdx.x; c < nchunk; c += 256) {
+      uint2 out = uint2{0u, 0u};
+      if (am != 0) codes8(xr[c], out.x, out.y);
+      qr[c] = out;
+    }
+  } else {
+    // output chunk j (16 bytes) = group g = j & 3 of 64-byte block j >> 2
+    u32x4* qr = (u32x4*)(q + (size_t)t * K);
+    for (int j = threadIdx.x; j < (K >> 4); j += 256) {
+      u32x4 out = u32x4{0u, 0u, 0u, 0u};
+      if (am != 0) {
+        const int blk = j >> 2, g = j & 3;
+        uint32_t L0, L1, H0, H1;
+        codes8(xr[blk * 8 + g], L0, L1);      // k = 64 blk + 8g .. +7
+        codes8(xr[blk * 8 + 4 + g], H0, H1);  // k = 64 blk + 32 + 8g .. +7
+        out = s8_operand_order(L0, L1, H0, H1);
+      }
+      qr[j] = out;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// s8 kernel: int8 activations x ternary weights on the i8 matrix cores
+// --------------------------------------------------------------------------
+//
+// Block: 4 waves, tile of 64 tokens x 256 outputs; wave w owns the 64 x 64
+// block of outputs [64w, 64w + 64) = 4 strips, as 4 x 4 v_mfma_i32_16x16x64_i8
+// tiles (A = activations, rows = tokens; B = weights, columns = outputs).
+// Per 256-wide k-tile:
+//  * the block's 64 x 256 activation tile goes to LDS (double buffered) by
+//    direct buffer-to-LDS loads, rows of 256 bytes with the 16-byte chunks of
+//    row r stored at chunk index (c ^ (r & 15)) so that the 16 rows of an
+//    operand fragment read without bank conflicts; the 4 waves share it;
+//  * each wave reads its own 4 strips' packed codes with one 16-byte load per
+//    lane per strip -- exactly the lane's B-operand codes -- and decodes each
+//    word into an MFMA operand with one shift and one mask per 4 weights:
+//    (word << 2i) & 0xC0C0C0C0 leaves every code in bits 7:6 of a byte, i.e.
+//    the int8 value 64*w. The MFMA accumulates 64*acc (|64*acc| <= 64*127*G,
+//    exact in int32 and in fp32), and the 2^-6 goes into the fp32 scale:
+//    fma(float(64*acc), s/64, total) rounds exactly like fma(acc, s, total);
+//  * epilogue per scale group and strip: total = fma(float(acc), s[n][g],
+//    total), groups ascending; at the end y = total * scale_t.
+
+constexpr int kS8BM = 64;
+
+__device__ __forceinline__ i32x4 weights_operand_i8(uint32_t word) {
+  return i32x4{(int)(word & 0xC0C0C0C0u), (int)((word << 2) & 0xC0C0C0C0u),
+               (int)((word << 4) & 0xC0C0C0C0u), (int)((word << 6) & 0xC0C0C0C0u)};
+}
+
+template <int GPT>
+struct S8Stage {
+  u32x4 code[4];            // the lane's 16 bytes of each of the wave's 4 strips
+  uint32_t sw[4][GPT / 2];  // fp16 scale pairs of row (lane & 15) of each strip
+};
+
+template <int GPT, bool DEBUG_ACC, bool QPERM>
+__global__ void __launch_bounds__(256) tern_s8_kernel(const int8_t* __restrict__ q,
+                                                      const float* __restrict__ act_scale, int T,
+                                                      int K, const u32x4* __restrict__ codes,
+                                                      const uint16_t* __restrict__ scales,
+                                                      float* __restrict__ y,
+                                                      int32_t* __restrict__ acc_out, int N) {
+  __shared__ __attribute__((aligned(1024))) int8_t As[2][kS8BM * 256];
+  constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int NS = N >> 4;
+  const int KT = K >> 8;
+  const int NG = K / (256 / GPT);
+  const int t0 = blockIdx.y * kS8BM;
+  const int nt = min(kS8BM, T - t0);
+  const int st0 = blockIdx.x * 16 + wave * 4;  // first strip of this wave
+  const int nst = max(0, min(4, NS - st0));     // strips of this wave that exist
+
+  const rsrc_t qr = make_rsrc(q + (size_t)t0 * K, (uint32_t)nt * K);
+  const rsrc_t cr = make_rsrc(codes + (size_t)min(st0, NS) * KT * 64, (uint32_t)nst * KT * 1024);
+  const rsrc_t sr = make_rsrc(scales + (size_t)min(st0, NS) * KT * 16 * GPT,
+                              (uint32_t)nst * KT * 16 * GPT * 2);
+
+  // Activation staging. QPERM (q already in operand order): wave w loads rows
+  // 16w .. 16w+15 with 4 direct-to-LDS loads of 4 rows each; lane i of load j
+  // writes LDS chunk (row 16w + 4j + i/16, chunk i % 16) and so fetches the
+  // global chunk (i % 16) ^ (row & 15). Otherwise (row-major q): thread ->
+  // (row, 64-byte block), byte permute in registers, then ds_write.
+  const int qrow_d = 16 * wave + (lane >> 4);  // + 4j
+  auto stage_a_direct = [&](int kt, int buf) {
+    kt = __builtin_amdgcn_readfirstlane(kt);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = qrow_d + 4 * j;
+      const int chunk = (lane & 15) ^ (row & 15);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qr, (__attribute__((address_space(3))) void*)&As[buf][(16 * wave + 4 * j) * 256], 16,
+          row * K + chunk * 16, kt * 256, 0, kAuxNontemporal);
+    }
+  };
+  const int arow = tid >> 2, ablk = tid & 3;
+  auto load_a_regs = [&](int kt, u32x4 (&v)[4]) {
+    kt = __builtin_amdgcn_readfirstlane(kt);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           qr, arow * K + ablk * 64 + 16 * c, kt * 256, 0));
+  };
+  auto store_a_regs = [&](int buf, const u32x4 (&v)[4]) {
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const u32x4 lo = v[gg >> 1], hi = v[2 + (gg >> 1)];
+      const int d = (gg & 1) * 2;
+      const int chunk = (ablk * 4 + gg) ^ (arow & 15);
+      *(u32x4*)&As[buf][arow * 256 + chunk * 16] =
+          s8_operand_order(lo[d], lo[d + 1], hi[d], hi[d + 1]);
+    }
+  };
+  auto load_w = [&](int kt, S8Stage<GPT>& b) {
+    kt = __builtin_amdgcn_readfirstlane(kt);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int je = min(j, max(nst - 1, 0));
+      b.code[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, lane * 16, (je * KT + kt) * 1024,
+                                                       kAuxNontemporal));
+      const int soff = (je * KT + kt) * 16 * GPT * 2;
+      if (GPT == 2) {
+        b.sw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(sr, r * GPT * 2, soff, 0);
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, r * GPT * 2, soff, 0);
+        b.sw[j][0] = v[0];
+        b.sw[j][GPT / 2 - 1] = v[1];
+      }
+    }
+  };
+
+  f32x4 tot[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tot[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int kt, int buf, const S8Stage<GPT>& b) {
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      // A fragments of this group's k-blocks, reused by the 4 strips
+      i32x4 af[KBPG][4];
+#pragma unroll
+      for (int kk = 0; kk < KBPG; ++kk)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int row = a * 16 + r;
+          const int chunk = (4 * (gi * KBPG + kk) + g) ^ r;  // row & 15 == r
+          af[kk][a] = *(const i32x4*)&As[buf][row * 256 + chunk * 16];
+        }
+      const int gidx = kt * GPT + gi;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        i32x4 acc[4];
+#pragma unroll
+        for (int kk = 0; kk < KBPG; ++kk) {
+          const i32x4 bf = weights_operand_i8(b.code[c][gi * KBPG + kk]);
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            acc[a] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                af[kk][a], bf, kk == 0 ? i32x4{0, 0, 0, 0} : acc[a], 0, 0, 0);
+        }
+        const int n = (st0 + c) * 16 + r;  // accumulator column of this lane
+        if (DEBUG_ACC) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int tl = a * 16 + 4 * g + i;
+              if (tl < nt && c < nst)
+                acc_out[((size_t)(t0 + tl) * N + n) * NG + gidx] = acc[a][i] >> 6;
+            }
+        } else {
+          const uint32_t sp = b.sw[c][gi >> 1];
+          const float sv =
+              half_bits_to_float((uint16_t)((gi & 1) ? (sp >> 16) : (sp & 0xffffu))) * 0.015625f;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              tot[a][c][i] = __builtin_fmaf((float)acc[a][i], sv, tot[a][c][i]);
+        }
+      }
+    }
+  };
+
+  // Pipeline, one barrier per k-tile: the activation tile of k-tile kt+1 and
+  // the codes/scales of kt+1 are requested before the MFMAs of k-tile kt;
+  // then the wave waits for its loads and meets the others at the barrier,
+  // after which every wave's part of tile kt+1 is in LDS and nobody reads
+  // tile kt's buffer any more. Past the last k-tile the loads repeat it.
+  S8Stage<GPT> wA, wB;
+  u32x4 av[4];
+  if (QPERM) {
+    stage_a_direct(0, 0);
+  } else {
+    load_a_regs(0, av);
+  }
+  load_w(0, wA);
+  if (!QPERM) store_a_regs(0, av);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+    const int k1 = min(kt + 1, KT - 1);
+    if (QPERM) stage_a_direct(k1, 1); else load_a_regs(k1, av);
+    load_w(k1, wB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt, 0, wA);
+    if (!QPERM) store_a_regs(1, av);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 >= KT) break;
+    const int k2 = min(kt + 2, KT - 1);
+    if (QPERM) stage_a_direct(k2, 0); else load_a_regs(k2, av);
+    load_w(k2, wA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt + 1, 1, wB);
+    if (!QPERM) store_a_regs(0, av);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (!DEBUG_ACC) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tl = a * 16 + 4 * g + i;
+        if (tl >= nt) continue;
+        const float as = act_scale[t0 + tl];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (c < nst) y[(size_t)(t0 + tl) * N + (st0 + c) * 16 + r] = tot[a][c][i] * as;
+      }
+  }
+}
+
+template <bool DEBUG_ACC, bool QPERM>
+hipError_t launch_s8_v(const S8Args& a, hipStream_t st) {
+  const int NS = a.N / 16;
+  dim3 grid((NS + 15) / 16, (a.T + kS8BM - 1) / kS8BM);
+  if (a.G == 128)
+    hipLaunchKernelGGL((tern_s8_kernel<2, DEBUG_ACC, QPERM>), grid, dim3(256), 0, st, a.q,
+                       a.act_scale, a.T, a.K, (const u32x4*)a.codes, a.scales, a.y, a.acc_out, a.N);
+  else
+    hipLaunchKernelGGL((tern_s8_kernel<4, DEBUG_ACC, QPERM>), grid, dim3(256), 0, st, a.q,
+                       a.act_scale, a.T, a.K, (const u32x4*)a.codes, a.scales, a.y, a.acc_out, a.N);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
+                    void* stream) {
+  if (T <= 0) return 0;
+  if (operand_order)
+    hipLaunchKernelGGL(tern_quant_s8_kernel<true>, dim3(T), dim3(256), 0, (hipStream_t)stream, x, K,
+                       q, scale);
+  else
+    hipLaunchKernelGGL(tern_quant_s8_kernel<false>, dim3(T), dim3(256), 0, (hipStream_t)stream, x,
+                       K, q, scale);
+  return (int)hipGetLastError();
+}
+
+int launch_s8(const S8Args& a, const S8Plan& p, void* stream) {
+  (void)p;
+  hipStream_t st = (hipStream_t)stream;
+  const bool dbg = a.acc_out != nullptr;
+  if (dbg)
+    return (int)(a.q_operand_order ? launch_s8_v<true, true>(a, st) : launch_s8_v<true, false>(a, st));
+  return (int)(a.q_operand_order ? launch_s8_v<false, true>(a, st) : launch_s8_v<false, false>(a, st));
+}
+
+}  // namespace tern

@@ -62,6 +62,20 @@ def run(tl, torch, x_dev, W, rung):
     return y.cpu().numpy()
 
 
+def operand_order(q):
+    """Rearrange row-major int8 codes into the documented s8 operand order:
+    byte 64b + 16g + 4i + e of a row holds k = 64b + 8g + m(i, e)."""
+    T, K = q.shape
+    src = np.empty(64, np.int64)
+    for g in range(4):
+        for i in range(4):
+            for e, m in enumerate((32 + 2 * i, 2 * i, 33 + 2 * i, 2 * i + 1)):
+                src[16 * g + 4 * i + e] = 8 * g + m
+    assert sorted(src.tolist()) == list(range(64))
+    idx = (np.arange(K // 64)[:, None] * 64 + src[None, :]).reshape(-1)
+    return q[:, idx]
+
+
 def check_s8(tl, torch, xbits, x_dev, W, w, s, y, rows=None):
     """q/scale bit-exact, acc bit-exact, y within 1e-6 (and bit-exact to the
     fixed fp32 order the kernel documents)."""
@@ -76,10 +90,18 @@ def check_s8(tl, torch, xbits, x_dev, W, w, s, y, rows=None):
     assert rel_l2(ycols, ref) <= S8_GATE
     ordered = oracle.linear_s8_fp32_ordered(q_ref, sc_ref, ws, ss)
     assert np.array_equal(ycols.view(np.uint32), ordered.view(np.uint32))
-    # the same contraction on the pre-quantised activations
+    # the same contraction on the pre-quantised activations, in both layouts
     y2 = tl.linear_s8_q(q, sc, W)
     torch.cuda.synchronize()
     assert np.array_equal(y2.cpu().numpy().view(np.uint32), y.view(np.uint32))
+    if q_ref.shape[1] % 64 == 0:
+        qo, sco = tl.quant_act_s8(x_dev, layout="operand_order")
+        torch.cuda.synchronize()
+        assert np.array_equal(qo.cpu().numpy(), operand_order(q_ref))
+        assert np.array_equal(sco.cpu().numpy().view(np.uint32), sc_ref.view(np.uint32))
+        y3 = tl.linear_s8_q(qo, sco, W, layout="operand_order")
+        torch.cuda.synchronize()
+        assert np.array_equal(y3.cpu().numpy().view(np.uint32), y.view(np.uint32))
 
 
 # ---------------------------------------------------------- small shape

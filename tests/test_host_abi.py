@@ -170,8 +170,10 @@ def test_linear_validation_happens_before_any_hip_call(tl):
     # nothing was counted by the probe
     assert all(v == 0 for v in tl.probe_snapshot().values())
     assert tl.last_rung() == "auto"
-    assert L.tern_quant_act_s8(None, 1, 256, 0x100000, 0x200000, None) == 1
-    assert L.tern_quant_act_s8(0x100000, 1, 100, 0x200000, 0x300000, None) == 2
+    assert L.tern_quant_act_s8(None, 1, 256, 0x100000, 0x200000, 0, None) == 1
+    assert L.tern_quant_act_s8(0x100000, 1, 100, 0x200000, 0x300000, 0, None) == 2
+    assert L.tern_quant_act_s8(0x100000, 1, 72, 0x200000, 0x300000, 1, None) == 2  # 64 | K
+    assert L.tern_quant_act_s8(0x100000, 1, 256, 0x200000, 0x300000, 7, None) == 4
 
 
 def _run_env(env_extra: dict, code: str) -> str:
