@@ -35,7 +35,8 @@ I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POPS
 MALL_BYTES = 256 * 2**20
 ROTATE_BYTES = 600e6  # > 2x the Infinity Cache
 METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
-KERNEL_SRC = os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", "tern_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
+               for f in ("tern_kernels.hip", "tern_s8.hip", "tern_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -49,8 +50,11 @@ def algorithmic_bytes(T, n, k, group):
 
 
 def kernel_source_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(kernel_key):
@@ -111,6 +115,37 @@ def cpu_baseline(wts_list, x_list, budget_s=12.0):
                       f"through oracle_linear_bf16 (fp64, single thread), {el:.1f} s"}
 
 
+def kernels_only(torch, ts, tl, dev, n):
+    """For rocprofv3 --pmc runs: n launches each of the gemv kernel (gate_up,
+    T=1) and the s8 rung (quant + contraction, gate_up, T=2048), weights
+    rotated over > 512 MB, then a plain 64 MiB device copy whose byte counters
+    calibrate FETCH_SIZE / WRITE_SIZE."""
+    w = ts.weights(ts.GATE_UP)
+    b = tl.TernaryWeights.from_host(w.w, w.s, device=dev)
+    sets = [b] + [tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group)
+                  for _ in range(max(1, math.ceil(ROTATE_BYTES / b.nbytes)) - 1)]
+    x1 = torch.from_numpy(ts.activations(w, 1).view(np.int16)).to(dev).view(torch.bfloat16)
+    y1 = torch.empty((1, b.n), dtype=torch.float32, device=dev)
+    T = 2048
+    x8 = torch.from_numpy(ts.activations(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
+    y8 = torch.empty((T, b.n), dtype=torch.float32, device=dev)
+    ws = torch.empty((tl.workspace_bytes(T, b.n, b.k, b.group),), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for i in range(n):
+        tl.linear(x1, sets[i % len(sets)], y=y1)
+    torch.cuda.synchronize()
+    for i in range(max(1, n // 10)):
+        tl.linear(x8, sets[i % len(sets)], y=y8, workspace=ws)
+    torch.cuda.synchronize()
+    src = torch.empty(64 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("kernels-only done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +154,9 @@ def main():
     ap.add_argument("--s8-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-s8", action="store_true")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="plain launches of the two dominant kernels and a 64 MiB copy, for "
+                         "rocprofv3 counter runs (no timing, no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the layer is not sharded across "
@@ -134,6 +172,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tl.lib()
+
+    if args.kernels_only:
+        kernels_only(torch, ts, tl, dev, args.steps)
+        return
 
     shapes = (ts.GATE_UP, ts.DOWN)
     log("drawing weights")
