@@ -36,7 +36,7 @@ MALL_BYTES = 256 * 2**20
 ROTATE_BYTES = 600e6  # > 2x the Infinity Cache
 METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
 KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
-               for f in ("tern_kernels.hip", "tern_s8.hip", "tern_device.h")]
+               for f in ("tern_kernels.hip", "tern_s8.hip", "tern_tile.hip", "tern_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

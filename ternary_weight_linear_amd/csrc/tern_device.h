@@ -49,5 +49,22 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
                                            0x00020000);
 }
 constexpr int kAuxNontemporal = 2;  // "nt": streamed once, do not keep in cache
+// A voffset past the end of every resource: the load is dropped and reads 0.
+constexpr int kOffPastEnd = 0x40000000;
+
+// Max over the 64 lanes of a wavefront of non-negative float bit patterns
+// (integer order equals float order for them). DPP inside each row of 16
+// lanes, then the four row results through readlane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
 }  // namespace dev
 }  // namespace tern

@@ -57,6 +57,7 @@ struct Config {
   int tune_strips = 0;                // TERN_TUNE_STRIPS (0 = heuristic)
   int tune_waves = 0;                 // TERN_TUNE_WAVES (0 = heuristic)
   int tune_s8_bm = 0;                 // TERN_TUNE_S8_BM (0 = heuristic)
+  int tune_kparts = 0;                // TERN_TUNE_KPARTS (0 = heuristic)
 };
 
 bool parse_int(const char* s, long lo, long hi, long* out) {
@@ -134,6 +135,12 @@ Config read_config() {
       c.tune_waves = (int)v;
     else
       bad("TERN_TUNE_WAVES", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_KPARTS")) {
+    if (parse_int(s, 0, 64, &v))
+      c.tune_kparts = (int)v;
+    else
+      bad("TERN_TUNE_KPARTS", s);
   }
   if (const char* s = getenv("TERN_TUNE_S8_BM")) {
     if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 64 || v == 128))
@@ -214,8 +221,32 @@ tern_status resolve(int T, tern_rung req, tern_rung* out) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t workspace_for(int T, int k, tern_rung r) {
+// Launch shape of the activation-tiled kernel (small_t, small_t_tiled), from
+// a sweep on MI355X over (S, Ws, Pk) at T = 4 and 16: one strip per wave;
+// wide layers (N >= 16k) take 4 waves per workgroup and no K split, narrower
+// ones 8 waves and K split 4 ways (partials through the workspace).
+tern::TilePlan plan_tile(int T, int n, int k) {
+  const Config& c = config();
+  tern::TilePlan p;
+  const int NS = n / 16, KT = k / 256;
+  const bool wide = NS >= 1024;
+  p.rows = T <= 8 ? 8 : 16;
+  p.strips_per_wave = c.tune_strips ? c.tune_strips : 1;
+  int Ws = c.tune_waves ? c.tune_waves : (wide ? 4 : 8);
+  Ws = std::min(Ws, 8);                    // launch bounds
+  if (p.rows == 16) Ws = std::max(Ws, 2);  // at most 4 activation load steps per wave
+  p.waves = Ws;
+  p.token_tiles = (T + 15) / 16;
+  p.strip_blocks = (NS + Ws * p.strips_per_wave - 1) / (Ws * p.strips_per_wave);
+  int Pk = c.tune_kparts ? c.tune_kparts : (wide ? 1 : 4);
+  p.k_parts = std::max(1, std::min(Pk, KT));
+  return p;
+}
+
+size_t workspace_for(int T, int n, int k, tern_rung r) {
   if (r == TERN_RUNG_S8) return align256((size_t)T * k) + align256((size_t)T * sizeof(float));
+  if (r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED)
+    return tern::tile_workspace_bytes(plan_tile(T, n, k), n);
   return 0;
 }
 
@@ -386,7 +417,7 @@ size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung) {
   if (check_shape(n, k, group) != TERN_OK) return (size_t)-1;
   tern_rung r;
   if (resolve(T, rung, &r) != TERN_OK) return (size_t)-1;
-  return workspace_for(T, k, r);
+  return workspace_for(T, n, k, r);
 }
 
 int tern_resolve_rung(int T, tern_rung rung) {
@@ -423,7 +454,7 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
   tern_rung r;
   st = resolve(T, rung, &r);
   if (st != TERN_OK) return st;
-  const size_t need = workspace_for(T, W->k, r);
+  const size_t need = workspace_for(T, W->n, W->k, r);
   if (need) {
     if (!ws || ws_bytes < need)
       return fail(TERN_ERR_WORKSPACE, "rung %s needs %zu bytes of workspace, got %zu%s",
@@ -441,8 +472,13 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
     if (err) return hip_fail(err, "s8 launch");
   } else {
     tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
-    int err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
-    if (err) return hip_fail(err, "small_t launch");
+    if (r == TERN_RUNG_GEMV) {
+      int err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
+      if (err) return hip_fail(err, "gemv launch");
+    } else {
+      int err = tern::launch_tile(a, plan_tile(T, n, k), ws, stream);
+      if (err) return hip_fail(err, "small_t launch");
+    }
   }
   probe_hit(r, T, n, k, G);
   return ok();

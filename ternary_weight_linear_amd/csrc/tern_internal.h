@@ -40,8 +40,22 @@ struct S8Args {
   bool q_operand_order;  // q is in the s8 operand order (from launch_quant_s8(..., true, ...))
 };
 
+// Launch shape of the activation-tiled small-T kernel (tern_tile.hip).
+struct TilePlan {
+  int rows;             // activation rows staged per tile: 8 (T <= 8) or 16
+  int strips_per_wave;  // S: 1, 2 or 4
+  int waves;            // Ws: waves per workgroup (1..8), each owning S strips
+  int strip_blocks;     // grid.x = ceil(NS / (Ws * S))
+  int k_parts;          // grid.y = Pk: K split across workgroups (partials in the workspace)
+  int token_tiles;      // grid.z = ceil(T / 16)
+};
+
 // All launchers return 0 on success or a hipError_t value.
 int launch_small_t(const SmallTArgs& a, const SmallTPlan& p, void* stream);
+// ws: tile_workspace_bytes(p, N) bytes of fp32 partials (k_parts > 1, added
+// by a second kernel); may be NULL when that is 0.
+int launch_tile(const SmallTArgs& a, const TilePlan& p, void* ws, void* stream);
+size_t tile_workspace_bytes(const TilePlan& p, int N);
 // Largest waves-per-block the bf16 kernel accepts for this variant (LDS and
 // register limits; 0 if none fits).
 int small_t_max_waves(int tokens_per_tile, int strips, int K);

@@ -67,9 +67,6 @@ struct SmallTAddr {
   int nstrips;    // strips of this block that exist (<= S)
 };
 
-// A voffset past the end of every resource: the load is dropped and reads 0.
-constexpr int kOffPastEnd = 0x40000000;
-
 template <int TT, int S, int GPT>
 __device__ __forceinline__ void small_t_load(SmallTStage<TT, S, GPT>& b, const SmallTAddr& a,
                                              int kt, bool valid) {

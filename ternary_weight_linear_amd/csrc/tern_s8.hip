@@ -16,21 +16,6 @@ using namespace dev;
 // per-token int8 activation quantisation
 // --------------------------------------------------------------------------
 
-// Max over the 64 lanes of a wavefront of non-negative float bit patterns
-// (integer order equals float order for them). DPP inside each row of 16
-// lanes, then the four row results through readlane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(a, b), max(c, d));
-}
-
 __device__ __forceinline__ uint32_t quant_byte(uint32_t xbits, float sc) {
   const float r = rintf(__uint_as_float(xbits) / sc);  // IEEE division, ties-to-even rounding
   const float c = fminf(fmaxf(r, -127.f), 127.f);

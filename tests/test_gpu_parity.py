@@ -355,3 +355,55 @@ def test_launch_shapes_keep_parity(strips, waves, G):
     assert r.returncode == 0, r.stderr[-2000:]
     worst = float(r.stdout.split("WORST")[1])
     assert worst <= 1e-6, worst
+
+
+# ------------------------------------- activation dynamic range (bf16 rungs)
+
+
+def _range_case(name, T, k, rng):
+    if name == "outliers":
+        x = rng.standard_normal((T, k)).astype(np.float32)
+        x[:, rng.choice(k, 20, replace=False)] *= 1000.0
+        x[:, rng.choice(k, 40, replace=False)] *= 1e-5
+    elif name == "subnormal":
+        # magnitudes around the bf16 subnormal range (2^-133 .. 2^-120)
+        x = (rng.standard_normal((T, k)) * 2.0 ** -126).astype(np.float32)
+    elif name == "wide":
+        # log-uniform over 16 decades, random signs
+        x = (10.0 ** rng.uniform(-8, 8, (T, k)) * rng.choice([-1, 1], (T, k))).astype(np.float32)
+    elif name == "huge":
+        x = (rng.standard_normal((T, k)) * 1e30).astype(np.float32)
+    else:
+        raise ValueError(name)
+    xb = ts.f32_to_bf16_bits(x)
+    xb[0, :] = 0  # an all-zero token row
+    return xb
+
+
+@pytest.mark.parametrize("case", ["outliers", "subnormal", "wide", "huge"])
+def test_bf16_rungs_activation_range(tl, torch, case):
+    """Per-element bound on every bf16-activation rung for activation rows
+    with extreme ranges. Products w*x are exact and sums are fp32, so the
+    error of each output is a bounded number of fp32 roundings of
+    sum_k |s w x| (at most 2^-16 of it here, K = 2048); the
+    gemv kernel's three-piece bf8 split adds at most 2^-30 * absmax(x_t) per
+    activation that lies more than 2^22 below absmax(x_t)."""
+    n, k, G, T = 256, 2048, 128, 3
+    rng = np.random.default_rng(["outliers", "subnormal", "wide", "huge"].index(case) + 77)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.draw_scales(rng, n, k, G)
+    xb = _range_case(case, T, k, rng)
+    W = tl.TernaryWeights.from_host(w, s)
+    x_dev = to_dev_bf16(torch, xb)
+    ref = oracle.linear_bf16(xb, w, s)
+    xf = ts.bf16_bits_to_f32(xb).astype(np.float64)
+    sw = np.abs(w.astype(np.float64) * np.repeat(ts.f16_bits_to_f32(s).astype(np.float64), G, axis=1))
+    absdot = np.abs(xf) @ sw.T                                   # [T, n]
+    amax = np.abs(xf).max(axis=1, keepdims=True)                 # [T, 1]
+    bound = 2.0 ** -16 * absdot + 2.0 ** -29 * amax * sw.sum(axis=1)[None, :]
+    for rung in ("gemv", "small_t", "small_t_tiled"):
+        y = run(tl, torch, x_dev, W, rung).astype(np.float64)
+        assert np.all(np.isfinite(y)), rung
+        assert np.all(y[0] == 0), rung
+        err = np.abs(y - ref)
+        assert np.all(err <= bound), (rung, float((err / np.maximum(bound, 1e-300)).max()))
