@@ -157,7 +157,10 @@ tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float
 
 /*
  * Device workspace tern_linear needs for this call (bytes, 0 if none). The s8
- * rung keeps the int8 activations and their scales there. Every scratch
+ * rung keeps the int8 activations and their scales there; small_t and
+ * small_t_tiled keep fp32 partial sums there when they split K across
+ * workgroups (narrow layers; then a second kernel adds the parts in a fixed
+ * order). The contents need no initialisation and are not preserved. Every scratch
  * buffer of every rung is counted here; a call given less fails with
  * TERN_ERR_WORKSPACE ("NINFER ternary perf-tuning" notes, section 5 item 8:
  * the workspace capacity declaration must cover every scratch).
