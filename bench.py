@@ -115,6 +115,56 @@ def cpu_baseline(wts_list, x_list, budget_s=12.0):
                       f"through oracle_linear_bf16 (fp64, single thread), {el:.1f} s"}
 
 
+def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
+    """The 64-layer stack (q, k, v, o 5120->5120; gate, up 5120->17408; down
+    17408->5120 per layer): one T=1 decode pass (448 calls) and one
+    2048-token prefill in two 1024-token chunks (896 s8 calls), each pass
+    captured in one graph and timed over several replays. Every layer has its
+    own device copy of the weights (6.3 GB resident, streamed from HBM each
+    pass); the copies are layer 0's matrices, drawn with layer 0's seeds."""
+    base, xs1, xsp = [], [], []
+    for proj in range(len(ts.STACK_PROJ)):
+        w = ts.weights(ts.stack_shape(0, proj))
+        base.append(tl.TernaryWeights.from_host(w.w, w.s, device=dev))
+        xs1.append(torch.from_numpy(ts.activations(w, 1).view(np.int16)).to(dev).view(torch.bfloat16))
+        xsp.append(torch.from_numpy(ts.activations(w, 2048).view(np.int16)).to(dev).view(torch.bfloat16))
+    layers = [base] + [[tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group)
+                        for b in base] for _ in range(ts.STACK_LAYERS - 1)]
+    nbytes = sum(b.nbytes for L in layers for b in L)
+    y1 = [torch.empty((1, b.n), dtype=torch.float32, device=dev) for b in base]
+    yp = [torch.empty((1024, b.n), dtype=torch.float32, device=dev) for b in base]
+    wsz = max(tl.workspace_bytes(1024, b.n, b.k, b.group) for b in base)
+    wsp = torch.empty((wsz,), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"stack: {ts.STACK_LAYERS} layers x {len(base)} projections, {nbytes / 1e9:.2f} GB resident")
+
+    def decode_pass(_):
+        for L in layers:
+            for j, b in enumerate(L):
+                tl.linear(xs1[j], b, y=y1[j])
+
+    def prefill_pass(_):
+        for c in range(2):
+            for L in layers:
+                for j, b in enumerate(L):
+                    tl.linear(xsp[j][1024 * c:1024 * (c + 1)], b, y=yp[j], workspace=wsp)
+
+    t_dec = graph_time(torch, decode_pass, decode_reps, 1) / decode_reps
+    ops = sum(2 * 2048 * b.n * b.k for L in layers for b in L)
+    t_pre = graph_time(torch, prefill_pass, prefill_reps, 1) / prefill_reps
+    dec_bytes = sum(algorithmic_bytes(1, b.n, b.k, b.group) for L in layers for b in L)
+    log(f"stack decode pass {t_dec * 1e3:.3f} ms ({dec_bytes / t_dec / 1e9:.0f} GB/s), "
+        f"prefill pass {t_pre * 1e3:.2f} ms ({ops / t_pre / 1e12:.0f} TOPS)")
+    return {"workload": "64-layer stack, 448 projections (6.33 GB packed); decode T=1 pass; "
+                        "2048-token prefill in two 1024-token chunks (s8)",
+            "decode": {"ms_per_pass": round(t_dec * 1e3, 4), "GB/s": round(dec_bytes / t_dec / 1e9, 1),
+                       "frac_of_hbm_peak": round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4),
+                       "launches": ts.STACK_LAYERS * len(base)},
+            "prefill": {"ms_per_pass": round(t_pre * 1e3, 3), "TOPS": round(ops / t_pre / 1e12, 1),
+                        "frac_of_i8_peak": round(ops / t_pre / 1e12 / I8_PEAK_TOPS, 4),
+                        "tokens_per_s": round(2048 / t_pre, 1)}}
+
+
 def kernels_only(torch, ts, tl, dev, n):
     """For rocprofv3 --pmc runs: n launches each of the gemv kernel (gate_up,
     T=1) and the s8 rung (quant + contraction, gate_up, T=2048), weights
@@ -154,6 +204,7 @@ def main():
     ap.add_argument("--s8-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-s8", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 64-layer stack passes")
     ap.add_argument("--kernels-only", action="store_true",
                     help="plain launches of the two dominant kernels and a 64 MiB copy, for "
                          "rocprofv3 counter runs (no timing, no JSON line)")
@@ -266,6 +317,12 @@ def main():
                            "kernel": f"tern_s8_kernel on {dom}, T={T}"}}
         log(f"s8 prefill step {el8 / K8 * 1e3:.3f} ms, {tops:.1f} TOPS")
 
+    stack = None
+    if not args.no_stack:
+        del sets  # the rotation copies; the stack holds 6.3 GB of its own
+        torch.cuda.empty_cache()
+        stack = stack_leg(torch, ts, tl, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -278,7 +335,7 @@ def main():
                                   "ternary weights (2-bit packed), fp16 scale per 128, bf16 x",
                       "T": 1, "rotation_sets": nsets, "bytes_per_step": step_bytes,
                       "per_shape": per_shape, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-           "roofline": roofline, "s8_prefill": s8, "cpu_baseline": cpu}
+           "roofline": roofline, "s8_prefill": s8, "stack": stack, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
 
