@@ -1,5 +1,6 @@
 // tern_device.h -- device-side helpers shared by the gfx950 kernels of this
-// library (tern_kernels.hip, tern_s8.hip). Internal, not installed.
+// library (tern_kernels.hip, tern_s8.hip, tern_tile.hip, tern_limb.hip).
+// Internal, not installed.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,6 +32,14 @@ __device__ __forceinline__ bf16x8 weights_operand(const uint4& P, int m) {
   b.z = code_pair(word, j0 + 2);
   b.w = code_pair(word, j0 + 3);
   return __builtin_bit_cast(bf16x8, b);
+}
+
+// int8 B operand of v_mfma_i32_16x16x64_i8 from one packed code word (16
+// weights): (word << 2i) & 0xC0C0C0C0 leaves every code in bits 7:6 of a byte,
+// i.e. the int8 value 64*w (01 -> 64, 11 -> -64, 00 -> 0).
+__device__ __forceinline__ i32x4 weights_operand_i8(uint32_t word) {
+  return i32x4{(int)(word & 0xC0C0C0C0u), (int)((word << 2) & 0xC0C0C0C0u),
+               (int)((word << 4) & 0xC0C0C0C0u), (int)((word << 6) & 0xC0C0C0C0u)};
 }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));

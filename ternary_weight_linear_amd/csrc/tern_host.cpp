@@ -58,6 +58,10 @@ struct Config {
   int tune_waves = 0;                 // TERN_TUNE_WAVES (0 = heuristic)
   int tune_s8_bm = 0;                 // TERN_TUNE_S8_BM (0 = heuristic)
   int tune_kparts = 0;                // TERN_TUNE_KPARTS (0 = heuristic)
+  int tune_wn = 0;                    // TERN_TUNE_WN (0 = heuristic)
+  int tune_wk = 0;                    // TERN_TUNE_WK (0 = heuristic)
+  int tune_depth = 0;                 // TERN_TUNE_DEPTH (0 = heuristic)
+  bool gemv_bf16 = false;             // TERN_TUNE_GEMV=bf16: time the bf16-operand gemv kernel (default: limb)
 };
 
 bool parse_int(const char* s, long lo, long hi, long* out) {
@@ -141,6 +145,30 @@ Config read_config() {
       c.tune_kparts = (int)v;
     else
       bad("TERN_TUNE_KPARTS", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_WN")) {
+    if (parse_int(s, 0, 16, &v))
+      c.tune_wn = (int)v;
+    else
+      bad("TERN_TUNE_WN", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_WK")) {
+    if (parse_int(s, 0, 16, &v))
+      c.tune_wk = (int)v;
+    else
+      bad("TERN_TUNE_WK", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_DEPTH")) {
+    if (parse_int(s, 0, 8, &v) && (v == 0 || v == 2 || v == 4 || v == 8))
+      c.tune_depth = (int)v;
+    else
+      bad("TERN_TUNE_DEPTH", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_GEMV")) {
+    if (strcmp(s, "bf16") == 0)
+      c.gemv_bf16 = true;
+    else if (strcmp(s, "limb") != 0)
+      bad("TERN_TUNE_GEMV", s);
   }
   if (const char* s = getenv("TERN_TUNE_S8_BM")) {
     if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 64 || v == 128))
@@ -276,6 +304,32 @@ tern::SmallTPlan plan_small_t(int T, int n, int k, int group, tern_rung r) {
   p.strips_per_wave = S;
   p.waves = W;
   return p;
+}
+
+// Launch shape of the integer-limb decode kernel, from a sweep on MI355X at
+// T = 1 over (waves per strip group, K shares, ring depth): wide layers (>= 1024
+// strips) take four waves per workgroup, one strip each over the whole K;
+// narrow layers two strips per workgroup with K split 8 ways (K >= 12288) or
+// 4 ways, so that the few strips still give every SIMD several waves. Every
+// wave keeps 4 k-tiles of codes in flight.
+tern::LimbPlan plan_limb(int T, int n, int k) {
+  (void)T;
+  const Config& c = config();
+  tern::LimbPlan p;
+  const int NS = n / 16, KT = k / 256;
+  const bool wide = NS >= 1024;
+  p.strips_per_wave = c.tune_strips ? c.tune_strips : 1;
+  p.wn = c.tune_wn ? c.tune_wn : (wide ? 4 : 2);
+  p.wk = c.tune_wk ? c.tune_wk : (wide ? 1 : (KT >= 48 ? 8 : 4));
+  p.wk = std::min(p.wk, KT);
+  while (p.wn * p.wk > 16) --p.wn;
+  p.depth = c.tune_depth ? c.tune_depth : (p.strips_per_wave == 1 ? 4 : 2);
+  return p;
+}
+
+// The integer-limb kernel takes T <= 5 with its activation limbs in LDS.
+bool limb_fits(int T, int k, int group, const tern::LimbPlan& p) {
+  return T <= 5 && tern::limb_lds_bytes(T, k, group, p) <= tern::kLimbMaxLds;
 }
 
 tern::S8Plan plan_s8(int T) {
@@ -473,7 +527,12 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
   } else {
     tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
     if (r == TERN_RUNG_GEMV) {
-      int err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
+      const tern::LimbPlan fp = plan_limb(T, n, k);
+      int err;
+      if (!config().gemv_bf16 && limb_fits(T, k, G, fp))
+        err = tern::launch_limb(a, fp, stream);
+      else
+        err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
       if (err) return hip_fail(err, "gemv launch");
     } else {
       int err = tern::launch_tile(a, plan_tile(T, n, k), ws, stream);

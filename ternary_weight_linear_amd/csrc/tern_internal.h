@@ -50,12 +50,24 @@ struct TilePlan {
   int token_tiles;      // grid.z = ceil(T / 16)
 };
 
+// Launch shape of the integer-limb decode kernel (tern_limb.hip), T <= 5.
+struct LimbPlan {
+  int strips_per_wave;  // S: 1, 2 or 4
+  int wn;               // strip groups per workgroup (waves own different strips)
+  int wk;               // K shares per workgroup (waves split the k-tiles); wn * wk <= 16
+  int depth;            // k-tiles of codes in flight per wave: 2, 4 or 8
+};
+constexpr int kLimbMaxLds = 65536;
+
 // All launchers return 0 on success or a hipError_t value.
 int launch_small_t(const SmallTArgs& a, const SmallTPlan& p, void* stream);
 // ws: tile_workspace_bytes(p, N) bytes of fp32 partials (k_parts > 1, added
 // by a second kernel); may be NULL when that is 0.
 int launch_tile(const SmallTArgs& a, const TilePlan& p, void* ws, void* stream);
 size_t tile_workspace_bytes(const TilePlan& p, int N);
+// T <= 5 tokens; needs limb_lds_bytes(T, K, G, p) <= kLimbMaxLds.
+int launch_limb(const SmallTArgs& a, const LimbPlan& p, void* stream);
+int limb_lds_bytes(int T, int K, int G, const LimbPlan& p);
 // Largest waves-per-block the bf16 kernel accepts for this variant (LDS and
 // register limits; 0 if none fits).
 int small_t_max_waves(int tokens_per_tile, int strips, int K);

@@ -1,0 +1,402 @@
+// tern_limb.hip -- decode kernel for up to five tokens (the T = 1 gemv rung)
+// on the gfx950 integer matrix cores.
+//
+// y[t][n] = sum_g s[n][g] * sum_{k in g} w[n][k] * x[t][k], w in {-1,0,+1},
+// one fp16 scale per G weights along K ("NInfer sm_89 fork" article, section
+// 9 item 2); T = 1 is the decode rung of the rung map ("NINFER ternary
+// perf-tuning" notes, section 2).
+//
+// At T = 1 the layer reads every weight once and does one multiply-add with
+// it, so what competes with the HBM stream is turning packed codes into
+// matrix-core operands (the notes, section 6, measure that decode arithmetic
+// as a quarter of the kernel time on their card). Decoded as int8 for
+// v_mfma_i32_16x16x64_i8, a 32-bit code word becomes four operand registers
+// with one AND and three shift+AND pairs -- 7 ALU operations per 16 weights,
+// against 15 for bf16 operands.
+//
+// The bf16 activations then have to enter the integer MFMA exactly. Every
+// 256-wide k-tile of a token is turned into fixed point relative to its own
+// largest magnitude: with 2^E <= max|x| < 2^(E+1) over the tile and d = E - 21,
+// v = rne(x * 2^-d) is an integer with |v| <= 2^22, exact for every activation
+// within 2^14 of the tile maximum (bf16 carries 8 significant bits) and within
+// 2^(d-1) <= 2^-22 * max|x| otherwise. v is split into three balanced int8
+// limbs v = l0 + 256 l1 + 65536 l2 (l0, l1 in [-128, 127], |l2| <= 64) that
+// occupy A rows 3t, 3t+1, 3t+2, so five tokens fit one 16-row operand. The
+// MFMA sums 64 * w * l exactly in int32 (codes decode to +-64), and per scale
+// group the fp32 epilogue adds s * 2^(d - 6 + 8L) * acc to the total of row
+// 3t + L, so that every partial sum carries its true magnitude (this keeps
+// tiny activations out of the fp32 denormal range). At the end
+//   y[t][n] = (R[3t+2] + R[3t+1]) + R[3t]
+// with R the per-row fp32 totals. The only approximations are the fixed-point
+// rounding above and fp32 accumulation over the groups; the integer part is
+// exact (the mixed-format fp8/fp4 matrix core would decode cheaper still, but
+// it sums each run of 8 products with about 13 bits below their largest one,
+// which loses small activations next to large ones).
+//
+// Operand order: limb rows are stored in LDS in the order of the s8 rung's
+// quantised activations (include/tern.h, TERN_Q_OPERAND_ORDER): inside each
+// 64-wide k-block, byte 16g + 4i + e holds k = 8g + m(i, e), m(i, .) =
+// {32+2i, 2i, 33+2i, 2i+1}, which is how weights_operand_i8 lays out the codes
+// of packed layout v1. Lane 16g + r then reads its 16-byte A operand for
+// k-block b at row r, offset 64b + 16g.
+//
+// Work split. A workgroup owns Wn*S strips of 16 outputs over the whole K; its
+// Wn*Wk waves take S strips each over a 1/Wk share of the k-tiles (wide layers
+// use Wk = 1, narrow ones split K so that enough waves stream). Each wave keeps
+// D k-tiles of codes in flight; the partial sums of the Wk shares are added
+// through LDS in a fixed order (deterministic, no atomics).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "tern_device.h"
+#include "tern_internal.h"
+
+namespace tern {
+namespace {
+using namespace dev;
+
+template <int S>
+struct LimbStage {
+  u32x4 P[S];  // the lane's 16 code bytes of each of the wave's strips
+};
+
+// Largest |x| over 8 bf16 (as fp32 bit patterns: integer order = magnitude order).
+__device__ __forceinline__ uint32_t absmax8(const u32x4& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max((v[i] << 16) & 0x7fff0000u, v[i] & 0x7fff0000u));
+  return m;
+}
+
+// Max over the 16 lanes of a DPP row (each lane ends with the row's max).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+  return v;
+}
+
+// Fixed-point bits of one activation: f = x * 2^-d + 1.5 * 2^23 rounds x * 2^-d
+// to the nearest integer v (ties to even) and holds 0x4B400000 + v. The limb
+// bytes are then byte 0 of f, byte 1 of f + 128 and byte 2 of f + 32896 -
+// 0x400000 (balanced base-256 digits of v; the 0x4B400000 offset does not
+// reach bytes 0 and 1 and is taken out of byte 2).
+struct LimbSrc {
+  uint32_t u0, u1, u2;
+};
+__device__ __forceinline__ LimbSrc limb_src(uint32_t xbits_f32, int d) {
+  const float f = __builtin_ldexpf(__uint_as_float(xbits_f32), -d) + 12582912.0f;
+  const uint32_t b = __float_as_uint(f);
+  return LimbSrc{b, b + 128u, b - 0x3F7F80u};
+}
+
+// Operand-order dword from four elements' limb sources: bytes [ya, xa, yb, xb]
+// at byte position L of each (x = k 2i, 2i+1 of the low half, y = k 32+2i,
+// 33+2i of the high half of the 64-wide block).
+template <int L>
+__device__ __forceinline__ uint32_t limb_dword(uint32_t xa, uint32_t xb, uint32_t ya, uint32_t yb) {
+  constexpr uint32_t sel = (4u + L) | ((uint32_t)L << 8) | 0x0c0c0000u;
+  const uint32_t p = __builtin_amdgcn_perm(ya, xa, sel);  // [ya.L, xa.L, 0, 0]
+  const uint32_t q = __builtin_amdgcn_perm(yb, xb, sel);  // [yb.L, xb.L, 0, 0]
+  return __builtin_amdgcn_perm(q, p, 0x05040100u);        // [ya.L, xa.L, yb.L, xb.L]
+}
+
+// TT: 1 (single token: rows 0..2) or 5 (T <= 5 tokens: rows 0..3T-1).
+// Dynamic LDS (limb_lds_bytes): 3T limb rows of K + 16 bytes, the tile
+// exponents d [T][K/256] (int), then the workgroup's scales in their packed
+// order [strip][k-tile][row][group]; all of it is reused for the final
+// reduction.
+template <int TT, int S, int GPT, int D>
+__global__ void __launch_bounds__(1024) tern_limb_kernel(
+    const uint16_t* __restrict__ x, int T, int K, const u32x4* __restrict__ codes,
+    const uint16_t* __restrict__ scales, float* __restrict__ y, int N, int Wn, int Wk) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  static_assert(GPT == 2 || GPT == 4, "G must be 128 or 64");
+  constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nth = blockDim.x;
+  const int NS = N >> 4, KT = K >> 8;
+  const int wn = wave % Wn, wk = wave / Wn;
+  const int strip0 = (blockIdx.x * Wn + wn) * S;
+  const int nstrips = min(S, NS - strip0);  // <= 0: this wave only helps with the activations
+  const int kt0 = (wk * KT) / Wk;
+  const int nkt = ((wk + 1) * KT) / Wk - kt0;
+  const int NR = 3 * T;  // A rows in use
+  const int rs = K + 16;  // LDS bytes per limb row (padded)
+  const int r = lane & 15, g = lane >> 4;
+  const int SB = Wn * S;                      // strips of the workgroup
+  const int wstrip0 = blockIdx.x * SB;
+  const int nsb = min(SB, NS - wstrip0);      // of which exist
+  int* dexp = (int*)(smem + (size_t)NR * rs);  // [T][KT]
+  char* lsc = smem + (size_t)NR * rs + (size_t)T * KT * 4;  // [SB][KT][16][GPT] fp16
+
+  const rsrc_t xr = make_rsrc(x, (uint32_t)T * K * 2);
+  // The workgroup's scales, 16-byte chunks (2*GPT per strip and k-tile).
+  const int nsc = nsb * KT * 2 * GPT;
+  const rsrc_t wsr = make_rsrc(scales + (size_t)wstrip0 * KT * 16 * GPT, (uint32_t)nsc * 16);
+
+  // 1. The activations are requested first, so that they do not queue behind
+  //    the weight stream. Chunk c covers token c / (K/16), k-block j >> 2 and
+  //    lane group j & 3 (j = c mod K/16): natural k = 64(j>>2) + 8(j&3) + 0..7
+  //    (lo) and + 32 (hi). The 16 chunks of a k-tile sit in one DPP row.
+  const int KC16 = K >> 4;
+  const int nchunk = T * KC16;
+  auto chunk_x = [&](int c, u32x4& lo, u32x4& hi) {
+    const int t = c / KC16, j = c - t * KC16;
+    const int base = t * K + 64 * (j >> 2) + 8 * (j & 3);
+    lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, base * 2, 0, 0));
+    hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (base + 32) * 2, 0, 0));
+  };
+  // Up to two chunks and two scale chunks per thread are requested up front.
+  u32x4 xpre[2][2], spre[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (tid + it * nth < nchunk) chunk_x(tid + it * nth, xpre[it][0], xpre[it][1]);
+    if (tid + it * nth < nsc)
+      spre[it] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wsr, (tid + it * nth) * 16, 0, 0));
+  }
+
+  // 2. Weight prefetch ring: the first D - 1 k-tiles of this wave's strips.
+  //    (The codes are read once: non-temporal.)
+  const int sclamp = max(min(strip0, NS - 1), 0);
+  const rsrc_t crs = make_rsrc(codes + (size_t)sclamp * KT * 64, (uint32_t)max(nstrips, 0) * KT * 1024);
+  auto load = [&](LimbStage<S>& b, int i) {
+    const int kt = __builtin_amdgcn_readfirstlane(min(kt0 + i, KT - 1));
+    const int cv = i < nkt ? lane * 16 : kOffPastEnd;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int se = max(min(s, nstrips - 1), 0);
+      b.P[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             crs, cv, (se * KT + kt) * 1024, kAuxNontemporal));
+    }
+  };
+  LimbStage<S> ring[D];
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) load(ring[j], j);
+
+  // 3. Limbs into LDS: per chunk, the k-tile maximum over its DPP row, the
+  //    exponent shift d, then three 16-byte limb chunks (rows 3t + L, byte
+  //    offset 16j). Rows of 16 lanes are wholly inside or outside [0, nchunk)
+  //    since nchunk and the thread count are multiples of 16.
+  for (int c0 = 0; c0 < nchunk; c0 += nth) {
+    const int c = c0 + tid;
+    u32x4 lo, hi;
+    if (c0 == 0) {
+      lo = xpre[0][0];
+      hi = xpre[0][1];
+    } else if (c0 == nth) {
+      lo = xpre[1][0];
+      hi = xpre[1][1];
+    } else if (c < nchunk) {
+      chunk_x(c, lo, hi);
+    }
+    if (c < nchunk) {
+      const uint32_t m = row16_max_u32(max(absmax8(lo), absmax8(hi)));
+      const int d = (int)(m >> 23) - 127 - 21;
+      const int t = c / KC16, j = c - t * KC16;
+      u32x4 out0, out1, out2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const LimbSrc xa = limb_src(lo[i] << 16, d), xb = limb_src(lo[i] & 0xffff0000u, d);
+        const LimbSrc ya = limb_src(hi[i] << 16, d), yb = limb_src(hi[i] & 0xffff0000u, d);
+        out0[i] = limb_dword<0>(xa.u0, xb.u0, ya.u0, yb.u0);
+        out1[i] = limb_dword<1>(xa.u1, xb.u1, ya.u1, yb.u1);
+        out2[i] = limb_dword<2>(xa.u2, xb.u2, ya.u2, yb.u2);
+      }
+      char* row = smem + (size_t)(3 * t) * rs + 16 * j;
+      *(u32x4*)row = out0;
+      *(u32x4*)(row + rs) = out1;
+      *(u32x4*)(row + 2 * rs) = out2;
+      if ((j & 15) == 0) dexp[t * KT + (j >> 4)] = d;
+    }
+  }
+  for (int c = tid; c < nsc; c += nth) {
+    const u32x4 v = c < nth ? spre[0]
+                  : c < 2 * nth ? spre[1]
+                                : __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wsr, c * 16, 0, 0));
+    *(u32x4*)(lsc + 16 * c) = v;
+  }
+  __syncthreads();
+
+  // 4. Main loop. Lanes whose A row is unused (r >= NR) read row 0 again;
+  //    their output rows are never read. Row q of this lane's accumulators
+  //    (q = 4g + e) belongs to token q / 3.
+  f32x4 total[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) total[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const char* abase = smem + (size_t)(r < NR ? r : 0) * rs + 16 * g;
+  int tok[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) tok[e] = TT == 1 ? 0 : min((4 * g + e) / 3, T - 1);
+  // Scales of this wave's strips in LDS: strip s, k-tile kt, row r.
+  const char* wsc = lsc + ((size_t)(wn * S) * KT * 16 + r) * GPT * 2;
+  auto compute = [&](const LimbStage<S>& b, int i) {
+    const int kt = kt0 + i;
+    i32x4 a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = *(const i32x4*)(abase + 64 * (4 * kt + q));
+    // TT = 1: the three limbs of the token are accumulators 0..2 of lanes
+    // 0..15; they are combined per group in fp32, (65536 a2 + 256 a1) + a0,
+    // and 2^(d - 6) then undoes the fixed point and the 64x code decode.
+    // TT = 5: each row keeps its own total, scaled by 2^(d - 6 + 8L) (limb
+    // L = row mod 3) so that every partial sum carries its true magnitude.
+    int dsh[4];
+    if (TT == 1) {
+      dsh[0] = dexp[kt] - 6;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsh[e] = dexp[tok[e] * KT + kt] - 6 + 8 * ((4 * g + e) % 3);
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const u32x4 P = b.P[s];
+      uint32_t sw[GPT / 2];
+      const char* sp = wsc + ((size_t)s * KT + kt) * 16 * GPT * 2;
+      if (GPT == 2) {
+        sw[0] = *(const uint32_t*)sp;
+      } else {
+        const uint2 v = *(const uint2*)sp;
+        sw[0] = v.x;
+        sw[GPT / 2 - 1] = v.y;
+      }
+#pragma unroll
+      for (int gi = 0; gi < GPT; ++gi) {
+        i32x4 acc = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KBPG; ++kk) {
+          const int q = gi * KBPG + kk;
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[q], weights_operand_i8(P[q]), acc, 0, 0, 0);
+        }
+        const uint32_t spair = sw[gi >> 1];
+        const float sc = half_bits_to_float((uint16_t)((gi & 1) ? (spair >> 16) : (spair & 0xffffu)));
+        if (TT == 1) {
+          const float v = __builtin_fmaf(65536.0f, (float)acc[2], 256.0f * (float)acc[1]) + (float)acc[0];
+          total[s][0] = __builtin_fmaf(sc, __builtin_ldexpf(v, dsh[0]), total[s][0]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            total[s][e] = __builtin_fmaf(sc, __builtin_ldexpf((float)acc[e], dsh[e]), total[s][e]);
+        }
+      }
+    }
+  };
+  int i = 0;
+  for (; i + D <= nkt; i += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      load(ring[(j + D - 1) % D], i + j + D - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ring[j], i + j);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j)
+    if (i + j < nkt) compute(ring[j], i + j);
+
+  // 5. y. Accumulator e of lane l is row 4(l >> 4) + e, column l & 15. With
+  //    one token and no K split, lanes 0..15 hold finished outputs. Otherwise
+  //    a fixed-order reduction over the Wk shares through LDS (the limbs,
+  //    exponents and scales are no longer read).
+  if (TT == 1 && Wk == 1) {
+    if (lane < 16) {
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (s < nstrips) y[(size_t)(strip0 + s) * 16 + lane] = total[s][0];
+    }
+    return;
+  }
+  __syncthreads();
+  float* red = (float*)smem;  // [Wk][Wn*S strips][16 rows][16 columns]
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    float* dst = red + (((size_t)wk * SB + wn * S + s) * 16 + 4 * g) * 16 + r;
+    if (TT == 1) {
+      // the whole token sits in row 0 already (rows 1, 2 are zero)
+      if (g == 0) {
+        dst[0] = total[s][0];
+        dst[16] = 0.f;
+        dst[32] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * g + e < NR) dst[e * 16] = total[s][e];
+    }
+  }
+  __syncthreads();
+  const int nout = T * SB * 16;
+  for (int e = tid; e < nout; e += nth) {
+    const int t = e / (SB * 16);
+    const int rem = e - t * (SB * 16);
+    const int ls = rem >> 4, col = rem & 15;
+    const int st = blockIdx.x * SB + ls;
+    if (st >= NS) continue;
+    float sum = 0.f;
+    for (int w = 0; w < Wk; ++w) {
+      const float* src = red + (((size_t)w * SB + ls) * 16 + 3 * t) * 16 + col;
+      sum += (src[32] + src[16]) + src[0];
+    }
+    y[(size_t)t * N + st * 16 + col] = sum;
+  }
+}
+
+template <int TT, int S, int GPT>
+hipError_t launch_limb_g(const SmallTArgs& a, const LimbPlan& p, hipStream_t st) {
+  const int NS = a.N / 16;
+  dim3 grid((NS + p.wn * S - 1) / (p.wn * S));
+  dim3 block(64 * p.wn * p.wk);
+  const size_t lds = (size_t)limb_lds_bytes(a.T, a.K, a.G, p);
+  switch (p.depth) {
+#define TERN_LIMB_LAUNCH(D)                                                                        \
+  case D:                                                                                          \
+    hipLaunchKernelGGL((tern_limb_kernel<TT, S, GPT, D>), grid, block, lds, st, a.x, a.T, a.K,     \
+                       (const u32x4*)a.codes, a.scales, a.y, a.N, p.wn, p.wk);                     \
+    break;
+    TERN_LIMB_LAUNCH(2)
+    TERN_LIMB_LAUNCH(4)
+    TERN_LIMB_LAUNCH(8)
+#undef TERN_LIMB_LAUNCH
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int TT, int S>
+hipError_t launch_limb_s(const SmallTArgs& a, const LimbPlan& p, hipStream_t st) {
+  return a.G == 128 ? launch_limb_g<TT, S, 2>(a, p, st) : launch_limb_g<TT, S, 4>(a, p, st);
+}
+
+template <int TT>
+hipError_t launch_limb_t(const SmallTArgs& a, const LimbPlan& p, hipStream_t st) {
+  switch (p.strips_per_wave) {
+    case 1: return launch_limb_s<TT, 1>(a, p, st);
+    case 2: return launch_limb_s<TT, 2>(a, p, st);
+    case 4: return launch_limb_s<TT, 4>(a, p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int limb_lds_bytes(int T, int K, int G, const LimbPlan& p) {
+  const size_t SB = (size_t)p.wn * p.strips_per_wave;
+  const size_t main = (size_t)3 * T * (K + 16) + (size_t)T * (K / 256) * 4 + SB * (K / 256) * 16 * (256 / G) * 2;
+  const size_t red = (size_t)p.wk * SB * 256 * 4;
+  return (int)std::max(main, red);
+}
+
+int launch_limb(const SmallTArgs& a, const LimbPlan& p, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int W = p.wn * p.wk;
+  if (a.T < 1 || a.T > 5 || p.wn < 1 || p.wk < 1 || W > 16) return (int)hipErrorInvalidValue;
+  if (limb_lds_bytes(a.T, a.K, a.G, p) > kLimbMaxLds) return (int)hipErrorInvalidValue;
+  return (int)(a.T == 1 ? launch_limb_t<1>(a, p, st) : launch_limb_t<5>(a, p, st));
+}
+
+}  // namespace tern

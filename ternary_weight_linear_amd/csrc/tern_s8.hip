@@ -122,10 +122,6 @@ __global__ void __launch_bounds__(256) tern_quant_s8_kernel(const uint16_t* __re
 
 constexpr int kS8BM = 64;
 
-__device__ __forceinline__ i32x4 weights_operand_i8(uint32_t word) {
-  return i32x4{(int)(word & 0xC0C0C0C0u), (int)((word << 2) & 0xC0C0C0C0u),
-               (int)((word << 4) & 0xC0C0C0C0u), (int)((word << 6) & 0xC0C0C0C0u)};
-}
 
 template <int GPT>
 struct S8Stage {

@@ -385,9 +385,10 @@ def test_bf16_rungs_activation_range(tl, torch, case):
     """Per-element bound on every bf16-activation rung for activation rows
     with extreme ranges. Products w*x are exact and sums are fp32, so the
     error of each output is a bounded number of fp32 roundings of
-    sum_k |s w x| (at most 2^-16 of it here, K = 2048); the
-    gemv kernel's three-piece bf8 split adds at most 2^-30 * absmax(x_t) per
-    activation that lies more than 2^22 below absmax(x_t)."""
+    sum_k |s w x| (at most 2^-16 of it here, K = 2048). The gemv kernel
+    carries each activation as a 22-bit fixed-point number relative to the
+    largest magnitude M of its 256-wide k-tile, which rounds it by at most
+    2^-22 * M; that adds sum over k-tiles of 2^-22 * M * sum_{k in tile} |s w|."""
     n, k, G, T = 256, 2048, 128, 3
     rng = np.random.default_rng(["outliers", "subnormal", "wide", "huge"].index(case) + 77)
     w = ts.draw_weights(rng, n, k, 0.4)
@@ -399,8 +400,9 @@ def test_bf16_rungs_activation_range(tl, torch, case):
     xf = ts.bf16_bits_to_f32(xb).astype(np.float64)
     sw = np.abs(w.astype(np.float64) * np.repeat(ts.f16_bits_to_f32(s).astype(np.float64), G, axis=1))
     absdot = np.abs(xf) @ sw.T                                   # [T, n]
-    amax = np.abs(xf).max(axis=1, keepdims=True)                 # [T, 1]
-    bound = 2.0 ** -16 * absdot + 2.0 ** -29 * amax * sw.sum(axis=1)[None, :]
+    tmax = np.abs(xf).reshape(T, k // 256, 256).max(axis=2)     # [T, k-tiles]
+    swt = sw.reshape(n, k // 256, 256).sum(axis=2)               # [n, k-tiles]
+    bound = 2.0 ** -16 * absdot + 2.0 ** -22 * (tmax @ swt.T)
     for rung in ("gemv", "small_t", "small_t_tiled"):
         y = run(tl, torch, x_dev, W, rung).astype(np.float64)
         assert np.all(np.isfinite(y)), rung
