@@ -6,8 +6,9 @@ rotated over enough device copies (> 512 MB) that every step streams them
 from HBM rather than from the 256 MiB Infinity Cache. The headline value is
 the whole step's algorithmic bytes per second (GB/s = 1e9 B/s). The same
 line reports the s8 prefill rung at T = 2048 on the same two shapes in int8
-TOPS, the roofline fraction of the dominant kernel of each, and the CPU
-oracle timed on the host as a baseline.
+TOPS, the draft-verify batches T = 2..16 in GB/s, the 64-layer stack, the
+roofline fraction of the dominant kernel of each, and the CPU oracle timed
+on the host as a baseline.
 
 Timing: the K timed steps are captured once into a HIP graph (PyTorch's
 CUDAGraph on ROCm) and replayed between HIP events recorded on the same
@@ -165,6 +166,46 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
                         "tokens_per_s": round(2048 / t_pre, 1)}}
 
 
+SMALL_T = (2, 4, 8, 12, 16)
+
+
+def small_t_leg(torch, ts, tl, dev, steps=100):
+    """The draft-verify batches: T in {2, 4, 8, 12, 16} through gate_up, down
+    and the 5120 -> 5120 out-projection with the rung the dispatcher picks
+    (small_t for T <= 8, small_t_tiled above), weights rotated over > 600 MB
+    so that they stream from HBM. Algorithmic bytes per launch as for T = 1
+    (codes + scales + x + y); GB/s is that over the event-timed launch."""
+    out = {}
+    for shape in (ts.GATE_UP, ts.DOWN, ts.OUT_PROJ):
+        w = ts.weights(shape)
+        base = tl.TernaryWeights.from_host(w.w, w.s, device=dev)
+        nsets = max(2, math.ceil(ROTATE_BYTES / base.nbytes))
+        sets = [base] + [tl.TernaryWeights(base.codes.clone(), base.scales.clone(), base.n, base.k,
+                                           base.group) for _ in range(nsets - 1)]
+        per_t = {}
+        for T in SMALL_T:
+            x = torch.from_numpy(ts.activations(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
+            y = torch.empty((T, shape.n), dtype=torch.float32, device=dev)
+            wsz = tl.workspace_bytes(T, shape.n, shape.k, shape.group)
+            wsp = torch.empty((max(1, wsz),), dtype=torch.uint8, device=dev)
+            rung = tl.resolve_rung(T)
+
+            def one(i):
+                tl.linear(x, sets[i % nsets], y=y, workspace=wsp)
+
+            t = graph_time(torch, one, steps, 5) / steps
+            b = algorithmic_bytes(T, shape.n, shape.k, shape.group)
+            per_t[f"T{T}"] = {"rung": rung, "us_per_launch": round(t * 1e6, 2),
+                              "GB/s": round(b / t / 1e9, 1),
+                              "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"  small-T {shape.name} T={T} ({rung}): {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s")
+        out[shape.name] = per_t
+        del sets, base
+        torch.cuda.empty_cache()
+    return {"workload": "draft-verify batches T in {2,4,8,12,16} on gate_up 5120->34816, "
+                        "down 17408->5120 and o_proj 5120->5120", "per_shape": out}
+
+
 def kernels_only(torch, ts, tl, dev, n):
     """For rocprofv3 --pmc runs: n launches each of the gemv kernel (gate_up,
     T=1) and the s8 rung (quant + contraction, gate_up, T=2048), weights
@@ -205,6 +246,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-s8", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 64-layer stack passes")
+    ap.add_argument("--no-small-t", action="store_true", help="skip the T = 2..16 batches")
     ap.add_argument("--kernels-only", action="store_true",
                     help="plain launches of the two dominant kernels and a 64 MiB copy, for "
                          "rocprofv3 counter runs (no timing, no JSON line)")
@@ -317,6 +359,10 @@ def main():
                            "kernel": f"tern_s8_kernel on {dom}, T={T}"}}
         log(f"s8 prefill step {el8 / K8 * 1e3:.3f} ms, {tops:.1f} TOPS")
 
+    small = None
+    if not args.no_small_t:
+        small = small_t_leg(torch, ts, tl, dev)
+
     stack = None
     if not args.no_stack:
         del sets  # the rotation copies; the stack holds 6.3 GB of its own
@@ -335,7 +381,8 @@ def main():
                                   "ternary weights (2-bit packed), fp16 scale per 128, bf16 x",
                       "T": 1, "rotation_sets": nsets, "bytes_per_step": step_bytes,
                       "per_shape": per_shape, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-           "roofline": roofline, "s8_prefill": s8, "stack": stack, "cpu_baseline": cpu}
+           "roofline": roofline, "s8_prefill": s8, "small_t": small, "stack": stack,
+           "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
 

@@ -62,6 +62,7 @@ struct Config {
   int tune_wk = 0;                    // TERN_TUNE_WK (0 = heuristic)
   int tune_depth = 0;                 // TERN_TUNE_DEPTH (0 = heuristic)
   bool gemv_bf16 = false;             // TERN_TUNE_GEMV=bf16: time the bf16-operand gemv kernel (default: limb)
+  int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave
 };
 
 bool parse_int(const char* s, long lo, long hi, long* out) {
@@ -170,6 +171,14 @@ Config read_config() {
     else if (strcmp(s, "limb") != 0)
       bad("TERN_TUNE_GEMV", s);
   }
+  if (const char* s = getenv("TERN_TUNE_SMALLT")) {
+    if (strcmp(s, "tile") == 0)
+      c.smallt_kernel = 1;
+    else if (strcmp(s, "wave") == 0)
+      c.smallt_kernel = 2;
+    else
+      bad("TERN_TUNE_SMALLT", s);
+  }
   if (const char* s = getenv("TERN_TUNE_S8_BM")) {
     if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 64 || v == 128))
       c.tune_s8_bm = (int)v;
@@ -271,9 +280,19 @@ tern::TilePlan plan_tile(int T, int n, int k) {
   return p;
 }
 
+// Kernel of the small_t / small_t_tiled rungs. Narrow layers (< 1024 strips)
+// give the activation-tiled kernel too few workgroups; there the per-wave
+// kernel (each wave loads its own activation fragments, no barriers) was
+// faster on MI355X for T <= 8, and for any T <= 16 when K <= 8192.
+bool small_t_per_wave(int T, int n, int k) {
+  const Config& c = config();
+  if (c.smallt_kernel) return c.smallt_kernel == 2;
+  return n / 16 < 1024 && (T <= 8 || k <= 8192);
+}
+
 size_t workspace_for(int T, int n, int k, tern_rung r) {
   if (r == TERN_RUNG_S8) return align256((size_t)T * k) + align256((size_t)T * sizeof(float));
-  if (r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED)
+  if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && !small_t_per_wave(T, n, k))
     return tern::tile_workspace_bytes(plan_tile(T, n, k), n);
   return 0;
 }
@@ -297,7 +316,7 @@ tern::SmallTPlan plan_small_t(int T, int n, int k, int group, tern_rung r) {
   // everywhere except wide 16-token tiles (S = 4, which share the activation
   // fragments across more strips).
   int W = (int)(4352.0 / (double)(nsb * (long)std::max(1, p.token_tiles)) + 0.5);
-  if (p.tokens_per_tile == 16 && NS >= 1024 && !c.tune_strips) W = 4;
+  if (p.tokens_per_tile == 16 && !c.tune_strips) W = 4;
   const int wmax = std::max(1, tern::small_t_max_waves(p.tokens_per_tile, S, k));
   W = std::max(1, std::min(W, std::min(wmax, KT)));
   if (c.tune_waves) W = std::max(1, std::min(std::min(c.tune_waves, wmax), KT));
@@ -534,6 +553,9 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
       else
         err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
       if (err) return hip_fail(err, "gemv launch");
+    } else if (small_t_per_wave(T, n, k)) {
+      int err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
+      if (err) return hip_fail(err, "small_t launch");
     } else {
       int err = tern::launch_tile(a, plan_tile(T, n, k), ws, stream);
       if (err) return hip_fail(err, "small_t launch");

@@ -105,7 +105,7 @@ __device__ __forceinline__ uint32_t limb_dword(uint32_t xa, uint32_t xb, uint32_
 }
 
 // TT: 1 (single token: rows 0..2) or 5 (T <= 5 tokens: rows 0..3T-1).
-// Dynamic LDS (limb_lds_bytes): 3T limb rows of K + 16 bytes, the tile
+// Dynamic LDS (limb_lds_bytes): 3T limb rows of K + 64 bytes, the tile
 // exponents d [T][K/256] (int), then the workgroup's scales in their packed
 // order [strip][k-tile][row][group]; all of it is reused for the final
 // reduction.
@@ -127,7 +127,8 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
   const int kt0 = (wk * KT) / Wk;
   const int nkt = ((wk + 1) * KT) / Wk - kt0;
   const int NR = 3 * T;  // A rows in use
-  const int rs = K + 16;  // LDS bytes per limb row (padded)
+  const int rs = K + 64;  // LDS bytes per limb row; the 64-byte pad puts the 12
+                          // A-operand reads of rows 0..2 on distinct banks
   const int r = lane & 15, g = lane >> 4;
   const int SB = Wn * S;                      // strips of the workgroup
   const int wstrip0 = blockIdx.x * SB;
@@ -291,6 +292,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       load(ring[(j + D - 1) % D], i + j + D - 1);
+      // keep the prefetch ahead of the MFMAs: the scheduler must not sink it
       __builtin_amdgcn_sched_barrier(0);
       compute(ring[j], i + j);
     }
@@ -386,7 +388,7 @@ hipError_t launch_limb_t(const SmallTArgs& a, const LimbPlan& p, hipStream_t st)
 
 int limb_lds_bytes(int T, int K, int G, const LimbPlan& p) {
   const size_t SB = (size_t)p.wn * p.strips_per_wave;
-  const size_t main = (size_t)3 * T * (K + 16) + (size_t)T * (K / 256) * 4 + SB * (K / 256) * 16 * (256 / G) * 2;
+  const size_t main = (size_t)3 * T * (K + 64) + (size_t)T * (K / 256) * 4 + SB * (K / 256) * 16 * (256 / G) * 2;
   const size_t red = (size_t)p.wk * SB * 256 * 4;
   return (int)std::max(main, red);
 }
