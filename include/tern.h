@@ -204,11 +204,13 @@ tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
 /*
  * Debug export of the s8 rung's integer group accumulators (device, async):
  * acc[t][n][g] = sum_{k in group g} q[t][k] * w[n][k], int32 [T][N][K/G].
- * Runs the s8 contraction kernel with its epilogue replaced by a store of the
- * accumulators, so the integer path can be checked bit for bit.
+ * Runs the s8 contraction kernel that tern_linear_s8_q runs for `layout`
+ * (TERN_Q_OPERAND_ORDER: the one tern_linear's s8 rung uses) with its
+ * epilogue replaced by a store of the accumulators, so the integer path can
+ * be checked bit for bit. q: device int8 [T][K] in `layout`, 16-byte aligned.
  */
 tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int32_t* acc_out,
-                              void* stream); /* q row-major */
+                              tern_q_layout layout, void* stream);
 
 /* Rung probe: number of kernel launches per rung since the last reset,
  * counted at the launch site of the kernel that actually ran. */

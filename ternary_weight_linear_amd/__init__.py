@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
         "tern_workspace_bytes": (sz, [i, i, i, i, i]),
         "tern_linear": (st, [p, i, ctypes.POINTER(_Weights), p, i, p, sz, p]),
         "tern_linear_s8_q": (st, [p, p, i, ctypes.POINTER(_Weights), p, i, p]),
-        "tern_debug_s8_acc": (st, [p, i, ctypes.POINTER(_Weights), p, p]),
+        "tern_debug_s8_acc": (st, [p, i, ctypes.POINTER(_Weights), p, i, p]),
         "tern_probe_snapshot": (None, [p]),
         "tern_probe_reset": (None, []),
         "tern_last_rung": (i, []),
@@ -286,13 +286,15 @@ def linear_s8_q(q, scale, W: TernaryWeights, y=None, stream=None, layout="row_ma
     return y
 
 
-def debug_s8_acc(q, W: TernaryWeights, acc=None, stream=None):
-    """int32 [T, N, K/G] group accumulators of the s8 contraction."""
+def debug_s8_acc(q, W: TernaryWeights, acc=None, stream=None, layout="row_major"):
+    """int32 [T, N, K/G] group accumulators of the s8 contraction on q in
+    `layout` (each layout runs its own kernel)."""
     torch = _torch()
     _dev(q, torch.int8, "q")
     T = q.shape[0]
     if acc is None:
         acc = torch.empty((T, W.n, W.k // W.group), dtype=torch.int32, device=q.device)
     _dev(acc, torch.int32, "acc")
-    _check(lib().tern_debug_s8_acc(q.data_ptr(), T, W.ref(), acc.data_ptr(), _stream(stream)))
+    _check(lib().tern_debug_s8_acc(q.data_ptr(), T, W.ref(), acc.data_ptr(), Q_LAYOUTS[layout],
+                                   _stream(stream)))
     return acc

@@ -57,6 +57,8 @@ struct Config {
   int tune_strips = 0;                // TERN_TUNE_STRIPS (0 = heuristic)
   int tune_waves = 0;                 // TERN_TUNE_WAVES (0 = heuristic)
   int tune_s8_bm = 0;                 // TERN_TUNE_S8_BM (0 = heuristic)
+  int tune_s8_strips = 0;             // TERN_TUNE_S8_STRIPS (0 = heuristic)
+  int tune_s8_raster = 0;             // TERN_TUNE_S8_RASTER: 0 heuristic, 1 plain, 2 xcd
   int tune_kparts = 0;                // TERN_TUNE_KPARTS (0 = heuristic)
   int tune_wn = 0;                    // TERN_TUNE_WN (0 = heuristic)
   int tune_wk = 0;                    // TERN_TUNE_WK (0 = heuristic)
@@ -180,10 +182,24 @@ Config read_config() {
       bad("TERN_TUNE_SMALLT", s);
   }
   if (const char* s = getenv("TERN_TUNE_S8_BM")) {
-    if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 64 || v == 128))
+    if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 64 || v == 128))  // tokens per wave tile
       c.tune_s8_bm = (int)v;
     else
       bad("TERN_TUNE_S8_BM", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_S8_STRIPS")) {
+    if (parse_int(s, 0, 4, &v) && (v == 0 || v == 2 || v == 4))
+      c.tune_s8_strips = (int)v;
+    else
+      bad("TERN_TUNE_S8_STRIPS", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_S8_RASTER")) {
+    if (strcmp(s, "plain") == 0)
+      c.tune_s8_raster = 1;
+    else if (strcmp(s, "xcd") == 0)
+      c.tune_s8_raster = 2;
+    else
+      bad("TERN_TUNE_S8_RASTER", s);
   }
   return c;
 }
@@ -351,13 +367,22 @@ bool limb_fits(int T, int k, int group, const tern::LimbPlan& p) {
   return T <= 5 && tern::limb_lds_bytes(T, k, group, p) <= tern::kLimbMaxLds;
 }
 
-tern::S8Plan plan_s8(int T) {
+tern::S8Plan plan_s8(int T, int n) {
   const Config& c = config();
   tern::S8Plan p;
-  int bm = T >= 128 ? 128 : (T >= 48 ? 64 : 32);
-  if (c.tune_s8_bm) bm = c.tune_s8_bm;
-  p.bm = bm;
-  p.bn = bm == 128 ? 128 : 64;
+  // Wave tile 64 tokens x 64 outputs (4 token blocks x 4 strips) where that
+  // still gives at least 4 workgroups per CU; 64 x 32 otherwise (narrow
+  // layers); 32-token tiles for short prefills so padded tokens do not waste
+  // the matrix cores. (128-token tiles cost registers, and occupancy, without
+  // paying back on either 27B-class shape.)
+  const int tb = c.tune_s8_bm ? c.tune_s8_bm / 16 : (T > 32 ? 4 : 2);
+  const long tiles4 = (long)((n / 16 + 15) / 16) * ((T + 16 * tb - 1) / (16 * tb));
+  int strips = tiles4 >= 1024 ? 4 : 2;
+  if (c.tune_s8_strips) strips = c.tune_s8_strips;
+  if (tb == 8) strips = 2;
+  p.token_blocks = tb;
+  p.strips = strips;
+  p.xcd_order = c.tune_s8_raster != 1;
   return p;
 }
 
@@ -541,7 +566,7 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
     int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, true, stream);
     if (err) return hip_fail(err, "quant_s8 launch");
     tern::S8Args a{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr, true};
-    err = tern::launch_s8(a, plan_s8(T), stream);
+    err = tern::launch_s8(a, plan_s8(T, n), stream);
     if (err) return hip_fail(err, "s8 launch");
   } else {
     tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
@@ -578,23 +603,26 @@ tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
   if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
   tern::S8Args a{q,       act_scale, T,       W->k,    W->n, W->group, W->codes,
                  W->scales, y,       nullptr, layout == TERN_Q_OPERAND_ORDER};
-  int err = tern::launch_s8(a, plan_s8(T), stream);
+  int err = tern::launch_s8(a, plan_s8(T, W->n), stream);
   if (err) return hip_fail(err, "s8 launch");
   probe_hit(TERN_RUNG_S8, T, W->n, W->k, W->group);
   return ok();
 }
 
 tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int32_t* acc_out,
-                              void* stream) {
+                              tern_q_layout layout, void* stream) {
   if (!q || !acc_out) return fail(TERN_ERR_NULL, "tern_debug_s8_acc: NULL pointer");
   tern_status st = check_weights(W);
   if (st != TERN_OK) return st;
   if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
+  if (layout != TERN_Q_ROW_MAJOR && layout != TERN_Q_OPERAND_ORDER)
+    return fail(TERN_ERR_VALUE, "unknown q layout %d", (int)layout);
   if (!aligned16(q)) return fail(TERN_ERR_ALIGN, "q must be 16-byte aligned");
   const Config& c = config();
   if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
-  tern::S8Args a{q, nullptr, T, W->k, W->n, W->group, W->codes, W->scales, nullptr, acc_out, false};
-  int err = tern::launch_s8(a, plan_s8(T), stream);
+  tern::S8Args a{q,       nullptr, T,      W->k, W->n, W->group, W->codes, W->scales,
+                 nullptr, acc_out, layout == TERN_Q_OPERAND_ORDER};
+  int err = tern::launch_s8(a, plan_s8(T, W->n), stream);
   if (err) return hip_fail(err, "s8 debug launch");
   return ok();
 }

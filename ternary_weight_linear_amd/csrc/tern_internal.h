@@ -23,10 +23,14 @@ struct SmallTArgs {
   float* y;  // [T][N]
 };
 
-// Launch shape of the s8 integer MFMA kernel.
+// Launch shape of the s8 integer MFMA kernel for operand-order activations
+// (tern_s8mma.hip): a wave tile of token_blocks x 16 tokens by strips x 16
+// outputs, (tb, s) in {(2,2), (2,4), (4,2), (4,4), (8,2)}. The kernel for
+// row-major activations (tern_s8.hip) has one fixed shape.
 struct S8Plan {
-  int bm;  // tokens per workgroup tile
-  int bn;  // outputs per workgroup tile
+  int token_blocks;
+  int strips;
+  bool xcd_order;  // give each XCD a contiguous run of tiles (else plain block order)
 };
 
 struct S8Args {
@@ -77,6 +81,7 @@ int small_t_lds_bytes(int tokens_per_tile, int strips, int waves, int K);
 int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
                     void* stream);
 int launch_s8(const S8Args& a, const S8Plan& p, void* stream);
+int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* stream);
 const char* hip_error_string(int err);
 
 }  // namespace tern

@@ -344,7 +344,7 @@ int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bo
 }
 
 int launch_s8(const S8Args& a, const S8Plan& p, void* stream) {
-  (void)p;
+  if (a.q_operand_order) return launch_s8_operand_order(a, p, stream);
   hipStream_t st = (hipStream_t)stream;
   const bool dbg = a.acc_out != nullptr;
   if (dbg)

@@ -1,0 +1,243 @@
+// tern_s8mma.hip -- the s8 rung's contraction for activations quantised in
+// the operand order (include/tern.h, TERN_Q_OPERAND_ORDER): int8 activations
+// x ternary weights on v_mfma_i32_16x16x64_i8, fp32 scale epilogue.
+//
+// y[t][n] = scale_t * sum_g s[n][g] * acc[t][n][g], acc = sum_{k in g} q[t][k] * w[n][k]
+// ("NInfer sm_89 fork" article, sections 7 and 9 item 2: prefill activations
+// quantised per token to int8, the product an integer contraction).
+//
+// Cost model on MI355X. Per 16x16 output tile and 128-wide scale group the
+// matrix core runs 2 MFMAs (32 cycles) and the vector ALU converts and scales
+// 4 accumulators per lane (8 instructions, about the same time); measured on
+// the part, the two units hardly overlap, so the kernel spends as little ALU
+// time per MFMA as it can:
+//  * wave tile TB x 16 tokens by S x 16 outputs (TB token blocks, S strips):
+//    each decoded weight operand feeds TB MFMAs, each A fragment S MFMAs;
+//  * the codes decode straight into int8 B operands, (word << 2i) &
+//    0xC0C0C0C0 = 64*w (weights_operand_i8); the 2^-6 goes into the scale, and
+//    fma(float(64*acc), s/64, total) rounds exactly like fma(acc, s, total);
+//  * the epilogue per group and accumulator is one convert and one fma, in
+//    ascending group order, then y = total * scale_t.
+// Workgroup: 4 waves share one TB x 16-token activation tile in LDS (double
+// buffered, filled by direct buffer-to-LDS loads; the 16-byte chunks of row r
+// sit at chunk ^ (r & 15) so that the 16 rows of a fragment read hits 16
+// different banks) and take S strips each.
+// Tile order (optional): workgroups go to the 8 XCDs round-robin; each XCD is
+// then given a contiguous run of tiles (output blocks fastest), so the
+// workgroups it runs at the same time share their activation tile in its L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tern_device.h"
+#include "tern_internal.h"
+
+namespace tern {
+namespace {
+using namespace dev;
+
+template <int GPT, int S>
+struct S8mStage {
+  u32x4 code[S];            // the lane's 16 code bytes of each strip
+  uint32_t sw[S][GPT / 2];  // fp16 scale pairs of row (lane & 15)
+};
+
+template <int GPT, int TB, int S, bool DEBUG_ACC>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) tern_s8m_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ act_scale, int T, int K,
+    const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int N, int nx, int ny, int per_xcd) {
+  constexpr int BM = 16 * TB;    // tokens per tile
+  constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
+  constexpr int kS8WgStrips = 4 * S;
+  __shared__ __attribute__((aligned(1024))) int8_t As[2][BM * 256];
+
+  // XCD-aware tile: block b runs on XCD b % 8 as its (b / 8)-th block there.
+  // (per_xcd == 0: plain order, tile = block index)
+  const int tile = per_xcd ? (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  if (tile >= nx * ny) return;  // uniform over the workgroup
+  const int ty = tile / nx, tx = tile - ty * nx;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int NS = N >> 4, KT = K >> 8, NG = K / (256 / GPT);
+  const int t0 = ty * BM;
+  const int nt = min(BM, T - t0);
+  const int st0 = tx * kS8WgStrips + wave * S;  // first strip of this wave
+  const int nst = max(0, min(S, NS - st0));     // of which exist
+
+  const rsrc_t qr = make_rsrc(q + (size_t)t0 * K, (uint32_t)nt * K);
+  const rsrc_t cr = make_rsrc(codes + (size_t)min(st0, NS) * KT * 64, (uint32_t)nst * KT * 1024);
+  const rsrc_t sr = make_rsrc(scales + (size_t)min(st0, NS) * KT * 16 * GPT,
+                              (uint32_t)nst * KT * 16 * GPT * 2);
+
+  // Activation tile kt into buffer buf: BM rows of 256 bytes, 4 rows per
+  // direct-to-LDS load (64 lanes x 16 bytes); wave w loads rows
+  // [w*4*TB, (w+1)*4*TB). Lane i of a load writes LDS chunk i % 16 of row
+  // base + i / 16 and fetches the row's global chunk (i % 16) ^ (row & 15).
+  // Rows past the last token read as zeros (buffer range check).
+  auto stage_a = [&](int kt, int buf) {
+    kt = __builtin_amdgcn_readfirstlane(kt);
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int rbase = wave * 4 * TB + 4 * j;
+      const int row = rbase + (lane >> 4);
+      const int chunk = (lane & 15) ^ (row & 15);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qr, (__attribute__((address_space(3))) void*)&As[buf][rbase * 256], 16, row * K + chunk * 16,
+          kt * 256, 0, kAuxNontemporal);
+    }
+  };
+  auto load_w = [&](int kt, S8mStage<GPT, S>& b) {
+    kt = __builtin_amdgcn_readfirstlane(kt);
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      const int ce = min(c, max(nst - 1, 0));
+      b.code[c] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, lane * 16, (ce * KT + kt) * 1024, kAuxNontemporal));
+      const int soff = (ce * KT + kt) * 16 * GPT * 2;
+      if (GPT == 2) {
+        b.sw[c][0] = __builtin_amdgcn_raw_buffer_load_b32(sr, r * GPT * 2, soff, 0);
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, r * GPT * 2, soff, 0);
+        b.sw[c][0] = v[0];
+        b.sw[c][1] = v[1];
+      }
+    }
+  };
+
+  f32x4 tot[TB][S];
+#pragma unroll
+  for (int a = 0; a < TB; ++a)
+#pragma unroll
+    for (int c = 0; c < S; ++c) tot[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One k-tile: per scale group, the A fragments of its k-blocks (shared by
+  // both strips), then per strip KBPG x TB MFMAs and the group's epilogue.
+  auto compute = [&](int kt, int buf, const S8mStage<GPT, S>& b) {
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      i32x4 af[KBPG][TB];
+#pragma unroll
+      for (int kk = 0; kk < KBPG; ++kk)
+#pragma unroll
+        for (int a = 0; a < TB; ++a) {
+          const int chunk = (4 * (gi * KBPG + kk) + g) ^ r;  // row & 15 == r
+          af[kk][a] = *(const i32x4*)&As[buf][(a * 16 + r) * 256 + chunk * 16];
+        }
+      const int gidx = kt * GPT + gi;
+#pragma unroll
+      for (int c = 0; c < S; ++c) {
+        i32x4 acc[TB];
+#pragma unroll
+        for (int kk = 0; kk < KBPG; ++kk) {
+          const i32x4 bf = weights_operand_i8(b.code[c][gi * KBPG + kk]);
+#pragma unroll
+          for (int a = 0; a < TB; ++a)
+            acc[a] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[kk][a], bf,
+                                                           kk == 0 ? i32x4{0, 0, 0, 0} : acc[a], 0, 0, 0);
+        }
+        if (DEBUG_ACC) {
+          const int n = (st0 + c) * 16 + r;  // accumulator column of this lane
+#pragma unroll
+          for (int a = 0; a < TB; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int tl = a * 16 + 4 * g + e;
+              if (tl < nt && c < nst) acc_out[((size_t)(t0 + tl) * N + n) * NG + gidx] = acc[a][e] >> 6;
+            }
+        } else {
+          const uint32_t sp = b.sw[c][gi >> 1];
+          const float sv = half_bits_to_float((uint16_t)((gi & 1) ? (sp >> 16) : (sp & 0xffffu))) * 0.015625f;
+#pragma unroll
+          for (int a = 0; a < TB; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tot[a][c][e] = __builtin_fmaf((float)acc[a][e], sv, tot[a][c][e]);
+        }
+      }
+    }
+  };
+
+  // Pipeline, one barrier per k-tile: the activation tile and the codes of
+  // k-tile kt+1 are requested before the MFMAs of k-tile kt; then each wave
+  // waits for its loads and meets the others at the barrier, after which
+  // tile kt+1 is complete in LDS and nobody reads tile kt's buffer any more.
+  // Past the last k-tile the loads repeat it.
+  S8mStage<GPT, S> wA, wB;
+  stage_a(0, 0);
+  load_w(0, wA);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+    const int k1 = min(kt + 1, KT - 1);
+    stage_a(k1, 1);
+    load_w(k1, wB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt, 0, wA);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 >= KT) break;
+    const int k2 = min(kt + 2, KT - 1);
+    stage_a(k2, 0);
+    load_w(k2, wA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt + 1, 1, wB);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (!DEBUG_ACC) {
+#pragma unroll
+    for (int a = 0; a < TB; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tl = a * 16 + 4 * g + e;
+        if (tl >= nt) continue;
+        const float as = act_scale[t0 + tl];
+#pragma unroll
+        for (int c = 0; c < S; ++c)
+          if (c < nst) y[(size_t)(t0 + tl) * N + (st0 + c) * 16 + r] = tot[a][c][e] * as;
+      }
+  }
+}
+
+template <int GPT, int TB, int S, bool DEBUG_ACC>
+hipError_t launch_s8m_t(const S8Args& a, bool xcd_order, hipStream_t st) {
+  constexpr int kS8WgStrips = 4 * S;
+  const int NS = a.N / 16;
+  const int nx = (NS + kS8WgStrips - 1) / kS8WgStrips;
+  const int ny = (a.T + 16 * TB - 1) / (16 * TB);
+  const int per_xcd = xcd_order ? (nx * ny + 7) / 8 : 0;
+  const int blocks = xcd_order ? 8 * per_xcd : nx * ny;
+  hipLaunchKernelGGL((tern_s8m_kernel<GPT, TB, S, DEBUG_ACC>), dim3(blocks), dim3(256), 0, st, a.q,
+                     a.act_scale, a.T, a.K, (const u32x4*)a.codes, a.scales, a.y, a.acc_out, a.N, nx,
+                     ny, per_xcd);
+  return hipGetLastError();
+}
+
+template <int GPT, bool DEBUG_ACC>
+hipError_t launch_s8m_g(const S8Args& a, int tb, int s, bool x, hipStream_t st) {
+  switch (tb * 16 + s) {
+    case 2 * 16 + 2: return launch_s8m_t<GPT, 2, 2, DEBUG_ACC>(a, x, st);
+    case 2 * 16 + 4: return launch_s8m_t<GPT, 2, 4, DEBUG_ACC>(a, x, st);
+    case 4 * 16 + 2: return launch_s8m_t<GPT, 4, 2, DEBUG_ACC>(a, x, st);
+    case 4 * 16 + 4: return launch_s8m_t<GPT, 4, 4, DEBUG_ACC>(a, x, st);
+    case 8 * 16 + 2: return launch_s8m_t<GPT, 8, 2, DEBUG_ACC>(a, x, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const bool dbg = a.acc_out != nullptr;
+  const int tb = p.token_blocks, s = p.strips;
+  const bool x = p.xcd_order;
+  if (a.G == 128)
+    return (int)(dbg ? launch_s8m_g<2, true>(a, tb, s, x, st) : launch_s8m_g<2, false>(a, tb, s, x, st));
+  return (int)(dbg ? launch_s8m_g<4, true>(a, tb, s, x, st) : launch_s8m_g<4, false>(a, tb, s, x, st));
+}
+
+}  // namespace tern

@@ -133,9 +133,11 @@ def test_small_case_s8_accumulators_bit_exact(tl, torch, small):
     wts, W = small
     xbits = ts.activations(wts, 4)
     q_ref, _ = oracle.quant_s8(xbits)
-    acc = tl.debug_s8_acc(torch.from_numpy(q_ref).cuda(), W)
-    torch.cuda.synchronize()
-    assert np.array_equal(acc.cpu().numpy(), oracle.s8_acc(q_ref, wts.w, 64))
+    expect = oracle.s8_acc(q_ref, wts.w, 64)
+    for layout, qh in (("row_major", q_ref), ("operand_order", operand_order(q_ref))):
+        acc = tl.debug_s8_acc(torch.from_numpy(np.ascontiguousarray(qh)).cuda(), W, layout=layout)
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), expect), layout
 
 
 # ------------------------------------------------ exact (integer) inputs
@@ -307,12 +309,18 @@ def test_prefill_s8_sampled(tl, torch, big, shape, T):
     y = run(tl, torch, x_dev, W, "auto")
     assert tl.resolve_rung(T) == "s8"
     check_s8(tl, torch, xbits, x_dev, W, wts.w, wts.s, y, rows=rows)
-    if T <= 36:
+    if T <= 36 or T == 508:
         q_ref, _ = oracle.quant_s8(xbits)
-        acc = tl.debug_s8_acc(torch.from_numpy(q_ref).cuda(), W)
-        torch.cuda.synchronize()
-        acc = acc.cpu().numpy()
-        assert np.array_equal(acc[:, rows], oracle.s8_acc(q_ref, wts.w[rows], 128))
+        expect = oracle.s8_acc(q_ref, wts.w[rows], 128)
+        layouts = (("operand_order", operand_order(q_ref)),)
+        if T <= 36:
+            layouts += (("row_major", q_ref),)
+        for layout, qh in layouts:
+            acc = tl.debug_s8_acc(torch.from_numpy(np.ascontiguousarray(qh)).cuda(), W, layout=layout)
+            torch.cuda.synchronize()
+            acc = acc.cpu().numpy()
+            assert np.array_equal(acc[:, rows], expect), layout
+            del acc
 
 
 # ------------------------------------------------ launch-shape variants
