@@ -37,7 +37,8 @@ MALL_BYTES = 256 * 2**20
 ROTATE_BYTES = 600e6  # > 2x the Infinity Cache
 METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
 KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
-               for f in ("tern_kernels.hip", "tern_s8.hip", "tern_tile.hip", "tern_device.h")]
+               for f in ("tern_kernels.hip", "tern_s8.hip", "tern_s8mma.hip", "tern_tile.hip",
+                         "tern_limb.hip", "tern_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -313,7 +314,7 @@ def main():
     traffic = stored_traffic(f"gemv:{dom}")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": f"tern_small_t_kernel (gemv rung, T=1) on {dom}",
+                "kernel": f"tern_limb_kernel (gemv rung, T=1) on {dom}",
                 "algorithmic_bytes_per_launch": per_shape[dom]["bytes"],
                 "us_per_launch": per_shape[dom]["us_per_launch"]}
 
@@ -356,7 +357,7 @@ def main():
               "roofline": {"bound": "mfma", "achieved": ach, "peak": I8_PEAK_TOPS, "unit": "TOPS",
                            "frac": round(ach / I8_PEAK_TOPS, 4),
                            "traffic": stored_traffic(f"s8:{dom}"),
-                           "kernel": f"tern_s8_kernel on {dom}, T={T}"}}
+                           "kernel": f"tern_s8m_kernel (s8 rung contraction) on {dom}, T={T}"}}
         log(f"s8 prefill step {el8 / K8 * 1e3:.3f} ms, {tops:.1f} TOPS")
 
     small = None

@@ -22,9 +22,10 @@
 // buffered, filled by direct buffer-to-LDS loads; the 16-byte chunks of row r
 // sit at chunk ^ (r & 15) so that the 16 rows of a fragment read hits 16
 // different banks) and take S strips each.
-// Tile order (optional): workgroups go to the 8 XCDs round-robin; each XCD is
-// then given a contiguous run of tiles (output blocks fastest), so the
-// workgroups it runs at the same time share their activation tile in its L2.
+// Tile order: workgroups go to the 8 XCDs round-robin. When the token tiles
+// split evenly over the XCDs, each XCD takes its own token tiles with the
+// token tile fastest, so each code block is fetched into its L2 once and
+// shared by the workgroups it runs together.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,17 +46,28 @@ template <int GPT, int TB, int S, bool DEBUG_ACC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) tern_s8m_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ act_scale, int T, int K,
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y,
-    int32_t* __restrict__ acc_out, int N, int nx, int ny, int per_xcd) {
+    int32_t* __restrict__ acc_out, int N, int nx, int ny, int xrows) {
   constexpr int BM = 16 * TB;    // tokens per tile
   constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
   constexpr int kS8WgStrips = 4 * S;
   __shared__ __attribute__((aligned(1024))) int8_t As[2][BM * 256];
 
-  // XCD-aware tile: block b runs on XCD b % 8 as its (b / 8)-th block there.
-  // (per_xcd == 0: plain order, tile = block index)
-  const int tile = per_xcd ? (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
-  if (tile >= nx * ny) return;  // uniform over the workgroup
-  const int ty = tile / nx, tx = tile - ty * nx;
+  // Tile (ty, tx) of this workgroup. xrows == 0: plain order, output blocks
+  // fastest. xrows > 0 (ny == 8 * xrows): block b runs on XCD b % 8 as its
+  // (b / 8)-th block there, and XCD x takes token tiles [x * xrows, (x + 1) *
+  // xrows) with the token tile fastest: the workgroups it runs together share
+  // each code block, and its few activation tiles stay in its L2.
+  int ty, tx;
+  if (xrows) {
+    const int xcd = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
+    ty = xcd * xrows + slot % xrows;
+    tx = slot / xrows;
+  } else {
+    ty = (int)blockIdx.x / nx;
+    tx = (int)blockIdx.x - ty * nx;
+  }
+  const int tile = ty * nx + tx;
+  if (tile >= nx * ny) return;  // uniform over the workgroup (never taken: the grid is nx * ny)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,7 +98,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
       const int chunk = (lane & 15) ^ (row & 15);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           qr, (__attribute__((address_space(3))) void*)&As[buf][rbase * 256], 16, row * K + chunk * 16,
-          kt * 256, 0, kAuxNontemporal);
+          kt * 256, 0, 0);  // cached: every workgroup of this token tile on the XCD reads it
     }
   };
   auto load_w = [&](int kt, S8mStage<GPT, S>& b) {
@@ -163,21 +175,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
   // k-tile kt+1 are requested before the MFMAs of k-tile kt; then each wave
   // waits for its loads and meets the others at the barrier, after which
   // tile kt+1 is complete in LDS and nobody reads tile kt's buffer any more.
-  // Past the last k-tile the loads repeat it.
+  // The loop runs k-tiles in pairs (buffers 0 then 1) with no exit in
+  // between, so the totals keep their registers; with an even tile count the
+  // last pair re-requests the last tile, with an odd one the tail computes
+  // it from buffer 0.
   S8mStage<GPT, S> wA, wB;
   stage_a(0, 0);
   load_w(0, wA);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < KT; kt += 2) {
-    const int k1 = min(kt + 1, KT - 1);
-    stage_a(k1, 1);
-    load_w(k1, wB);
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    stage_a(kt + 1, 1);
+    load_w(kt + 1, wB);
     __builtin_amdgcn_sched_barrier(0);
     compute(kt, 0, wA);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 >= KT) break;
     const int k2 = min(kt + 2, KT - 1);
     stage_a(k2, 0);
     load_w(k2, wA);
@@ -186,6 +200,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  if (kt < KT) compute(kt, 0, wA);
 
   if (!DEBUG_ACC) {
 #pragma unroll
@@ -208,11 +223,11 @@ hipError_t launch_s8m_t(const S8Args& a, bool xcd_order, hipStream_t st) {
   const int NS = a.N / 16;
   const int nx = (NS + kS8WgStrips - 1) / kS8WgStrips;
   const int ny = (a.T + 16 * TB - 1) / (16 * TB);
-  const int per_xcd = xcd_order ? (nx * ny + 7) / 8 : 0;
-  const int blocks = xcd_order ? 8 * per_xcd : nx * ny;
+  const int xrows = (xcd_order && ny % 8 == 0) ? ny / 8 : 0;
+  const int blocks = nx * ny;
   hipLaunchKernelGGL((tern_s8m_kernel<GPT, TB, S, DEBUG_ACC>), dim3(blocks), dim3(256), 0, st, a.q,
                      a.act_scale, a.T, a.K, (const u32x4*)a.codes, a.scales, a.y, a.acc_out, a.N, nx,
-                     ny, per_xcd);
+                     ny, xrows);
   return hipGetLastError();
 }
 
