@@ -275,9 +275,11 @@ tern_status resolve(int T, tern_rung req, tern_rung* out) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Launch shape of the activation-tiled kernel (small_t, small_t_tiled), from
-// a sweep on MI355X over (S, Ws, Pk) at T = 4 and 16: one strip per wave;
-// wide layers (N >= 16k) take 4 waves per workgroup and no K split, narrower
-// ones 8 waves and K split 4 ways (partials through the workspace).
+// sweeps on MI355X over (S, Ws, Pk, D) at T = 4..16: one strip per wave;
+// wide layers (N >= 16k) take 4 compute waves per workgroup, no K split and
+// 2 k-tiles in flight (67 VGPRs, 7 waves per SIMD), narrower ones 8 waves, K
+// split 4 ways (partials through the workspace) and 4 k-tiles in flight.
+// Deeper rings cost occupancy and were slower on both.
 tern::TilePlan plan_tile(int T, int n, int k) {
   const Config& c = config();
   tern::TilePlan p;
@@ -286,9 +288,11 @@ tern::TilePlan plan_tile(int T, int n, int k) {
   p.rows = T <= 8 ? 8 : 16;
   p.strips_per_wave = c.tune_strips ? c.tune_strips : 1;
   int Ws = c.tune_waves ? c.tune_waves : (wide ? 4 : 8);
-  Ws = std::min(Ws, 8);                    // launch bounds
-  if (p.rows == 16) Ws = std::max(Ws, 2);  // at most 4 activation load steps per wave
+  Ws = std::min(Ws, 8);  // launch bounds
   p.waves = Ws;
+  int D = c.tune_depth ? c.tune_depth : (wide ? 2 : 4);
+  while (D > 2 && p.strips_per_wave * D > 8) D /= 2;  // code registers: S * D <= 8
+  p.depth = D;
   p.token_tiles = (T + 15) / 16;
   p.strip_blocks = (NS + Ws * p.strips_per_wave - 1) / (Ws * p.strips_per_wave);
   int Pk = c.tune_kparts ? c.tune_kparts : (wide ? 1 : 4);
@@ -296,10 +300,11 @@ tern::TilePlan plan_tile(int T, int n, int k) {
   return p;
 }
 
-// Kernel of the small_t / small_t_tiled rungs. Narrow layers (< 1024 strips)
-// give the activation-tiled kernel too few workgroups; there the per-wave
-// kernel (each wave loads its own activation fragments, no barriers) was
-// faster on MI355X for T <= 8, and for any T <= 16 when K <= 8192.
+// Kernel of the small_t / small_t_tiled rungs, from A/B runs on MI355X over
+// T = 2..16: wide layers (>= 1024 strips) run the activation-tiled kernel;
+// narrow ones give it too few workgroups and run the per-wave kernel (each
+// wave loads its own activation fragments, no barriers), except for T > 8
+// with a long K, where the per-wave activation traffic grows too large.
 bool small_t_per_wave(int T, int n, int k) {
   const Config& c = config();
   if (c.smallt_kernel) return c.smallt_kernel == 2;

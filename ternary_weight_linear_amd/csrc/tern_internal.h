@@ -48,7 +48,8 @@ struct S8Args {
 struct TilePlan {
   int rows;             // activation rows staged per tile: 8 (T <= 8) or 16
   int strips_per_wave;  // S: 1, 2 or 4
-  int waves;            // Ws: waves per workgroup (1..8), each owning S strips
+  int waves;            // Ws: compute waves per workgroup (1..8), each owning S strips; plus a loader wave
+  int depth;            // D: k-tiles of codes (per wave) and of activations in flight: 2, 4 or 8
   int strip_blocks;     // grid.x = ceil(NS / (Ws * S))
   int k_parts;          // grid.y = Pk: K split across workgroups (partials in the workspace)
   int token_tiles;      // grid.z = ceil(T / 16)

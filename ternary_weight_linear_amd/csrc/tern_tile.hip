@@ -9,10 +9,20 @@
 // The activation tile (16 tokens x 256 k, bf16) is the A operand of
 // v_mfma_f32_16x16x32_bf16 and the decoded codes of one 16-row strip its B
 // operand, as in the single-token kernel. What differs is where the
-// activation tile comes from: every wave of a workgroup owns different strips
-// over the same k range, and the workgroup stages each k-tile of activations
-// once in LDS (triple-buffered, one barrier per k-tile), so the activation
-// traffic from L2 is one tile per workgroup instead of one per wave.
+// activation tile comes from: every compute wave of a workgroup owns
+// different strips over the same k range, and each k-tile of activations is
+// staged once per workgroup in LDS, so the activation traffic from L2 is one
+// tile per workgroup instead of one per wave.
+//
+// Bytes in flight. The codes stream from HBM at about 2 us of latency, so a
+// CU needs tens of KB of requests outstanding. Each compute wave keeps D
+// k-tiles of its codes in flight in registers. The activation tiles are
+// staged by one extra loader wave with direct buffer-to-LDS loads, D tiles
+// ahead in a ring of D + 1 LDS buffers: the loader waits only for its own
+// loads (the vector-memory counter retires loads in order, so a wave that
+// staged activations and prefetched codes would have to wait for codes it
+// does not need yet), and the compute waves only for their codes. One
+// barrier per k-tile hands each tile over.
 //
 // Long K and narrow N (the down projection: 320 strips, 68 k-tiles) need more
 // parallelism than the strips give, so K can also be split across Pk
@@ -61,38 +71,38 @@ __device__ __forceinline__ void tile_load_codes(TileStage<S, GPT>& b, rsrc_t crs
 
 // Activation tile in LDS: ROWS x 32 chunks of 16 bytes (8 bf16); chunk c of
 // row t sits at position t*32 + (c ^ (t & 15)), so the 16 rows that an MFMA
-// operand read touches fall in different banks. Loaded in 64-lane steps:
-// step c covers positions [64c, 64c + 64); wave w of Ws issues steps
-// w, w + Ws, ... (NXI of them) into registers, stored to LDS two k-tiles
-// later.
-template <int NXI>
-struct XRegs {
-  u32x4 v[NXI];
-};
-
-template <int ROWS, int NXI>
-__device__ __forceinline__ void tile_load_x(XRegs<NXI>& r, rsrc_t xrs, int K, int kt, int wave,
-                                            int Ws, int lane, bool valid) {
-  kt = __builtin_amdgcn_readfirstlane(min(max(kt, 0), (K >> 8) - 1));
+// operand read touches fall in different banks. The loader wave fills a tile
+// with ROWS/2 direct loads of 64 lanes x 16 bytes: lane l of load c writes
+// position 64c + l, i.e. row t = (64c + l) / 32, and fetches that row's
+// global chunk (position ^ (t & 15)). Rows past the last token, and k-tiles
+// past the last one (voffset beyond the resource), read as zeros.
+template <int ROWS>
+__device__ __forceinline__ void tile_stage_x(rsrc_t xrs, char* buf, int K, int kt, int lane, bool valid) {
+  kt = __builtin_amdgcn_readfirstlane(kt);
 #pragma unroll
-  for (int j = 0; j < NXI; ++j) {
-    const int c = wave + Ws * j;
+  for (int c = 0; c < ROWS / 2; ++c) {
     const int p = 64 * c + lane;
     const int t = p >> 5;
     const int cl = (p & 31) ^ (t & 15);
-    const int off = valid && c < ROWS / 2 ? (t * K + cl * 8) * 2 : kOffPastEnd;
-    r.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, kt * 512, 0));
+    const int off = valid ? (t * K + cl * 8) * 2 : kOffPastEnd;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void*)(buf + 1024 * c),
+                                             16, off, kt * 512, 0, 0);
   }
 }
 
-template <int ROWS, int NXI>
-__device__ __forceinline__ void tile_store_x(const XRegs<NXI>& r, char* buf, int wave, int Ws,
-                                             int lane) {
-#pragma unroll
-  for (int j = 0; j < NXI; ++j) {
-    const int c = wave + Ws * j;
-    if (c < ROWS / 2) *(u32x4*)(buf + (64 * c + lane) * 16) = r.v[j];
-  }
+// The loader's side of a k-tile handoff: wait until at most N of its
+// buffer-to-LDS loads are outstanding (vmcnt <= N; the loads retire in
+// order), then the workgroup barrier. The barrier is issued without the
+// workgroup fence of __syncthreads(): that fence would wait for every
+// outstanding buffer-to-LDS load (vmcnt(0)) and so throw away the loader's
+// lead. The "memory" clobber keeps the compiler from moving the next tile's
+// loads above the barrier; the compute waves pass their own barriers through
+// __syncthreads().
+template <int N>
+__device__ __forceinline__ void loader_handoff() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // One k-tile: A fragments from the LDS tile, S strips x 8 MFMAs, fp32 scale
@@ -128,76 +138,78 @@ __device__ __forceinline__ void tile_compute(const TileStage<S, GPT>& b, f32x4 (
   }
 }
 
-constexpr int kTileDepth = 2;  // code stages in flight per wave (even: the x ring has 2 slots)
-
 // Grid: x = strip blocks (Ws*S strips), y = K parts (Pk), z = 16-token tiles.
-// Block: Ws waves, wave w owns strips [sb*Ws*S + w*S, +S) over the block's K
-// part. Dynamic LDS: 3 activation tiles of ROWS*512 bytes.
-template <int ROWS, int S, int GPT, int NXI>
-__global__ void __launch_bounds__(512) tern_tile_kernel(
+// Block: Ws compute waves, wave w owning strips [sb*Ws*S + w*S, +S) over the
+// block's K part, then the loader wave. Dynamic LDS: D + 1 activation tiles
+// of ROWS*512 bytes.
+template <int ROWS, int S, int GPT, int D>
+__global__ void __launch_bounds__(576) tern_tile_kernel(
     const uint16_t* __restrict__ x, int T, int K, const u32x4* __restrict__ codes,
     const uint16_t* __restrict__ scales, float* __restrict__ y, int N, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TILE = ROWS * 512;
+  constexpr int NB = D + 1;  // LDS tile ring
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int Ws = blockDim.x >> 6;
+  const int Ws = (blockDim.x >> 6) - 1;  // compute waves; wave Ws is the loader
   const int NS = N >> 4, KT = K >> 8;
   const int sb = blockIdx.x, pk = blockIdx.y, tile = blockIdx.z;
   const int Pk = gridDim.y;
   const int kt0 = (pk * KT) / Pk;
   const int nkt = ((pk + 1) * KT) / Pk - kt0;
-  const int strip0 = (sb * Ws + wave) * S;
-  const int nstrips = min(S, NS - strip0);  // <= 0: this wave only helps stage activations
   const int t0 = tile * 16;
 
+  if (wave == Ws) {
+    // Loader: tiles 0..D-1, then per k-tile i the tile i + D into the buffer
+    // of tile i - 1 (finished by every wave before the previous barrier),
+    // and a wait until tile i + 1 has landed (D - 1 tiles may stay in flight).
+    const rsrc_t xrs = make_rsrc(x + (size_t)t0 * K, (uint32_t)min(16, T - t0) * K * 2);
+#pragma unroll
+    for (int j = 0; j < D; ++j) tile_stage_x<ROWS>(xrs, smem + j * TILE, K, kt0 + j, lane, j < nkt);
+    loader_handoff<(D - 1) * (ROWS / 2)>();
+    for (int i = 0; i < nkt; ++i) {
+      tile_stage_x<ROWS>(xrs, smem + ((i + D) % NB) * TILE, K, kt0 + i + D, lane, i + D < nkt);
+      loader_handoff<(D - 1) * (ROWS / 2)>();
+    }
+    return;
+  }
+
+  const int strip0 = (sb * Ws + wave) * S;
+  const int nstrips = min(S, NS - strip0);  // <= 0: the wave only keeps the barriers
   const rsrc_t crs = make_rsrc(codes + (size_t)max(min(strip0, NS - 1), 0) * KT * 64,
                                (uint32_t)max(nstrips, 0) * KT * 1024);
   const rsrc_t srs = make_rsrc(scales + (size_t)max(min(strip0, NS - 1), 0) * KT * 16 * GPT,
                                (uint32_t)max(nstrips, 0) * KT * 16 * GPT * 2);
-  const rsrc_t xrs = make_rsrc(x + (size_t)t0 * K, (uint32_t)min(16, T - t0) * K * 2);
 
   f32x4 total[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) total[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Prologue: activation tile 0 into LDS buffer 0, tiles 1 and 2 in registers,
-  // the first kTileDepth - 1 code stages in flight.
-  XRegs<NXI> xr[2];
-  TileStage<S, GPT> cb[kTileDepth];
-  tile_load_x<ROWS, NXI>(xr[0], xrs, K, kt0, wave, Ws, lane, 0 < nkt);
+  // Code ring: stage j holds k-tile i + j; k-tile i + D - 1 is requested
+  // before k-tile i is computed.
+  TileStage<S, GPT> cb[D];
 #pragma unroll
-  for (int j = 0; j < kTileDepth - 1; ++j)
+  for (int j = 0; j < D - 1; ++j)
     tile_load_codes(cb[j], crs, srs, lane, KT, nstrips, kt0 + j, j < nkt);
-  tile_load_x<ROWS, NXI>(xr[1], xrs, K, kt0 + 1, wave, Ws, lane, 1 < nkt);
-  tile_store_x<ROWS, NXI>(xr[0], smem, wave, Ws, lane);
-  tile_load_x<ROWS, NXI>(xr[0], xrs, K, kt0 + 2, wave, Ws, lane, 2 < nkt);
   __syncthreads();
 
-  // Iteration i: store activation tile i+1 (registers -> LDS), load tile
-  // i+3 and code stage i+kTileDepth-1, compute k-tile i, barrier. Tile i was
-  // stored before the previous barrier; the buffer written here last held
-  // tile i-2, which every wave finished before that barrier.
   int i = 0;
-  for (; i + kTileDepth <= nkt; i += kTileDepth) {
+  for (; i + D <= nkt; i += D) {
 #pragma unroll
-    for (int j = 0; j < kTileDepth; ++j) {
+    for (int j = 0; j < D; ++j) {
       const int ii = i + j;
-      tile_store_x<ROWS, NXI>(xr[(j + 1) & 1], smem + ((ii + 1) % 3) * TILE, wave, Ws, lane);
-      tile_load_x<ROWS, NXI>(xr[(j + 1) & 1], xrs, K, kt0 + ii + 3, wave, Ws, lane, ii + 3 < nkt);
-      tile_load_codes(cb[(j + kTileDepth - 1) % kTileDepth], crs, srs, lane, KT, nstrips,
-                      kt0 + ii + kTileDepth - 1, ii + kTileDepth - 1 < nkt);
+      tile_load_codes(cb[(j + D - 1) % D], crs, srs, lane, KT, nstrips, kt0 + ii + D - 1,
+                      ii + D - 1 < nkt);
       __builtin_amdgcn_sched_barrier(0);
-      tile_compute<ROWS>(cb[j], total, smem + (ii % 3) * TILE, lane);
+      tile_compute<ROWS>(cb[j], total, smem + (ii % NB) * TILE, lane);
       __syncthreads();
     }
   }
 #pragma unroll
-  for (int j = 0; j < kTileDepth - 1; ++j) {
+  for (int j = 0; j < D - 1; ++j) {
     if (i + j < nkt) {  // uniform over the block
       const int ii = i + j;
-      tile_store_x<ROWS, NXI>(xr[(j + 1) & 1], smem + ((ii + 1) % 3) * TILE, wave, Ws, lane);
-      tile_compute<ROWS>(cb[j], total, smem + (ii % 3) * TILE, lane);
+      tile_compute<ROWS>(cb[j], total, smem + (ii % NB) * TILE, lane);
       __syncthreads();
     }
   }
@@ -239,28 +251,28 @@ __global__ void __launch_bounds__(256) tern_tile_reduce_kernel(const float* __re
   ((f32x4*)(y + (size_t)t * N))[c] = sum * 0.5f;
 }
 
-// Load steps per wave for one activation tile (ROWS/2 steps of 64 lanes over
-// Ws waves), rounded up to a power of two.
-int tile_load_steps(int rows, int waves) {
-  const int n = (rows / 2 + waves - 1) / waves;
-  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8;
-}
-
 template <int ROWS, int S, int GPT>
 hipError_t launch_tile_g(const SmallTArgs& a, const TilePlan& p, float* part, hipStream_t st) {
   dim3 grid(p.strip_blocks, p.k_parts, p.token_tiles);
-  dim3 block(64 * p.waves);
-  const size_t lds = (size_t)3 * ROWS * 512;
-#define TERN_TILE_LAUNCH(NX)                                                                   \
-  hipLaunchKernelGGL((tern_tile_kernel<ROWS, S, GPT, NX>), grid, block, lds, st, a.x, a.T, a.K, \
-                     (const u32x4*)a.codes, a.scales, a.y, a.N, part)
-  switch (tile_load_steps(ROWS, p.waves)) {
-    case 1: TERN_TILE_LAUNCH(1); break;
-    case 2: TERN_TILE_LAUNCH(2); break;
-    case 4: TERN_TILE_LAUNCH(4); break;
+  dim3 block(64 * (p.waves + 1));
+  const size_t lds = (size_t)(p.depth + 1) * ROWS * 512;
+  // S * D <= 8: more code registers than that would not fit the 168 VGPRs a
+  // 9-wave workgroup leaves each wave.
+  switch (p.depth) {
+#define TERN_TILE_LAUNCH(D)                                                                       \
+  case D:                                                                                         \
+    if constexpr (S * D <= 8)                                                                     \
+      hipLaunchKernelGGL((tern_tile_kernel<ROWS, S, GPT, D>), grid, block, lds, st, a.x, a.T, a.K, \
+                         (const u32x4*)a.codes, a.scales, a.y, a.N, part);                        \
+    else                                                                                          \
+      return hipErrorInvalidValue;                                                                \
+    break;
+    TERN_TILE_LAUNCH(2)
+    TERN_TILE_LAUNCH(4)
+    TERN_TILE_LAUNCH(8)
+#undef TERN_TILE_LAUNCH
     default: return hipErrorInvalidValue;
   }
-#undef TERN_TILE_LAUNCH
   return hipGetLastError();
 }
 
@@ -291,7 +303,7 @@ int launch_tile(const SmallTArgs& a, const TilePlan& p, void* ws, void* stream) 
   hipStream_t st = (hipStream_t)stream;
   if (p.waves < 1 || p.waves > 8 || p.k_parts < 1 || p.token_tiles < 1 || p.strip_blocks < 1)
     return (int)hipErrorInvalidValue;
-  if (tile_load_steps(p.rows, p.waves) > 4) return (int)hipErrorInvalidValue;
+  if (p.depth != 2 && p.depth != 4 && p.depth != 8) return (int)hipErrorInvalidValue;
   float* part = p.k_parts > 1 ? (float*)ws : nullptr;
   hipError_t e = p.rows == 8 ? launch_tile_r<8>(a, p, part, st)
                : p.rows == 16 ? launch_tile_r<16>(a, p, part, st) : hipErrorInvalidValue;

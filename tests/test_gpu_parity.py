@@ -365,6 +365,26 @@ def test_launch_shapes_keep_parity(strips, waves, G):
     assert worst <= 1e-6, worst
 
 
+@pytest.mark.parametrize("strips,waves,depth,kparts", [(1, 4, 2, 1), (1, 4, 8, 1), (2, 3, 4, 2),
+                                                    (4, 2, 2, 4), (1, 8, 4, 3)])
+def test_tile_kernel_shapes_keep_parity(strips, waves, depth, kparts):
+    """The activation-tiled small-T kernel forced for every T: 8- and 16-row
+    activation tiles, two 16-token tiles (T = 23), code/activation rings of 2,
+    4 and 8 k-tiles, K split over 1..4 workgroups (16 k-tiles), partial strip
+    blocks and waves without strips."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, TERN_TUNE_SMALLT="tile", TERN_TUNE_STRIPS=str(strips),
+               TERN_TUNE_WAVES=str(waves), TERN_TUNE_DEPTH=str(depth), TERN_TUNE_KPARTS=str(kparts))
+    r = subprocess.run([sys.executable, "-c", _TUNE_CHILD, root, "128"], env=env,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    worst = float(r.stdout.split("WORST")[1])
+    assert worst <= 1e-6, worst
+
+
 # ------------------------------------- activation dynamic range (bf16 rungs)
 
 

@@ -131,9 +131,11 @@ def test_workspace_sizes(tl):
     assert tl.workspace_bytes(1, 128, 256, 64) == 0
     assert tl.workspace_bytes(1, 5120, 17408, 128) == 0  # gemv
     assert tl.workspace_bytes(4, 128, 256, 64) == 0  # one k-tile: K is not split
-    # the per-wave small-T kernel of narrow layers keeps no partial sums
+    # the per-wave small-T kernel (narrow layers: T <= 8, or K <= 8192) and
+    # the activation-tiled kernel of wide layers (no K split) keep no partial sums
     assert tl.workspace_bytes(16, 5120, 5120, 128) == 0
     assert tl.workspace_bytes(4, 5120, 17408, 128) == 0
+    assert tl.workspace_bytes(8, 34816, 5120, 128) == 0
     # the activation-tiled kernel splits a long K over workgroups: fp32
     # partials of one 16-token tile per K part
     ws16 = tl.workspace_bytes(16, 5120, 17408, 128)
