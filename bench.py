@@ -36,9 +36,11 @@ I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POPS
 MALL_BYTES = 256 * 2**20
 ROTATE_BYTES = 600e6  # > 2x the Infinity Cache
 METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
+# Sources of the kernels whose HBM traffic is stored (gemv, quant, s8) and of
+# their launch plans: a change to any of them voids the stored counters.
 KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
-               for f in ("tern_kernels.hip", "tern_s8.hip", "tern_s8mma.hip", "tern_tile.hip",
-                         "tern_limb.hip", "tern_device.h")]
+               for f in ("tern_limb.hip", "tern_s8.hip", "tern_s8mma.hip", "tern_device.h",
+                         "tern_internal.h", "tern_host.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

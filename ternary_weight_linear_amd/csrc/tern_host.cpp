@@ -376,13 +376,13 @@ tern::S8Plan plan_s8(int T, int n) {
   const Config& c = config();
   tern::S8Plan p;
   // Wave tile 64 tokens x 64 outputs (4 token blocks x 4 strips) where that
-  // still gives at least 2 workgroups per CU; 64 x 32 otherwise (narrow
+  // still gives at least 4 workgroups per CU; 64 x 32 otherwise (narrow
   // layers, short prefills); 32-token tiles for T <= 32 so padded tokens do
   // not waste the matrix cores. (128-token tiles cost registers, and
   // occupancy, without paying back on either 27B-class shape.)
   const int tb = c.tune_s8_bm ? c.tune_s8_bm / 16 : (T > 32 ? 4 : 2);
   const long tiles4 = (long)((n / 16 + 15) / 16) * ((T + 16 * tb - 1) / (16 * tb));
-  int strips = tiles4 >= 512 ? 4 : 2;
+  int strips = tiles4 >= 1024 ? 4 : 2;
   if (c.tune_s8_strips) strips = c.tune_s8_strips;
   if (tb == 8) strips = 2;
   p.token_blocks = tb;

@@ -243,8 +243,10 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = *(const i32x4*)(abase + 64 * (4 * kt + q));
     // TT = 1: the three limbs of the token are accumulators 0..2 of lanes
-    // 0..15; they are combined per group in fp32, (65536 a2 + 256 a1) + a0,
-    // and 2^(d - 6) then undoes the fixed point and the 64x code decode.
+    // 0..15. Per group they are combined as 65536 a2 + (256 a1 + a0), the
+    // bracket exact in int32 (|a_L| <= 2^20), and scaled; the groups of the
+    // k-tile are summed first and 2^(d - 6), which undoes the fixed point and
+    // the 64x code decode, is applied once per k-tile.
     // TT = 5: each row keeps its own total, scaled by 2^(d - 6 + 8L) (limb
     // L = row mod 3) so that every partial sum carries its true magnitude.
     int dsh[4];
@@ -266,6 +268,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
         sw[0] = v.x;
         sw[GPT / 2 - 1] = v.y;
       }
+      float part = 0.f;  // TT = 1: this k-tile's groups, before 2^(d - 6)
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
         i32x4 acc = i32x4{0, 0, 0, 0};
@@ -277,14 +280,16 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
         const uint32_t spair = sw[gi >> 1];
         const float sc = half_bits_to_float((uint16_t)((gi & 1) ? (spair >> 16) : (spair & 0xffffu)));
         if (TT == 1) {
-          const float v = __builtin_fmaf(65536.0f, (float)acc[2], 256.0f * (float)acc[1]) + (float)acc[0];
-          total[s][0] = __builtin_fmaf(sc, __builtin_ldexpf(v, dsh[0]), total[s][0]);
+          const int low = (int)(((uint32_t)acc[1] << 8) + (uint32_t)acc[0]);  // 256 a1 + a0
+          const float v = __builtin_fmaf(65536.0f, (float)acc[2], (float)low);
+          part = gi == 0 ? sc * v : __builtin_fmaf(sc, v, part);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             total[s][e] = __builtin_fmaf(sc, __builtin_ldexpf((float)acc[e], dsh[e]), total[s][e]);
         }
       }
+      if (TT == 1) total[s][0] += __builtin_ldexpf(part, dsh[0]);
     }
   };
   int i = 0;

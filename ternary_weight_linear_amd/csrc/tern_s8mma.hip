@@ -14,10 +14,13 @@
 //  * wave tile TB x 16 tokens by S x 16 outputs (TB token blocks, S strips):
 //    each decoded weight operand feeds TB MFMAs, each A fragment S MFMAs;
 //  * the codes decode straight into int8 B operands, (word << 2i) &
-//    0xC0C0C0C0 = 64*w (weights_operand_i8); the 2^-6 goes into the scale, and
-//    fma(float(64*acc), s/64, total) rounds exactly like fma(acc, s, total);
+//    0xC0C0C0C0 = 64*w (weights_operand_i8), so the totals carry a factor 64:
+//    fma(float(64*acc), s, 64*total) = 64 * fma(acc, s, total) exactly (every
+//    term is a multiple of 2^-24, so nothing is subnormal), and the fp16 scale
+//    feeds the fma directly (v_fma_mix_f32, no conversion);
 //  * the epilogue per group and accumulator is one convert and one fma, in
-//    ascending group order, then y = total * scale_t.
+//    ascending group order, then y = (total * 2^-6) * scale_t, bit-identical
+//    to summing acc * s and multiplying by scale_t.
 // Workgroup: 4 waves share one TB x 16-token activation tile in LDS (double
 // buffered, filled by direct buffer-to-LDS loads; the 16-byte chunks of row r
 // sit at chunk ^ (r & 15) so that the 16 rows of a fragment read hits 16
@@ -161,7 +164,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
             }
         } else {
           const uint32_t sp = b.sw[c][gi >> 1];
-          const float sv = half_bits_to_float((uint16_t)((gi & 1) ? (sp >> 16) : (sp & 0xffffu))) * 0.015625f;
+          const float sv = half_bits_to_float((uint16_t)((gi & 1) ? (sp >> 16) : (sp & 0xffffu)));
 #pragma unroll
           for (int a = 0; a < TB; ++a)
 #pragma unroll
@@ -212,7 +215,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
         const float as = act_scale[t0 + tl];
 #pragma unroll
         for (int c = 0; c < S; ++c)
-          if (c < nst) y[(size_t)(t0 + tl) * N + (st0 + c) * 16 + r] = tot[a][c][e] * as;
+          if (c < nst) y[(size_t)(t0 + tl) * N + (st0 + c) * 16 + r] = (tot[a][c][e] * 0.015625f) * as;
       }
   }
 }
