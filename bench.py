@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8.0 TB/s
 I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POPS
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 MALL_BYTES = 256 * 2**20
 ROTATE_BYTES = 600e6  # > 2x the Infinity Cache
 METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
@@ -361,6 +362,24 @@ def main():
                            "traffic": stored_traffic(f"s8:{dom}"),
                            "kernel": f"tern_s8m_kernel (s8 rung contraction) on {dom}, T={T}"}}
         log(f"s8 prefill step {el8 / K8 * 1e3:.3f} ms, {tops:.1f} TOPS")
+
+        # The bf16 prefill path (small_t_tiled at T = 2048, where T >= 17 goes
+        # with the s8 rung switched off): no activation quantisation.
+        b16 = {}
+        for j, s in enumerate(shapes):
+            def b1(i, j=j):
+                tl.linear(xs[j], sets[i % nsets][j], rung="small_t_tiled", y=ys[j], workspace=wsp)
+            t = graph_time(torch, b1, K8, 2) / K8
+            o = 2 * T * s.n * s.k
+            b16[s.name] = {"us": round(t * 1e6, 2), "TFLOPs": round(o / t / 1e12, 1)}
+            log(f"  bf16 prefill {s.name}: {t * 1e6:.1f} us ({o / t / 1e12:.0f} TFLOP/s)")
+        ach16 = b16[dom]["TFLOPs"]
+        s8["bf16_prefill"] = {
+            "metric": "bf16 TFLOP/s at T=2048 (rung small_t_tiled, no activation quantisation)",
+            "per_shape": b16,
+            "roofline": {"bound": "mfma", "achieved": ach16, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach16 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": f"tern_b16m_kernel (bf16 prefill) on {dom}, T={T}"}}
 
     small = None
     if not args.no_small_t:

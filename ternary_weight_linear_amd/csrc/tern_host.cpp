@@ -311,8 +311,13 @@ bool small_t_per_wave(int T, int n, int k) {
   return n / 16 < 1024 && (T <= 8 || k <= 8192);
 }
 
+// small_t_tiled above one 16-token tile runs the bf16 prefill contraction
+// (tern_b16mma.hip), which needs no workspace.
+bool b16_prefill(int T, tern_rung r) { return r == TERN_RUNG_SMALL_T_TILED && T > 16; }
+
 size_t workspace_for(int T, int n, int k, tern_rung r) {
   if (r == TERN_RUNG_S8) return align256((size_t)T * k) + align256((size_t)T * sizeof(float));
+  if (b16_prefill(T, r)) return 0;
   if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && !small_t_per_wave(T, n, k))
     return tern::tile_workspace_bytes(plan_tile(T, n, k), n);
   return 0;
@@ -583,6 +588,9 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
       else
         err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
       if (err) return hip_fail(err, "gemv launch");
+    } else if (b16_prefill(T, r)) {
+      int err = tern::launch_b16_prefill(a, plan_s8(T, n), stream);
+      if (err) return hip_fail(err, "bf16 prefill launch");
     } else if (small_t_per_wave(T, n, k)) {
       int err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
       if (err) return hip_fail(err, "small_t launch");

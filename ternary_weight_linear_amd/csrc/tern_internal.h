@@ -83,6 +83,9 @@ int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bo
                     void* stream);
 int launch_s8(const S8Args& a, const S8Plan& p, void* stream);
 int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* stream);
+// bf16 prefill contraction (tern_b16mma.hip): the small_t_tiled rung above
+// one 16-token tile; same tile plan as the s8 contraction.
+int launch_b16_prefill(const SmallTArgs& a, const S8Plan& p, void* stream);
 const char* hip_error_string(int err);
 
 }  // namespace tern

@@ -241,14 +241,29 @@ def test_output_guard_bands_and_determinism(tl, torch, mid):
 
 
 def test_batch_invariance(tl, torch, mid):
+    """A token's output does not depend on the other rows of its batch:
+    bitwise when the other rows change (same T, same kernel). For s8 also
+    across batch sizes (per-token quantisation, fixed group order in every
+    tile shape). small_t_tiled runs different kernels at T = 1 and T = 24
+    (the per-wave kernel splits K over waves, the prefill kernel does not),
+    so across batch sizes it is held to the fp32-accumulation bound only."""
     wts, W = mid
     xbits = ts.activations(wts, 24)
-    x_dev = to_dev_bf16(torch, xbits)
+    other = ts.activations(wts, 24, salt=5)
+    keep = [0, 11, 23]
+    mixed = other.copy()
+    mixed[keep] = xbits[keep]
+    x_dev, m_dev = to_dev_bf16(torch, xbits), to_dev_bf16(torch, mixed)
     for rung in ("small_t_tiled", "s8"):
         y = tl.linear(x_dev, W, rung=rung).cpu()
-        for t in (0, 11, 23):
+        ym = tl.linear(m_dev, W, rung=rung).cpu()
+        assert torch.equal(ym[keep].view(torch.int32), y[keep].view(torch.int32)), rung
+        for t in keep:
             yt = tl.linear(x_dev[t:t + 1].contiguous(), W, rung=rung).cpu()
-            assert torch.equal(yt[0].view(torch.int32), y[t].view(torch.int32)), (rung, t)
+            if rung == "s8":
+                assert torch.equal(yt[0].view(torch.int32), y[t].view(torch.int32)), (rung, t)
+            else:
+                assert rel_l2(yt[0].numpy(), y[t].numpy()) <= 1e-6, (rung, t)
 
 
 # ------------------------------------------------------ full layer shapes
@@ -297,6 +312,22 @@ def test_small_T_batches_sampled(tl, torch, big, shape, T):
     for rung in ("auto", "small_t", "small_t_tiled"):
         y = run(tl, torch, x_dev, W, rung)
         assert rel_l2(y[:, rows], ref) <= BF16_GATE, rung
+
+
+@pytest.mark.parametrize("shape", [ts.GATE_UP, ts.DOWN])
+@pytest.mark.parametrize("T", [17, 36, 508, 2048])
+def test_prefill_bf16_sampled(tl, torch, big, shape, T):
+    """The bf16 prefill path (small_t_tiled above one 16-token tile, where
+    T >= 17 goes with the s8 rung switched off): exact bf16 x {-1,0,+1}
+    products summed in fp32, so well inside the 2e-3 gate."""
+    wts, W = big(shape)
+    xbits = ts.activations(wts, T)
+    x_dev = to_dev_bf16(torch, xbits)
+    rows = sample_rows(W.n, T + 7)
+    y = run(tl, torch, x_dev, W, "small_t_tiled")
+    ref = oracle.linear_bf16(xbits, wts.w[rows], wts.s[rows])
+    assert rel_l2(y[:, rows], ref) <= BF16_GATE
+    assert rel_l2(y[:, rows], ref) <= 1e-6
 
 
 @pytest.mark.parametrize("shape", [ts.GATE_UP, ts.DOWN])
@@ -368,10 +399,10 @@ def test_launch_shapes_keep_parity(strips, waves, G):
 @pytest.mark.parametrize("strips,waves,depth,kparts", [(1, 4, 2, 1), (1, 4, 8, 1), (2, 3, 4, 2),
                                                     (4, 2, 2, 4), (1, 8, 4, 3)])
 def test_tile_kernel_shapes_keep_parity(strips, waves, depth, kparts):
-    """The activation-tiled small-T kernel forced for every T: 8- and 16-row
-    activation tiles, two 16-token tiles (T = 23), code/activation rings of 2,
-    4 and 8 k-tiles, K split over 1..4 workgroups (16 k-tiles), partial strip
-    blocks and waves without strips."""
+    """The activation-tiled small-T kernel forced for T <= 16 (above that
+    small_t_tiled runs the prefill kernel): 8- and 16-row activation tiles,
+    code/activation rings of 2, 4 and 8 k-tiles, K split over 1..4
+    workgroups (16 k-tiles), partial strip blocks and waves without strips."""
     import os
     import subprocess
     import sys

@@ -140,7 +140,8 @@ def test_workspace_sizes(tl):
     # partials of one 16-token tile per K part
     ws16 = tl.workspace_bytes(16, 5120, 17408, 128)
     assert ws16 > 0 and ws16 % (16 * 5120 * 4) == 0
-    assert tl.workspace_bytes(40, 5120, 17408, 128, "small_t_tiled") == 3 * ws16
+    # above one 16-token tile small_t_tiled runs the prefill kernel: no K split
+    assert tl.workspace_bytes(40, 5120, 17408, 128, "small_t_tiled") == 0
     need = tl.workspace_bytes(17, 5120, 5120, 128)
     assert need >= 17 * 5120 + 17 * 4
     assert tl.workspace_bytes(3, 5120, 5120, 128, "s8") >= 3 * 5120 + 12
