@@ -158,9 +158,9 @@ tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float
 /*
  * Device workspace tern_linear needs for this call (bytes, 0 if none). The s8
  * rung keeps the int8 activations and their scales there; small_t and
- * small_t_tiled keep fp32 partial sums there when they split K across
- * workgroups (narrow layers; then a second kernel adds the parts in a fixed
- * order). The contents need no initialisation and are not preserved. Every scratch
+ * small_t_tiled (up to 16 tokens) keep fp32 partial sums there when they
+ * split K across workgroups (narrow layers with a long K; then a second
+ * kernel adds the parts in a fixed order). The contents need no initialisation and are not preserved. Every scratch
  * buffer of every rung is counted here; a call given less fails with
  * TERN_ERR_WORKSPACE ("NINFER ternary perf-tuning" notes, section 5 item 8:
  * the workspace capacity declaration must cover every scratch).
@@ -175,13 +175,17 @@ size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung);
  *  W:  host struct describing device codes and scales (layout v1)
  *  y:  device float [T][N], 16-byte aligned; fully overwritten
  *  rung: TERN_RUNG_AUTO picks by T (after TERN_RUNG); any other value forces
- *        that rung. small_t takes T <= 16 (one 16-token tile); gemv runs
- *        one token per grid row (T <= 65535); small_t_tiled (16-token tiles
- *        in grid y) and s8 take any T >= 1.
+ *        that rung. small_t takes T <= 16 (one 16-token tile); gemv takes
+ *        T <= 65535; small_t_tiled and s8 take any T >= 1 (small_t_tiled
+ *        above 16 tokens runs the bf16 prefill contraction, the path T >= 17
+ *        takes with TERN_S8=0).
  *  ws, ws_bytes: device workspace (16-byte aligned) of at least
  *        tern_workspace_bytes(T, N, K, G, rung) bytes (may be NULL/0 if that is 0)
  * Output numerics: the bf16-activation rungs (gemv, small_t, small_t_tiled)
- * accumulate exact bf16 x {-1,0,+1} products in fp32; s8 computes exact int32
+ * accumulate exact bf16 x {-1,0,+1} products in fp32, except that the gemv
+ * kernel carries each activation as a 22-bit fixed-point number relative to
+ * the largest magnitude M of its 256-wide k-tile (exact for values down to
+ * 2^-14 M, rounded by at most 2^-22 M below that); s8 computes exact int32
  * group accumulators and y = scale_t * sum_g s[n][g] * acc in fp32, groups in
  * ascending order.
  */
