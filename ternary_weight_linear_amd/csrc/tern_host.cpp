@@ -311,12 +311,16 @@ bool small_t_per_wave(int T, int n, int k) {
   return n / 16 < 1024 && (T <= 8 || k <= 8192);
 }
 
+tern::S8Plan plan_s8(int T, int n, int k, bool allow_split);
+
 // small_t_tiled above one 16-token tile runs the bf16 prefill contraction
 // (tern_b16mma.hip), which needs no workspace.
 bool b16_prefill(int T, tern_rung r) { return r == TERN_RUNG_SMALL_T_TILED && T > 16; }
 
 size_t workspace_for(int T, int n, int k, tern_rung r) {
-  if (r == TERN_RUNG_S8) return align256((size_t)T * k) + align256((size_t)T * sizeof(float));
+  if (r == TERN_RUNG_S8)
+    return align256((size_t)T * k) + align256((size_t)T * sizeof(float)) +
+           tern::s8_partial_bytes(plan_s8(T, n, k, true), T, n);
   if (b16_prefill(T, r)) return 0;
   if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && !small_t_per_wave(T, n, k))
     return tern::tile_workspace_bytes(plan_tile(T, n, k), n);
@@ -377,7 +381,7 @@ bool limb_fits(int T, int k, int group, const tern::LimbPlan& p) {
   return T <= 5 && tern::limb_lds_bytes(T, k, group, p) <= tern::kLimbMaxLds;
 }
 
-tern::S8Plan plan_s8(int T, int n) {
+tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   const Config& c = config();
   tern::S8Plan p;
   // Wave tile 64 tokens x 64 outputs (4 token blocks x 4 strips) where that
@@ -393,6 +397,23 @@ tern::S8Plan plan_s8(int T, int n) {
   p.token_blocks = tb;
   p.strips = strips;
   p.xcd_order = c.tune_s8_raster != 1;
+  // Short prefills on narrow layers give too few tiles to keep HBM busy:
+  // split K over workgroups until there are about 512 of them (each part at
+  // least 4 k-tiles) when there are fewer tiles than CUs, or fewer than 512
+  // with a long K; the parts cost a second kernel, which only pays there
+  // (A/B runs on MI355X at T = 17..508). Short prefills also keep 3 k-tiles
+  // in flight instead of 1.
+  const long tiles = (long)((n / 16 + 4 * strips - 1) / (4 * strips)) * ((T + 16 * tb - 1) / (16 * tb));
+  const int KT = k / 256;
+  int pk = 1;
+  if (allow_split && tb != 8 && (tiles < 256 || (tiles < 512 && KT >= 32)))
+    pk = (int)std::min<long>((512 + tiles - 1) / tiles, 16);
+  pk = std::max(1, std::min(pk, KT / 4));
+  if (c.tune_kparts && allow_split) pk = std::max(1, std::min(c.tune_kparts, KT));
+  p.k_parts = pk;
+  p.depth = (tb != 8 && (T <= 64 || pk > 1)) ? 4 : 2;
+  if (c.tune_depth == 2 || (c.tune_depth == 4 && tb != 8)) p.depth = c.tune_depth;
+  if (tb * strips >= 16) p.depth = 2;  // the 64 x 64 wave tile runs double-buffered only
   return p;
 }
 
@@ -575,8 +596,9 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
     float* sc = (float*)((char*)ws + align256((size_t)T * k));
     int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, true, stream);
     if (err) return hip_fail(err, "quant_s8 launch");
+    float* part = (float*)((char*)ws + align256((size_t)T * k) + align256((size_t)T * sizeof(float)));
     tern::S8Args a{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr, true};
-    err = tern::launch_s8(a, plan_s8(T, n), stream);
+    err = tern::launch_s8(a, plan_s8(T, n, k, true), part, stream);
     if (err) return hip_fail(err, "s8 launch");
   } else {
     tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
@@ -589,7 +611,7 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
         err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
       if (err) return hip_fail(err, "gemv launch");
     } else if (b16_prefill(T, r)) {
-      int err = tern::launch_b16_prefill(a, plan_s8(T, n), stream);
+      int err = tern::launch_b16_prefill(a, plan_s8(T, n, k, false), stream);
       if (err) return hip_fail(err, "bf16 prefill launch");
     } else if (small_t_per_wave(T, n, k)) {
       int err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
@@ -616,7 +638,7 @@ tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
   if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
   tern::S8Args a{q,       act_scale, T,       W->k,    W->n, W->group, W->codes,
                  W->scales, y,       nullptr, layout == TERN_Q_OPERAND_ORDER};
-  int err = tern::launch_s8(a, plan_s8(T, W->n), stream);
+  int err = tern::launch_s8(a, plan_s8(T, W->n, W->k, false), nullptr, stream);
   if (err) return hip_fail(err, "s8 launch");
   probe_hit(TERN_RUNG_S8, T, W->n, W->k, W->group);
   return ok();
@@ -635,7 +657,9 @@ tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int
   if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
   tern::S8Args a{q,       nullptr, T,      W->k, W->n, W->group, W->codes, W->scales,
                  nullptr, acc_out, layout == TERN_Q_OPERAND_ORDER};
-  int err = tern::launch_s8(a, plan_s8(T, W->n), stream);
+  tern::S8Plan p = plan_s8(T, W->n, W->k, false);
+  p.depth = 2;  // the export runs the double-buffered pipeline
+  int err = tern::launch_s8(a, p, nullptr, stream);
   if (err) return hip_fail(err, "s8 debug launch");
   return ok();
 }

@@ -24,13 +24,16 @@ struct SmallTArgs {
 };
 
 // Launch shape of the s8 integer MFMA kernel for operand-order activations
-// (tern_s8mma.hip): a wave tile of token_blocks x 16 tokens by strips x 16
-// outputs, (tb, s) in {(2,2), (2,4), (4,2), (4,4), (8,2)}. The kernel for
-// row-major activations (tern_s8.hip) has one fixed shape.
+// (tern_s8mma.hip), also used by the bf16 prefill kernel (tern_b16mma.hip):
+// a wave tile of token_blocks x 16 tokens by strips x 16 outputs, (tb, s) in
+// {(2,2), (2,4), (4,2), (4,4), (8,2)}. The kernel for row-major activations
+// (tern_s8.hip) has one fixed shape.
 struct S8Plan {
   int token_blocks;
   int strips;
   bool xcd_order;  // give each XCD a contiguous run of tiles (else plain block order)
+  int k_parts;     // s8: K split over workgroups (> 1: fp32 partials in the workspace, then a reduce kernel)
+  int depth;       // s8: k-tiles in flight, 2 or 4
 };
 
 struct S8Args {
@@ -81,8 +84,11 @@ int small_t_lds_bytes(int tokens_per_tile, int strips, int waves, int K);
 // instead of row-major.
 int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
                     void* stream);
-int launch_s8(const S8Args& a, const S8Plan& p, void* stream);
-int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* stream);
+// ws: s8_partial_bytes(p, T, N) bytes of fp32 partials (k_parts > 1; operand
+// order only), may be NULL when that is 0.
+int launch_s8(const S8Args& a, const S8Plan& p, void* ws, void* stream);
+size_t s8_partial_bytes(const S8Plan& p, int T, int N);
+int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* ws, void* stream);
 // bf16 prefill contraction (tern_b16mma.hip): the small_t_tiled rung above
 // one 16-token tile; same tile plan as the s8 contraction.
 int launch_b16_prefill(const SmallTArgs& a, const S8Plan& p, void* stream);

@@ -343,8 +343,9 @@ int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bo
   return (int)hipGetLastError();
 }
 
-int launch_s8(const S8Args& a, const S8Plan& p, void* stream) {
-  if (a.q_operand_order) return launch_s8_operand_order(a, p, stream);
+int launch_s8(const S8Args& a, const S8Plan& p, void* ws, void* stream) {
+  if (a.q_operand_order) return launch_s8_operand_order(a, p, ws, stream);
+  if (p.k_parts != 1) return (int)hipErrorInvalidValue;
   hipStream_t st = (hipStream_t)stream;
   const bool dbg = a.acc_out != nullptr;
   if (dbg)

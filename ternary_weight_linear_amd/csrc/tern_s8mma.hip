@@ -45,15 +45,35 @@ struct S8mStage {
   uint32_t sw[S][GPT / 2];  // fp16 scale pairs of row (lane & 15)
 };
 
-template <int GPT, int TB, int S, bool DEBUG_ACC>
+// The workgroup's side of a k-tile handoff in the D-deep pipeline: wait until
+// at most N of this wave's loads are outstanding (they retire in order), then
+// the barrier, without the workgroup fence of __syncthreads() (that fence
+// would wait for every outstanding buffer-to-LDS load and throw the lead
+// away). The "memory" clobber keeps the compiler from moving loads or LDS
+// reads across it.
+template <int N>
+__device__ __forceinline__ void s8m_handoff() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// D: k-tiles in flight. D = 2 is the double-buffered pipeline of the
+// compute-bound shapes; D = 4 keeps three k-tiles of activations and codes in
+// flight for the short, memory-bound prefills. gridDim.y = Pk splits the
+// k-tiles over workgroups (Pk > 1: fp32 partial totals to part[Pk][T][N],
+// added by tern_s8m_reduce_kernel).
+template <int GPT, int TB, int S, int D, bool DEBUG_ACC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) tern_s8m_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ act_scale, int T, int K,
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y,
-    int32_t* __restrict__ acc_out, int N, int nx, int ny, int xrows) {
+    int32_t* __restrict__ acc_out, int N, int nx, int ny, int xrows, float* __restrict__ part) {
   constexpr int BM = 16 * TB;    // tokens per tile
   constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
   constexpr int kS8WgStrips = 4 * S;
-  __shared__ __attribute__((aligned(1024))) int8_t As[2][BM * 256];
+  static_assert(D == 2 || D == 4, "pipeline depth");
+  static_assert(!DEBUG_ACC || D == 2, "the accumulator export uses the double-buffered pipeline");
+  __shared__ __attribute__((aligned(1024))) int8_t As[D][BM * 256];
 
   // Tile (ty, tx) of this workgroup. xrows == 0: plain order, output blocks
   // fastest. xrows > 0 (ny == 8 * xrows): block b runs on XCD b % 8 as its
@@ -77,6 +97,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int NS = N >> 4, KT = K >> 8, NG = K / (256 / GPT);
+  const int Pk = gridDim.y, pk = blockIdx.y;
+  const int kt0 = (pk * KT) / Pk;
+  const int nkt = ((pk + 1) * KT) / Pk - kt0;  // >= 1: Pk <= KT
   const int t0 = ty * BM;
   const int nt = min(BM, T - t0);
   const int st0 = tx * kS8WgStrips + wave * S;  // first strip of this wave
@@ -174,37 +197,93 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
     }
   };
 
-  // Pipeline, one barrier per k-tile: the activation tile and the codes of
-  // k-tile kt+1 are requested before the MFMAs of k-tile kt; then each wave
-  // waits for its loads and meets the others at the barrier, after which
-  // tile kt+1 is complete in LDS and nobody reads tile kt's buffer any more.
-  // The loop runs k-tiles in pairs (buffers 0 then 1) with no exit in
-  // between, so the totals keep their registers; with an even tile count the
-  // last pair re-requests the last tile, with an odd one the tail computes
-  // it from buffer 0.
-  S8mStage<GPT, S> wA, wB;
-  stage_a(0, 0);
-  load_w(0, wA);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    stage_a(kt + 1, 1);
-    load_w(kt + 1, wB);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kt, 0, wA);
+  if constexpr (D == 2) {
+    // Pipeline, one barrier per k-tile: the activation tile and the codes of
+    // k-tile kt+1 are requested before the MFMAs of k-tile kt; then each wave
+    // waits for its loads and meets the others at the barrier, after which
+    // tile kt+1 is complete in LDS and nobody reads tile kt's buffer any more.
+    // The loop runs k-tiles in pairs (buffers 0 then 1) with no exit in
+    // between, so the totals keep their registers; with an even tile count the
+    // last pair re-requests the last tile, with an odd one the tail computes
+    // it from buffer 0.
+    const int klast = kt0 + nkt - 1;
+    S8mStage<GPT, S> wA, wB;
+    stage_a(kt0, 0);
+    load_w(kt0, wA);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int k2 = min(kt + 2, KT - 1);
-    stage_a(k2, 0);
-    load_w(k2, wA);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kt + 1, 1, wB);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    int kt = kt0;
+    for (; kt + 2 <= kt0 + nkt; kt += 2) {
+      stage_a(kt + 1, 1);
+      load_w(kt + 1, wB);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kt, 0, wA);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const int k2 = min(kt + 2, klast);
+      stage_a(k2, 0);
+      load_w(k2, wA);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kt + 1, 1, wB);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (kt <= klast) compute(kt, 0, wA);
+  } else {
+    // Ring of D buffers: k-tile i sits in activation buffer i % D and code
+    // stage i % D (i counted from kt0). Iteration i requests k-tile i + D - 1
+    // (clamped to the last one, so every iteration issues the same TB + 2S
+    // loads per wave) into the buffer of k-tile i - 1, which every wave
+    // finished before the previous barrier, computes k-tile i, and hands over
+    // k-tile i + 1: at most (D - 2) iterations of loads may stay outstanding.
+    constexpr int L = TB + 2 * S;  // loads per wave per k-tile
+    S8mStage<GPT, S> ring[D];
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) {
+      const int kn = kt0 + min(j, nkt - 1);
+      stage_a(kn, j);
+      load_w(kn, ring[j]);
+    }
+    s8m_handoff<(D - 2) * L>();
+    int i = 0;
+    for (; i + D <= nkt; i += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int kn = kt0 + min(i + j + D - 1, nkt - 1);
+        stage_a(kn, (j + D - 1) % D);
+        load_w(kn, ring[(j + D - 1) % D]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kt0 + i + j, j, ring[j]);
+        s8m_handoff<(D - 2) * L>();
+      }
+    }
+    // Tail: fewer than D k-tiles left, all requested already; k-tile i is in
+    // place, the others are waited for one by one.
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) {
+      if (i + j < nkt) {  // uniform over the workgroup
+        if (j > 0) s8m_handoff<0>();
+        compute(kt0 + i + j, j, ring[j]);
+      }
+    }
   }
-  if (kt < KT) compute(kt, 0, wA);
 
+  if (!DEBUG_ACC && Pk > 1) {
+    // Partial totals of this K part, 2^-6 taken out; the reduce kernel adds
+    // the parts in ascending order and applies the token scales.
+    float* mine = part + (size_t)pk * T * N;
+#pragma unroll
+    for (int a = 0; a < TB; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tl = a * 16 + 4 * g + e;
+        if (tl >= nt) continue;
+#pragma unroll
+        for (int c = 0; c < S; ++c)
+          if (c < nst) mine[(size_t)(t0 + tl) * N + (st0 + c) * 16 + r] = tot[a][c][e] * 0.015625f;
+      }
+    return;
+  }
   if (!DEBUG_ACC) {
 #pragma unroll
     for (int a = 0; a < TB; ++a)
@@ -220,42 +299,79 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
   }
 }
 
-template <int GPT, int TB, int S, bool DEBUG_ACC>
-hipError_t launch_s8m_t(const S8Args& a, bool xcd_order, hipStream_t st) {
+// y[t][n] = act_scale[t] * sum_{p < Pk} part[p][t][n], parts in ascending
+// order; four outputs per thread.
+__global__ void __launch_bounds__(256) tern_s8m_reduce_kernel(const float* __restrict__ part,
+                                                             const float* __restrict__ act_scale,
+                                                             float* __restrict__ y, int T, int N, int Pk) {
+  const int n4 = N >> 2;
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)T * n4) return;
+  const int t = (int)(i / n4);
+  const f32x4* src = (const f32x4*)part + i;
+  f32x4 sum = src[0];
+  for (int p = 1; p < Pk; ++p) sum += __builtin_nontemporal_load(src + (size_t)p * T * n4);
+  ((f32x4*)y)[i] = sum * act_scale[t];
+}
+
+template <int GPT, int TB, int S, int D, bool DEBUG_ACC>
+hipError_t launch_s8m_t(const S8Args& a, const S8Plan& p, float* part, hipStream_t st) {
   constexpr int kS8WgStrips = 4 * S;
   const int NS = a.N / 16;
   const int nx = (NS + kS8WgStrips - 1) / kS8WgStrips;
   const int ny = (a.T + 16 * TB - 1) / (16 * TB);
-  const int xrows = (xcd_order && ny % 8 == 0) ? ny / 8 : 0;
-  const int blocks = nx * ny;
-  hipLaunchKernelGGL((tern_s8m_kernel<GPT, TB, S, DEBUG_ACC>), dim3(blocks), dim3(256), 0, st, a.q,
-                     a.act_scale, a.T, a.K, (const u32x4*)a.codes, a.scales, a.y, a.acc_out, a.N, nx,
-                     ny, xrows);
+  const int xrows = (p.xcd_order && ny % 8 == 0) ? ny / 8 : 0;
+  hipLaunchKernelGGL((tern_s8m_kernel<GPT, TB, S, D, DEBUG_ACC>), dim3(nx * ny, p.k_parts), dim3(256), 0,
+                     st, a.q, a.act_scale, a.T, a.K, (const u32x4*)a.codes, a.scales, a.y, a.acc_out,
+                     a.N, nx, ny, xrows, part);
   return hipGetLastError();
 }
 
+template <int GPT, int TB, int S, bool DEBUG_ACC>
+hipError_t launch_s8m_d(const S8Args& a, const S8Plan& p, float* part, hipStream_t st) {
+  if constexpr (DEBUG_ACC || TB * S >= 16) {
+    // (the 64 x 64 wave tile has no registers left for two more code stages)
+    return launch_s8m_t<GPT, TB, S, 2, DEBUG_ACC>(a, p, part, st);
+  } else {
+    return p.depth == 4 ? launch_s8m_t<GPT, TB, S, 4, false>(a, p, part, st)
+                        : launch_s8m_t<GPT, TB, S, 2, false>(a, p, part, st);
+  }
+}
+
 template <int GPT, bool DEBUG_ACC>
-hipError_t launch_s8m_g(const S8Args& a, int tb, int s, bool x, hipStream_t st) {
-  switch (tb * 16 + s) {
-    case 2 * 16 + 2: return launch_s8m_t<GPT, 2, 2, DEBUG_ACC>(a, x, st);
-    case 2 * 16 + 4: return launch_s8m_t<GPT, 2, 4, DEBUG_ACC>(a, x, st);
-    case 4 * 16 + 2: return launch_s8m_t<GPT, 4, 2, DEBUG_ACC>(a, x, st);
-    case 4 * 16 + 4: return launch_s8m_t<GPT, 4, 4, DEBUG_ACC>(a, x, st);
-    case 8 * 16 + 2: return launch_s8m_t<GPT, 8, 2, DEBUG_ACC>(a, x, st);
+hipError_t launch_s8m_g(const S8Args& a, const S8Plan& p, float* part, hipStream_t st) {
+  switch (p.token_blocks * 16 + p.strips) {
+    case 2 * 16 + 2: return launch_s8m_d<GPT, 2, 2, DEBUG_ACC>(a, p, part, st);
+    case 2 * 16 + 4: return launch_s8m_d<GPT, 2, 4, DEBUG_ACC>(a, p, part, st);
+    case 4 * 16 + 2: return launch_s8m_d<GPT, 4, 2, DEBUG_ACC>(a, p, part, st);
+    case 4 * 16 + 4: return launch_s8m_d<GPT, 4, 4, DEBUG_ACC>(a, p, part, st);
+    case 8 * 16 + 2: return launch_s8m_t<GPT, 8, 2, 2, DEBUG_ACC>(a, p, part, st);  // LDS: double buffer only
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* stream) {
+int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* ws, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool dbg = a.acc_out != nullptr;
-  const int tb = p.token_blocks, s = p.strips;
-  const bool x = p.xcd_order;
+  if (p.k_parts < 1 || p.k_parts > a.K / 256 || (p.depth != 2 && p.depth != 4)) return (int)hipErrorInvalidValue;
+  if (p.k_parts > 1 && (dbg || ws == nullptr || a.N % 4 != 0)) return (int)hipErrorInvalidValue;
+  float* part = p.k_parts > 1 ? (float*)ws : nullptr;
+  hipError_t e;
   if (a.G == 128)
-    return (int)(dbg ? launch_s8m_g<2, true>(a, tb, s, x, st) : launch_s8m_g<2, false>(a, tb, s, x, st));
-  return (int)(dbg ? launch_s8m_g<4, true>(a, tb, s, x, st) : launch_s8m_g<4, false>(a, tb, s, x, st));
+    e = dbg ? launch_s8m_g<2, true>(a, p, part, st) : launch_s8m_g<2, false>(a, p, part, st);
+  else
+    e = dbg ? launch_s8m_g<4, true>(a, p, part, st) : launch_s8m_g<4, false>(a, p, part, st);
+  if (e != hipSuccess || p.k_parts == 1) return (int)e;
+  const long n = (long)a.T * (a.N / 4);
+  hipLaunchKernelGGL(tern_s8m_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     (const float*)part, a.act_scale, a.y, a.T, a.N, p.k_parts);
+  return (int)hipGetLastError();
+}
+
+size_t s8_partial_bytes(const S8Plan& p, int T, int N) {
+  return p.k_parts > 1 ? (size_t)p.k_parts * T * N * sizeof(float) : 0;
 }
 
 }  // namespace tern
