@@ -157,7 +157,9 @@ tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float
 
 /*
  * Device workspace tern_linear needs for this call (bytes, 0 if none). The s8
- * rung keeps the int8 activations and their scales there; small_t and
+ * rung keeps the int8 activations and their scales there, and on short
+ * prefills of narrow layers also fp32 partial totals when it splits K across
+ * workgroups (a second kernel adds them in a fixed order); small_t and
  * small_t_tiled (up to 16 tokens) keep fp32 partial sums there when they
  * split K across workgroups (narrow layers with a long K; then a second
  * kernel adds the parts in a fixed order). The contents need no initialisation and are not preserved. Every scratch
@@ -187,7 +189,8 @@ size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung);
  * the largest magnitude M of its 256-wide k-tile (exact for values down to
  * 2^-14 M, rounded by at most 2^-22 M below that); s8 computes exact int32
  * group accumulators and y = scale_t * sum_g s[n][g] * acc in fp32, groups in
- * ascending order.
+ * ascending order (when K is split across workgroups: ascending within each
+ * part, then the parts' totals added in ascending order).
  */
 tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float* y,
                         tern_rung rung, void* ws, size_t ws_bytes, void* stream);
@@ -197,7 +200,8 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
  * tern_quant_act_s8 (device, async): y[t][n] = scale_t * sum_g s[n][g] *
  * acc[t][n][g] in fp32, groups ascending -- the same kernel and numerics as
  * tern_linear(..., TERN_RUNG_S8, ...) after its quantisation step (which uses
- * TERN_Q_OPERAND_ORDER). Lets a caller quantise one activation once and apply
+ * TERN_Q_OPERAND_ORDER), except that this call never splits K (it takes no
+ * workspace). Lets a caller quantise one activation once and apply
  * several projections to it. q: device int8 [T][K] in `layout` (16-byte
  * aligned); act_scale: device float [T]; y: device float [T][N] (16-byte
  * aligned). Counts as an s8 launch in the probe.
