@@ -209,6 +209,8 @@ hipError_t launch_b16m_t(const SmallTArgs& a, bool xcd_order, hipStream_t st) {
 template <int GPT>
 hipError_t launch_b16m_g(const SmallTArgs& a, int tb, int s, bool x, hipStream_t st) {
   switch (tb * 16 + s) {
+    case 2 * 16 + 1: return launch_b16m_t<GPT, 2, 1>(a, x, st);
+    case 4 * 16 + 1: return launch_b16m_t<GPT, 4, 1>(a, x, st);
     case 2 * 16 + 2: return launch_b16m_t<GPT, 2, 2>(a, x, st);
     case 2 * 16 + 4: return launch_b16m_t<GPT, 2, 4>(a, x, st);
     case 4 * 16 + 2: return launch_b16m_t<GPT, 4, 2>(a, x, st);

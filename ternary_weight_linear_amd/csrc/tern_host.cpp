@@ -188,7 +188,7 @@ Config read_config() {
       bad("TERN_TUNE_S8_BM", s);
   }
   if (const char* s = getenv("TERN_TUNE_S8_STRIPS")) {
-    if (parse_int(s, 0, 4, &v) && (v == 0 || v == 2 || v == 4))
+    if (parse_int(s, 0, 4, &v) && (v == 0 || v == 1 || v == 2 || v == 4))
       c.tune_s8_strips = (int)v;
     else
       bad("TERN_TUNE_S8_STRIPS", s);
@@ -386,14 +386,16 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   tern::S8Plan p;
   // Wave tile 64 tokens x 64 outputs (4 token blocks x 4 strips) where that
   // still gives at least 4 workgroups per CU; 64 x 32 otherwise (narrow
-  // layers, short prefills); 32-token tiles for T <= 32 so padded tokens do
-  // not waste the matrix cores. (128-token tiles cost registers, and
-  // occupancy, without paying back on either 27B-class shape.)
+  // layers); 32-token tiles for T <= 32 so padded tokens do not waste the
+  // matrix cores, and one strip per wave up to T = 64, where the kernel is
+  // bound by load latency and wants as many waves streaming as it can get.
+  // (128-token tiles cost registers, and occupancy, without paying back on
+  // either 27B-class shape.)
   const int tb = c.tune_s8_bm ? c.tune_s8_bm / 16 : (T > 32 ? 4 : 2);
   const long tiles4 = (long)((n / 16 + 15) / 16) * ((T + 16 * tb - 1) / (16 * tb));
-  int strips = tiles4 >= 1024 ? 4 : 2;
+  int strips = T <= 64 ? 1 : (tiles4 >= 1024 ? 4 : 2);
   if (c.tune_s8_strips) strips = c.tune_s8_strips;
-  if (tb == 8) strips = 2;
+  if (tb == 8) strips = 2;  // the one 128-token shape
   p.token_blocks = tb;
   p.strips = strips;
   p.xcd_order = c.tune_s8_raster != 1;
