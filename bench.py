@@ -160,6 +160,48 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
     dec_bytes = sum(algorithmic_bytes(1, b.n, b.k, b.group) for L in layers for b in L)
     log(f"stack decode pass {t_dec * 1e3:.3f} ms ({dec_bytes / t_dec / 1e9:.0f} GB/s), "
         f"prefill pass {t_pre * 1e3:.2f} ms ({ops / t_pre / 1e12:.0f} TOPS)")
+
+    # Fused variant: q|k|v and gate|up share their input, so each pair or
+    # triple is one matrix (the packed layout is strip-major, so stacking
+    # along N is concatenating the code and scale buffers): 4 launches per
+    # layer instead of 7, the same bytes.
+    del layers
+    torch.cuda.empty_cache()
+    groups = [(0, 1, 2), (3,), (4, 5), (6,)]
+
+    def fuse(parts):
+        if len(parts) == 1:
+            b = base[parts[0]]
+            return tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group)
+        bs = [base[i] for i in parts]
+        return tl.TernaryWeights(torch.cat([b.codes for b in bs]), torch.cat([b.scales for b in bs]),
+                                 sum(b.n for b in bs), bs[0].k, bs[0].group)
+
+    flayers = [[fuse(g) for g in groups] for _ in range(ts.STACK_LAYERS)]
+    fx1 = [xs1[g[0]] for g in groups]
+    fxp = [xsp[g[0]] for g in groups]
+    fy1 = [torch.empty((1, b.n), dtype=torch.float32, device=dev) for b in flayers[0]]
+    fyp = [torch.empty((1024, b.n), dtype=torch.float32, device=dev) for b in flayers[0]]
+    fwsz = max(tl.workspace_bytes(1024, b.n, b.k, b.group) for b in flayers[0])
+    fwsp = torch.empty((fwsz,), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def fdecode_pass(_):
+        for L in flayers:
+            for j, b in enumerate(L):
+                tl.linear(fx1[j], b, y=fy1[j])
+
+    def fprefill_pass(_):
+        for c in range(2):
+            for L in flayers:
+                for j, b in enumerate(L):
+                    tl.linear(fxp[j][1024 * c:1024 * (c + 1)], b, y=fyp[j], workspace=fwsp)
+
+    f_dec = graph_time(torch, fdecode_pass, decode_reps, 1) / decode_reps
+    f_pre = graph_time(torch, fprefill_pass, prefill_reps, 1) / prefill_reps
+    f_bytes = sum(algorithmic_bytes(1, b.n, b.k, b.group) for L in flayers for b in L)
+    log(f"stack, fused q|k|v and gate|up: decode pass {f_dec * 1e3:.3f} ms "
+        f"({f_bytes / f_dec / 1e9:.0f} GB/s), prefill pass {f_pre * 1e3:.2f} ms ({ops / f_pre / 1e12:.0f} TOPS)")
     return {"workload": "64-layer stack, 448 projections (6.33 GB packed); decode T=1 pass; "
                         "2048-token prefill in two 1024-token chunks (s8)",
             "decode": {"ms_per_pass": round(t_dec * 1e3, 4), "GB/s": round(dec_bytes / t_dec / 1e9, 1),
@@ -167,7 +209,13 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
                        "launches": ts.STACK_LAYERS * len(base)},
             "prefill": {"ms_per_pass": round(t_pre * 1e3, 3), "TOPS": round(ops / t_pre / 1e12, 1),
                         "frac_of_i8_peak": round(ops / t_pre / 1e12 / I8_PEAK_TOPS, 4),
-                        "tokens_per_s": round(2048 / t_pre, 1)}}
+                        "tokens_per_s": round(2048 / t_pre, 1)},
+            "fused_qkv_gate_up": {
+                "launches_per_pass": ts.STACK_LAYERS * len(groups),
+                "decode": {"ms_per_pass": round(f_dec * 1e3, 4), "GB/s": round(f_bytes / f_dec / 1e9, 1),
+                           "frac_of_hbm_peak": round(f_bytes / f_dec / 1e9 / HBM_PEAK_GBS, 4)},
+                "prefill": {"ms_per_pass": round(f_pre * 1e3, 3), "TOPS": round(ops / f_pre / 1e12, 1),
+                            "tokens_per_s": round(2048 / f_pre, 1)}}}
 
 
 SMALL_T = (2, 4, 8, 12, 16)

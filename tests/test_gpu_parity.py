@@ -283,6 +283,26 @@ def test_batch_invariance(tl, torch, mid):
                 assert rel_l2(yt[0].numpy(), y[t].numpy()) <= 1e-6, (rung, t)
 
 
+def test_stacked_matrices_concatenate(tl, torch):
+    """The packed layout is strip-major, so matrices stacked along N (fused
+    q|k|v, gate|up) are their code and scale buffers concatenated; on exact
+    inputs every rung gives each part's outputs bit for bit."""
+    k, G = 768, 128
+    rng = np.random.default_rng(71)
+    parts = [(ts.draw_weights(rng, n, k, 0.4), ts.pow2_scales(n, k, G, seed=n)) for n in (48, 96, 32)]
+    Ws = [tl.TernaryWeights.from_host(w, s) for w, s in parts]
+    F = tl.TernaryWeights(torch.cat([W.codes for W in Ws]), torch.cat([W.scales for W in Ws]),
+                          sum(W.n for W in Ws), k, G)
+    for T in (1, 5, 23):
+        x_dev = to_dev_bf16(torch, ts.integer_activations(k, T, seed=T + 70))
+        for rung in RUNGS:
+            if not rung_ok(rung, T):
+                continue
+            yf = tl.linear(x_dev, F, rung=rung).cpu().numpy()
+            ys = np.concatenate([tl.linear(x_dev, W, rung=rung).cpu().numpy() for W in Ws], axis=1)
+            assert np.array_equal(yf.view(np.uint32), ys.view(np.uint32)), (rung, T)
+
+
 # ------------------------------------------------------ full layer shapes
 
 
