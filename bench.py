@@ -259,9 +259,10 @@ def small_t_leg(torch, ts, tl, dev, steps=100):
 
 
 def kernels_only(torch, ts, tl, dev, n):
-    """For rocprofv3 --pmc runs: n launches each of the gemv kernel (gate_up,
-    T=1) and the s8 rung (quant + contraction, gate_up, T=2048), weights
-    rotated over > 512 MB, then a plain 64 MiB device copy whose byte counters
+    """For rocprofv3 --pmc runs, all on gate_up with weights rotated over
+    > 512 MB: n launches of the gemv kernel (T=1), n/10 of the s8 rung (quant
+    + contraction, T=2048), n/10 of the bf16 prefill (T=2048), n of the T=8
+    draft-verify batch, then plain 64 MiB device copies whose byte counters
     calibrate FETCH_SIZE / WRITE_SIZE."""
     w = ts.weights(ts.GATE_UP)
     b = tl.TernaryWeights.from_host(w.w, w.s, device=dev)
@@ -279,6 +280,14 @@ def kernels_only(torch, ts, tl, dev, n):
     torch.cuda.synchronize()
     for i in range(max(1, n // 10)):
         tl.linear(x8, sets[i % len(sets)], y=y8, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(max(1, n // 10)):  # bf16 prefill (small_t_tiled above 16 tokens)
+        tl.linear(x8, sets[i % len(sets)], rung="small_t_tiled", y=y8)
+    torch.cuda.synchronize()
+    x16 = torch.from_numpy(ts.activations(w, 8).view(np.int16)).to(dev).view(torch.bfloat16)
+    y16 = torch.empty((8, b.n), dtype=torch.float32, device=dev)
+    for i in range(n):  # draft-verify batch T = 8 (activation-tiled kernel on this wide layer)
+        tl.linear(x16, sets[i % len(sets)], y=y16)
     torch.cuda.synchronize()
     src = torch.empty(64 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
