@@ -37,11 +37,12 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 MALL_BYTES = 256 * 2**20
 ROTATE_BYTES = 600e6  # > 2x the Infinity Cache
 METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
-# Sources of the kernels whose HBM traffic is stored (gemv, quant, s8) and of
+# Sources of the kernels whose HBM traffic is stored (gemv, quant, s8, bf16
+# prefill, activation-tiled small-T) and of
 # their launch plans: a change to any of them voids the stored counters.
 KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
-               for f in ("tern_limb.hip", "tern_s8.hip", "tern_s8mma.hip", "tern_device.h",
-                         "tern_internal.h", "tern_host.cpp")]
+               for f in ("tern_limb.hip", "tern_s8.hip", "tern_s8mma.hip", "tern_b16mma.hip",
+                         "tern_tile.hip", "tern_device.h", "tern_internal.h", "tern_host.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -435,7 +436,8 @@ def main():
             "metric": "bf16 TFLOP/s at T=2048 (rung small_t_tiled, no activation quantisation)",
             "per_shape": b16,
             "roofline": {"bound": "mfma", "achieved": ach16, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ach16 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(ach16 / BF16_PEAK_TFLOPS, 4),
+                         "traffic": stored_traffic(f"bf16_prefill:{dom}"),
                          "kernel": f"tern_b16m_kernel (bf16 prefill) on {dom}, T={T}"}}
 
     small = None
