@@ -162,7 +162,8 @@ tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float
  * workgroups (a second kernel adds them in a fixed order); small_t and
  * small_t_tiled (up to 16 tokens) keep fp32 partial sums there when they
  * split K across workgroups (narrow layers with a long K; then a second
- * kernel adds the parts in a fixed order). The contents need no initialisation and are not preserved. Every scratch
+ * kernel adds the parts in a fixed order), or, on wide layers at T <= 4, the
+ * int8 limbs of the activations and their per-k-tile exponents. The contents need no initialisation and are not preserved. Every scratch
  * buffer of every rung is counted here; a call given less fails with
  * TERN_ERR_WORKSPACE ("NINFER ternary perf-tuning" notes, section 5 item 8:
  * the workspace capacity declaration must cover every scratch).
@@ -185,7 +186,8 @@ size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung);
  *        tern_workspace_bytes(T, N, K, G, rung) bytes (may be NULL/0 if that is 0)
  * Output numerics: the bf16-activation rungs (gemv, small_t, small_t_tiled)
  * accumulate exact bf16 x {-1,0,+1} products in fp32, except that the gemv
- * kernel carries each activation as a 22-bit fixed-point number relative to
+ * kernel and, on wide layers at T <= 4, small_t and small_t_tiled carry each
+ * activation as a 22-bit fixed-point number relative to
  * the largest magnitude M of its 256-wide k-tile (exact for values down to
  * 2^-14 M, rounded by at most 2^-22 M below that); s8 computes exact int32
  * group accumulators and y = scale_t * sum_g s[n][g] * acc in fp32, groups in

@@ -64,7 +64,7 @@ struct Config {
   int tune_wk = 0;                    // TERN_TUNE_WK (0 = heuristic)
   int tune_depth = 0;                 // TERN_TUNE_DEPTH (0 = heuristic)
   bool gemv_bf16 = false;             // TERN_TUNE_GEMV=bf16: time the bf16-operand gemv kernel (default: limb)
-  int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave
+  int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave, 3 = limb
 };
 
 bool parse_int(const char* s, long lo, long hi, long* out) {
@@ -178,6 +178,8 @@ Config read_config() {
       c.smallt_kernel = 1;
     else if (strcmp(s, "wave") == 0)
       c.smallt_kernel = 2;
+    else if (strcmp(s, "limb") == 0)
+      c.smallt_kernel = 3;
     else
       bad("TERN_TUNE_SMALLT", s);
   }
@@ -305,6 +307,30 @@ tern::TilePlan plan_tile(int T, int n, int k) {
 // narrow ones give it too few workgroups and run the per-wave kernel (each
 // wave loads its own activation fragments, no barriers), except for T > 8
 // with a long K, where the per-wave activation traffic grows too large.
+// The small_t limb path (tern_limbtile.hip) takes T <= 8; by default it runs
+// wide layers (>= 1024 strips) at T <= 4, one row block, where it beat the
+// bf16 activation-tiled kernel in A/B runs on MI355X (gate_up: 15.3 against
+// 15.9-16.6 us); at T = 5..8 (two row blocks) and on narrow layers it lost.
+bool small_t_limb(int T, int n, int k) {
+  (void)k;
+  const Config& c = config();
+  if (c.smallt_kernel) return c.smallt_kernel == 3 && T <= 8;
+  return T <= 4 && n / 16 >= 1024;
+}
+
+tern::LimbTilePlan plan_limbtile(int T, int n, int k) {
+  (void)T;
+  (void)k;
+  const Config& c = config();
+  tern::LimbTilePlan p;
+  const int NS = n / 16;
+  p.strips_per_wave = c.tune_strips == 2 ? 2 : 1;
+  p.waves = c.tune_waves ? std::min(c.tune_waves, 8) : 4;
+  p.depth = c.tune_depth == 4 ? 4 : 2;
+  p.strip_blocks = (NS + p.waves * p.strips_per_wave - 1) / (p.waves * p.strips_per_wave);
+  return p;
+}
+
 bool small_t_per_wave(int T, int n, int k) {
   const Config& c = config();
   if (c.smallt_kernel) return c.smallt_kernel == 2;
@@ -322,6 +348,8 @@ size_t workspace_for(int T, int n, int k, tern_rung r) {
     return align256((size_t)T * k) + align256((size_t)T * sizeof(float)) +
            tern::s8_partial_bytes(plan_s8(T, n, k, true), T, n);
   if (b16_prefill(T, r)) return 0;
+  if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && small_t_limb(T, n, k))
+    return tern::limbtile_workspace_bytes(T, k);
   if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && !small_t_per_wave(T, n, k))
     return tern::tile_workspace_bytes(plan_tile(T, n, k), n);
   return 0;
@@ -612,6 +640,9 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
       else
         err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
       if (err) return hip_fail(err, "gemv launch");
+    } else if (small_t_limb(T, n, k)) {
+      int err = tern::launch_limbtile(a, plan_limbtile(T, n, k), ws, stream);
+      if (err) return hip_fail(err, "small_t limb launch");
     } else if (b16_prefill(T, r)) {
       int err = tern::launch_b16_prefill(a, plan_s8(T, n, k, false), stream);
       if (err) return hip_fail(err, "bf16 prefill launch");

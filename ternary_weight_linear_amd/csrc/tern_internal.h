@@ -67,6 +67,14 @@ struct LimbPlan {
 };
 constexpr int kLimbMaxLds = 65536;
 
+// Launch shape of the small_t limb path (tern_limbtile.hip), T <= 8.
+struct LimbTilePlan {
+  int strips_per_wave;  // S: 1 or 2
+  int waves;            // Ws: compute waves per workgroup (1..8); plus a loader wave
+  int depth;            // D: k-tiles in flight, 2 or 4
+  int strip_blocks;     // grid.x = ceil(NS / (Ws * S))
+};
+
 // All launchers return 0 on success or a hipError_t value.
 int launch_small_t(const SmallTArgs& a, const SmallTPlan& p, void* stream);
 // ws: tile_workspace_bytes(p, N) bytes of fp32 partials (k_parts > 1, added
@@ -75,6 +83,10 @@ int launch_tile(const SmallTArgs& a, const TilePlan& p, void* ws, void* stream);
 size_t tile_workspace_bytes(const TilePlan& p, int N);
 // T <= 5 tokens; needs limb_lds_bytes(T, K, G, p) <= kLimbMaxLds.
 int launch_limb(const SmallTArgs& a, const LimbPlan& p, void* stream);
+// T <= 8: limbs made by a prep kernel into ws (limbtile_workspace_bytes(T, K)
+// bytes), then the contraction.
+int launch_limbtile(const SmallTArgs& a, const LimbTilePlan& p, void* ws, void* stream);
+size_t limbtile_workspace_bytes(int T, int K);
 int limb_lds_bytes(int T, int K, int G, const LimbPlan& p);
 // Largest waves-per-block the bf16 kernel accepts for this variant (LDS and
 // register limits; 0 if none fits).

@@ -62,48 +62,6 @@ struct LimbStage {
   u32x4 P[S];  // the lane's 16 code bytes of each of the wave's strips
 };
 
-// Largest |x| over 8 bf16 (as fp32 bit patterns: integer order = magnitude order).
-__device__ __forceinline__ uint32_t absmax8(const u32x4& v) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m = max(m, max((v[i] << 16) & 0x7fff0000u, v[i] & 0x7fff0000u));
-  return m;
-}
-
-// Max over the 16 lanes of a DPP row (each lane ends with the row's max).
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
-  return v;
-}
-
-// Fixed-point bits of one activation: f = x * 2^-d + 1.5 * 2^23 rounds x * 2^-d
-// to the nearest integer v (ties to even) and holds 0x4B400000 + v. The limb
-// bytes are then byte 0 of f, byte 1 of f + 128 and byte 2 of f + 32896 -
-// 0x400000 (balanced base-256 digits of v; the 0x4B400000 offset does not
-// reach bytes 0 and 1 and is taken out of byte 2).
-struct LimbSrc {
-  uint32_t u0, u1, u2;
-};
-__device__ __forceinline__ LimbSrc limb_src(uint32_t xbits_f32, int d) {
-  const float f = __builtin_ldexpf(__uint_as_float(xbits_f32), -d) + 12582912.0f;
-  const uint32_t b = __float_as_uint(f);
-  return LimbSrc{b, b + 128u, b - 0x3F7F80u};
-}
-
-// Operand-order dword from four elements' limb sources: bytes [ya, xa, yb, xb]
-// at byte position L of each (x = k 2i, 2i+1 of the low half, y = k 32+2i,
-// 33+2i of the high half of the 64-wide block).
-template <int L>
-__device__ __forceinline__ uint32_t limb_dword(uint32_t xa, uint32_t xb, uint32_t ya, uint32_t yb) {
-  constexpr uint32_t sel = (4u + L) | ((uint32_t)L << 8) | 0x0c0c0000u;
-  const uint32_t p = __builtin_amdgcn_perm(ya, xa, sel);  // [ya.L, xa.L, 0, 0]
-  const uint32_t q = __builtin_amdgcn_perm(yb, xb, sel);  // [yb.L, xb.L, 0, 0]
-  return __builtin_amdgcn_perm(q, p, 0x05040100u);        // [ya.L, xa.L, yb.L, xb.L]
-}
-
 // TT: 1 (single token: rows 0..2) or 5 (T <= 5 tokens: rows 0..3T-1).
 // Dynamic LDS (limb_lds_bytes): 3T limb rows of K + 64 bytes, the tile
 // exponents d [T][K/256] (int), then the workgroup's scales in their packed

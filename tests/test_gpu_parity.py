@@ -493,6 +493,49 @@ def test_s8_k_split_exact(kparts, depth, G):
     assert r.stdout.split("BAD")[1].strip() == "[]", r.stdout
 
 
+_LIMBTILE_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import oracle, tern_synth as ts, ternary_weight_linear_amd as tl
+n, k, G = 96, 2560, int(sys.argv[2])
+rng = np.random.default_rng(k + G + 1)
+w = ts.draw_weights(rng, n, k, 0.4)
+s = ts.pow2_scales(n, k, G, seed=13)
+W = tl.TernaryWeights.from_host(w, s)
+bad = []
+for T in (2, 3, 4, 5, 7, 8):
+    xb = ts.integer_activations(k, T, seed=T + 30)
+    x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    ref = oracle.linear_bf16(xb, w, s)
+    for rung in ("small_t", "small_t_tiled"):
+        tl.probe_reset()
+        y = tl.linear(x, W, rung=rung).cpu().numpy().astype(np.float64)
+        if not np.array_equal(y, ref):
+            bad.append((T, rung))
+print("BAD", bad)
+"""
+
+
+@pytest.mark.parametrize("strips,waves,depth,G", [(1, 4, 2, 128), (2, 3, 4, 64), (1, 8, 4, 128),
+                                                  (2, 4, 2, 128)])
+def test_small_t_limb_path_exact(strips, waves, depth, G):
+    """The small_t limb path (limbs made by a prep kernel, int8 MFMA) forced
+    for T = 2..8, one and two row blocks, on integer activations and
+    power-of-two scales, where the limbs and every fp32 sum are exact: y must
+    equal the oracle bit for bit. Partial strip blocks (6 strips) and waves
+    without strips included."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, TERN_TUNE_SMALLT="limb", TERN_TUNE_STRIPS=str(strips),
+               TERN_TUNE_WAVES=str(waves), TERN_TUNE_DEPTH=str(depth))
+    r = subprocess.run([sys.executable, "-c", _LIMBTILE_CHILD, root, str(G)], env=env,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split("BAD")[1].strip() == "[]", r.stdout
+
+
 # ------------------------------------- activation dynamic range (bf16 rungs)
 
 

@@ -136,6 +136,10 @@ def test_workspace_sizes(tl):
     assert tl.workspace_bytes(16, 5120, 5120, 128) == 0
     assert tl.workspace_bytes(4, 5120, 17408, 128) == 0
     assert tl.workspace_bytes(8, 34816, 5120, 128) == 0
+    # wide layers at T <= 4 take the limb path: one row block of 16 int8 limb
+    # rows and the per-token k-tile exponents, each 256-byte aligned
+    assert tl.workspace_bytes(4, 34816, 5120, 128) == 16 * 5120 + 512
+    assert tl.workspace_bytes(2, 34816, 5120, 128, "small_t_tiled") == 16 * 5120 + 512
     # the activation-tiled kernel splits a long K over workgroups: fp32
     # partials of one 16-token tile per K part
     ws16 = tl.workspace_bytes(16, 5120, 17408, 128)
