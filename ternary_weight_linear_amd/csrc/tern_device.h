@@ -81,12 +81,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // 2^E <= max|x| < 2^(E+1) and d = E - 21, v = rne(x * 2^-d) is split into
 // three balanced int8 digits v = l0 + 256 l1 + 65536 l2.
 
-// Largest |x| over 8 bf16 (as fp32 bit patterns: integer order = magnitude order).
-__device__ __forceinline__ uint32_t absmax8(const u32x4& v) {
-  uint32_t m = 0;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest |x| over the 16 bf16 of a chunk (lo, hi), as a bf16 magnitude bit
+// pattern (integer order = magnitude order), by packed 16-bit maxima.
+__device__ __forceinline__ uint32_t absmax16(const u32x4& lo, const u32x4& hi) {
+  u16x2 m = __builtin_bit_cast(u16x2, lo[0] & 0x7fff7fffu);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) m = max(m, max((v[i] << 16) & 0x7fff0000u, v[i] & 0x7fff0000u));
-  return m;
+  for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, lo[i] & 0x7fff7fffu));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, hi[i] & 0x7fff7fffu));
+  return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 // Max over the 16 lanes of a DPP row (each lane ends with the row's max).
@@ -98,29 +103,53 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   return v;
 }
 
-// Fixed-point bits of one activation: f = x * 2^-d + 1.5 * 2^23 rounds x * 2^-d
-// to the nearest integer v (ties to even) and holds 0x4B400000 + v. The limb
-// bytes are then byte 0 of f, byte 1 of f + 128 and byte 2 of f + 32896 -
-// 0x400000 (balanced base-256 digits of v; the 0x4B400000 offset does not
-// reach bytes 0 and 1 and is taken out of byte 2).
-struct LimbSrc {
-  uint32_t u0, u1, u2;
-};
-__device__ __forceinline__ LimbSrc limb_src(uint32_t xbits_f32, int d) {
-  const float f = __builtin_ldexpf(__uint_as_float(xbits_f32), -d) + 12582912.0f;
-  const uint32_t b = __float_as_uint(f);
-  return LimbSrc{b, b + 128u, b - 0x3F7F80u};
+// Exponent shift of a k-tile from its largest magnitude m (a bf16 bit
+// pattern): 2^E <= max|x| < 2^(E+1), d = E - 21.
+__device__ __forceinline__ int limb_shift(uint32_t m) { return (int)(m >> 7) - 127 - 21; }
+
+// Limb rows of one 16-element chunk. lo holds k = 2i, 2i+1 of the chunk's
+// first 8 activations in dword i, hi the 8 activations 32 further on; dword i
+// of limb row L gets the L-th digits of k = [32+2i, 2i, 33+2i, 2i+1] (the s8
+// operand order).
+//
+// Per activation f = x * 2^-d + 1.5 * 2^23, one fma: the add rounds x * 2^-d
+// to the nearest integer v (ties to even), so bits(f) = 0x4B400000 + v. The
+// balanced base-256 digits v = l0 + 256 l1 + 65536 l2 are then byte 0 of
+// bits(f), and, with w = bits(f) - 0x3F7F80 = 0x4B008080 + v, byte 1 of w
+// with its top bit flipped and byte 2 of w (adding 0x80 below each digit
+// makes the carries those of the balanced digits). Tiles whose maximum is
+// below 2^-105 (d < -126, where 2^-d is no longer a float) scale x by 2^64
+// first, which is exact.
+template <bool TINY>
+__device__ __forceinline__ void limb_chunk_t(const u32x4& lo, const u32x4& hi, float s, u32x4& o0, u32x4& o1,
+                                             u32x4& o2) {
+  constexpr float C = 12582912.0f;  // 1.5 * 2^23
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t e[4] = {lo[i] << 16, lo[i] & 0xffff0000u, hi[i] << 16, hi[i] & 0xffff0000u};  // xa xb ya yb
+    uint32_t b[4], w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float xj = TINY ? __uint_as_float(e[j]) * 0x1p64f : __uint_as_float(e[j]);
+      b[j] = __float_as_uint(__builtin_fmaf(xj, s, C));
+      w[j] = b[j] - 0x3F7F80u;
+    }
+    const uint32_t p0 = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0004u);    // [ya.0, xa.0, 0, 0]
+    const uint32_t q0 = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0004u);    // [yb.0, xb.0, 0, 0]
+    const uint32_t p12 = __builtin_amdgcn_perm(w[2], w[0], 0x02060105u);   // [ya.1, xa.1, ya.2, xa.2]
+    const uint32_t q12 = __builtin_amdgcn_perm(w[3], w[1], 0x02060105u);   // [yb.1, xb.1, yb.2, xb.2]
+    o0[i] = __builtin_amdgcn_perm(q0, p0, 0x05040100u);
+    o1[i] = __builtin_amdgcn_perm(q12, p12, 0x05040100u) ^ 0x80808080u;
+    o2[i] = __builtin_amdgcn_perm(q12, p12, 0x07060302u);
+  }
 }
 
-// Operand-order dword from four elements' limb sources: bytes [ya, xa, yb, xb]
-// at byte position L of each (x = k 2i, 2i+1 of the low half, y = k 32+2i,
-// 33+2i of the high half of the 64-wide block).
-template <int L>
-__device__ __forceinline__ uint32_t limb_dword(uint32_t xa, uint32_t xb, uint32_t ya, uint32_t yb) {
-  constexpr uint32_t sel = (4u + L) | ((uint32_t)L << 8) | 0x0c0c0000u;
-  const uint32_t p = __builtin_amdgcn_perm(ya, xa, sel);  // [ya.L, xa.L, 0, 0]
-  const uint32_t q = __builtin_amdgcn_perm(yb, xb, sel);  // [yb.L, xb.L, 0, 0]
-  return __builtin_amdgcn_perm(q, p, 0x05040100u);        // [ya.L, xa.L, yb.L, xb.L]
+__device__ __forceinline__ void limb_chunk(const u32x4& lo, const u32x4& hi, int d, u32x4& o0, u32x4& o1,
+                                           u32x4& o2) {
+  if (d < -126)
+    limb_chunk_t<true>(lo, hi, __builtin_ldexpf(1.0f, -d - 64), o0, o1, o2);
+  else
+    limb_chunk_t<false>(lo, hi, __builtin_ldexpf(1.0f, -d), o0, o1, o2);
 }
 }  // namespace dev
 }  // namespace tern

@@ -59,16 +59,8 @@ __global__ void __launch_bounds__(256) tern_limb_prep_kernel(const uint16_t* __r
     const uint16_t* src = x + (size_t)t * K + 64 * (j >> 2) + 8 * (j & 3);
     const u32x4 lo = *(const u32x4*)src;
     const u32x4 hi = *(const u32x4*)(src + 32);
-    const uint32_t m = row16_max_u32(max(absmax8(lo), absmax8(hi)));
-    d = (int)(m >> 23) - 127 - 21;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const LimbSrc xa = limb_src(lo[i] << 16, d), xb = limb_src(lo[i] & 0xffff0000u, d);
-      const LimbSrc ya = limb_src(hi[i] << 16, d), yb = limb_src(hi[i] & 0xffff0000u, d);
-      out0[i] = limb_dword<0>(xa.u0, xb.u0, ya.u0, yb.u0);
-      out1[i] = limb_dword<1>(xa.u1, xb.u1, ya.u1, yb.u1);
-      out2[i] = limb_dword<2>(xa.u2, xb.u2, ya.u2, yb.u2);
-    }
+    d = limb_shift(row16_max_u32(absmax16(lo, hi)));
+    limb_chunk(lo, hi, d, out0, out1, out2);
   }
   *(u32x4*)row = out0;
   *(u32x4*)(row + K) = out1;
