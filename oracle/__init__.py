@@ -60,6 +60,8 @@ def _load():
             "oracle_linear_s8": [p, p, i64, i64, p, p, i64, i64, p],
             "oracle_linear_s8_fp32_ordered": [p, p, i64, i64, p, p, i64, i64, p],
             "oracle_unpack_layout_v1": [p, p, i64, i64, i64, p, p],
+            "oracle_rotate_f32": [p, i64, i64, p],
+            "oracle_quant_s8_rot": [p, i64, i64, p, p],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -117,6 +119,27 @@ def quant_s8(x: np.ndarray):
     q = np.empty((T, K), np.int8)
     sc = np.empty((T,), np.float32)
     _check(_load().oracle_quant_s8(_ptr(x), T, K, _ptr(q), _ptr(sc)), "quant_s8")
+    return q, sc
+
+
+def rotate_f32(x: np.ndarray) -> np.ndarray:
+    """Blockwise (1024) orthonormal Hadamard rotation of bf16 x [T, K] in fp32
+    (fast Walsh-Hadamard butterflies, strides 1, 2, ..., 512): float32 [T, K]."""
+    x = _c(x, np.uint16)
+    T, K = x.shape
+    xr = np.empty((T, K), np.float32)
+    _check(_load().oracle_rotate_f32(_ptr(x), T, K, _ptr(xr)), "rotate_f32")
+    return xr
+
+
+def quant_s8_rot(x: np.ndarray):
+    """Rotated per-token int8 quantisation: quant_s8's rule applied to
+    rotate_f32(x). Returns (q int8 [T, K], scale float32 [T])."""
+    x = _c(x, np.uint16)
+    T, K = x.shape
+    q = np.empty((T, K), np.int8)
+    sc = np.empty((T,), np.float32)
+    _check(_load().oracle_quant_s8_rot(_ptr(x), T, K, _ptr(q), _ptr(sc)), "quant_s8_rot")
     return q, sc
 
 

@@ -36,6 +36,7 @@
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
@@ -197,6 +198,94 @@ int oracle_quant_s8(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* s
     }
   }
   fesetround(saved);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------ rotated activations */
+
+/*
+ * Blockwise Hadamard rotation of the activations. [ART] section 9 item 2:
+ * the Hadamard rotation of the original ternary model is done inside the
+ * activation quantisation, with no kernel of its own. [TUNE] section 6,
+ * constants table: the rotation works on 1024-wide blocks of a token.
+ *
+ * Readings (the pages give neither the matrix nor the arithmetic):
+ *  - per token and 1024-wide block of K, xr = (1/32) H x, H the Sylvester
+ *    Hadamard matrix of order 1024, H[i][j] = (-1)^popcount(i & j); the
+ *    factor 1/32 = 1/sqrt(1024) makes the rotation orthonormal;
+ *  - evaluated in IEEE single precision as the textbook in-place fast
+ *    Walsh-Hadamard transform: strides h = 1, 2, 4, ..., 512 in that order,
+ *    every pair (i, i + h) with (i & h) == 0 becoming (u + v, u - v), one
+ *    rounding each; then one multiply by 1/32 per element.
+ * K must be a multiple of 1024. xr: float [T][K].
+ */
+#define ROT_BLOCK 1024
+
+int oracle_rotate_f32(const uint16_t* x, int64_t T, int64_t K, float* xr) {
+  if (T < 0 || K <= 0 || K % ROT_BLOCK != 0) return ORACLE_ERR_ARGS;
+  for (int64_t i = 0; i < T * K; ++i)
+    if (!isfinite(bf16_to_float(x[i]))) return ORACLE_ERR_NONFINITE;
+  const int saved = fegetround();
+  fesetround(FE_TONEAREST);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t b = 0; b < K / ROT_BLOCK; ++b) {
+      const uint16_t* xb = x + t * K + b * ROT_BLOCK;
+      float* z = xr + t * K + b * ROT_BLOCK;
+      for (int i = 0; i < ROT_BLOCK; ++i) z[i] = bf16_to_float(xb[i]);
+      for (int h = 1; h < ROT_BLOCK; h <<= 1) {
+        for (int i = 0; i < ROT_BLOCK; ++i) {
+          if (i & h) continue;
+          const float u = z[i], v = z[i + h];
+          z[i] = u + v;
+          z[i + h] = u - v;
+        }
+      }
+      for (int i = 0; i < ROT_BLOCK; ++i) z[i] = z[i] * 0.03125f;
+    }
+  }
+  fesetround(saved);
+  return ORACLE_OK;
+}
+
+/*
+ * Rotated per-token int8 quantisation: the steps of oracle_quant_s8 applied
+ * to the rotated fp32 activations xr of oracle_rotate_f32:
+ *   a_t = max_k |xr[t][k]|;  scale_t = fl32(a_t / 127);
+ *   q[t][k] = clamp(round-half-even(fl32(xr[t][k] / scale_t)), -127, 127);
+ *   a_t == 0 gives scale_t = 0 and q[t][:] = 0.
+ */
+int oracle_quant_s8_rot(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* scale) {
+  if (T < 0 || K <= 0 || K % ROT_BLOCK != 0) return ORACLE_ERR_ARGS;
+  float* xr = (float*)malloc(sizeof(float) * (size_t)(T > 0 ? T * K : 1));
+  if (!xr) return ORACLE_ERR_ARGS;
+  const int rc = oracle_rotate_f32(x, T, K, xr);
+  if (rc != ORACLE_OK) {
+    free(xr);
+    return rc;
+  }
+  const int saved = fegetround();
+  fesetround(FE_TONEAREST);
+  for (int64_t t = 0; t < T; ++t) {
+    const float* v = xr + t * K;
+    float a = 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+      if (fabsf(v[k]) > a) a = fabsf(v[k]);
+    if (a == 0.0f) {
+      scale[t] = 0.0f;
+      for (int64_t k = 0; k < K; ++k) q[t * K + k] = 0;
+      continue;
+    }
+    const float sc = a / 127.0f;
+    scale[t] = sc;
+    for (int64_t k = 0; k < K; ++k) {
+      float r = nearbyintf(v[k] / sc);
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
+      q[t * K + k] = (int8_t)r;
+    }
+  }
+  fesetround(saved);
+  free(xr);
   return ORACLE_OK;
 }
 

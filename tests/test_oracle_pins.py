@@ -289,3 +289,145 @@ def test_quant_double_rounding_differs_from_single_rounding_somewhere():
             if once != exact.quant_code_exact(xv, sbits):
                 diffs += 1
     assert diffs > 0
+
+
+# ------------------------------------- rotated activations (1024-wide blocks)
+#
+# oracle.rotate_f32 / quant_s8_rot: the blockwise Hadamard rotation that the
+# "NInfer sm_89 fork" article (section 9 item 2) folds into the activation
+# quantisation, on the 1024-wide blocks of the "NINFER ternary perf-tuning"
+# notes (section 6, constants table). Pinned to the Hadamard matrix from
+# scipy, closed forms, invariants and a hand-worked fp32 case.
+
+
+def _sylvester(n):
+    from scipy.linalg import hadamard
+    return hadamard(n).astype(np.float64)
+
+
+def test_rotation_matches_hadamard_matrix_within_fp32_bound():
+    """fp64 product with scipy's Hadamard matrix: the fp32 butterflies may
+    differ only by rounding, at most 10 stages x 2^-24 of the magnitude sum."""
+    rng = np.random.default_rng(21)
+    T, K = 3, 3072
+    xf = rng.standard_normal((T, K)).astype(np.float32)
+    xf[:, rng.choice(K, 30, replace=False)] *= 20.0
+    x = bf16(xf)
+    xd = ts.bf16_bits_to_f32(x).astype(np.float64)
+    H = _sylvester(1024) / 32.0
+    got = oracle.rotate_f32(x).astype(np.float64)
+    for b in range(K // 1024):
+        blk = slice(1024 * b, 1024 * (b + 1))
+        want = xd[:, blk] @ H.T
+        bound = 10 * 2.0 ** -24 * np.abs(xd[:, blk]).sum(axis=1, keepdims=True) / 32.0 * 2
+        assert np.all(np.abs(got[:, blk] - want) <= bound)
+    rel = np.linalg.norm(got - np.concatenate([xd[:, 1024 * b:1024 * (b + 1)] @ H.T
+                                               for b in range(K // 1024)], axis=1)) / np.linalg.norm(got)
+    assert rel < 1e-6
+
+
+def test_rotation_exact_on_small_integers():
+    """Integer inputs up to 16 in magnitude keep every partial sum an integer
+    below 2^15: the fp32 butterflies are exact and equal the matrix product."""
+    rng = np.random.default_rng(22)
+    xi = rng.integers(-16, 17, size=(4, 2048)).astype(np.float32)
+    got = oracle.rotate_f32(bf16(xi))
+    H = _sylvester(1024)
+    want = np.concatenate([xi[:, :1024] @ H.T, xi[:, 1024:] @ H.T], axis=1) / 32.0
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_rotation_closed_forms():
+    """e_j goes to column j of H / 32; a block of ones to 32 e_0; blocks do
+    not mix."""
+    K = 2048
+    for j in (0, 1, 3, 5, 511, 1000, 1023):
+        x = np.zeros((1, K), np.uint16)
+        x[0, 1024 + j] = 0x3F80  # 1.0 in the second block
+        got = oracle.rotate_f32(x)[0]
+        assert not got[:1024].any()
+        i = np.arange(1024)
+        sign = 1 - 2 * (np.array([bin(v & j).count("1") for v in i]) & 1)
+        assert np.array_equal(got[1024:], (sign / 32.0).astype(np.float32))
+    ones = np.full((1, 1024), 0x3F80, np.uint16)
+    z = oracle.rotate_f32(ones)[0]
+    assert z[0] == 32.0 and not z[1:].any()
+
+
+def test_rotation_is_an_involution_and_odd():
+    """H H = 1024 I: rotating the rotated unit vectors (values +-1/32, exact
+    in bf16) gives them back exactly; rotate(-x) = -rotate(x) bitwise."""
+    for j in (0, 7, 640):
+        x = np.zeros((1, 1024), np.uint16)
+        x[0, j] = 0x3F80
+        z = oracle.rotate_f32(x)
+        back = oracle.rotate_f32(bf16(z))[0]
+        e = np.zeros(1024, np.float32)
+        e[j] = 1.0
+        assert np.array_equal(back, e)
+    x, _, _ = _small_case(T=2, K=1024)
+    z = oracle.rotate_f32(x)
+    zn = oracle.rotate_f32(x ^ np.uint16(0x8000))
+    assert np.array_equal(zn.view(np.uint32), (-z).view(np.uint32))
+
+
+def test_rotation_stage_order_hand_worked():
+    """Hand-worked fp32 case. x = (2^24, 1, 1, 1, 0, ...). Strides ascending:
+    h=1 gives (2^24 + 1 -> 2^24 [tie to even], 2^24 - 1, 2, 0); h=2 gives
+    (2^24 + 2, 2^24 - 1, 2^24 - 2, 2^24 - 1); later strides pair with zeros,
+    so z[i] = that value at i mod 4, over 32. The exactly rounded sums would
+    give (2^24 + 4)/32 at i = 0, and strides descending would swap the values
+    at 1 and 2: either mistake fails this test."""
+    x = np.zeros((1, 1024), np.uint16)
+    x[0, 0] = 0x4B80  # 2^24
+    x[0, 1:4] = 0x3F80
+    z = oracle.rotate_f32(x)[0].astype(np.float64)
+    want4 = np.array([2.0 ** 24 + 2, 2.0 ** 24 - 1, 2.0 ** 24 - 2, 2.0 ** 24 - 1]) / 32.0
+    assert np.array_equal(z, np.tile(want4, 256))
+
+
+def test_quant_s8_rot_equals_quant_of_exact_rotation():
+    """Where every rotated value is exact in bf16 (inputs in {0, +-1} on
+    four positions of a block: rotated values in {0, +-1/32, ..., +-4/32}),
+    the rotated quantisation must equal quant_s8 of the rotated values, whose
+    rule is pinned by brute force above."""
+    rng = np.random.default_rng(23)
+    T, K = 6, 3072
+    xf = np.zeros((T, K), np.float32)
+    for t in range(T):
+        for b in range(K // 1024):
+            pos = 1024 * b + rng.choice(1024, 4, replace=False)
+            xf[t, pos] = rng.integers(-1, 2, size=4)
+    xf[0, :] = 0.0  # an all-zero token
+    x = bf16(xf)
+    z = oracle.rotate_f32(x)
+    zb = bf16(z)
+    assert np.array_equal(ts.bf16_bits_to_f32(zb), z)
+    q, sc = oracle.quant_s8_rot(x)
+    q2, sc2 = oracle.quant_s8(zb)
+    assert np.array_equal(q, q2) and np.array_equal(sc.view(np.uint32), sc2.view(np.uint32))
+    assert sc[0] == 0.0 and not q[0].any()
+
+
+def test_quant_s8_rot_invariances():
+    x, _, _ = _small_case(T=4, K=2048)
+    xf = ts.bf16_bits_to_f32(x)
+    q, sc = oracle.quant_s8_rot(x)
+    q2, sc2 = oracle.quant_s8_rot(bf16(2 * xf))
+    assert np.array_equal(q2, q) and np.array_equal(sc2, 2 * sc)
+    qn, scn = oracle.quant_s8_rot(x ^ np.uint16(0x8000))
+    assert np.array_equal(qn, -q) and np.array_equal(scn, sc)
+    # the largest rotated magnitude maps to +-127
+    z = oracle.rotate_f32(x)
+    am = np.abs(z).argmax(axis=1)
+    assert np.array_equal(np.abs(q[np.arange(4), am]), np.full(4, 127, np.int8))
+    for t in range(4):
+        qt, st = oracle.quant_s8_rot(x[t:t + 1])
+        assert np.array_equal(qt[0], q[t]) and st[0] == sc[t]
+
+
+def test_rotation_rejects_ragged_blocks():
+    with pytest.raises(ValueError):
+        oracle.rotate_f32(np.zeros((1, 1536), np.uint16))
+    with pytest.raises(ValueError):
+        oracle.quant_s8_rot(np.zeros((1, 512), np.uint16))
