@@ -156,6 +156,30 @@ tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float
                               tern_q_layout layout, void* stream);
 
 /*
+ * Rotated per-token int8 activation quantisation (device, async): the
+ * Hadamard rotation that the pages fold into the activation quantisation
+ * ("NInfer sm_89 fork" article, section 9 item 2), on 1024-wide blocks
+ * ("NINFER ternary perf-tuning" notes, section 6, constants table), in the
+ * same kernel as the quantisation:
+ *   xr[t][1024b + i] = (1/32) sum_j H[i][j] x[t][1024b + j],
+ *     H[i][j] = (-1)^popcount(i & j) (Sylvester, order 1024), computed in
+ *     fp32 as the fast Walsh-Hadamard transform with strides 1, 2, ..., 512
+ *     in that order (each pair (u, v) -> (u + v, u - v), one rounding each),
+ *     then one multiply by 1/32;
+ *   then tern_quant_act_s8's rule on xr: a_t = max_k |xr[t][k]|,
+ *   scale_t = fl32(a_t / 127), q = clamp(round-half-even(fl32(xr / scale_t)),
+ *   -127, 127); a_t == 0 gives scale_t = 0 and zero codes.
+ * The result feeds tern_linear_s8_q with weights trained in the rotated basis.
+ * x: device bf16 [T][K]; q: device int8 [T][K] in `layout`; act_scale: device
+ * float [T]. K a multiple of 1024 in [1024, 32768]; x and q 16-byte aligned.
+ * The caller keeps |x| small enough that the block sums stay finite.
+ * Errors: TERN_ERR_NULL, TERN_ERR_SHAPE, TERN_ERR_VALUE (layout),
+ * TERN_ERR_ALIGN, all before any launch; TERN_ERR_HIP if the launch fails.
+ */
+tern_status tern_quant_act_s8_rot(const void* x_bf16, int T, int k, int8_t* q, float* act_scale,
+                                  tern_q_layout layout, void* stream);
+
+/*
  * Device workspace tern_linear needs for this call (bytes, 0 if none). The s8
  * rung keeps the int8 activations and their scales there, and on short
  * prefills of narrow layers also fp32 partial totals when it splits K across

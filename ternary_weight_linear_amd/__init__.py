@@ -10,6 +10,7 @@ Entry points mirror the C ABI in ``include/tern.h``:
 * ``pack`` / ``unpack``        -- offline relayout to packed layout v1 (host)
 * ``TernaryWeights``           -- packed codes + scales resident on the GPU
 * ``quant_act_s8``             -- per-token int8 activation quantisation
+* ``quant_act_s8_rot``         -- the same after a blockwise (1024) Hadamard rotation
 * ``linear``                   -- ``y = ternary_linear(x)`` with rung dispatch
 * ``linear_s8_q``              -- the s8 contraction on pre-quantised activations
 * ``debug_s8_acc``             -- the s8 rung's int32 group accumulators
@@ -35,7 +36,7 @@ STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_AL
 
 # Symbols declared in include/tern.h (checked by the host tests).
 EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpack",
-           "tern_quant_act_s8", "tern_workspace_bytes", "tern_linear", "tern_linear_s8_q",
+           "tern_quant_act_s8", "tern_quant_act_s8_rot", "tern_workspace_bytes", "tern_linear", "tern_linear_s8_q",
            "tern_debug_s8_acc",
            "tern_probe_snapshot", "tern_probe_reset", "tern_last_rung", "tern_resolve_rung",
            "tern_rung_name", "tern_last_error", "tern_abi_version")
@@ -72,6 +73,7 @@ def lib() -> ctypes.CDLL:
         "tern_pack": (st, [p, p, i, i, i, p, p]),
         "tern_unpack": (st, [p, p, i, i, i, p, p]),
         "tern_quant_act_s8": (st, [p, i, i, p, p, i, p]),
+        "tern_quant_act_s8_rot": (st, [p, i, i, p, p, i, p]),
         "tern_workspace_bytes": (sz, [i, i, i, i, i]),
         "tern_linear": (st, [p, i, ctypes.POINTER(_Weights), p, i, p, sz, p]),
         "tern_linear_s8_q": (st, [p, p, i, ctypes.POINTER(_Weights), p, i, p]),
@@ -243,6 +245,24 @@ def quant_act_s8(x, q=None, scale=None, stream=None, layout="row_major"):
     _dev(scale, torch.float32, "scale")
     _check(lib().tern_quant_act_s8(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
                                    Q_LAYOUTS[layout], _stream(stream)))
+    return q, scale
+
+
+def quant_act_s8_rot(x, q=None, scale=None, stream=None, layout="row_major"):
+    """Rotated per-token int8 quantisation: each 1024-wide block of x [T, K]
+    (bf16, device) rotated by the orthonormal Hadamard matrix, then quantised
+    as quant_act_s8 does. K a multiple of 1024, at most 32768."""
+    torch = _torch()
+    _dev(x, torch.bfloat16, "x")
+    T, K = x.shape
+    if q is None:
+        q = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _dev(q, torch.int8, "q")
+    _dev(scale, torch.float32, "scale")
+    _check(lib().tern_quant_act_s8_rot(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
+                                       Q_LAYOUTS[layout], _stream(stream)))
     return q, scale
 
 

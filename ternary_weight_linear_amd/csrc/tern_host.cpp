@@ -603,6 +603,22 @@ tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float
   return ok();
 }
 
+tern_status tern_quant_act_s8_rot(const void* x_bf16, int T, int k, int8_t* q, float* act_scale,
+                                  tern_q_layout layout, void* stream) {
+  if (!x_bf16 || !q || !act_scale) return fail(TERN_ERR_NULL, "tern_quant_act_s8_rot: NULL pointer");
+  if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
+  if (layout != TERN_Q_ROW_MAJOR && layout != TERN_Q_OPERAND_ORDER)
+    return fail(TERN_ERR_VALUE, "unknown q layout %d", (int)layout);
+  if (k < 1024 || k % 1024 != 0 || k > tern::kRotMaxK)
+    return fail(TERN_ERR_SHAPE, "K=%d must be a multiple of 1024 in [1024, %d]", k, tern::kRotMaxK);
+  if (!aligned16(x_bf16) || !aligned16(q))
+    return fail(TERN_ERR_ALIGN, "x and q must be 16-byte aligned");
+  int err = tern::launch_quant_s8_rot((const uint16_t*)x_bf16, T, k, q, act_scale,
+                                      layout == TERN_Q_OPERAND_ORDER, stream);
+  if (err) return hip_fail(err, "quant_s8_rot launch");
+  return ok();
+}
+
 tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float* y,
                         tern_rung rung, void* ws, size_t ws_bytes, void* stream) {
   if (!x_bf16 || !y) return fail(TERN_ERR_NULL, "tern_linear: x or y is NULL");

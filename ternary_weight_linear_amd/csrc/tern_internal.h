@@ -96,6 +96,10 @@ int small_t_lds_bytes(int tokens_per_tile, int strips, int waves, int K);
 // instead of row-major.
 int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
                     void* stream);
+// Rotated variant: 1024-wide blocks, K a multiple of 1024 up to kRotMaxK.
+constexpr int kRotMaxK = 32768;
+int launch_quant_s8_rot(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
+                        void* stream);
 // ws: s8_partial_bytes(p, T, N) bytes of fp32 partials (k_parts > 1; operand
 // order only), may be NULL when that is 0.
 int launch_s8(const S8Args& a, const S8Plan& p, void* ws, void* stream);

@@ -16,10 +16,13 @@ using namespace dev;
 // per-token int8 activation quantisation
 // --------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t quant_byte(uint32_t xbits, float sc) {
-  const float r = rintf(__uint_as_float(xbits) / sc);  // IEEE division, ties-to-even rounding
+__device__ __forceinline__ uint32_t quant_code(float v, float sc) {
+  const float r = rintf(v / sc);  // IEEE division, ties-to-even rounding
   const float c = fminf(fmaxf(r, -127.f), 127.f);
   return (uint32_t)((int)c) & 0xffu;
+}
+__device__ __forceinline__ uint32_t quant_byte(uint32_t xbits, float sc) {
+  return quant_code(__uint_as_float(xbits), sc);
 }
 
 // The s8 kernel's operand order inside every 64-byte k-block kb: byte
@@ -94,6 +97,166 @@ __global__ void __launch_bounds__(256) tern_quant_s8_kernel(const uint16_t* __re
         out = s8_operand_order(L0, L1, H0, H1);
       }
       qr[j] = out;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// rotated per-token int8 quantisation
+// --------------------------------------------------------------------------
+//
+// xr = (1/32) H x on every 1024-wide block of a token (H the Sylvester
+// Hadamard matrix of order 1024), then the quantisation above applied to xr.
+// The pages fold the rotation of the original ternary model into the
+// activation quantisation ("NInfer sm_89 fork" article, section 9 item 2) and
+// rotate 1024-wide blocks ("NINFER ternary perf-tuning" notes, section 6,
+// constants table); their rotation kernel, one warp per (block, token), was
+// bound by launch latency, not by its traffic.
+//
+// The rotation is computed in fp32 as the fast Walsh-Hadamard transform with
+// strides 1, 2, ..., 512 in that order, each pair (i, i + h) becoming
+// (u + v, u - v) with one rounding each, then a multiply by 1/32: fixing the
+// order fixes every rounding, so the codes are reproducible bit for bit.
+//
+// One workgroup per token; wave w rotates blocks w, w + 4, ... and keeps the
+// results in registers (NBW blocks at most) until the token's absmax is
+// known. Per block a lane holds 16 values in three layouts, element index i
+// (10 bits) split between 4 register bits and 6 lane bits:
+//   P1  i = 16 l + j                         (registers: bits 0-3)
+//   P2  i = (l & 15) + 16 j + 256 (l >> 4)  (registers: bits 4-7)
+//   P3  registers j: bits 0-2 and 5; lane l: bits 3-4, 6-7, 8-9 (l >> 4)
+// Strides 1..8 and 16..128 run inside the registers of P1 and P2; strides 256
+// and 512 pair lanes l and l ^ 16, l ^ 32 of P3, where the lane holding u
+// computes fma(+1, u, v) = u + v and the one holding v fma(-1, v, u) = u - v.
+// P3 is the output layout: a lane's 16 values are the k = 8g..8g+7 and
+// 32+8g..32+8g+7 of one 64-wide k-block, i.e. one 16-byte chunk of the s8
+// operand order (or two 8-byte pieces of a row-major row). The relayouts go
+// through 4 KiB of LDS per wave, positions XOR-swizzled so that all three
+// layouts read and write without bank conflicts.
+constexpr int kRotBlock = 1024;
+
+__device__ __forceinline__ int rot_pos(int i) {
+  return i ^ (((i >> 5) & 1) << 3) ^ (((i >> 6) & 3) << 1) ^ (((i >> 8) & 1) * 17);
+}
+__device__ __forceinline__ int rot_p2(int l, int j) { return (l & 15) + 16 * j + 256 * (l >> 4); }
+__device__ __forceinline__ int rot_p3(int l, int j) {
+  return (j & 7) | ((l & 3) << 3) | ((j >> 3) << 5) | (((l >> 2) & 3) << 6) | ((l >> 4) << 8);
+}
+
+// All lanes' LDS accesses before this point are ordered before those after it
+// (LDS instructions of a wave execute in order; this keeps the compiler from
+// moving them across).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The strides whose element bit lives in register bit 0..3.
+__device__ __forceinline__ void fwht_regs16(float (&z)[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (!(j & h)) {
+        const float u = z[j], v = z[j + h];
+        z[j] = u + v;
+        z[j + h] = u - v;
+      }
+}
+
+template <int NBW, bool PERM>
+__global__ void __launch_bounds__(256) tern_quant_rot_kernel(const uint16_t* __restrict__ x, int K,
+                                                             int8_t* __restrict__ q,
+                                                             float* __restrict__ scale) {
+  __shared__ float xbuf[4][kRotBlock];
+  __shared__ uint32_t wmax[4];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nb = K >> 10;
+  float* sb = xbuf[wave];
+  const float sg16 = (lane & 16) ? -1.0f : 1.0f;
+  const float sg32 = (lane & 32) ? -1.0f : 1.0f;
+
+  float v[NBW][16];
+  uint32_t m = 0;
+#pragma unroll
+  for (int jb = 0; jb < NBW; ++jb) {
+    const int b = wave + 4 * jb;
+    if (b >= nb) break;  // wave-uniform
+    float z[16];
+    {  // P1: 16 consecutive activations per lane
+      const uint16_t* src = x + (size_t)t * K + (size_t)b * kRotBlock + 16 * lane;
+      const u32x4 lo = *(const u32x4*)src;
+      const u32x4 hi = *(const u32x4*)(src + 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[2 * i] = __uint_as_float(lo[i] << 16);
+        z[2 * i + 1] = __uint_as_float(lo[i] & 0xffff0000u);
+        z[8 + 2 * i] = __uint_as_float(hi[i] << 16);
+        z[9 + 2 * i] = __uint_as_float(hi[i] & 0xffff0000u);
+      }
+    }
+    fwht_regs16(z);  // strides 1, 2, 4, 8
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sb[rot_pos(16 * lane + j)] = z[j];
+    wave_lds_order();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z[j] = sb[rot_pos(rot_p2(lane, j))];
+    wave_lds_order();
+    fwht_regs16(z);  // strides 16, 32, 64, 128
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sb[rot_pos(rot_p2(lane, j))] = z[j];
+    wave_lds_order();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z[j] = sb[rot_pos(rot_p3(lane, j))];
+    wave_lds_order();
+    // stride 256: lanes l, l ^ 16 (ds_swizzle, xor mask 16 within 32 lanes)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(z[j]), 0x401f));
+      z[j] = __builtin_fmaf(sg16, z[j], p);
+    }
+    // stride 512: lanes l, l ^ 32
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(z[j])));
+      z[j] = __builtin_fmaf(sg32, z[j], p);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      v[jb][j] = z[j] * 0.03125f;
+      m = max(m, __float_as_uint(v[jb][j]) & 0x7fffffffu);
+    }
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  const uint32_t am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float sc = __uint_as_float(am) / 127.0f;  // IEEE single division
+  if (threadIdx.x == 0) scale[t] = am == 0 ? 0.0f : sc;
+
+  // P3 lane l: 64-wide k-block c = ((l >> 2) & 3) + 4 (l >> 4) of the 1024
+  // block, 8-wide group g = l & 3; register j = (k & 7) + 8 * (k >= 32).
+  const int g = lane & 3, c = ((lane >> 2) & 3) | ((lane >> 4) << 2);
+#pragma unroll
+  for (int jb = 0; jb < NBW; ++jb) {
+    const int b = wave + 4 * jb;
+    if (b >= nb) break;
+    uint32_t w4[4] = {0u, 0u, 0u, 0u};  // codes of k = 8g+0..3, 8g+4..7, 32+8g+0..3, 32+8g+4..7
+    if (am != 0) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        w4[d] = quant_code(v[jb][4 * d], sc) | (quant_code(v[jb][4 * d + 1], sc) << 8) |
+                (quant_code(v[jb][4 * d + 2], sc) << 16) | (quant_code(v[jb][4 * d + 3], sc) << 24);
+    }
+    int8_t* dst = q + (size_t)t * K + (size_t)b * kRotBlock + 64 * c;
+    if (PERM) {
+      *(u32x4*)(dst + 16 * g) = s8_operand_order(w4[0], w4[1], w4[2], w4[3]);
+    } else {
+      *(uint2*)(dst + 8 * g) = uint2{w4[0], w4[1]};
+      *(uint2*)(dst + 32 + 8 * g) = uint2{w4[2], w4[3]};
     }
   }
 }
@@ -340,6 +503,34 @@ int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bo
   else
     hipLaunchKernelGGL(tern_quant_s8_kernel<false>, dim3(T), dim3(256), 0, (hipStream_t)stream, x,
                        K, q, scale);
+  return (int)hipGetLastError();
+}
+
+int launch_quant_s8_rot(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
+                        void* stream) {
+  if (T <= 0) return 0;
+  if (K < kRotBlock || K % kRotBlock != 0 || K > kRotMaxK) return (int)hipErrorInvalidValue;
+  const int nbw = (K / kRotBlock + 3) / 4;  // blocks per wave
+  hipStream_t st = (hipStream_t)stream;
+  switch (nbw) {
+#define TERN_ROT_LAUNCH(NBW)                                                                             \
+  case NBW:                                                                                              \
+    if (operand_order)                                                                                   \
+      hipLaunchKernelGGL((tern_quant_rot_kernel<NBW, true>), dim3(T), dim3(256), 0, st, x, K, q, scale);  \
+    else                                                                                                 \
+      hipLaunchKernelGGL((tern_quant_rot_kernel<NBW, false>), dim3(T), dim3(256), 0, st, x, K, q, scale); \
+    break;
+    TERN_ROT_LAUNCH(1)
+    TERN_ROT_LAUNCH(2)
+    TERN_ROT_LAUNCH(3)
+    TERN_ROT_LAUNCH(4)
+    TERN_ROT_LAUNCH(5)
+    TERN_ROT_LAUNCH(6)
+    TERN_ROT_LAUNCH(7)
+    TERN_ROT_LAUNCH(8)
+#undef TERN_ROT_LAUNCH
+    default: return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

@@ -588,3 +588,74 @@ def test_bf16_rungs_activation_range(tl, torch, case):
         assert np.all(y[0] == 0), rung
         err = np.abs(y - ref)
         assert np.all(err <= bound), (rung, float((err / np.maximum(bound, 1e-300)).max()))
+
+
+# ------------------------------------- rotated quantisation (1024-wide blocks)
+
+
+def _rot_inputs(T, K, seed):
+    rng = np.random.default_rng(seed)
+    xf = rng.standard_normal((T, K)).astype(np.float32)
+    xf[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20.0  # fixed outlier channels
+    xf[0] = 0.0                 # all-zero token
+    if T > 2:
+        xf[2] *= 1e-38          # subnormal range
+    if T > 3:
+        xf[3] *= 1e30           # large, block sums still finite
+    return ts.f32_to_bf16_bits(xf)
+
+
+@pytest.mark.parametrize("K", [1024, 2048, 5120, 17408, 32768])
+@pytest.mark.parametrize("layout", ["row_major", "operand_order"])
+def test_quant_rot_bit_exact(tl, torch, K, layout):
+    """The fused rotate-and-quantise kernel reproduces the oracle's codes and
+    scales bit for bit: 1, 2, 5, 17 and 32 blocks per token (1 to 8 blocks
+    per wave, ragged over the 4 waves), a zero token, a token in the
+    subnormal range, a large one."""
+    T = 7
+    x = _rot_inputs(T, K, 900 + K // 1024)
+    q_ref, s_ref = oracle.quant_s8_rot(x)
+    q, sc = tl.quant_act_s8_rot(to_dev_bf16(torch, x), layout=layout)
+    torch.cuda.synchronize()
+    want = q_ref if layout == "row_major" else operand_order(q_ref)
+    assert np.array_equal(q.cpu().numpy(), want)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [ts.GATE_UP, ts.DOWN])
+def test_quant_rot_full_prefill_exact(tl, torch, shape):
+    """At the prefill size (T = 2048 tokens of the layer's K, the launch
+    configuration the benchmark times) every code and scale is compared."""
+    T, K = 2048, shape.k
+    x = _rot_inputs(T, K, 77 + K)
+    q_ref, s_ref = oracle.quant_s8_rot(x)
+    q, sc = tl.quant_act_s8_rot(to_dev_bf16(torch, x), layout="operand_order")
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), operand_order(q_ref))
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_quant_rot_feeds_the_s8_contraction(tl, torch):
+    """Rotated codes through the s8 contraction: y within the s8 gate of the
+    oracle's exactly rounded s8 output on the same codes."""
+    rng = np.random.default_rng(31)
+    N, K, G, T = 256, 2048, 128, 40
+    w = ts.draw_weights(rng, N, K, 0.4)
+    s = ts.draw_scales(rng, N, K, G)
+    x = _rot_inputs(T, K, 32)
+    q_ref, s_ref = oracle.quant_s8_rot(x)
+    y_ref = oracle.linear_s8(q_ref, s_ref, w, s)
+    W = tl.TernaryWeights.from_host(w, s)
+    q, sc = tl.quant_act_s8_rot(to_dev_bf16(torch, x), layout="operand_order")
+    y = tl.linear_s8_q(q, sc, W, layout="operand_order")
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), y_ref) <= S8_GATE
+
+
+def test_quant_rot_rejects_bad_shapes(tl, torch):
+    x = torch.zeros((2, 1536), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tl.TernError):
+        tl.quant_act_s8_rot(x)
+    x = torch.zeros((2, 65536), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tl.TernError):
+        tl.quant_act_s8_rot(x)

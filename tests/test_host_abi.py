@@ -190,6 +190,13 @@ def test_linear_validation_happens_before_any_hip_call(tl):
     assert L.tern_quant_act_s8(0x100000, 1, 100, 0x200000, 0x300000, 0, None) == 2
     assert L.tern_quant_act_s8(0x100000, 1, 72, 0x200000, 0x300000, 1, None) == 2  # 64 | K
     assert L.tern_quant_act_s8(0x100000, 1, 256, 0x200000, 0x300000, 7, None) == 4
+    # rotated quantisation: 1024-wide blocks, K in [1024, 32768]
+    assert L.tern_quant_act_s8_rot(None, 1, 1024, 0x100000, 0x200000, 0, None) == 1
+    for k in (256, 1536, 0, 65536):
+        assert L.tern_quant_act_s8_rot(0x100000, 1, k, 0x200000, 0x300000, 0, None) == 2
+    assert L.tern_quant_act_s8_rot(0x100000, 0, 1024, 0x200000, 0x300000, 0, None) == 2
+    assert L.tern_quant_act_s8_rot(0x100000, 1, 1024, 0x200000, 0x300000, 7, None) == 4
+    assert L.tern_quant_act_s8_rot(0x100008, 1, 1024, 0x200000, 0x300000, 0, None) == 3
 
 
 def _run_env(env_extra: dict, code: str) -> str:
