@@ -42,7 +42,8 @@ METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
 # their launch plans: a change to any of them voids the stored counters.
 KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
                for f in ("tern_limb.hip", "tern_s8.hip", "tern_s8mma.hip", "tern_b16mma.hip",
-                         "tern_tile.hip", "tern_device.h", "tern_internal.h", "tern_host.cpp")]
+                         "tern_tile.hip", "tern_limbtile.hip", "tern_device.h", "tern_internal.h",
+                         "tern_host.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -263,8 +264,9 @@ def kernels_only(torch, ts, tl, dev, n):
     """For rocprofv3 --pmc runs, all on gate_up with weights rotated over
     > 512 MB: n launches of the gemv kernel (T=1), n/10 of the s8 rung (quant
     + contraction, T=2048), n/10 of the bf16 prefill (T=2048), n of the T=8
-    draft-verify batch, then plain 64 MiB device copies whose byte counters
-    calibrate FETCH_SIZE / WRITE_SIZE."""
+    draft-verify batch, n of the rotated quantisation (T=2048), then plain
+    64 MiB device copies whose byte counters calibrate FETCH_SIZE /
+    WRITE_SIZE."""
     w = ts.weights(ts.GATE_UP)
     b = tl.TernaryWeights.from_host(w.w, w.s, device=dev)
     sets = [b] + [tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group)
@@ -289,6 +291,11 @@ def kernels_only(torch, ts, tl, dev, n):
     y16 = torch.empty((8, b.n), dtype=torch.float32, device=dev)
     for i in range(n):  # draft-verify batch T = 8 (activation-tiled kernel on this wide layer)
         tl.linear(x16, sets[i % len(sets)], y=y16)
+    torch.cuda.synchronize()
+    qr = torch.empty((T, b.k), dtype=torch.int8, device=dev)
+    sr = torch.empty((T,), dtype=torch.float32, device=dev)
+    for i in range(n):  # rotated quantisation of the T = 2048 prefill activations
+        tl.quant_act_s8_rot(x8, q=qr, scale=sr, layout="operand_order")
     torch.cuda.synchronize()
     src = torch.empty(64 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
@@ -431,6 +438,28 @@ def main():
             o = 2 * T * s.n * s.k
             b16[s.name] = {"us": round(t * 1e6, 2), "TFLOPs": round(o / t / 1e12, 1)}
             log(f"  bf16 prefill {s.name}: {t * 1e6:.1f} us ({o / t / 1e12:.0f} TFLOP/s)")
+        # The rotated quantisation (1024-wide Hadamard blocks fused into the
+        # int8 quantisation): HBM bound, 2 B read + 1 B written per
+        # activation and 4 B per token scale.
+        rq = {}
+        for j, s in enumerate(shapes):
+            def r1(i, j=j):
+                tl.quant_act_s8_rot(xs[j], q=qs[j][0], scale=qs[j][1], layout="operand_order")
+            t = graph_time(torch, r1, K8, 2) / K8
+            by = 3 * T * s.k + 4 * T
+            rq[s.name] = {"us": round(t * 1e6, 2), "bytes": by, "GB/s": round(by / t / 1e9, 1),
+                          "us_plain_quant": gemm[s.name]["us_quant_kernel"]}
+            log(f"  rotated quant K={s.k}: {t * 1e6:.1f} us ({by / t / 1e9:.0f} GB/s)")
+        ach_r = rq[dom]["GB/s"]
+        s8["rotated_quant"] = {
+            "metric": "HBM GB/s of the fused rotate (1024-wide Hadamard) and int8 quantise kernel, T=2048",
+            "per_shape": rq,
+            "roofline": {"bound": "hbm", "achieved": ach_r, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach_r / HBM_PEAK_GBS, 4),
+                         "traffic": stored_traffic(f"quant_rot:{dom}"),
+                         "kernel": f"tern_quant_rot_kernel on the {dom} activations (K={shapes[0].k}), T={T}",
+                         "algorithmic_bytes_per_launch": rq[dom]["bytes"], "us_per_launch": rq[dom]["us"]}}
+
         ach16 = b16[dom]["TFLOPs"]
         s8["bf16_prefill"] = {
             "metric": "bf16 TFLOP/s at T=2048 (rung small_t_tiled, no activation quantisation)",

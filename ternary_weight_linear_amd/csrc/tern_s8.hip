@@ -25,6 +25,40 @@ __device__ __forceinline__ uint32_t quant_byte(uint32_t xbits, float sc) {
   return quant_code(__uint_as_float(xbits), sc);
 }
 
+// The same code from y = fl(v * r), r = fl(1 / sc), sc a normal float: with
+// |v| <= 127 sc, y is within 2^-16 of v / sc and the IEEE quotient within
+// 2^-17, so unless y lies within 2^-15 of a half-integer both round to the
+// same integer. Such values set `near`, and the caller redoes them with the
+// division.
+__device__ __forceinline__ uint32_t quant_code_rcp(float v, float r, bool& near) {
+#pragma clang fp contract(off)
+  const float y = v * r;
+  const float t = rintf(y);
+  near |= !(fabsf(y - t) < 0.5f - 0x1p-15f);
+  const float c = fminf(fmaxf(t, -127.f), 127.f);
+  return (uint32_t)((int)c) & 0xffu;
+}
+
+// Codes of 16 values (4 dwords, byte e of dword d = value 4d + e): by the
+// reciprocal when the token's scale allows it and no value is near a rounding
+// boundary, else by division.
+__device__ __forceinline__ void quant_codes16(const float (&v)[16], float sc, float r, bool rcp_ok,
+                                              uint32_t (&w)[4]) {
+  bool near = !rcp_ok;
+  if (rcp_ok) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      w[d] = quant_code_rcp(v[4 * d], r, near) | (quant_code_rcp(v[4 * d + 1], r, near) << 8) |
+             (quant_code_rcp(v[4 * d + 2], r, near) << 16) | (quant_code_rcp(v[4 * d + 3], r, near) << 24);
+  }
+  if (near) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      w[d] = quant_code(v[4 * d], sc) | (quant_code(v[4 * d + 1], sc) << 8) |
+             (quant_code(v[4 * d + 2], sc) << 16) | (quant_code(v[4 * d + 3], sc) << 24);
+  }
+}
+
 // The s8 kernel's operand order inside every 64-byte k-block kb: byte
 // 16g + 4i + beta holds k = 64kb + 8g + kmap(i, beta) with
 // kmap(i, .) = {32 + 2i, 2i, 33 + 2i, 2i + 1}. It is the order in which
@@ -98,6 +132,69 @@ __global__ void __launch_bounds__(256) tern_quant_s8_kernel(const uint16_t* __re
       }
       qr[j] = out;
     }
+  }
+}
+
+// Single-pass variant of the operand-order quantisation for K <= 256 * 16 * NU:
+// thread i holds the activations of output chunks i, i + 256, ... in
+// registers (both 8-element halves of each), so x is read once and all of
+// its loads go out before the absmax reduction.
+template <int NU>
+__global__ void __launch_bounds__(256) tern_quant_s8_perm_kernel(const uint16_t* __restrict__ x, int K,
+                                                                 int8_t* __restrict__ q,
+                                                                 float* __restrict__ scale) {
+  __shared__ uint32_t wmax[4];
+  const int t = blockIdx.x;
+  const uint4* xr = (const uint4*)(x + (size_t)t * K);
+  const int nu = K >> 4;  // 16-byte output chunks of the token
+  uint4 lo[NU], hi[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int j = threadIdx.x + 256 * u;
+    if (j < nu) {
+      const int blk = j >> 2, g = j & 3;
+      lo[u] = xr[blk * 8 + g];      // k = 64 blk + 8g .. +7
+      hi[u] = xr[blk * 8 + 4 + g];  // k = 64 blk + 32 + 8g .. +7
+    } else {
+      lo[u] = hi[u] = uint4{0u, 0u, 0u, 0u};
+    }
+  }
+  uint32_t m16 = 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    m16 = max(m16, absmax16(u32x4{lo[u].x, lo[u].y, lo[u].z, lo[u].w}, u32x4{hi[u].x, hi[u].y, hi[u].z, hi[u].w}));
+  uint32_t m = wave_max_u32(m16 << 16);  // as an fp32 bit pattern
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const uint32_t am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float sc = __uint_as_float(am) / 127.0f;  // IEEE single division
+  if (threadIdx.x == 0) scale[t] = am == 0 ? 0.0f : sc;
+  // (Codes by division here: the reciprocal shortcut of the rotated kernel
+  // keeps 16 more values live per chunk, which costs this kernel occupancy.)
+  u32x4* qr = (u32x4*)(q + (size_t)t * K);
+  auto codes8 = [&](const uint4 v, uint32_t& c0, uint32_t& c1) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b[2 * i] = quant_byte(w[i] << 16, sc);
+      b[2 * i + 1] = quant_byte(w[i] & 0xffff0000u, sc);
+    }
+    c0 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    c1 = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  };
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int j = threadIdx.x + 256 * u;
+    if (j >= nu) break;
+    u32x4 out = u32x4{0u, 0u, 0u, 0u};
+    if (am != 0) {
+      uint32_t L0, L1, H0, H1;
+      codes8(lo[u], L0, L1);
+      codes8(hi[u], H0, H1);
+      out = s8_operand_order(L0, L1, H0, H1);
+    }
+    qr[j] = out;
   }
 }
 
@@ -236,6 +333,8 @@ __global__ void __launch_bounds__(256) tern_quant_rot_kernel(const uint16_t* __r
   const uint32_t am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
   const float sc = __uint_as_float(am) / 127.0f;  // IEEE single division
   if (threadIdx.x == 0) scale[t] = am == 0 ? 0.0f : sc;
+  const float r = 1.0f / sc;
+  const bool rcp_ok = sc >= 0x1p-126f;  // a normal scale: r is finite
 
   // P3 lane l: 64-wide k-block c = ((l >> 2) & 3) + 4 (l >> 4) of the 1024
   // block, 8-wide group g = l & 3; register j = (k & 7) + 8 * (k >= 32).
@@ -245,12 +344,7 @@ __global__ void __launch_bounds__(256) tern_quant_rot_kernel(const uint16_t* __r
     const int b = wave + 4 * jb;
     if (b >= nb) break;
     uint32_t w4[4] = {0u, 0u, 0u, 0u};  // codes of k = 8g+0..3, 8g+4..7, 32+8g+0..3, 32+8g+4..7
-    if (am != 0) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        w4[d] = quant_code(v[jb][4 * d], sc) | (quant_code(v[jb][4 * d + 1], sc) << 8) |
-                (quant_code(v[jb][4 * d + 2], sc) << 16) | (quant_code(v[jb][4 * d + 3], sc) << 24);
-    }
+    if (am != 0) quant_codes16(v[jb], sc, r, rcp_ok, w4);
     int8_t* dst = q + (size_t)t * K + (size_t)b * kRotBlock + 64 * c;
     if (PERM) {
       *(u32x4*)(dst + 16 * g) = s8_operand_order(w4[0], w4[1], w4[2], w4[3]);
@@ -497,6 +591,27 @@ hipError_t launch_s8_v(const S8Args& a, hipStream_t st) {
 int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
                     void* stream) {
   if (T <= 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  const int nu = (K / 16 + 255) / 256;  // output chunks per thread
+  if (operand_order && nu <= 8) {
+    switch (nu) {
+#define TERN_QP_LAUNCH(NU)                                                                          \
+  case NU:                                                                                          \
+    hipLaunchKernelGGL((tern_quant_s8_perm_kernel<NU>), dim3(T), dim3(256), 0, st, x, K, q, scale); \
+    break;
+      TERN_QP_LAUNCH(1)
+      TERN_QP_LAUNCH(2)
+      TERN_QP_LAUNCH(3)
+      TERN_QP_LAUNCH(4)
+      TERN_QP_LAUNCH(5)
+      TERN_QP_LAUNCH(6)
+      TERN_QP_LAUNCH(7)
+      TERN_QP_LAUNCH(8)
+#undef TERN_QP_LAUNCH
+      default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+  }
   if (operand_order)
     hipLaunchKernelGGL(tern_quant_s8_kernel<true>, dim3(T), dim3(256), 0, (hipStream_t)stream, x, K,
                        q, scale);
