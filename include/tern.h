@@ -186,9 +186,12 @@ tern_status tern_quant_act_s8_rot(const void* x_bf16, int T, int k, int8_t* q, f
  * workgroups (a second kernel adds them in a fixed order); small_t and
  * small_t_tiled (up to 16 tokens) keep fp32 partial sums there when they
  * split K across workgroups (narrow layers with a long K; then a second
- * kernel adds the parts in a fixed order), or, on wide layers at T <= 4, the
- * int8 limbs of the activations and their per-k-tile exponents. The contents need no initialisation and are not preserved. Every scratch
- * buffer of every rung is counted here; a call given less fails with
+ * kernel adds the parts in a fixed order). (On wide layers at T <= 4 the
+ * int8 limbs of the activations are made inside the contraction kernel and
+ * need none; forced with TERN_TUNE_SMALLT=limb2, or at T = 5..8 with
+ * TERN_TUNE_SMALLT=limb, a prep kernel keeps them and their per-k-tile
+ * exponents here.) The contents need no initialisation and are not
+ * preserved. Every scratch buffer of every rung is counted here; a call given less fails with
  * TERN_ERR_WORKSPACE ("NINFER ternary perf-tuning" notes, section 5 item 8:
  * the workspace capacity declaration must cover every scratch).
  * rung may be TERN_RUNG_AUTO (resolved the way tern_linear resolves it).

@@ -65,6 +65,7 @@ struct Config {
   int tune_depth = 0;                 // TERN_TUNE_DEPTH (0 = heuristic)
   bool gemv_bf16 = false;             // TERN_TUNE_GEMV=bf16: time the bf16-operand gemv kernel (default: limb)
   int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave, 3 = limb
+  bool limb_unfused = false;          // TERN_TUNE_SMALLT=limb2: limbs by the separate prep kernel
 };
 
 bool parse_int(const char* s, long lo, long hi, long* out) {
@@ -180,7 +181,10 @@ Config read_config() {
       c.smallt_kernel = 2;
     else if (strcmp(s, "limb") == 0)
       c.smallt_kernel = 3;
-    else
+    else if (strcmp(s, "limb2") == 0) {
+      c.smallt_kernel = 3;
+      c.limb_unfused = true;
+    } else
       bad("TERN_TUNE_SMALLT", s);
   }
   if (const char* s = getenv("TERN_TUNE_S8_BM")) {
@@ -319,7 +323,6 @@ bool small_t_limb(int T, int n, int k) {
 }
 
 tern::LimbTilePlan plan_limbtile(int T, int n, int k) {
-  (void)T;
   (void)k;
   const Config& c = config();
   tern::LimbTilePlan p;
@@ -328,6 +331,8 @@ tern::LimbTilePlan plan_limbtile(int T, int n, int k) {
   p.waves = c.tune_waves ? std::min(c.tune_waves, 8) : 4;
   p.depth = c.tune_depth == 4 ? 4 : 2;
   p.strip_blocks = (NS + p.waves * p.strips_per_wave - 1) / (p.waves * p.strips_per_wave);
+  // Up to 4 tokens the loader wave makes the limbs (one launch, no workspace).
+  p.fused = T <= 4 && !c.limb_unfused;
   return p;
 }
 
@@ -349,7 +354,7 @@ size_t workspace_for(int T, int n, int k, tern_rung r) {
            tern::s8_partial_bytes(plan_s8(T, n, k, true), T, n);
   if (b16_prefill(T, r)) return 0;
   if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && small_t_limb(T, n, k))
-    return tern::limbtile_workspace_bytes(T, k);
+    return plan_limbtile(T, n, k).fused ? 0 : tern::limbtile_workspace_bytes(T, k);
   if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && !small_t_per_wave(T, n, k))
     return tern::tile_workspace_bytes(plan_tile(T, n, k), n);
   return 0;

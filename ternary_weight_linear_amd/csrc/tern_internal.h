@@ -73,6 +73,7 @@ struct LimbTilePlan {
   int waves;            // Ws: compute waves per workgroup (1..8); plus a loader wave
   int depth;            // D: k-tiles in flight, 2 or 4
   int strip_blocks;     // grid.x = ceil(NS / (Ws * S))
+  bool fused;           // T <= 4: the loader wave makes the limbs (one launch, no workspace)
 };
 
 // All launchers return 0 on success or a hipError_t value.

@@ -242,6 +242,193 @@ __global__ void __launch_bounds__(576) tern_limbtile_kernel(
   }
 }
 
+// Fused variant for T <= 4 (one row block): the loader wave makes the limbs
+// itself, k-tile by k-tile, so the call is one launch. Lane (u, j) of the
+// loader holds chunk j of token u's k-tile (D k-tiles of x in flight in its
+// registers), takes the tile exponent over its 16-lane DPP row and writes its
+// three limb chunks and, at j = 0, 2^(d - 6) as an exponent into the LDS stage;
+// two stages alternate. Rows of absent tokens (u >= T) and rows 4u + 3 are
+// never written: they only feed accumulators that are not stored.
+constexpr int kFuseTile = 16 * 256;        // limb rows of one k-tile
+constexpr int kFuseStage = kFuseTile + 16;  // + 4 ints of exponent shifts
+
+template <int S, int GPT, int D>
+__global__ void __launch_bounds__(576) tern_limbfuse_kernel(
+    const uint16_t* __restrict__ x, int T, int K, const u32x4* __restrict__ codes,
+    const uint16_t* __restrict__ scales, float* __restrict__ y, int N) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kFuseStage];
+  constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Ws = (blockDim.x >> 6) - 1;
+  const int NS = N >> 4, KT = K >> 8;
+
+  if (wave == Ws) {
+    const int u = lane >> 4, j = lane & 15;
+    const bool tok = u < T;
+    const rsrc_t xrs = make_rsrc(x, (uint32_t)T * K * 2);
+    // chunk j of a k-tile: k = 64 (j >> 2) + 8 (j & 3) + 0..7 and + 32
+    const int xoff = tok ? (u * K + 64 * (j >> 2) + 8 * (j & 3)) * 2 : kOffPastEnd;
+    u32x4 xl[D], xh[D];
+    auto fetch = [&](int slot, int kt) {
+      kt = __builtin_amdgcn_readfirstlane(min(kt, KT - 1));
+      xl[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff, kt * 512, 0));
+      xh[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff + 64, kt * 512, 0));
+    };
+    // Lanes of absent tokens skip the work: a DPP row (16 lanes) is one
+    // token, so each row is wholly in or out, and their all-zero chunks would
+    // otherwise send the wave through the tiny-tile branch of limb_chunk too.
+    auto prep = [&](int slot, char* st) {
+      if (!tok) return;
+      const int d = limb_shift(row16_max_u32(absmax16(xl[slot], xh[slot])));
+      u32x4 o0, o1, o2;
+      limb_chunk(xl[slot], xh[slot], d, o0, o1, o2);
+      const int r0 = 4 * u;
+      *(u32x4*)(st + ((r0 + 0) * 16 + (j ^ (r0 + 0))) * 16) = o0;
+      *(u32x4*)(st + ((r0 + 1) * 16 + (j ^ (r0 + 1))) * 16) = o1;
+      *(u32x4*)(st + ((r0 + 2) * 16 + (j ^ (r0 + 2))) * 16) = o2;
+      if (j == 0) *(int*)(st + kFuseTile + 4 * u) = d - 6;
+    };
+    // The handoff: the limb writes are done (lgkmcnt(0)), then the barrier
+    // without the workgroup fence (which would also wait for the x loads in
+    // flight).
+    auto handoff = [&]() {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      asm volatile("s_barrier" ::: "memory");
+    };
+#pragma unroll
+    for (int q = 0; q < D; ++q) fetch(q, q);
+    prep(0, smem);
+    handoff();
+    // Iteration i: request k-tile i + D into the slot of tile i, make tile
+    // i + 1 into stage (i + 1) & 1 (stage of tile i - 1, released at the
+    // previous barrier), hand it over.
+    int i = 0;
+    for (; i + D <= KT; i += D) {
+#pragma unroll
+      for (int q = 0; q < D; ++q) {
+        fetch(q, i + q + D);
+        if (i + q + 1 < KT) prep((q + 1) % D, smem + ((i + q + 1) & 1) * kFuseStage);
+        handoff();
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < D - 1; ++q) {
+      if (i + q < KT) {
+        if (i + q + 1 < KT) prep((q + 1) % D, smem + ((i + q + 1) & 1) * kFuseStage);
+        handoff();
+      }
+    }
+    return;
+  }
+
+  const int r = lane & 15, g = lane >> 4;
+  const int strip0 = (blockIdx.x * Ws + wave) * S;
+  const int nstrips = min(S, NS - strip0);  // <= 0: the wave only keeps the barriers
+  const rsrc_t crs = make_rsrc(codes + (size_t)max(min(strip0, NS - 1), 0) * KT * 64,
+                               (uint32_t)max(nstrips, 0) * KT * 1024);
+  const rsrc_t srs = make_rsrc(scales + (size_t)max(min(strip0, NS - 1), 0) * KT * 16 * GPT,
+                               (uint32_t)max(nstrips, 0) * KT * 16 * GPT * 2);
+
+  auto load = [&](LimbTileStage<S, GPT, 1>& b, int kt) {
+    kt = __builtin_amdgcn_readfirstlane(min(kt, KT - 1));
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int se = max(min(s, nstrips - 1), 0);  // absent strips re-read a present one (never stored)
+      b.P[s] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, lane * 16, (se * KT + kt) * 1024, kAuxNontemporal));
+      const int soff = (se * KT + kt) * 16 * GPT * 2;
+      if (GPT == 2) {
+        b.sw[s][0] = __builtin_amdgcn_raw_buffer_load_b32(srs, r * GPT * 2, soff, 0);
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(srs, r * GPT * 2, soff, 0);
+        b.sw[s][0] = v[0];
+        b.sw[s][1] = v[1];
+      }
+    }
+  };
+
+  float total[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) total[s] = 0.f;
+
+  auto compute = [&](const LimbTileStage<S, GPT, 1>& b, const char* st) {
+    float part[S];
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      i32x4 af[KBPG];
+#pragma unroll
+      for (int kk = 0; kk < KBPG; ++kk) {
+        const int q = 4 * (gi * KBPG + kk) + g;
+        af[kk] = *(const i32x4*)(st + (r * 16 + (q ^ r)) * 16);
+      }
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const uint32_t spair = b.sw[s][gi >> 1];
+        const float sc = half_bits_to_float((uint16_t)((gi & 1) ? (spair >> 16) : (spair & 0xffffu)));
+        i32x4 acc;
+#pragma unroll
+        for (int kk = 0; kk < KBPG; ++kk)
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[kk], weights_operand_i8(b.P[s][gi * KBPG + kk]),
+                                                      kk == 0 ? i32x4{0, 0, 0, 0} : acc, 0, 0, 0);
+        const int low = (int)(((uint32_t)acc[1] << 8) + (uint32_t)acc[0]);  // 256 a1 + a0
+        const float v = __builtin_fmaf(65536.0f, (float)acc[2], (float)low);
+        part[s] = gi == 0 ? sc * v : __builtin_fmaf(sc, v, part[s]);
+      }
+    }
+    const int dsh = *(const int*)(st + kFuseTile + 4 * g);
+#pragma unroll
+    for (int s = 0; s < S; ++s) total[s] += __builtin_ldexpf(part[s], dsh);
+  };
+
+  LimbTileStage<S, GPT, 1> cb[D];
+#pragma unroll
+  for (int q = 0; q < D - 1; ++q) load(cb[q], q);
+  __syncthreads();
+  int i = 0;
+  for (; i + D <= KT; i += D) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      const int ii = i + q;
+      load(cb[(q + D - 1) % D], ii + D - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(cb[q], smem + (ii & 1) * kFuseStage);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < D - 1; ++q) {
+    if (i + q < KT) {  // uniform over the block
+      compute(cb[q], smem + ((i + q) & 1) * kFuseStage);
+      __syncthreads();
+    }
+  }
+
+  // Lane (r, g): output row r of each strip for token g.
+  if (g < T) {
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (s < nstrips) y[(size_t)g * N + (strip0 + s) * 16 + r] = total[s];
+  }
+}
+
+template <int S, int GPT>
+hipError_t launch_limbfuse_g(const SmallTArgs& a, const LimbTilePlan& p, hipStream_t st) {
+  dim3 grid(p.strip_blocks), block(64 * (p.waves + 1));
+  switch (p.depth) {
+    case 2:
+      hipLaunchKernelGGL((tern_limbfuse_kernel<S, GPT, 2>), grid, block, 0, st, a.x, a.T, a.K,
+                         (const u32x4*)a.codes, a.scales, a.y, a.N);
+      break;
+    case 4:
+      hipLaunchKernelGGL((tern_limbfuse_kernel<S, GPT, 4>), grid, block, 0, st, a.x, a.T, a.K,
+                         (const u32x4*)a.codes, a.scales, a.y, a.N);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int RB, int S, int GPT>
 hipError_t launch_limbtile_g(const SmallTArgs& a, const LimbTilePlan& p, int8_t* limbs, int* dsh,
                              hipStream_t st) {
@@ -283,8 +470,16 @@ size_t limbtile_workspace_bytes(int T, int K) {
 
 int launch_limbtile(const SmallTArgs& a, const LimbTilePlan& p, void* ws, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  if (a.T < 1 || a.T > 8 || ws == nullptr) return (int)hipErrorInvalidValue;
   if (p.waves < 1 || p.waves > 8 || p.strip_blocks < 1) return (int)hipErrorInvalidValue;
+  if (p.fused) {
+    if (a.T < 1 || a.T > 4) return (int)hipErrorInvalidValue;
+    if (p.strips_per_wave == 1)
+      return (int)(a.G == 128 ? launch_limbfuse_g<1, 2>(a, p, st) : launch_limbfuse_g<1, 4>(a, p, st));
+    if (p.strips_per_wave == 2)
+      return (int)(a.G == 128 ? launch_limbfuse_g<2, 2>(a, p, st) : launch_limbfuse_g<2, 4>(a, p, st));
+    return (int)hipErrorInvalidValue;
+  }
+  if (a.T < 1 || a.T > 8 || ws == nullptr) return (int)hipErrorInvalidValue;
   const int RB = (a.T + 3) / 4, slots = 4 * RB;
   int8_t* limbs = (int8_t*)ws;
   int* dsh = (int*)((char*)ws + ((((size_t)RB * 16 * a.K) + 255) & ~(size_t)255));

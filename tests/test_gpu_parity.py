@@ -516,19 +516,22 @@ print("BAD", bad)
 """
 
 
-@pytest.mark.parametrize("strips,waves,depth,G", [(1, 4, 2, 128), (2, 3, 4, 64), (1, 8, 4, 128),
-                                                  (2, 4, 2, 128)])
-def test_small_t_limb_path_exact(strips, waves, depth, G):
-    """The small_t limb path (limbs made by a prep kernel, int8 MFMA) forced
-    for T = 2..8, one and two row blocks, on integer activations and
+@pytest.mark.parametrize("kernel,strips,waves,depth,G", [
+    ("limb", 1, 4, 2, 128), ("limb", 2, 3, 4, 64), ("limb", 1, 8, 4, 128), ("limb", 2, 4, 2, 128),
+    ("limb2", 1, 4, 2, 128), ("limb2", 2, 3, 4, 64)])
+def test_small_t_limb_path_exact(kernel, strips, waves, depth, G):
+    """The small_t limb path (int8 limbs of the activations, int8 MFMA)
+    forced for T = 2..8, one and two row blocks, on integer activations and
     power-of-two scales, where the limbs and every fp32 sum are exact: y must
-    equal the oracle bit for bit. Partial strip blocks (6 strips) and waves
-    without strips included."""
+    equal the oracle bit for bit. "limb": up to 4 tokens the loader wave makes
+    the limbs, above that a prep kernel does; "limb2": the prep kernel at
+    every T. Partial strip blocks (6 strips) and waves without strips
+    included."""
     import os
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    env = dict(os.environ, TERN_TUNE_SMALLT="limb", TERN_TUNE_STRIPS=str(strips),
+    env = dict(os.environ, TERN_TUNE_SMALLT=kernel, TERN_TUNE_STRIPS=str(strips),
                TERN_TUNE_WAVES=str(waves), TERN_TUNE_DEPTH=str(depth))
     r = subprocess.run([sys.executable, "-c", _LIMBTILE_CHILD, root, str(G)], env=env,
                        capture_output=True, text=True, timeout=240)
@@ -588,6 +591,51 @@ def test_bf16_rungs_activation_range(tl, torch, case):
         assert np.all(y[0] == 0), rung
         err = np.abs(y - ref)
         assert np.all(err <= bound), (rung, float((err / np.maximum(bound, 1e-300)).max()))
+
+
+_LIMB_RANGE_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import oracle, tern_synth as ts, ternary_weight_linear_amd as tl
+from tests.test_gpu_parity import _range_case
+n, k, G = 96, 2048, 128
+worst = 0.0
+for ci, case in enumerate(["outliers", "subnormal", "wide", "huge"]):
+    rng = np.random.default_rng(ci + 177)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.draw_scales(rng, n, k, G)
+    W = tl.TernaryWeights.from_host(w, s)
+    for T in (3, 4, 6):
+        xb = _range_case(case, T, k, rng)
+        ref = oracle.linear_bf16(xb, w, s)
+        xf = ts.bf16_bits_to_f32(xb).astype(np.float64)
+        sw = np.abs(w.astype(np.float64) * np.repeat(ts.f16_bits_to_f32(s).astype(np.float64), G, axis=1))
+        tmax = np.abs(xf).reshape(T, k // 256, 256).max(axis=2)
+        swt = sw.reshape(n, k // 256, 256).sum(axis=2)
+        bound = 2.0 ** -16 * (np.abs(xf) @ sw.T) + 2.0 ** -22 * (tmax @ swt.T)
+        x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        y = tl.linear(x, W, rung="small_t").cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(y)) and np.all(y[0] == 0), (case, T)
+        worst = max(worst, float((np.abs(y - ref) / np.maximum(bound, 1e-300)).max()))
+print("WORST", worst)
+"""
+
+
+@pytest.mark.parametrize("kernel", ["limb", "limb2"])
+def test_limb_path_activation_range(kernel):
+    """The activation-range bound of test_bf16_rungs_activation_range on the
+    small_t limb path (forced): limbs made by the loader wave (T <= 4) or by
+    the prep kernel, rows spanning 2^-40..2^40, subnormals, huge values and an
+    all-zero token."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, TERN_TUNE_SMALLT=kernel)
+    r = subprocess.run([sys.executable, "-c", _LIMB_RANGE_CHILD, root], env=env, capture_output=True,
+                       text=True, timeout=240, cwd=root)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert float(r.stdout.split("WORST")[1]) <= 1.0, r.stdout
 
 
 # ------------------------------------- rotated quantisation (1024-wide blocks)

@@ -136,10 +136,9 @@ def test_workspace_sizes(tl):
     assert tl.workspace_bytes(16, 5120, 5120, 128) == 0
     assert tl.workspace_bytes(4, 5120, 17408, 128) == 0
     assert tl.workspace_bytes(8, 34816, 5120, 128) == 0
-    # wide layers at T <= 4 take the limb path: one row block of 16 int8 limb
-    # rows and the per-token k-tile exponents, each 256-byte aligned
-    assert tl.workspace_bytes(4, 34816, 5120, 128) == 16 * 5120 + 512
-    assert tl.workspace_bytes(2, 34816, 5120, 128, "small_t_tiled") == 16 * 5120 + 512
+    # wide layers at T <= 4 run the limb path with the limbs made in the kernel
+    assert tl.workspace_bytes(4, 34816, 5120, 128) == 0
+    assert tl.workspace_bytes(2, 34816, 5120, 128, "small_t_tiled") == 0
     # the activation-tiled kernel splits a long K over workgroups: fp32
     # partials of one 16-token tile per K part
     ws16 = tl.workspace_bytes(16, 5120, 17408, 128)
@@ -197,6 +196,16 @@ def test_linear_validation_happens_before_any_hip_call(tl):
     assert L.tern_quant_act_s8_rot(0x100000, 0, 1024, 0x200000, 0x300000, 0, None) == 2
     assert L.tern_quant_act_s8_rot(0x100000, 1, 1024, 0x200000, 0x300000, 7, None) == 4
     assert L.tern_quant_act_s8_rot(0x100008, 1, 1024, 0x200000, 0x300000, 0, None) == 3
+
+
+def test_unfused_limb_path_declares_its_workspace():
+    """With the limbs made by the separate prep kernel (TERN_TUNE_SMALLT=limb2)
+    the workspace holds one row block of 16 int8 limb rows and the per-token
+    k-tile exponents, each 256-byte aligned; two row blocks above 4 tokens."""
+    out = _run_env({"TERN_TUNE_SMALLT": "limb2"},
+                   "import ternary_weight_linear_amd as tl\n"
+                   "print(tl.workspace_bytes(4, 34816, 5120, 128), tl.workspace_bytes(8, 34816, 5120, 128))")
+    assert out.split() == [str(16 * 5120 + 512), str(32 * 5120 + 768)]
 
 
 def _run_env(env_extra: dict, code: str) -> str:
