@@ -64,7 +64,7 @@ struct Config {
   int tune_wk = 0;                    // TERN_TUNE_WK (0 = heuristic)
   int tune_depth = 0;                 // TERN_TUNE_DEPTH (0 = heuristic)
   bool gemv_bf16 = false;             // TERN_TUNE_GEMV=bf16: time the bf16-operand gemv kernel (default: limb)
-  int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave, 3 = limb
+  int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave, 3 = limb, 4 = resident
   bool limb_unfused = false;          // TERN_TUNE_SMALLT=limb2: limbs by the separate prep kernel
 };
 
@@ -184,7 +184,9 @@ Config read_config() {
     else if (strcmp(s, "limb2") == 0) {
       c.smallt_kernel = 3;
       c.limb_unfused = true;
-    } else
+    } else if (strcmp(s, "resident") == 0)
+      c.smallt_kernel = 4;
+    else
       bad("TERN_TUNE_SMALLT", s);
   }
   if (const char* s = getenv("TERN_TUNE_S8_BM")) {
@@ -336,6 +338,27 @@ tern::LimbTilePlan plan_limbtile(int T, int n, int k) {
   return p;
 }
 
+tern::LimbPlan plan_limb(int T, int n, int k);
+bool limb_fits(int T, int k, int group, const tern::LimbPlan& p);
+
+// small_t on T <= 4 tokens through the gemv kernel's layout (the limbs of
+// the whole K made once per workgroup and kept in LDS, lane group u = token
+// u). By default on wide layers at T = 2, where making the limbs up front
+// costs less than the loader-wave pipeline; from T = 3 the up-front limbs
+// (and their LDS) grow and the fused limb path wins. Needs no workspace; the
+// LDS size does not depend on the group size.
+bool small_t_resident(int T, int n, int k) {
+  const Config& c = config();
+  if (c.smallt_kernel) {
+    if (c.smallt_kernel != 4 || T > 4) return false;
+  } else if (T != 2 || n / 16 < 1024) {
+    return false;
+  }
+  tern::LimbPlan p = plan_limb(T, n, k);
+  p.wk = 1;
+  return limb_fits(T, k, 128, p);
+}
+
 bool small_t_per_wave(int T, int n, int k) {
   const Config& c = config();
   if (c.smallt_kernel) return c.smallt_kernel == 2;
@@ -353,6 +376,7 @@ size_t workspace_for(int T, int n, int k, tern_rung r) {
     return align256((size_t)T * k) + align256((size_t)T * sizeof(float)) +
            tern::s8_partial_bytes(plan_s8(T, n, k, true), T, n);
   if (b16_prefill(T, r)) return 0;
+  if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && small_t_resident(T, n, k)) return 0;
   if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && small_t_limb(T, n, k))
     return plan_limbtile(T, n, k).fused ? 0 : tern::limbtile_workspace_bytes(T, k);
   if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && !small_t_per_wave(T, n, k))
@@ -661,6 +685,12 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
       else
         err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
       if (err) return hip_fail(err, "gemv launch");
+    } else if (small_t_resident(T, n, k)) {
+      tern::LimbPlan fp = plan_limb(T, n, k);
+      fp.wk = 1;
+      fp.token_lanes = true;
+      int err = tern::launch_limb(a, fp, stream);
+      if (err) return hip_fail(err, "small_t resident launch");
     } else if (small_t_limb(T, n, k)) {
       int err = tern::launch_limbtile(a, plan_limbtile(T, n, k), ws, stream);
       if (err) return hip_fail(err, "small_t limb launch");

@@ -64,6 +64,7 @@ struct LimbPlan {
   int wn;               // strip groups per workgroup (waves own different strips)
   int wk;               // K shares per workgroup (waves split the k-tiles); wn * wk <= 16
   int depth;            // k-tiles of codes in flight per wave: 2, 4 or 8
+  bool token_lanes = false;  // T <= 4, wk == 1: lane group u holds token u (cheap epilogue)
 };
 constexpr int kLimbMaxLds = 65536;
 

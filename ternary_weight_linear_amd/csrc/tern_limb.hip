@@ -62,7 +62,11 @@ struct LimbStage {
   u32x4 P[S];  // the lane's 16 code bytes of each of the wave's strips
 };
 
-// TT: 1 (single token: rows 0..2) or 5 (T <= 5 tokens: rows 0..3T-1).
+// TT: 1 (single token: rows 0..2), 5 (T <= 5 tokens: A row r = limb row r)
+// or 4 (T <= 4 tokens, Wk = 1: A row 4u + L reads token u's limb L, so lane
+// group u holds token u's three limbs and combines them as at TT = 1; rows
+// 4u + 3 and those of absent tokens read some stored row and only feed
+// accumulators that are not stored).
 // Dynamic LDS (limb_lds_bytes): 3T limb rows of K + 64 bytes, the tile
 // exponents d [T][K/256] (int), then the workgroup's scales in their packed
 // order [strip][k-tile][row][group]; all of it is reused for the final
@@ -181,7 +185,8 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
   f32x4 total[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) total[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const char* abase = smem + (size_t)(r < NR ? r : 0) * rs + 16 * g;
+  const int arow = TT == 4 ? ((r >> 2) < T ? 3 * (r >> 2) + min(r & 3, 2) : 0) : (r < NR ? r : 0);
+  const char* abase = smem + (size_t)arow * rs + 16 * g;
   int tok[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) tok[e] = TT == 1 ? 0 : min((4 * g + e) / 3, T - 1);
@@ -202,6 +207,8 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
     int dsh[4];
     if (TT == 1) {
       dsh[0] = dexp[kt] - 6;
+    } else if (TT == 4) {
+      dsh[0] = dexp[min(g, T - 1) * KT + kt] - 6;
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dsh[e] = dexp[tok[e] * KT + kt] - 6 + 8 * ((4 * g + e) % 3);
@@ -218,7 +225,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
         sw[0] = v.x;
         sw[GPT / 2 - 1] = v.y;
       }
-      float part = 0.f;  // TT = 1: this k-tile's groups, before 2^(d - 6)
+      float part = 0.f;  // TT = 1, 4: this k-tile's groups, before 2^(d - 6)
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
         i32x4 acc = i32x4{0, 0, 0, 0};
@@ -229,7 +236,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
         }
         const uint32_t spair = sw[gi >> 1];
         const float sc = half_bits_to_float((uint16_t)((gi & 1) ? (spair >> 16) : (spair & 0xffffu)));
-        if (TT == 1) {
+        if (TT != 5) {
           const int low = (int)(((uint32_t)acc[1] << 8) + (uint32_t)acc[0]);  // 256 a1 + a0
           const float v = __builtin_fmaf(65536.0f, (float)acc[2], (float)low);
           part = gi == 0 ? sc * v : __builtin_fmaf(sc, v, part);
@@ -239,7 +246,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
             total[s][e] = __builtin_fmaf(sc, __builtin_ldexpf((float)acc[e], dsh[e]), total[s][e]);
         }
       }
-      if (TT == 1) total[s][0] += __builtin_ldexpf(part, dsh[0]);
+      if (TT != 5) total[s][0] += __builtin_ldexpf(part, dsh[0]);
     }
   };
   int i = 0;
@@ -265,6 +272,14 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
 #pragma unroll
       for (int s = 0; s < S; ++s)
         if (s < nstrips) y[(size_t)(strip0 + s) * 16 + lane] = total[s][0];
+    }
+    return;
+  }
+  if (TT == 4) {  // Wk == 1: lane group g holds token g's outputs
+    if (g < T) {
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (s < nstrips) y[(size_t)g * N + (strip0 + s) * 16 + r] = total[s][0];
     }
     return;
   }
@@ -353,6 +368,10 @@ int launch_limb(const SmallTArgs& a, const LimbPlan& p, void* stream) {
   const int W = p.wn * p.wk;
   if (a.T < 1 || a.T > 5 || p.wn < 1 || p.wk < 1 || W > 16) return (int)hipErrorInvalidValue;
   if (limb_lds_bytes(a.T, a.K, a.G, p) > kLimbMaxLds) return (int)hipErrorInvalidValue;
+  if (p.token_lanes) {
+    if (a.T > 4 || p.wk != 1) return (int)hipErrorInvalidValue;
+    return (int)launch_limb_t<4>(a, p, st);
+  }
   return (int)(a.T == 1 ? launch_limb_t<1>(a, p, st) : launch_limb_t<5>(a, p, st));
 }
 

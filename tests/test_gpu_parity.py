@@ -518,7 +518,8 @@ print("BAD", bad)
 
 @pytest.mark.parametrize("kernel,strips,waves,depth,G", [
     ("limb", 1, 4, 2, 128), ("limb", 2, 3, 4, 64), ("limb", 1, 8, 4, 128), ("limb", 2, 4, 2, 128),
-    ("limb2", 1, 4, 2, 128), ("limb2", 2, 3, 4, 64)])
+    ("limb2", 1, 4, 2, 128), ("limb2", 2, 3, 4, 64),
+    ("resident", 1, 4, 4, 128), ("resident", 2, 4, 2, 64)])
 def test_small_t_limb_path_exact(kernel, strips, waves, depth, G):
     """The small_t limb path (int8 limbs of the activations, int8 MFMA)
     forced for T = 2..8, one and two row blocks, on integer activations and
@@ -621,7 +622,7 @@ print("WORST", worst)
 """
 
 
-@pytest.mark.parametrize("kernel", ["limb", "limb2"])
+@pytest.mark.parametrize("kernel", ["limb", "limb2", "resident"])
 def test_limb_path_activation_range(kernel):
     """The activation-range bound of test_bf16_rungs_activation_range on the
     small_t limb path (forced): limbs made by the loader wave (T <= 4) or by
