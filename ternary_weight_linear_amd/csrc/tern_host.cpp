@@ -339,24 +339,26 @@ tern::LimbTilePlan plan_limbtile(int T, int n, int k) {
 }
 
 tern::LimbPlan plan_limb(int T, int n, int k);
-bool limb_fits(int T, int k, int group, const tern::LimbPlan& p);
 
 // small_t on T <= 4 tokens through the gemv kernel's layout (the limbs of
 // the whole K made once per workgroup and kept in LDS, lane group u = token
-// u). By default on wide layers at T = 2, where making the limbs up front
-// costs less than the loader-wave pipeline; from T = 3 the up-front limbs
-// (and their LDS) grow and the fused limb path wins. Needs no workspace; the
-// LDS size does not depend on the group size.
+// u, the gemv's work split). By default at T <= 3 where the limbs take at
+// most 112 KiB of LDS: there making them up front beats both the loader-wave
+// pipeline (wide layers) and the per-wave bf16 kernel (narrow ones); at T = 4,
+// or with down's 157 KB at T = 3, the up-front work and the LDS lose (A/B on
+// the part). Needs no workspace; the LDS size does not depend on the group
+// size.
+tern::LimbPlan plan_resident(int T, int n, int k) {
+  tern::LimbPlan p = plan_limb(T, n, k);
+  p.token_lanes = true;
+  return p;
+}
+
 bool small_t_resident(int T, int n, int k) {
   const Config& c = config();
-  if (c.smallt_kernel) {
-    if (c.smallt_kernel != 4 || T > 4) return false;
-  } else if (T != 2 || n / 16 < 1024) {
-    return false;
-  }
-  tern::LimbPlan p = plan_limb(T, n, k);
-  p.wk = 1;
-  return limb_fits(T, k, 128, p);
+  const int lds = tern::limb_lds_bytes(T, k, 128, plan_resident(T, n, k));
+  if (c.smallt_kernel) return c.smallt_kernel == 4 && T <= 4 && lds <= tern::kLimbMaxLdsResident;
+  return T <= 3 && lds <= 112 * 1024;
 }
 
 bool small_t_per_wave(int T, int n, int k) {
@@ -686,10 +688,7 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
         err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
       if (err) return hip_fail(err, "gemv launch");
     } else if (small_t_resident(T, n, k)) {
-      tern::LimbPlan fp = plan_limb(T, n, k);
-      fp.wk = 1;
-      fp.token_lanes = true;
-      int err = tern::launch_limb(a, fp, stream);
+      int err = tern::launch_limb(a, plan_resident(T, n, k), stream);
       if (err) return hip_fail(err, "small_t resident launch");
     } else if (small_t_limb(T, n, k)) {
       int err = tern::launch_limbtile(a, plan_limbtile(T, n, k), ws, stream);

@@ -64,9 +64,10 @@ struct LimbPlan {
   int wn;               // strip groups per workgroup (waves own different strips)
   int wk;               // K shares per workgroup (waves split the k-tiles); wn * wk <= 16
   int depth;            // k-tiles of codes in flight per wave: 2, 4 or 8
-  bool token_lanes = false;  // T <= 4, wk == 1: lane group u holds token u (cheap epilogue)
+  bool token_lanes = false;  // T <= 4: lane group u holds token u (single-token epilogue)
 };
 constexpr int kLimbMaxLds = 65536;
+constexpr int kLimbMaxLdsResident = 160 * 1024;  // the resident small-T mode: all of a CU's LDS
 
 // Launch shape of the small_t limb path (tern_limbtile.hip), T <= 8.
 struct LimbTilePlan {

@@ -63,10 +63,10 @@ struct LimbStage {
 };
 
 // TT: 1 (single token: rows 0..2), 5 (T <= 5 tokens: A row r = limb row r)
-// or 4 (T <= 4 tokens, Wk = 1: A row 4u + L reads token u's limb L, so lane
-// group u holds token u's three limbs and combines them as at TT = 1; rows
-// 4u + 3 and those of absent tokens read some stored row and only feed
-// accumulators that are not stored).
+// or 4 (T <= 4 tokens: A row 4u + L reads token u's limb L, so lane group u
+// holds token u's three limbs and combines them as at TT = 1; rows 4u + 3 and
+// those of absent tokens read some stored row and only feed accumulators
+// that are not stored).
 // Dynamic LDS (limb_lds_bytes): 3T limb rows of K + 64 bytes, the tile
 // exponents d [T][K/256] (int), then the workgroup's scales in their packed
 // order [strip][k-tile][row][group]; all of it is reused for the final
@@ -275,11 +275,33 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
     }
     return;
   }
-  if (TT == 4) {  // Wk == 1: lane group g holds token g's outputs
-    if (g < T) {
+  if (TT == 4) {  // lane group g holds token g's outputs
+    if (Wk == 1) {
+      if (g < T) {
 #pragma unroll
-      for (int s = 0; s < S; ++s)
-        if (s < nstrips) y[(size_t)g * N + (strip0 + s) * 16 + r] = total[s][0];
+        for (int s = 0; s < S; ++s)
+          if (s < nstrips) y[(size_t)g * N + (strip0 + s) * 16 + r] = total[s][0];
+      }
+      return;
+    }
+    // The Wk shares through LDS ([Wk][Wn*S strips][4 tokens][16 columns]),
+    // added in ascending order.
+    __syncthreads();
+    float* red4 = (float*)smem;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (g < T) red4[(((size_t)wk * SB + wn * S + s) * 4 + g) * 16 + r] = total[s][0];
+    __syncthreads();
+    const int nout4 = T * SB * 16;
+    for (int e = tid; e < nout4; e += nth) {
+      const int t = e / (SB * 16);
+      const int rem = e - t * (SB * 16);
+      const int ls = rem >> 4, col = rem & 15;
+      const int st = blockIdx.x * SB + ls;
+      if (st >= NS) continue;
+      float sum = 0.f;
+      for (int w = 0; w < Wk; ++w) sum += red4[(((size_t)w * SB + ls) * 4 + t) * 16 + col];
+      y[(size_t)t * N + st * 16 + col] = sum;
     }
     return;
   }
@@ -367,9 +389,10 @@ int launch_limb(const SmallTArgs& a, const LimbPlan& p, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int W = p.wn * p.wk;
   if (a.T < 1 || a.T > 5 || p.wn < 1 || p.wk < 1 || W > 16) return (int)hipErrorInvalidValue;
-  if (limb_lds_bytes(a.T, a.K, a.G, p) > kLimbMaxLds) return (int)hipErrorInvalidValue;
+  if (limb_lds_bytes(a.T, a.K, a.G, p) > (p.token_lanes ? kLimbMaxLdsResident : kLimbMaxLds))
+    return (int)hipErrorInvalidValue;
   if (p.token_lanes) {
-    if (a.T > 4 || p.wk != 1) return (int)hipErrorInvalidValue;
+    if (a.T > 4) return (int)hipErrorInvalidValue;
     return (int)launch_limb_t<4>(a, p, st);
   }
   return (int)(a.T == 1 ? launch_limb_t<1>(a, p, st) : launch_limb_t<5>(a, p, st));
