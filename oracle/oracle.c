@@ -26,7 +26,11 @@
  *    single division), code = clamp(round-half-even(fl32(x / scale)),
  *    -127, 127), absmax == 0 gives scale 0 and all-zero codes;
  *  - s8 output: y = fl32(scale_t * sum_g s[n][g] * acc[t][n][g]) with the
- *    sum and product evaluated exactly and rounded once to fp32.
+ *    sum and product evaluated exactly and rounded once to fp32;
+ *  - rotated quantisation: per 1024-wide block, (1/32) times the Sylvester
+ *    Hadamard matrix, evaluated as fp32 fast Walsh-Hadamard butterflies with
+ *    strides 1, 2, ..., 512 in that order, then the s8 rule above (see
+ *    oracle_rotate_f32).
  *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off (see
  * oracle/__init__.py). float arithmetic must be IEEE single precision with
