@@ -135,22 +135,25 @@ __global__ void __launch_bounds__(256) tern_quant_s8_kernel(const uint16_t* __re
   }
 }
 
-// Single-pass variant of the operand-order quantisation for K <= 256 * 16 * NU:
-// thread i holds the activations of output chunks i, i + 256, ... in
+// Single-pass variant of the operand-order quantisation for K <= NT * 16 * NU:
+// thread i holds the activations of output chunks i, i + NT, ... in
 // registers (both 8-element halves of each), so x is read once and all of
-// its loads go out before the absmax reduction.
-template <int NU>
-__global__ void __launch_bounds__(256) tern_quant_s8_perm_kernel(const uint16_t* __restrict__ x, int K,
-                                                                 int8_t* __restrict__ q,
-                                                                 float* __restrict__ scale) {
-  __shared__ uint32_t wmax[4];
+// its loads go out before the absmax reduction. NT = 256 threads per token
+// for long batches; 1024 for short ones, where the few workgroups are a
+// latency chain and four times the threads make it a quarter as long.
+template <int NU, int NT>
+__global__ void __launch_bounds__(NT) tern_quant_s8_perm_kernel(const uint16_t* __restrict__ x, int K,
+                                                                int8_t* __restrict__ q,
+                                                                float* __restrict__ scale) {
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t wmax[NW];
   const int t = blockIdx.x;
   const uint4* xr = (const uint4*)(x + (size_t)t * K);
   const int nu = K >> 4;  // 16-byte output chunks of the token
   uint4 lo[NU], hi[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int j = threadIdx.x + 256 * u;
+    const int j = threadIdx.x + NT * u;
     if (j < nu) {
       const int blk = j >> 2, g = j & 3;
       lo[u] = xr[blk * 8 + g];      // k = 64 blk + 8g .. +7
@@ -166,7 +169,9 @@ __global__ void __launch_bounds__(256) tern_quant_s8_perm_kernel(const uint16_t*
   uint32_t m = wave_max_u32(m16 << 16);  // as an fp32 bit pattern
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  const uint32_t am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  uint32_t am = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) am = max(am, wmax[w]);
   const float sc = __uint_as_float(am) / 127.0f;  // IEEE single division
   if (threadIdx.x == 0) scale[t] = am == 0 ? 0.0f : sc;
   // (Codes by division here: the reciprocal shortcut of the rotated kernel
@@ -185,7 +190,7 @@ __global__ void __launch_bounds__(256) tern_quant_s8_perm_kernel(const uint16_t*
   };
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const int j = threadIdx.x + 256 * u;
+    const int j = threadIdx.x + NT * u;
     if (j >= nu) break;
     u32x4 out = u32x4{0u, 0u, 0u, 0u};
     if (am != 0) {
@@ -592,21 +597,27 @@ int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bo
                     void* stream) {
   if (T <= 0) return 0;
   hipStream_t st = (hipStream_t)stream;
-  const int nu = (K / 16 + 255) / 256;  // output chunks per thread
-  if (operand_order && nu <= 8) {
-    switch (nu) {
-#define TERN_QP_LAUNCH(NU)                                                                          \
-  case NU:                                                                                          \
-    hipLaunchKernelGGL((tern_quant_s8_perm_kernel<NU>), dim3(T), dim3(256), 0, st, x, K, q, scale); \
+  // Short batches (fewer tokens than CUs): 1024 threads per token, for K up
+  // to 32768 (two chunks per thread); otherwise 256.
+  const bool wide_wg = T < 256 && K <= 32768;
+  const int nt = wide_wg ? 1024 : 256;
+  const int nu = (K / 16 + nt - 1) / nt;  // output chunks per thread
+  if (operand_order && nu <= (wide_wg ? 2 : 8)) {
+    switch (nu * 2 + (wide_wg ? 1 : 0)) {
+#define TERN_QP_LAUNCH(NU, NT)                                                                        \
+  case NU * 2 + (NT == 1024 ? 1 : 0):                                                                 \
+    hipLaunchKernelGGL((tern_quant_s8_perm_kernel<NU, NT>), dim3(T), dim3(NT), 0, st, x, K, q, scale); \
     break;
-      TERN_QP_LAUNCH(1)
-      TERN_QP_LAUNCH(2)
-      TERN_QP_LAUNCH(3)
-      TERN_QP_LAUNCH(4)
-      TERN_QP_LAUNCH(5)
-      TERN_QP_LAUNCH(6)
-      TERN_QP_LAUNCH(7)
-      TERN_QP_LAUNCH(8)
+      TERN_QP_LAUNCH(1, 256)
+      TERN_QP_LAUNCH(2, 256)
+      TERN_QP_LAUNCH(3, 256)
+      TERN_QP_LAUNCH(4, 256)
+      TERN_QP_LAUNCH(5, 256)
+      TERN_QP_LAUNCH(6, 256)
+      TERN_QP_LAUNCH(7, 256)
+      TERN_QP_LAUNCH(8, 256)
+      TERN_QP_LAUNCH(1, 1024)
+      TERN_QP_LAUNCH(2, 1024)
 #undef TERN_QP_LAUNCH
       default: return (int)hipErrorInvalidValue;
     }
