@@ -224,7 +224,8 @@ hipError_t launch_b16m_g(const SmallTArgs& a, int tb, int s, bool x, hipStream_t
 int launch_b16_prefill(const SmallTArgs& a, const S8Plan& p, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (a.T < 1) return (int)hipErrorInvalidValue;
-  const int tb = p.token_blocks > 4 ? 4 : p.token_blocks;  // 8 blocks would not fit the registers
+  // 8 blocks would not fit the registers; 3 (the s8 plan's 48-token tile) runs as 4
+  const int tb = p.token_blocks > 2 ? 4 : p.token_blocks;
   return (int)(a.G == 128 ? launch_b16m_g<2>(a, tb, p.strips, p.xcd_order, st)
                           : launch_b16m_g<4>(a, tb, p.strips, p.xcd_order, st));
 }

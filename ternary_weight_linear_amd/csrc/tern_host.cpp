@@ -190,7 +190,7 @@ Config read_config() {
       bad("TERN_TUNE_SMALLT", s);
   }
   if (const char* s = getenv("TERN_TUNE_S8_BM")) {
-    if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 64 || v == 128))  // tokens per wave tile
+    if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 48 || v == 64 || v == 128))  // tokens per wave tile
       c.tune_s8_bm = (int)v;
     else
       bad("TERN_TUNE_S8_BM", s);
@@ -445,12 +445,12 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   tern::S8Plan p;
   // Wave tile 64 tokens x 64 outputs (4 token blocks x 4 strips) where that
   // still gives at least 4 workgroups per CU; 64 x 32 otherwise (narrow
-  // layers); 32-token tiles for T <= 32 so padded tokens do not waste the
-  // matrix cores, and one strip per wave up to T = 64, where the kernel is
+  // layers); 32- and 48-token tiles for T <= 32 and T <= 48 so padded tokens
+  // do not waste the matrix cores, and one strip per wave up to T = 64, where the kernel is
   // bound by load latency and wants as many waves streaming as it can get.
   // (128-token tiles cost registers, and occupancy, without paying back on
   // either 27B-class shape.)
-  const int tb = c.tune_s8_bm ? c.tune_s8_bm / 16 : (T > 32 ? 4 : 2);
+  const int tb = c.tune_s8_bm ? c.tune_s8_bm / 16 : (T > 48 ? 4 : T > 32 ? 3 : 2);
   const long tiles4 = (long)((n / 16 + 15) / 16) * ((T + 16 * tb - 1) / (16 * tb));
   int strips = T <= 64 ? 1 : (tiles4 >= 1024 ? 4 : 2);
   if (c.tune_s8_strips) strips = c.tune_s8_strips;

@@ -342,6 +342,7 @@ template <int GPT, bool DEBUG_ACC>
 hipError_t launch_s8m_g(const S8Args& a, const S8Plan& p, float* part, hipStream_t st) {
   switch (p.token_blocks * 16 + p.strips) {
     case 2 * 16 + 1: return launch_s8m_d<GPT, 2, 1, DEBUG_ACC>(a, p, part, st);
+    case 3 * 16 + 1: return launch_s8m_d<GPT, 3, 1, DEBUG_ACC>(a, p, part, st);
     case 4 * 16 + 1: return launch_s8m_d<GPT, 4, 1, DEBUG_ACC>(a, p, part, st);
     case 2 * 16 + 2: return launch_s8m_d<GPT, 2, 2, DEBUG_ACC>(a, p, part, st);
     case 2 * 16 + 4: return launch_s8m_d<GPT, 2, 4, DEBUG_ACC>(a, p, part, st);
