@@ -459,15 +459,18 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   p.strips = strips;
   p.xcd_order = c.tune_s8_raster != 1;
   // Short prefills on narrow layers give too few tiles to keep HBM busy:
-  // split K over workgroups until there are about 512 of them (each part at
-  // least 4 k-tiles) when there are fewer tiles than CUs, or fewer than 512
-  // with a long K; the parts cost a second kernel, which only pays there
-  // (A/B runs on MI355X at T = 17..508). Short prefills also keep 3 k-tiles
-  // in flight instead of 1.
+  // split K over workgroups (each part at least 4 k-tiles). With fewer tiles
+  // than CUs, into as many parts as keep the grid within 512 workgroups (two
+  // per CU, one round: a 513th would start a second round); with fewer than
+  // 512 tiles and a long K, into enough parts for about 512. The parts cost a
+  // second kernel, which only pays there (A/B runs on MI355X at T =
+  // 17..508). Short prefills also keep 3 k-tiles in flight instead of 1.
   const long tiles = (long)((n / 16 + 4 * strips - 1) / (4 * strips)) * ((T + 16 * tb - 1) / (16 * tb));
   const int KT = k / 256;
   int pk = 1;
-  if (allow_split && tb != 8 && (tiles < 256 || (tiles < 512 && KT >= 32)))
+  if (allow_split && tb != 8 && tiles < 256)
+    pk = (int)std::min<long>(512 / tiles, 16);
+  else if (allow_split && tb != 8 && tiles < 512 && KT >= 32)
     pk = (int)std::min<long>((512 + tiles - 1) / tiles, 16);
   pk = std::max(1, std::min(pk, KT / 4));
   if (c.tune_kparts && allow_split) pk = std::max(1, std::min(c.tune_kparts, KT));
