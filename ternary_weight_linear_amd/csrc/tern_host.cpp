@@ -459,7 +459,7 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   p.strips = strips;
   p.xcd_order = c.tune_s8_raster != 1;
   // Short prefills on narrow layers give too few tiles to keep HBM busy:
-  // split K over workgroups (each part at least 4 k-tiles). With fewer tiles
+  // split K over workgroups (each part at least 6 k-tiles). With fewer tiles
   // than CUs, into as many parts as keep the grid within 512 workgroups (two
   // per CU, one round: a 513th would start a second round); with fewer than
   // 512 tiles and a long K, into enough parts for about 512. The parts cost a
@@ -472,7 +472,7 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
     pk = (int)std::min<long>(512 / tiles, 16);
   else if (allow_split && tb != 8 && tiles < 512 && KT >= 32)
     pk = (int)std::min<long>((512 + tiles - 1) / tiles, 16);
-  pk = std::max(1, std::min(pk, KT / 4));
+  pk = std::max(1, std::min(pk, KT / 6));  // parts of at least 6 k-tiles (o_proj: 3 parts beat 5 by 6-17 %)
   if (c.tune_kparts && allow_split) pk = std::max(1, std::min(c.tune_kparts, KT));
   p.k_parts = pk;
   p.depth = (tb != 8 && (T <= 64 || pk > 1)) ? 4 : 2;
