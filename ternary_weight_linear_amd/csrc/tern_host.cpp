@@ -465,14 +465,32 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   // 512 tiles and a long K, into enough parts for about 512. The parts cost a
   // second kernel, which only pays there (A/B runs on MI355X at T =
   // 17..508). Short prefills also keep 3 k-tiles in flight instead of 1.
-  const long tiles = (long)((n / 16 + 4 * strips - 1) / (4 * strips)) * ((T + 16 * tb - 1) / (16 * tb));
   const int KT = k / 256;
-  int pk = 1;
-  if (allow_split && tb != 8 && tiles < 256)
-    pk = (int)std::min<long>(512 / tiles, 16);
-  else if (allow_split && tb != 8 && tiles < 512 && KT >= 32)
-    pk = (int)std::min<long>((512 + tiles - 1) / tiles, 16);
-  pk = std::max(1, std::min(pk, KT / 6));  // parts of at least 6 k-tiles (o_proj: 3 parts beat 5 by 6-17 %)
+  auto tiles_for = [&](int st) {
+    return (long)((n / 16 + 4 * st - 1) / (4 * st)) * ((T + 16 * tb - 1) / (16 * tb));
+  };
+  auto parts_for = [&](long tiles) {
+    int pk = 1;
+    if (allow_split && tb != 8 && tiles < 256)
+      pk = (int)std::min<long>(512 / tiles, 16);
+    else if (allow_split && tb != 8 && tiles < 512 && KT >= 32)
+      pk = (int)std::min<long>((512 + tiles - 1) / tiles, 16);
+    return std::max(1, std::min(pk, KT / 6));  // parts of at least 6 k-tiles (o_proj: 3 parts beat 5 by 6-17 %)
+  };
+  // Share of the workgroup slots (512 per round) a grid of w workgroups fills.
+  auto fill = [](long w) { return (double)w / (512.0 * (double)((w + 511) / 512)); };
+  int pk = parts_for(tiles_for(strips));
+  // A split that fills its last round poorly: 4 strips per wave, with its own
+  // split, when that fills the rounds better (down at T = 508: 640
+  // workgroups in 2 parts against 480 in 3, 87 -> 79 us).
+  if (!c.tune_s8_strips && strips == 2 && pk > 1) {
+    const int pk4 = parts_for(tiles_for(4));
+    if (fill(tiles_for(4) * pk4) > fill(tiles_for(2) * pk)) {
+      strips = 4;
+      pk = pk4;
+      p.strips = strips;
+    }
+  }
   if (c.tune_kparts && allow_split) pk = std::max(1, std::min(c.tune_kparts, KT));
   p.k_parts = pk;
   p.depth = (tb != 8 && (T <= 64 || pk > 1)) ? 4 : 2;
