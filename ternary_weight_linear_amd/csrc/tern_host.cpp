@@ -340,25 +340,33 @@ tern::LimbTilePlan plan_limbtile(int T, int n, int k) {
 
 tern::LimbPlan plan_limb(int T, int n, int k);
 
-// small_t on T <= 4 tokens through the gemv kernel's layout (the limbs of
-// the whole K made once per workgroup and kept in LDS, lane group u = token
-// u, the gemv's work split). By default at T <= 3 where the limbs take at
-// most 112 KiB of LDS: there making them up front beats both the loader-wave
-// pipeline (wide layers) and the per-wave bf16 kernel (narrow ones); at T = 4,
-// or with down's 157 KB at T = 3, the up-front work and the LDS lose (A/B on
-// the part). Needs no workspace; the LDS size does not depend on the group
-// size.
+// small_t on T <= 8 tokens through the gemv kernel's layout (the limbs of
+// the whole K made once per workgroup and kept in LDS, lane group u = tokens
+// u and 4 + u, the gemv's work split). By default at T <= 3 where the limbs
+// take at most 112 KiB of LDS: there making them up front beats both the
+// loader-wave pipeline (wide layers) and the per-wave bf16 kernel (narrow
+// ones); at T = 4, or with down's 157 KB at T = 3, the up-front work and the
+// LDS lose (A/B on the part). Needs no workspace; the LDS size does not
+// depend on the group size.
 tern::LimbPlan plan_resident(int T, int n, int k) {
   tern::LimbPlan p = plan_limb(T, n, k);
   p.token_lanes = true;
+  // Limbs of more than 80 KiB leave room for one workgroup per CU: make it
+  // wide enough that one round of workgroups covers the strips.
+  const int NS = n / 16;
+  if (p.wk == 1 && tern::limb_lds_bytes(T, k, 128, p) > 80 * 1024)
+    p.wn = std::min(16, std::max(p.wn, (NS + 255) / 256));
   return p;
 }
 
 bool small_t_resident(int T, int n, int k) {
   const Config& c = config();
   const int lds = tern::limb_lds_bytes(T, k, 128, plan_resident(T, n, k));
-  if (c.smallt_kernel) return c.smallt_kernel == 4 && T <= 4 && lds <= tern::kLimbMaxLdsResident;
-  return T <= 3 && lds <= 112 * 1024;
+  if (c.smallt_kernel) return c.smallt_kernel == 4 && T <= 8 && lds <= tern::kLimbMaxLdsResident;
+  if (T <= 3) return lds <= 112 * 1024;
+  // Two row blocks of tokens (one workgroup per CU): ahead of the bf16 tile
+  // kernel on wide layers at T = 5, 6 (5-8 %), behind it from T = 7.
+  return (T == 5 || T == 6) && n / 16 >= 1024 && lds <= tern::kLimbMaxLdsResident;
 }
 
 bool small_t_per_wave(int T, int n, int k) {

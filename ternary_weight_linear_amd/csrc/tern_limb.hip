@@ -63,10 +63,11 @@ struct LimbStage {
 };
 
 // TT: 1 (single token: rows 0..2), 5 (T <= 5 tokens: A row r = limb row r)
-// or 4 (T <= 4 tokens: A row 4u + L reads token u's limb L, so lane group u
-// holds token u's three limbs and combines them as at TT = 1; rows 4u + 3 and
-// those of absent tokens read some stored row and only feed accumulators
-// that are not stored).
+// or 4 / 8 (T <= 4 / 8 tokens, one / two A operands: row 4u + L of operand b
+// reads token 4b + u's limb L, so lane group u holds tokens u and 4 + u and
+// combines each one's three limbs as at TT = 1; rows 4u + 3 and those of
+// absent tokens read some stored row and only feed accumulators that are not
+// stored).
 // Dynamic LDS (limb_lds_bytes): 3T limb rows of K + 64 bytes, the tile
 // exponents d [T][K/256] (int), then the workgroup's scales in their packed
 // order [strip][k-tile][row][group]; all of it is reused for the final
@@ -185,8 +186,12 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
   f32x4 total[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) total[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int arow = TT == 4 ? ((r >> 2) < T ? 3 * (r >> 2) + min(r & 3, 2) : 0) : (r < NR ? r : 0);
+  constexpr bool TL = TT == 4 || TT == 8;  // token per lane group
+  constexpr int RB = TT == 8 ? 2 : 1;       // A operands (row blocks)
+  auto token_row = [&](int u) { return u < T ? 3 * u + min(r & 3, 2) : 0; };
+  const int arow = TL ? token_row(r >> 2) : (r < NR ? r : 0);
   const char* abase = smem + (size_t)arow * rs + 16 * g;
+  const char* abase1 = smem + (size_t)(RB == 2 ? token_row(4 + (r >> 2)) : 0) * rs + 16 * g;
   int tok[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) tok[e] = TT == 1 ? 0 : min((4 * g + e) / 3, T - 1);
@@ -194,9 +199,13 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
   const char* wsc = lsc + ((size_t)(wn * S) * KT * 16 + r) * GPT * 2;
   auto compute = [&](const LimbStage<S>& b, int i) {
     const int kt = kt0 + i;
-    i32x4 a[4];
+    i32x4 a[4], a1[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = *(const i32x4*)(abase + 64 * (4 * kt + q));
+    if (RB == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a1[q] = *(const i32x4*)(abase1 + 64 * (4 * kt + q));
+    }
     // TT = 1: the three limbs of the token are accumulators 0..2 of lanes
     // 0..15. Per group they are combined as 65536 a2 + (256 a1 + a0), the
     // bracket exact in int32 (|a_L| <= 2^20), and scaled; the groups of the
@@ -207,8 +216,9 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
     int dsh[4];
     if (TT == 1) {
       dsh[0] = dexp[kt] - 6;
-    } else if (TT == 4) {
+    } else if (TL) {
       dsh[0] = dexp[min(g, T - 1) * KT + kt] - 6;
+      if (RB == 2) dsh[1] = dexp[min(g + 4, T - 1) * KT + kt] - 6;
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dsh[e] = dexp[tok[e] * KT + kt] - 6 + 8 * ((4 * g + e) % 3);
@@ -225,14 +235,16 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
         sw[0] = v.x;
         sw[GPT / 2 - 1] = v.y;
       }
-      float part = 0.f;  // TT = 1, 4: this k-tile's groups, before 2^(d - 6)
+      float part = 0.f, part1 = 0.f;  // TT = 1, 4, 8: this k-tile's groups, before 2^(d - 6)
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
-        i32x4 acc = i32x4{0, 0, 0, 0};
+        i32x4 acc = i32x4{0, 0, 0, 0}, acc1 = acc;
 #pragma unroll
         for (int kk = 0; kk < KBPG; ++kk) {
           const int q = gi * KBPG + kk;
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[q], weights_operand_i8(P[q]), acc, 0, 0, 0);
+          const i32x4 bq = weights_operand_i8(P[q]);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[q], bq, acc, 0, 0, 0);
+          if (RB == 2) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[q], bq, acc1, 0, 0, 0);
         }
         const uint32_t spair = sw[gi >> 1];
         const float sc = half_bits_to_float((uint16_t)((gi & 1) ? (spair >> 16) : (spair & 0xffffu)));
@@ -240,6 +252,11 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
           const int low = (int)(((uint32_t)acc[1] << 8) + (uint32_t)acc[0]);  // 256 a1 + a0
           const float v = __builtin_fmaf(65536.0f, (float)acc[2], (float)low);
           part = gi == 0 ? sc * v : __builtin_fmaf(sc, v, part);
+          if (RB == 2) {
+            const int low1 = (int)(((uint32_t)acc1[1] << 8) + (uint32_t)acc1[0]);
+            const float v1 = __builtin_fmaf(65536.0f, (float)acc1[2], (float)low1);
+            part1 = gi == 0 ? sc * v1 : __builtin_fmaf(sc, v1, part1);
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -247,6 +264,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
         }
       }
       if (TT != 5) total[s][0] += __builtin_ldexpf(part, dsh[0]);
+      if (RB == 2) total[s][1] += __builtin_ldexpf(part1, dsh[1]);
     }
   };
   int i = 0;
@@ -275,22 +293,26 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
     }
     return;
   }
-  if (TT == 4) {  // lane group g holds token g's outputs
+  if (TL) {  // lane group g holds the outputs of tokens g and (RB = 2) 4 + g
     if (Wk == 1) {
-      if (g < T) {
 #pragma unroll
-        for (int s = 0; s < S; ++s)
-          if (s < nstrips) y[(size_t)g * N + (strip0 + s) * 16 + r] = total[s][0];
-      }
+      for (int b = 0; b < RB; ++b)
+        if (4 * b + g < T) {
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            if (s < nstrips) y[(size_t)(4 * b + g) * N + (strip0 + s) * 16 + r] = total[s][b];
+        }
       return;
     }
-    // The Wk shares through LDS ([Wk][Wn*S strips][4 tokens][16 columns]),
+    // The Wk shares through LDS ([Wk][Wn*S strips][4 RB tokens][16 columns]),
     // added in ascending order.
     __syncthreads();
     float* red4 = (float*)smem;
 #pragma unroll
     for (int s = 0; s < S; ++s)
-      if (g < T) red4[(((size_t)wk * SB + wn * S + s) * 4 + g) * 16 + r] = total[s][0];
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+        if (4 * b + g < T) red4[(((size_t)wk * SB + wn * S + s) * 4 * RB + 4 * b + g) * 16 + r] = total[s][b];
     __syncthreads();
     const int nout4 = T * SB * 16;
     for (int e = tid; e < nout4; e += nth) {
@@ -300,7 +322,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
       const int st = blockIdx.x * SB + ls;
       if (st >= NS) continue;
       float sum = 0.f;
-      for (int w = 0; w < Wk; ++w) sum += red4[(((size_t)w * SB + ls) * 4 + t) * 16 + col];
+      for (int w = 0; w < Wk; ++w) sum += red4[(((size_t)w * SB + ls) * 4 * RB + t) * 16 + col];
       y[(size_t)t * N + st * 16 + col] = sum;
     }
     return;
@@ -388,12 +410,12 @@ int limb_lds_bytes(int T, int K, int G, const LimbPlan& p) {
 int launch_limb(const SmallTArgs& a, const LimbPlan& p, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int W = p.wn * p.wk;
-  if (a.T < 1 || a.T > 5 || p.wn < 1 || p.wk < 1 || W > 16) return (int)hipErrorInvalidValue;
+  if (a.T < 1 || a.T > (p.token_lanes ? 8 : 5) || p.wn < 1 || p.wk < 1 || W > 16) return (int)hipErrorInvalidValue;
   if (limb_lds_bytes(a.T, a.K, a.G, p) > (p.token_lanes ? kLimbMaxLdsResident : kLimbMaxLds))
     return (int)hipErrorInvalidValue;
   if (p.token_lanes) {
-    if (a.T > 4) return (int)hipErrorInvalidValue;
-    return (int)launch_limb_t<4>(a, p, st);
+    if (a.T > 8) return (int)hipErrorInvalidValue;
+    return (int)(a.T <= 4 ? launch_limb_t<4>(a, p, st) : launch_limb_t<8>(a, p, st));
   }
   return (int)(a.T == 1 ? launch_limb_t<1>(a, p, st) : launch_limb_t<5>(a, p, st));
 }
