@@ -1,5 +1,6 @@
-// tern_limb.hip -- decode kernel for up to five tokens (the T = 1 gemv rung)
-// on the gfx950 integer matrix cores.
+// tern_limb.hip -- decode kernel on the gfx950 integer matrix cores: the
+// T = 1 gemv rung, and the small_t rung for short batches (tokens in their
+// own lane groups, TT = 4 and 8 below).
 //
 // y[t][n] = sum_g s[n][g] * sum_{k in g} w[n][k] * x[t][k], w in {-1,0,+1},
 // one fp16 scale per G weights along K ("NInfer sm_89 fork" article, section

@@ -1,6 +1,8 @@
 // tern_limbtile.hip -- small_t rung (T = 2..8) on the integer matrix cores:
 // the bf16 activations as int8 limbs, as in the gemv kernel (tern_limb.hip),
-// with the limbs made once per call by a small kernel.
+// made k-tile by k-tile by the loader wave of the contraction
+// (tern_limbfuse_kernel, T <= 4) or once per call by a small kernel
+// (tern_limb_prep_kernel + tern_limbtile_kernel).
 //
 // y[t][n] = sum_g s[n][g] * sum_{k in g} w[n][k] * x[t][k], w in {-1,0,+1},
 // one fp16 scale per G weights along K ("NInfer sm_89 fork" article, section
@@ -13,9 +15,11 @@
 // the integer MFMA as limbs: per token and 256-wide k-tile, with 2^E <=
 // max|x| < 2^(E+1) and d = E - 21, v = rne(x * 2^-d) = l0 + 256 l1 + 65536 l2
 // (tern_device.h), exact for every activation within 2^14 of the tile
-// maximum. Making the limbs inside the contraction would cost every
-// workgroup the whole activation row; here tern_limb_prep_kernel makes them
-// once, and the contraction reads them like any other operand.
+// maximum. Made up front inside the contraction they would cost every
+// workgroup the whole activation row before its first k-tile; the fused
+// kernel makes each k-tile's limbs in its loader wave just ahead of use, the
+// two-kernel path has tern_limb_prep_kernel make them once for the
+// contraction to read like any other operand.
 //
 // Operand layout: row block b (16 rows) holds tokens 4b..4b+3, token 4b + u
 // in rows 4u (l0), 4u + 1 (l1), 4u + 2 (l2), row 4u + 3 zero. An MFMA
