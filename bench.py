@@ -12,7 +12,12 @@ on the host as a baseline.
 
 Timing: the K timed steps are captured once into a HIP graph (PyTorch's
 CUDAGraph on ROCm) and replayed between HIP events recorded on the same
-stream, so host launch overhead does not enter the measurement.
+stream, so host launch overhead does not enter the measurement. The spread
+(p10 / p50 / p90 per step) comes from 20 replays of a graph of K / 20 steps,
+each between its own events. Each T <= 16 launch is also rated against the
+self-measured streaming-read ceiling: the fastest of a few plans of a
+read-only kernel (tern_stream_read) over the same number of bytes, from
+buffers rotated past the Infinity Cache like the weights.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -102,6 +107,60 @@ def graph_time(torch, fn, steps, warmup):
     end.synchronize()
     torch.cuda.synchronize()
     return start.elapsed_time(end) * 1e-3
+
+
+def graph_batches(torch, fn, warmup, per=50, batches=20):
+    """The spread of per-step times: a graph of `per` steps captured once and
+    replayed `batches` times, each replay between its own events (so each
+    batch also carries one graph launch, about 1-2 us over `per` steps).
+    Returns (mean, p10, p50, p90) seconds per step."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(max(1, warmup)):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(batches)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e-3 / per for a, b in ev])
+    return (float(t.mean()),) + tuple(float(v) for v in np.percentile(t, [10, 50, 90]))
+
+
+def read_ceiling(torch, tl, dev, nbytes, reps=100):
+    """Self-measured streaming-read ceiling for one launch over `nbytes`: the
+    fastest of a few (depth, waves per CU) plans of the read-only kernel,
+    rotating over a pool larger than the Infinity Cache. Returns seconds per
+    launch."""
+    nb = (nbytes + 1023) // 1024 * 1024
+    pool_bytes = max(int(ROTATE_BYTES) + nb, 2 * nb) // 4096 * 4096 + 4096
+    pool = torch.ones((pool_bytes,), dtype=torch.uint8, device=dev)
+    sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+    nslots = max(2, (pool_bytes - nb) // ((nb + 4095) // 4096 * 4096))
+    stride = (pool_bytes - nb) // nslots // 4096 * 4096
+    best = None
+    for depth in (4, 8, 16):
+        for waves in (4, 8, 16):
+            def one(i, depth=depth, waves=waves):
+                off = (i % nslots) * stride
+                tl.stream_read(pool[off:off + nb], depth=depth, waves_per_cu=waves, sink=sink)
+            t = graph_time(torch, one, reps, 3) / reps
+            if best is None or t < best[0]:
+                best = (t, depth, waves)
+    del pool
+    torch.cuda.empty_cache()
+    return best
 
 
 def cpu_baseline(wts_list, x_list, budget_s=12.0):
@@ -223,12 +282,14 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
 SMALL_T = (2, 4, 8, 12, 16)
 
 
-def small_t_leg(torch, ts, tl, dev, steps=100):
+def small_t_leg(torch, ts, tl, dev, steps=1000):
     """The draft-verify batches: T in {2, 4, 8, 12, 16} through gate_up, down
     and the 5120 -> 5120 out-projection with the rung the dispatcher picks
     (small_t for T <= 8, small_t_tiled above), weights rotated over > 600 MB
     so that they stream from HBM. Algorithmic bytes per launch as for T = 1
-    (codes + scales + x + y); GB/s is that over the event-timed launch."""
+    (codes + scales + x + y); GB/s is that over the mean event-timed launch
+    of 20 replays of a 50-launch graph (the spread over the replays is kept
+    as p10 / p50 / p90)."""
     out = {}
     for shape in (ts.GATE_UP, ts.DOWN, ts.OUT_PROJ):
         w = ts.weights(shape)
@@ -247,12 +308,23 @@ def small_t_leg(torch, ts, tl, dev, steps=100):
             def one(i):
                 tl.linear(x, sets[i % nsets], y=y, workspace=wsp)
 
-            t = graph_time(torch, one, steps, 5) / steps
+            t, p10, p50, p90 = graph_batches(torch, one, 5, per=steps // 20)
             b = algorithmic_bytes(T, shape.n, shape.k, shape.group)
             per_t[f"T{T}"] = {"rung": rung, "us_per_launch": round(t * 1e6, 2),
+                              "us_p10_p50_p90": [round(v * 1e6, 2) for v in (p10, p50, p90)],
                               "GB/s": round(b / t / 1e9, 1),
                               "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
-            log(f"  small-T {shape.name} T={T} ({rung}): {t * 1e6:.2f} us, {b / t / 1e9:.0f} GB/s")
+            log(f"  small-T {shape.name} T={T} ({rung}): {t * 1e6:.2f} us (p10/p50/p90 {p10 * 1e6:.2f}/"
+                f"{p50 * 1e6:.2f}/{p90 * 1e6:.2f}), {b / t / 1e9:.0f} GB/s")
+        # the read ceiling for each launch's bytes, after the layer's timings
+        for T in SMALL_T:
+            e = per_t[f"T{T}"]
+            tc = read_ceiling(torch, tl, dev, algorithmic_bytes(T, shape.n, shape.k, shape.group), reps=50)[0]
+            e["read_ceiling_us"] = round(tc * 1e6, 2)
+            e["frac_of_read_ceiling"] = round(tc * 1e6 / e["us_per_launch"], 4)
+        log(f"  small-T {shape.name}: read ceiling " + ", ".join(
+            f"T={T} {per_t[f'T{T}']['read_ceiling_us']:.2f} us ({per_t[f'T{T}']['frac_of_read_ceiling']:.0%})"
+            for T in SMALL_T))
         out[shape.name] = per_t
         del sets, base
         torch.cuda.empty_cache()
@@ -366,17 +438,30 @@ def main():
     el = graph_time(torch, decode_step, K, Wm)
     value = K * step_bytes / el / 1e9
     ms_per_step = el / K * 1e3
-    log(f"decode step {ms_per_step * 1e3:.2f} us, {value:.1f} GB/s")
+    _, d10, d50, d90 = graph_batches(torch, decode_step, Wm)
+    log(f"decode step {ms_per_step * 1e3:.2f} us, {value:.1f} GB/s (per-step p10/p50/p90 "
+        f"{d10 * 1e6:.2f}/{d50 * 1e6:.2f}/{d90 * 1e6:.2f} us over 20 batches of 50)")
 
     per_shape = {}
     for j, s in enumerate(shapes):
         def one(i, j=j):
             tl.linear(x1[j], sets[i % nsets][j], y=y1[j])
         t = graph_time(torch, one, K, Wm) / K
+        _, p10, p50, p90 = graph_batches(torch, one, Wm)
         b = algorithmic_bytes(1, s.n, s.k, s.group)
         per_shape[s.name] = {"rung": "gemv", "us_per_launch": round(t * 1e6, 3),
+                             "us_p10_p50_p90": [round(v * 1e6, 3) for v in (p10, p50, p90)],
                              "bytes": b, "GB/s": round(b / t / 1e9, 1)}
-        log(f"  {s.name}: {t * 1e6:.2f} us/launch, {b / t / 1e9:.1f} GB/s")
+        log(f"  {s.name}: {t * 1e6:.2f} us/launch (p10/p50/p90 {p10 * 1e6:.2f}/{p50 * 1e6:.2f}/"
+            f"{p90 * 1e6:.2f}), {b / t / 1e9:.1f} GB/s")
+    for s in shapes:  # the read ceiling for the same bytes, after the layer timings
+        e = per_shape[s.name]
+        tc, dc, wc = read_ceiling(torch, tl, dev, e["bytes"])
+        e["read_ceiling"] = {"us": round(tc * 1e6, 3), "GB/s": round(e["bytes"] / tc / 1e9, 1),
+                             "depth": dc, "waves_per_cu": wc}
+        e["frac_of_read_ceiling"] = round(tc * 1e6 / e["us_per_launch"], 4)
+        log(f"  {s.name}: read ceiling {tc * 1e6:.2f} us ({e['bytes'] / tc / 1e9:.0f} GB/s); the "
+            f"kernel reaches {e['frac_of_read_ceiling']:.0%} of it")
     dom = shapes[0].name
     achieved = per_shape[dom]["GB/s"]
     traffic = stored_traffic(f"gemv:{dom}")
@@ -384,7 +469,10 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": f"tern_limb_kernel (gemv rung, T=1) on {dom}",
                 "algorithmic_bytes_per_launch": per_shape[dom]["bytes"],
-                "us_per_launch": per_shape[dom]["us_per_launch"]}
+                "us_per_launch": per_shape[dom]["us_per_launch"],
+                "read_ceiling_GB/s": per_shape[dom]["read_ceiling"]["GB/s"],
+                "frac_of_read_ceiling": per_shape[dom]["frac_of_read_ceiling"]}
+    ceil_step = sum(v["read_ceiling"]["us"] for v in per_shape.values()) * 1e-6
 
     s8 = None
     if not args.no_s8:
@@ -490,7 +578,10 @@ def main():
            "config": {"workload": "decode T=1 through gate_up 5120->34816 and down 17408->5120, "
                                   "ternary weights (2-bit packed), fp16 scale per 128, bf16 x",
                       "T": 1, "rotation_sets": nsets, "bytes_per_step": step_bytes,
-                      "per_shape": per_shape, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+                      "per_shape": per_shape, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                      "us_per_step_p10_p50_p90": [round(v * 1e6, 3) for v in (d10, d50, d90)],
+                      "read_ceiling_us_per_step": round(ceil_step * 1e6, 3),
+                      "frac_of_read_ceiling": round(ceil_step / (el / K), 4)},
            "roofline": roofline, "s8_prefill": s8, "small_t": small, "stack": stack,
            "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)

@@ -249,6 +249,27 @@ tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
 tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int32_t* acc_out,
                               tern_q_layout layout, void* stream);
 
+/*
+ * Streaming-read ceiling (device, async): one launch that reads `bytes` of
+ * device memory at `buf` once, with 128-bit non-temporal loads and no other
+ * work, so that its duration is the floor of any single launch that streams
+ * as many bytes. The tuning notes on the pages rate the decode kernels
+ * against such a self-measured read-only ceiling ("NINFER ternary
+ * perf-tuning" notes, section 6, measured constants).
+ *   buf: device, 16-byte aligned, `bytes` readable; bytes a positive
+ *        multiple of 1024.
+ *   depth: loads in flight per wave, 4, 8 or 16; waves_per_cu: 1..32, the
+ *        number of waves per CU the bytes are spread over (one contiguous run
+ *        per wave). The fastest pair depends on the size; sweep a few.
+ *   sink: device, one uint32; written only when the XOR of a lane's loads
+ *        equals an arbitrary constant, so normally left untouched.
+ * Errors: NULL pointers (TERN_ERR_NULL), bad size (TERN_ERR_SHAPE), bad
+ * depth or waves (TERN_ERR_VALUE), misalignment (TERN_ERR_ALIGN); launch
+ * failures TERN_ERR_HIP. Counts as no rung in the probe.
+ */
+tern_status tern_stream_read(const void* buf, size_t bytes, int depth, int waves_per_cu,
+                             uint32_t* sink, void* stream);
+
 /* Rung probe: number of kernel launches per rung since the last reset,
  * counted at the launch site of the kernel that actually ran. */
 void tern_probe_snapshot(uint64_t out[TERN_RUNG_COUNT]);

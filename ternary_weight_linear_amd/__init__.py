@@ -37,7 +37,7 @@ STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_AL
 # Symbols declared in include/tern.h (checked by the host tests).
 EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpack",
            "tern_quant_act_s8", "tern_quant_act_s8_rot", "tern_workspace_bytes", "tern_linear", "tern_linear_s8_q",
-           "tern_debug_s8_acc",
+           "tern_debug_s8_acc", "tern_stream_read",
            "tern_probe_snapshot", "tern_probe_reset", "tern_last_rung", "tern_resolve_rung",
            "tern_rung_name", "tern_last_error", "tern_abi_version")
 
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "tern_linear": (st, [p, i, ctypes.POINTER(_Weights), p, i, p, sz, p]),
         "tern_linear_s8_q": (st, [p, p, i, ctypes.POINTER(_Weights), p, i, p]),
         "tern_debug_s8_acc": (st, [p, i, ctypes.POINTER(_Weights), p, i, p]),
+        "tern_stream_read": (st, [p, sz, i, i, p, p]),
         "tern_probe_snapshot": (None, [p]),
         "tern_probe_reset": (None, []),
         "tern_last_rung": (i, []),
@@ -264,6 +265,26 @@ def quant_act_s8_rot(x, q=None, scale=None, stream=None, layout="row_major"):
     _check(lib().tern_quant_act_s8_rot(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
                                        Q_LAYOUTS[layout], _stream(stream)))
     return q, scale
+
+
+def stream_read(buf, nbytes=None, depth=8, waves_per_cu=8, sink=None, stream=None):
+    """One launch of the streaming-read ceiling kernel over the first `nbytes`
+    bytes of the device tensor `buf` (default: all of it; a multiple of 1024).
+    `sink` is a device int32/uint32 tensor of at least one element."""
+    torch = _torch()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    total = buf.numel() * buf.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if nbytes > total:
+        raise ValueError(f"nbytes={nbytes} exceeds the buffer's {total} bytes")
+    if sink is None:
+        sink = torch.zeros((1,), dtype=torch.int32, device=buf.device)
+    if not sink.is_cuda or sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must be a device tensor of at least 4 bytes")
+    _check(lib().tern_stream_read(buf.data_ptr(), nbytes, depth, waves_per_cu, sink.data_ptr(),
+                                  _stream(stream)))
+    return sink
 
 
 def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=None):

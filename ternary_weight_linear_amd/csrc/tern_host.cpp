@@ -679,6 +679,22 @@ tern_status tern_quant_act_s8_rot(const void* x_bf16, int T, int k, int8_t* q, f
   return ok();
 }
 
+tern_status tern_stream_read(const void* buf, size_t bytes, int depth, int waves_per_cu,
+                             uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(TERN_ERR_NULL, "tern_stream_read: NULL pointer");
+  if (bytes < 1024 || bytes % 1024 != 0 || bytes / 1024 > 0x7fffffffu)
+    return fail(TERN_ERR_SHAPE, "bytes=%zu must be a positive multiple of 1024 below 2 TiB", bytes);
+  if (depth != 4 && depth != 8 && depth != 16)
+    return fail(TERN_ERR_VALUE, "depth=%d must be 4, 8 or 16", depth);
+  if (waves_per_cu < 1 || waves_per_cu > 32)
+    return fail(TERN_ERR_VALUE, "waves_per_cu=%d must be in [1, 32]", waves_per_cu);
+  if (!aligned16(buf) || ((uintptr_t)sink & 3u) != 0)
+    return fail(TERN_ERR_ALIGN, "buf must be 16-byte and sink 4-byte aligned");
+  const int err = tern::launch_stream_read(buf, bytes, depth, waves_per_cu, sink, stream);
+  if (err) return hip_fail(err, "stream_read launch");
+  return ok();
+}
+
 tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float* y,
                         tern_rung rung, void* ws, size_t ws_bytes, void* stream) {
   if (!x_bf16 || !y) return fail(TERN_ERR_NULL, "tern_linear: x or y is NULL");

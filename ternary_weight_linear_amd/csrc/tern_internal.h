@@ -111,6 +111,12 @@ int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* ws, void* st
 // bf16 prefill contraction (tern_b16mma.hip): the small_t_tiled rung above
 // one 16-token tile; same tile plan as the s8 contraction.
 int launch_b16_prefill(const SmallTArgs& a, const S8Plan& p, void* stream);
+
+// Streaming-read ceiling probe (tern_probe.hip): one launch that reads
+// `bytes` (a multiple of 1024) with `depth` (4, 8, 16) loads in flight per
+// wave and about waves_per_cu waves per CU.
+int launch_stream_read(const void* buf, size_t bytes, int depth, int waves_per_cu, uint32_t* sink,
+                       void* stream);
 const char* hip_error_string(int err);
 
 }  // namespace tern

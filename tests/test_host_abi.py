@@ -196,6 +196,15 @@ def test_linear_validation_happens_before_any_hip_call(tl):
     assert L.tern_quant_act_s8_rot(0x100000, 0, 1024, 0x200000, 0x300000, 0, None) == 2
     assert L.tern_quant_act_s8_rot(0x100000, 1, 1024, 0x200000, 0x300000, 7, None) == 4
     assert L.tern_quant_act_s8_rot(0x100008, 1, 1024, 0x200000, 0x300000, 0, None) == 3
+    # streaming-read ceiling probe: size, depth, waves and alignment checked first
+    assert L.tern_stream_read(None, 1024, 8, 8, 0x200000, None) == 1
+    assert L.tern_stream_read(0x100000, 1024, 8, 8, None, None) == 1
+    for nbytes in (0, 512, 1536):
+        assert L.tern_stream_read(0x100000, nbytes, 8, 8, 0x200000, None) == 2
+    for depth, waves in ((2, 8), (32, 8), (8, 0), (8, 33)):
+        assert L.tern_stream_read(0x100000, 1024, depth, waves, 0x200000, None) == 4
+    assert L.tern_stream_read(0x100008, 1024, 8, 8, 0x200000, None) == 3
+    assert L.tern_stream_read(0x100000, 1024, 8, 8, 0x200002, None) == 3
 
 
 def test_unfused_limb_path_declares_its_workspace():
