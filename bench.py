@@ -499,13 +499,16 @@ def main():
                 tl.linear_s8_q(qs[j][0], qs[j][1], sets[i % nsets][j], y=ys[j],
                                layout="operand_order")
             t = graph_time(torch, g1, K8, 2) / K8
+            _, g10, g50, g90 = graph_batches(torch, g1, 2, per=5)
             def q1(i, j=j):
                 tl.quant_act_s8(xs[j], q=qs[j][0], scale=qs[j][1], layout="operand_order")
             tq = graph_time(torch, q1, K8, 2) / K8
             o = 2 * T * s.n * s.k
             gemm[s.name] = {"us_s8_kernel": round(t * 1e6, 2), "TOPS_s8_kernel": round(o / t / 1e12, 1),
+                            "us_s8_kernel_p10_p50_p90": [round(v * 1e6, 2) for v in (g10, g50, g90)],
                             "us_quant_kernel": round(tq * 1e6, 2)}
-            log(f"  s8 {s.name}: gemm {t * 1e6:.1f} us ({o / t / 1e12:.0f} TOPS), quant {tq * 1e6:.1f} us")
+            log(f"  s8 {s.name}: gemm {t * 1e6:.1f} us ({o / t / 1e12:.0f} TOPS; p10/p50/p90 over 20 replays "
+                f"of 5: {g10 * 1e6:.1f}/{g50 * 1e6:.1f}/{g90 * 1e6:.1f} us), quant {tq * 1e6:.1f} us")
         ach = gemm[dom]["TOPS_s8_kernel"]
         s8 = {"metric": "int8 TOPS at T=2048 (quant + s8 contraction, both shapes)",
               "value": round(tops, 1), "unit": "TOPS", "ms_per_step": round(el8 / K8 * 1e3, 4),
