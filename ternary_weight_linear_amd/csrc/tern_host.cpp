@@ -314,9 +314,11 @@ tern::TilePlan plan_tile(int T, int n, int k) {
 // wave loads its own activation fragments, no barriers), except for T > 8
 // with a long K, where the per-wave activation traffic grows too large.
 // The small_t limb path (tern_limbtile.hip) takes T <= 8; by default it runs
-// wide layers (>= 1024 strips) at T <= 4, one row block, where it beat the
-// bf16 activation-tiled kernel in A/B runs on MI355X (gate_up: 15.3 against
-// 15.9-16.6 us); at T = 5..8 (two row blocks) and on narrow layers it lost.
+// wide layers (>= 1024 strips) at T <= 4, one row block, where the resident
+// limb kernel (checked first) does not fit its LDS (long K): there it beat
+// the bf16 activation-tiled kernel in A/B runs on MI355X (gate_up: 14.0-15.3
+// against 15.9-16.6 us); at T = 5..8 (two row blocks) and on narrow layers it
+// lost.
 bool small_t_limb(int T, int n, int k) {
   (void)k;
   const Config& c = config();
@@ -351,11 +353,27 @@ tern::LimbPlan plan_limb(int T, int n, int k);
 tern::LimbPlan plan_resident(int T, int n, int k) {
   tern::LimbPlan p = plan_limb(T, n, k);
   p.token_lanes = true;
-  // Limbs of more than 80 KiB leave room for one workgroup per CU: make it
-  // wide enough that one round of workgroups covers the strips.
   const int NS = n / 16;
-  if (p.wk == 1 && tern::limb_lds_bytes(T, k, 128, p) > 80 * 1024)
+  // narrow layers with a long K keep 8 K shares here (the gemv's 6 measured
+  // 1 % slower at T = 2 on down)
+  if (NS < 1024 && !config().tune_wk && k / 256 >= 48) {
+    p.wk = 8;
+    while (p.wn * p.wk > 16) --p.wn;
+  }
+  // Wide layers: the gemv's twelve waves per workgroup (one round of
+  // workgroups, one per CU: at T = 2..4 on gate_up 10.5-10.8 us against
+  // 12.0-17.9 with four waves, whose 544 workgroups of 36-78 KB of LDS need
+  // up to three rounds), fewer where the LDS would not hold them, but never
+  // fewer than one round of one workgroup per CU needs.
+  if (p.wk == 1 && NS >= 1024 && !config().tune_wn) {
+    p.wn = 12;
+    const int floor_wn = (NS + 255) / 256;
+    while (p.wn > floor_wn && tern::limb_lds_bytes(T, k, 128, p) > tern::kLimbMaxLdsResident) --p.wn;
+  } else if (p.wk == 1 && tern::limb_lds_bytes(T, k, 128, p) > 80 * 1024) {
+    // Limbs of more than 80 KiB leave room for one workgroup per CU: make it
+    // wide enough that one round of workgroups covers the strips.
     p.wn = std::min(16, std::max(p.wn, (NS + 255) / 256));
+  }
   return p;
 }
 
@@ -364,9 +382,10 @@ bool small_t_resident(int T, int n, int k) {
   const int lds = tern::limb_lds_bytes(T, k, 128, plan_resident(T, n, k));
   if (c.smallt_kernel) return c.smallt_kernel == 4 && T <= 8 && lds <= tern::kLimbMaxLdsResident;
   if (T <= 3) return lds <= 112 * 1024;
-  // Two row blocks of tokens (one workgroup per CU): ahead of the bf16 tile
-  // kernel on wide layers at T = 5, 6 (5-8 %), behind it from T = 7.
-  return (T == 5 || T == 6) && n / 16 >= 1024 && lds <= tern::kLimbMaxLdsResident;
+  // Wide layers in one round of twelve-wave workgroups: ahead of the fused
+  // limb kernel at T = 4 (10.8 against 14.2 us on gate_up) and, with two row
+  // blocks of tokens, of the bf16 tile kernel at T = 5, 6.
+  return T <= 6 && n / 16 >= 1024 && lds <= tern::kLimbMaxLdsResident;
 }
 
 bool small_t_per_wave(int T, int n, int k) {
@@ -422,24 +441,31 @@ tern::SmallTPlan plan_small_t(int T, int n, int k, int group, tern_rung r) {
   return p;
 }
 
-// Launch shape of the integer-limb decode kernel, from a sweep on MI355X at
+// Launch shape of the integer-limb decode kernel, from sweeps on MI355X at
 // T = 1 over (waves per strip group, K shares, ring depth): wide layers (>= 1024
-// strips) take four waves per workgroup, one strip each over the whole K;
-// narrow layers two strips per workgroup with K split 8 ways (K >= 12288) or
-// 4 ways, so that the few strips still give every SIMD several waves. Every
-// wave keeps 4 k-tiles of codes in flight.
+// strips) take twelve waves per workgroup (three per SIMD), one strip each
+// over the whole K, so that 2176 strips make 182 workgroups, one round of one
+// per CU (gate_up 10.2 us against 11.0 with four waves and 544 workgroups;
+// 8 waves give 272 workgroups and a second round, 16 waves too few CUs);
+// narrow layers two strips per workgroup with K split 6 ways (K >= 12288;
+// 12 waves, down 8.4 us against 8.7 with 8 ways) or 4 ways, so that the few strips still give every SIMD several waves. Every
+// wave keeps 4 k-tiles of codes in flight. Wide layers whose limbs and
+// scales would not fit the kernel's LDS take fewer waves.
 tern::LimbPlan plan_limb(int T, int n, int k) {
-  (void)T;
   const Config& c = config();
   tern::LimbPlan p;
   const int NS = n / 16, KT = k / 256;
   const bool wide = NS >= 1024;
   p.strips_per_wave = c.tune_strips ? c.tune_strips : 1;
-  p.wn = c.tune_wn ? c.tune_wn : (wide ? 4 : 2);
-  p.wk = c.tune_wk ? c.tune_wk : (wide ? 1 : (KT >= 48 ? 8 : 4));
+  p.wn = c.tune_wn ? c.tune_wn : (wide ? 12 : 2);
+  p.wk = c.tune_wk ? c.tune_wk : (wide ? 1 : (KT >= 48 ? 6 : 4));
   p.wk = std::min(p.wk, KT);
   while (p.wn * p.wk > 16) --p.wn;
   p.depth = c.tune_depth ? c.tune_depth : (p.strips_per_wave == 1 ? 4 : 2);
+  // (the scales of the workgroup's strips share the LDS with the limbs;
+  // G = 64 is the larger of the two)
+  if (wide && !c.tune_wn)
+    while (p.wn > 4 && tern::limb_lds_bytes(T, k, 64, p) > tern::kLimbMaxLds) --p.wn;
   return p;
 }
 
