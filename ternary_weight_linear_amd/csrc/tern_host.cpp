@@ -341,6 +341,7 @@ tern::LimbTilePlan plan_limbtile(int T, int n, int k) {
 }
 
 tern::LimbPlan plan_limb(int T, int n, int k);
+int wide_waves(int NS);
 
 // small_t on T <= 8 tokens through the gemv kernel's layout (the limbs of
 // the whole K made once per workgroup and kept in LDS, lane group u = tokens
@@ -360,13 +361,13 @@ tern::LimbPlan plan_resident(int T, int n, int k) {
     p.wk = 8;
     while (p.wn * p.wk > 16) --p.wn;
   }
-  // Wide layers: the gemv's twelve waves per workgroup (one round of
-  // workgroups, one per CU: at T = 2..4 on gate_up 10.5-10.8 us against
-  // 12.0-17.9 with four waves, whose 544 workgroups of 36-78 KB of LDS need
-  // up to three rounds), fewer where the LDS would not hold them, but never
-  // fewer than one round of one workgroup per CU needs.
+  // Wide layers: the gemv's wide workgroups (one round, one per CU: at
+  // T = 2..4 on gate_up, twelve waves, 10.5-10.8 us against 12.0-17.9 with
+  // four waves, whose 544 workgroups of 36-78 KB of LDS need up to three
+  // rounds), fewer waves where the LDS would not hold them, but never fewer
+  // than one round of one workgroup per CU needs.
   if (p.wk == 1 && NS >= 1024 && !config().tune_wn) {
-    p.wn = 12;
+    p.wn = wide_waves(NS);
     const int floor_wn = (NS + 255) / 256;
     while (p.wn > floor_wn && tern::limb_lds_bytes(T, k, 128, p) > tern::kLimbMaxLdsResident) --p.wn;
   } else if (p.wk == 1 && tern::limb_lds_bytes(T, k, 128, p) > 80 * 1024) {
@@ -443,21 +444,25 @@ tern::SmallTPlan plan_small_t(int T, int n, int k, int group, tern_rung r) {
 
 // Launch shape of the integer-limb decode kernel, from sweeps on MI355X at
 // T = 1 over (waves per strip group, K shares, ring depth): wide layers (>= 1024
-// strips) take twelve waves per workgroup (three per SIMD), one strip each
-// over the whole K, so that 2176 strips make 182 workgroups, one round of one
-// per CU (gate_up 10.2 us against 11.0 with four waves and 544 workgroups;
-// 8 waves give 272 workgroups and a second round, 16 waves too few CUs);
+// strips) take one strip per wave over the whole K and NS / 136 waves per
+// workgroup, 4 to 12, so that the workgroups make one round of one per CU:
+// 2176 strips take 12 waves and 182 workgroups (10.2 us against 11.0 with four
+// waves and 544 workgroups, up to three per CU; 8 waves give 272 workgroups
+// and a second round, 16 waves too few CUs), 1088 strips 8 waves and 136
+// workgroups (7.6 us; 8.4 with four waves, 9.3 with twelve);
 // narrow layers two strips per workgroup with K split 6 ways (K >= 12288;
 // 12 waves, down 8.4 us against 8.7 with 8 ways) or 4 ways, so that the few strips still give every SIMD several waves. Every
 // wave keeps 4 k-tiles of codes in flight. Wide layers whose limbs and
 // scales would not fit the kernel's LDS take fewer waves.
+int wide_waves(int NS) { return std::min(12, std::max(4, NS / 136)); }
+
 tern::LimbPlan plan_limb(int T, int n, int k) {
   const Config& c = config();
   tern::LimbPlan p;
   const int NS = n / 16, KT = k / 256;
   const bool wide = NS >= 1024;
   p.strips_per_wave = c.tune_strips ? c.tune_strips : 1;
-  p.wn = c.tune_wn ? c.tune_wn : (wide ? 12 : 2);
+  p.wn = c.tune_wn ? c.tune_wn : (wide ? wide_waves(NS) : 2);
   p.wk = c.tune_wk ? c.tune_wk : (wide ? 1 : (KT >= 48 ? 6 : 4));
   p.wk = std::min(p.wk, KT);
   while (p.wn * p.wk > 16) --p.wn;
