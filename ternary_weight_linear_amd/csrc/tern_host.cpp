@@ -64,6 +64,7 @@ struct Config {
   int tune_wk = 0;                    // TERN_TUNE_WK (0 = heuristic)
   int tune_depth = 0;                 // TERN_TUNE_DEPTH (0 = heuristic)
   bool gemv_bf16 = false;             // TERN_TUNE_GEMV=bf16: time the bf16-operand gemv kernel (default: limb)
+  bool t5_lanes = false;              // TERN_TUNE_T5=lanes: resident limbs at T = 5 in two token-lane row blocks
   int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave, 3 = limb, 4 = resident
   bool limb_unfused = false;          // TERN_TUNE_SMALLT=limb2: limbs by the separate prep kernel
 };
@@ -173,6 +174,12 @@ Config read_config() {
       c.gemv_bf16 = true;
     else if (strcmp(s, "limb") != 0)
       bad("TERN_TUNE_GEMV", s);
+  }
+  if (const char* s = getenv("TERN_TUNE_T5")) {
+    if (strcmp(s, "lanes") == 0)
+      c.t5_lanes = true;
+    else if (strcmp(s, "rows") != 0)
+      bad("TERN_TUNE_T5", s);
   }
   if (const char* s = getenv("TERN_TUNE_SMALLT")) {
     if (strcmp(s, "tile") == 0)
@@ -353,7 +360,11 @@ int wide_waves(int NS);
 // depend on the group size.
 tern::LimbPlan plan_resident(int T, int n, int k) {
   tern::LimbPlan p = plan_limb(T, n, k);
-  p.token_lanes = true;
+  p.resident = true;
+  // Five tokens fill one 16-row operand as rows 3t + L with per-row totals
+  // (the kernel's TT = 5 mode); more need the token-lane mode's second
+  // operand. TERN_TUNE_T5=lanes keeps T = 5 on the token lanes.
+  p.token_lanes = !(T == 5 && !config().t5_lanes);
   const int NS = n / 16;
   // narrow layers with a long K keep 8 K shares here (the gemv's 6 measured
   // 1 % slower at T = 2 on down)

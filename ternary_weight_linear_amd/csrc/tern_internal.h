@@ -65,6 +65,7 @@ struct LimbPlan {
   int wk;               // K shares per workgroup (waves split the k-tiles); wn * wk <= 16
   int depth;            // k-tiles of codes in flight per wave: 2, 4 or 8
   bool token_lanes = false;  // T <= 4: lane group u holds token u (single-token epilogue)
+  bool resident = false;     // limbs of the whole K in up to kLimbMaxLdsResident of LDS (one workgroup per CU)
 };
 constexpr int kLimbMaxLds = 65536;
 constexpr int kLimbMaxLdsResident = 160 * 1024;  // the resident small-T mode: all of a CU's LDS

@@ -412,7 +412,7 @@ int launch_limb(const SmallTArgs& a, const LimbPlan& p, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int W = p.wn * p.wk;
   if (a.T < 1 || a.T > (p.token_lanes ? 8 : 5) || p.wn < 1 || p.wk < 1 || W > 16) return (int)hipErrorInvalidValue;
-  if (limb_lds_bytes(a.T, a.K, a.G, p) > (p.token_lanes ? kLimbMaxLdsResident : kLimbMaxLds))
+  if (limb_lds_bytes(a.T, a.K, a.G, p) > (p.token_lanes || p.resident ? kLimbMaxLdsResident : kLimbMaxLds))
     return (int)hipErrorInvalidValue;
   if (p.token_lanes) {
     if (a.T > 8) return (int)hipErrorInvalidValue;
