@@ -160,21 +160,23 @@ def test_small_case_s8_accumulators_bit_exact(tl, torch, small):
 # ------------------------------------------------ wide-layer limb plans
 
 
-@pytest.mark.parametrize("ns", [1024, 1100, 2176])
-def test_wide_limb_plans_exact(tl, torch, ns):
+@pytest.mark.parametrize("ns,k", [(1024, 512), (1100, 512), (2176, 512), (1024, 16384)])
+def test_wide_limb_plans_exact(tl, torch, ns, k):
     """Layers of 1024 strips or more run the gemv (T = 1) and the resident
     limb kernel (T = 2..6) in workgroups of NS / 136 waves, 4 to 12, one strip
     per wave: 7, 8 and 12 waves here, with a ragged last workgroup at 1100 and
-    2176 strips. Integer activations and power-of-two scales make every
-    product and sum exact in fp32, so each T must match the oracle bit for
-    bit, rows of every workgroup included."""
-    n, k, G = 16 * ns, 512, 128
+    2176 strips. With K = 16384 the limbs and scales outgrow the LDS: the
+    gemv falls back to the bf16 kernel, T = 2..4 take the fused limb kernel
+    (the resident limbs would need 128-165 KB) and T = 5, 6 the tile kernel. Integer activations and power-of-two scales make every product
+    and sum exact in fp32, so each T must match the oracle bit for bit, rows
+    of every workgroup included."""
+    n, G = 16 * ns, 128
     rng = np.random.default_rng(ns)
     w = ts.draw_weights(rng, n, k, 0.4)
     s = ts.pow2_scales(n, k, G, seed=ns)
     W = tl.TernaryWeights.from_host(w, s)
     for T in range(1, 7):
-        print("wide plan", ns, "strips, T", T, flush=True)
+        print("wide plan", ns, "strips, K", k, "T", T, flush=True)
         xbits = ts.integer_activations(k, T, seed=ns + T)
         ref = oracle.linear_bf16(xbits, w, s)
         assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
