@@ -173,7 +173,9 @@ def linear_s8(q: np.ndarray, scale: np.ndarray, w: np.ndarray, s: np.ndarray) ->
 
 def linear_s8_fp32_ordered(q: np.ndarray, scale: np.ndarray, w: np.ndarray,
                            s: np.ndarray) -> np.ndarray:
-    """Diagnostic: s8 output in one fixed fp32 order (groups ascending, fmaf)."""
+    """s8 output in the canonical fp32 order (groups ascending, one fmaf each,
+    then one multiply by the token scale): the bitwise reference for kernels
+    that keep that order."""
     q = _c(q, np.int8)
     scale = _c(scale, np.float32)
     w = _c(w, np.int8)

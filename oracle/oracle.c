@@ -399,10 +399,13 @@ int oracle_linear_s8(const int8_t* q, const float* scale, int64_t T, int64_t K,
 }
 
 /*
- * Diagnostic only (not a gate): the same output in one fixed fp32 order,
+ * The same output in one fixed fp32 order (the canonical epilogue order):
  *   acc_f = 0; for g ascending: acc_f = fmaf((float)acc_g, (float)s_g, acc_f);
  *   y = acc_f * scale_t
- * A kernel that keeps this order reproduces it bit for bit.
+ * Every step is one IEEE single rounding (fmaf rounds acc*s + acc_f once).
+ * A kernel that keeps this order reproduces it bit for bit, and the GPU
+ * tests hold such kernels to it bitwise; the gate of the s8 rung itself is
+ * the 1e-6 relative distance from oracle_linear_s8.
  */
 int oracle_linear_s8_fp32_ordered(const int8_t* q, const float* scale, int64_t T, int64_t K,
                                   const int8_t* w, const uint16_t* s, int64_t N, int64_t G,

@@ -244,6 +244,44 @@ def test_linear_s8_within_gate_of_fp32_order():
     assert np.linalg.norm(yo - y) / np.linalg.norm(y) < 1e-6
 
 
+def _runs(runs, dtype) -> np.ndarray:
+    return np.concatenate([np.full(n, v, dtype) for v, n in runs])
+
+
+def test_hand_s8_fp32_ordered(hand):
+    """The canonical fp32 epilogue order, pinned on hand-worked cases where
+    it differs from descending groups, from a separate multiply and add and
+    from an fp64 accumulator (derivations in the golden file)."""
+    for c in hand["s8_fp32_ordered"]["cases"]:
+        q = _runs(c["q_runs"], np.int8)[None, :]
+        w = _runs(c["w_runs"], np.int8)[None, :]
+        s = f16([c["s"]])
+        assert oracle.s8_acc(q, w, c["G"])[0, 0].tolist() == c["acc"], c["derivation"]
+        sc = np.asarray([c["scale"]], np.float32)
+        yo = oracle.linear_s8_fp32_ordered(q, sc, w, s)
+        assert exact.f32_bits(float(yo[0, 0])) == int(c["y_ordered_bits"], 16), c["derivation"]
+        ye = oracle.linear_s8(q, sc, w, s)
+        assert exact.f32_bits(float(ye[0, 0])) == int(c["y_exact_bits"], 16), c["derivation"]
+
+
+def test_s8_fp32_order_step_by_step_in_rationals():
+    """The same order on random data, every step evaluated exactly in
+    rationals and rounded once to fp32 (an fma is one rounding of
+    acc * s + total; the final product one rounding of total * scale)."""
+    x, w, s = _small_case(seed=21, T=4, N=16, K=8192, G=128)
+    q, sc = oracle.quant_s8(x)
+    yo = oracle.linear_s8_fp32_ordered(q, sc, w, s)
+    acc = oracle.s8_acc(q, w, 128)
+    for t in range(4):
+        st = exact.f32_to_fraction(float(sc[t]))
+        for n in range(16):
+            tot = Fraction(0)
+            for g in range(64):
+                r = exact.half_bits_to_fraction(int(s[n, g])) * int(acc[t, n, g]) + tot
+                tot = exact.f32_to_fraction(exact.bits_f32(exact.fraction_to_f32_bits(r)))
+            assert exact.f32_bits(float(yo[t, n])) == exact.fraction_to_f32_bits(tot * st)
+
+
 def _all_positive_bf16_upto(a: float) -> np.ndarray:
     b = np.arange(1, 0x7F80, dtype=np.uint32).astype(np.uint16)  # positive finite
     v = ts.bf16_bits_to_f32(b)
