@@ -37,7 +37,10 @@
  *      TERN_S8=0|1                 0 sends T >= TERN_S8_MIN_T to small_t_tiled
  *      TERN_S8_MIN_T=<int>=1..>    first T of the s8 rung (default 17)
  *      TERN_SMALL_T_MAX=<int>      last T of small_t (default 8, at most 16)
- *      TERN_SMALL_T_TILED_MAX=<int> last T of small_t_tiled before s8 (default 16)
+ *      TERN_SMALL_T_TILED_MAX=<int> last T of small_t_tiled before s8 (default 16);
+ *                                  the same threshold as TERN_S8_MIN_T - 1: set
+ *                                  either, or both consistently (else
+ *                                  TERN_ERR_CONFIG); at least TERN_SMALL_T_MAX
  *      TERN_DEBUG=0|1, TERN_DEBUG_MIN_T=<int>, TERN_DEBUG_BUDGET=<int>
  *                                  print "rung=<name> T= N= K= G=" lines to
  *                                  stderr for calls with T >= MIN_T, at most
@@ -71,7 +74,8 @@ typedef enum {
 typedef enum {
   TERN_OK = 0,
   TERN_ERR_NULL = 1,      /* a required pointer is NULL */
-  TERN_ERR_SHAPE = 2,     /* T < 1, N % 16, K % 256, K % G, G not 64/128, size overflow */
+  TERN_ERR_SHAPE = 2,     /* T < 1 or T > 2^19, N % 16, K % 256, K % G, G not 64/128,
+                             K > 2^20 or N > 2^24 (the kernels' 32-bit offsets) */
   TERN_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
   TERN_ERR_VALUE = 4,     /* a weight outside {-1,0,+1}, a code 10 in packed data */
   TERN_ERR_RUNG = 5,      /* unknown rung, or a forced rung that cannot take this T */
@@ -273,7 +277,53 @@ tern_status tern_stream_read(const void* buf, size_t bytes, int depth, int waves
 /* Rung probe: number of kernel launches per rung since the last reset,
  * counted at the launch site of the kernel that actually ran. */
 void tern_probe_snapshot(uint64_t out[TERN_RUNG_COUNT]);
+/* Resets the rung probe and the kernel probe. */
 void tern_probe_reset(void);
+
+/*
+ * Kernel probe: every kernel this library launches, one id each. A rung is
+ * served by several kernels chosen by layer shape (and by TERN_TUNE_* knobs),
+ * so the rung probe alone cannot say which one produced a result; the kernel
+ * probe counts every successful launch per kernel, at its launch site
+ * ("NINFER ternary perf-tuning" notes, section 2: every reachable branch
+ * reports itself).
+ */
+typedef enum {
+  TERN_KERNEL_QUANT_S8 = 0,       /* per-token int8 quantisation, q in operand order (s8 rung) */
+  TERN_KERNEL_QUANT_S8_ROW,       /* the same with row-major q (tern_quant_act_s8 only) */
+  TERN_KERNEL_QUANT_S8_ROT,       /* Hadamard-rotated quantisation (tern_quant_act_s8_rot) */
+  TERN_KERNEL_GEMV_LIMB,          /* gemv: x as int8 limbs on the i8 matrix cores */
+  TERN_KERNEL_GEMV_BF16,          /* gemv: bf16-operand kernel with one-token rows (limbs do not fit LDS) */
+  TERN_KERNEL_SMALLT_RESIDENT,    /* small_t: limb kernel, every token's limbs resident in LDS */
+  TERN_KERNEL_SMALLT_LIMB_FUSED,  /* small_t: limb contraction, limbs made by a loader wave */
+  TERN_KERNEL_SMALLT_LIMB_PREP,   /* small_t: separate limb preparation (limbs to the workspace) */
+  TERN_KERNEL_SMALLT_LIMB_TILE,   /* small_t: limb contraction on the prepared limbs */
+  TERN_KERNEL_SMALLT_WAVE,        /* small_t / small_t_tiled: per-wave bf16 kernel, 16-token tile */
+  TERN_KERNEL_SMALLT_TILE,        /* small_t / small_t_tiled: activation tile shared in LDS */
+  TERN_KERNEL_SMALLT_TILE_REDUCE, /* adds the K-split partial sums of SMALLT_TILE */
+  TERN_KERNEL_B16_PREFILL,        /* small_t_tiled above 16 tokens: bf16 MFMA contraction */
+  TERN_KERNEL_S8_MMA,             /* s8 contraction on operand-order q */
+  TERN_KERNEL_S8_REDUCE,          /* adds the K-split partial totals of S8_MMA */
+  TERN_KERNEL_S8_ROW,             /* s8 contraction on row-major q (tern_linear_s8_q) */
+  TERN_KERNEL_S8_ACC_EXPORT,      /* tern_debug_s8_acc */
+  TERN_KERNEL_STREAM_READ,        /* tern_stream_read */
+  TERN_KERNEL_COUNT
+} tern_kernel;
+
+/* Launches per kernel since the last tern_probe_reset (all threads). */
+void tern_kernel_probe_snapshot(uint64_t out[TERN_KERNEL_COUNT]);
+/* Bit i set: kernel i was launched by the most recent successful call on this
+ * thread of tern_linear, tern_linear_s8_q, tern_debug_s8_acc,
+ * tern_quant_act_s8, tern_quant_act_s8_rot or tern_stream_read (0 before
+ * any). With TERN_DEBUG=1 the rung line of tern_linear names them too. */
+uint64_t tern_last_kernels(void);
+/* Host-only dry run of the dispatcher (no HIP call): the kernel-id bit mask
+ * (as tern_last_kernels) that tern_linear(T, N, K, G, rung) would launch
+ * under the frozen configuration, 0 if the shape, rung or configuration is
+ * invalid (tern_last_error says why). */
+uint64_t tern_plan_kernels(int T, int n, int k, int group, tern_rung rung);
+/* Name of a kernel id ("gemv_limb", "smallt_tile", ...; "invalid" if out of range). */
+const char* tern_kernel_name(tern_kernel kernel);
 /* Rung of the most recent successful tern_linear call on any thread
  * (TERN_RUNG_AUTO if none yet). */
 tern_rung tern_last_rung(void);

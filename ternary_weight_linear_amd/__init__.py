@@ -15,6 +15,13 @@ Entry points mirror the C ABI in ``include/tern.h``:
 * ``linear_s8_q``              -- the s8 contraction on pre-quantised activations
 * ``debug_s8_acc``             -- the s8 rung's int32 group accumulators
 * ``probe_snapshot`` / ``probe_reset`` / ``last_rung`` / ``resolve_rung``
+* ``kernel_probe_snapshot`` / ``last_kernels`` -- which kernels ran
+
+Streams: every device call enqueues on ``stream`` (default: the current
+stream). Tensors the binding allocates for such a call (outputs, workspace)
+are recorded on that stream when it is not the current one, so the caching
+allocator does not hand their memory to other work before the call's kernels
+are done with it.
 """
 from __future__ import annotations
 
@@ -34,12 +41,20 @@ STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_AL
           4: "TERN_ERR_VALUE", 5: "TERN_ERR_RUNG", 6: "TERN_ERR_WORKSPACE", 7: "TERN_ERR_CONFIG",
           8: "TERN_ERR_HIP", 9: "TERN_ERR_LAYOUT"}
 
+# Kernel ids of the kernel probe, in the order of tern_kernel in tern.h.
+KERNELS = ("quant_s8", "quant_s8_row", "quant_s8_rot", "gemv_limb", "gemv_bf16",
+           "smallt_resident", "smallt_limb_fused", "smallt_limb_prep", "smallt_limb_tile",
+           "smallt_wave", "smallt_tile", "smallt_tile_reduce", "b16_prefill", "s8_mma",
+           "s8_reduce", "s8_row", "s8_acc_export", "stream_read")
+
 # Symbols declared in include/tern.h (checked by the host tests).
 EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpack",
            "tern_quant_act_s8", "tern_quant_act_s8_rot", "tern_workspace_bytes", "tern_linear", "tern_linear_s8_q",
            "tern_debug_s8_acc", "tern_stream_read",
            "tern_probe_snapshot", "tern_probe_reset", "tern_last_rung", "tern_resolve_rung",
-           "tern_rung_name", "tern_last_error", "tern_abi_version")
+           "tern_rung_name", "tern_last_error", "tern_abi_version",
+           "tern_kernel_probe_snapshot", "tern_last_kernels", "tern_kernel_name",
+           "tern_plan_kernels")
 
 
 class TernError(RuntimeError):
@@ -86,6 +101,10 @@ def lib() -> ctypes.CDLL:
         "tern_rung_name": (ctypes.c_char_p, [i]),
         "tern_last_error": (ctypes.c_char_p, []),
         "tern_abi_version": (i, []),
+        "tern_kernel_probe_snapshot": (None, [p]),
+        "tern_last_kernels": (ctypes.c_uint64, []),
+        "tern_kernel_name": (ctypes.c_char_p, [i]),
+        "tern_plan_kernels": (ctypes.c_uint64, [i, i, i, i, i]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -173,6 +192,31 @@ def last_rung() -> str:
     return RUNGS[lib().tern_last_rung()]
 
 
+def kernel_probe_snapshot() -> dict:
+    """Launches per kernel (name -> count) since the last probe_reset()."""
+    arr = (ctypes.c_uint64 * len(KERNELS))()
+    lib().tern_kernel_probe_snapshot(arr)
+    return {KERNELS[i]: int(arr[i]) for i in range(len(KERNELS))}
+
+
+def _names(mask: int) -> list:
+    return [KERNELS[i] for i in range(len(KERNELS)) if mask >> i & 1]
+
+
+def last_kernels() -> list:
+    """Names of the kernels the last successful call on this thread launched."""
+    return _names(lib().tern_last_kernels())
+
+
+def plan_kernels(T: int, n: int, k: int, group: int, rung="auto") -> list:
+    """Names of the kernels linear() would launch for this call (host-only
+    dry run of the dispatcher)."""
+    m = lib().tern_plan_kernels(T, n, k, group, _rung(rung))
+    if m == 0:
+        raise TernError(5, lib().tern_last_error().decode())
+    return _names(m)
+
+
 # ----------------------------------------------------------------- device
 
 
@@ -188,6 +232,27 @@ def _stream(stream):
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _side_stream(stream):
+    """The torch stream object of `stream` when it is not the current stream
+    (None when the call runs on the current stream)."""
+    if stream is None:
+        return None
+    torch = _torch()
+    s = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return None
+    return s
+
+
+def _keep_for(stream, *tensors) -> None:
+    """Record the tensors this binding allocated on the launch stream."""
+    s = _side_stream(stream)
+    if s is not None:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
 
 
 def _dev(t, dtype, name):
@@ -238,14 +303,16 @@ def quant_act_s8(x, q=None, scale=None, stream=None, layout="row_major"):
     torch = _torch()
     _dev(x, torch.bfloat16, "x")
     T, K = x.shape
-    if q is None:
+    new_q, new_scale = q is None, scale is None
+    if new_q:
         q = torch.empty((T, K), dtype=torch.int8, device=x.device)
-    if scale is None:
+    if new_scale:
         scale = torch.empty((T,), dtype=torch.float32, device=x.device)
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
     _check(lib().tern_quant_act_s8(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
                                    Q_LAYOUTS[layout], _stream(stream)))
+    _keep_for(stream, q if new_q else None, scale if new_scale else None)
     return q, scale
 
 
@@ -256,14 +323,16 @@ def quant_act_s8_rot(x, q=None, scale=None, stream=None, layout="row_major"):
     torch = _torch()
     _dev(x, torch.bfloat16, "x")
     T, K = x.shape
-    if q is None:
+    new_q, new_scale = q is None, scale is None
+    if new_q:
         q = torch.empty((T, K), dtype=torch.int8, device=x.device)
-    if scale is None:
+    if new_scale:
         scale = torch.empty((T,), dtype=torch.float32, device=x.device)
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
     _check(lib().tern_quant_act_s8_rot(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
                                        Q_LAYOUTS[layout], _stream(stream)))
+    _keep_for(stream, q if new_q else None, scale if new_scale else None)
     return q, scale
 
 
@@ -278,12 +347,14 @@ def stream_read(buf, nbytes=None, depth=8, waves_per_cu=8, sink=None, stream=Non
     nbytes = total if nbytes is None else int(nbytes)
     if nbytes > total:
         raise ValueError(f"nbytes={nbytes} exceeds the buffer's {total} bytes")
-    if sink is None:
+    new_sink = sink is None
+    if new_sink:
         sink = torch.zeros((1,), dtype=torch.int32, device=buf.device)
     if not sink.is_cuda or sink.numel() * sink.element_size() < 4:
         raise ValueError("sink must be a device tensor of at least 4 bytes")
     _check(lib().tern_stream_read(buf.data_ptr(), nbytes, depth, waves_per_cu, sink.data_ptr(),
                                   _stream(stream)))
+    _keep_for(stream, sink if new_sink else None)
     return sink
 
 
@@ -294,19 +365,22 @@ def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=Non
     T, K = x.shape
     if K != W.k:
         raise ValueError(f"x has K={K}, weights have K={W.k}")
-    if y is None:
+    new_y = y is None
+    if new_y:
         y = torch.empty((T, W.n), dtype=torch.float32, device=x.device)
     _dev(y, torch.float32, "y")
     r = _rung(rung)
     need = lib().tern_workspace_bytes(T, W.n, W.k, W.group, r)
     if need == ctypes.c_size_t(-1).value:
         raise TernError(5, lib().tern_last_error().decode())
-    if workspace is None and need:
+    new_ws = workspace is None and need > 0
+    if new_ws:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().tern_linear(x.data_ptr(), T, W.ref(), y.data_ptr(), r, ws_ptr, ws_bytes,
                              _stream(stream)))
+    _keep_for(stream, y if new_y else None, workspace if new_ws else None)
     return y
 
 
@@ -319,11 +393,13 @@ def linear_s8_q(q, scale, W: TernaryWeights, y=None, stream=None, layout="row_ma
     T, K = q.shape
     if K != W.k:
         raise ValueError(f"q has K={K}, weights have K={W.k}")
-    if y is None:
+    new_y = y is None
+    if new_y:
         y = torch.empty((T, W.n), dtype=torch.float32, device=q.device)
     _dev(y, torch.float32, "y")
     _check(lib().tern_linear_s8_q(q.data_ptr(), scale.data_ptr(), T, W.ref(), y.data_ptr(),
                                   Q_LAYOUTS[layout], _stream(stream)))
+    _keep_for(stream, y if new_y else None)
     return y
 
 
@@ -333,9 +409,11 @@ def debug_s8_acc(q, W: TernaryWeights, acc=None, stream=None, layout="row_major"
     torch = _torch()
     _dev(q, torch.int8, "q")
     T = q.shape[0]
-    if acc is None:
+    new_acc = acc is None
+    if new_acc:
         acc = torch.empty((T, W.n, W.k // W.group), dtype=torch.int32, device=q.device)
     _dev(acc, torch.int32, "acc")
     _check(lib().tern_debug_s8_acc(q.data_ptr(), T, W.ref(), acc.data_ptr(), Q_LAYOUTS[layout],
                                    _stream(stream)))
+    _keep_for(stream, acc if new_acc else None)
     return acc

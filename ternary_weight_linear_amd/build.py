@@ -18,21 +18,30 @@ LIB = os.path.join(PKG, "libtern.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Device code: MI355X only. Packed-fp32 VALU ops are disabled; fp32 division
-# is the correctly rounded IEEE one (the s8 quantisation relies on it);
-# fp32 denormals are kept.
+# Device code: MI355X only. Packed-fp32 VALU ops are disabled (hipcc hands the
+# target feature to the host pass as well, which ignores it with a warning that
+# _run drops); fp32 division is the correctly rounded IEEE one (the s8
+# quantisation relies on it); fp32 denormals are kept.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     "-ffp-contract=off", "-Wall",
 ]
+# The host pass's note that it does not know the gfx950 feature above.
+_HOST_FEATURE_NOTE = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 
 def _run(cmd):
     print("+", " ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "".join(line for line in r.stdout.splitlines(keepends=True)
+                  if line.strip() != _HOST_FEATURE_NOTE)
+    if out:
+        print(out, end="", flush=True)
+    if r.returncode:
+        raise subprocess.CalledProcessError(r.returncode, cmd)
 
 
 # The s8 contraction reads every MFMA accumulator in its fp32 epilogue: keep

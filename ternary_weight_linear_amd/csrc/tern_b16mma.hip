@@ -203,7 +203,7 @@ hipError_t launch_b16m_t(const SmallTArgs& a, bool xcd_order, hipStream_t st) {
   const int xrows = (xcd_order && ny % 8 == 0) ? ny / 8 : 0;
   hipLaunchKernelGGL((tern_b16m_kernel<GPT, TB, S>), dim3(nx * ny), dim3(256), 0, st, a.x, a.T, a.K,
                      (const u32x4*)a.codes, a.scales, a.y, a.N, nx, ny, xrows);
-  return hipGetLastError();
+  return (hipError_t)kernel_launched((int)hipGetLastError(), TERN_KERNEL_B16_PREFILL);
 }
 
 template <int GPT>

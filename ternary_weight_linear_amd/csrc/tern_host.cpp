@@ -1,7 +1,8 @@
 // tern_host.cpp -- host side of the C ABI declared in include/tern.h:
 // argument validation, the offline weight relayout (tern_pack / tern_unpack),
-// the T-based rung dispatcher with its environment knobs and probe counters,
-// and the launches of the gfx950 kernels (tern_kernels.hip).
+// the T-based rung dispatcher with its environment knobs, the rung and kernel
+// probes, and the choice of kernel and launch plan per call (the launchers
+// live next to their kernels in tern_*.hip, behind tern_internal.h).
 //
 // Dispatcher: rung map, env-switchable thresholds, one probe per branch and
 // env read once per process follow the "NINFER ternary perf-tuning" notes,
@@ -42,6 +43,13 @@ tern_status ok() {
 
 const char* const kRungNames[TERN_RUNG_COUNT] = {"auto", "gemv", "small_t", "small_t_tiled", "s8"};
 
+const char* const kKernelNames[TERN_KERNEL_COUNT] = {
+    "quant_s8",        "quant_s8_row",      "quant_s8_rot",   "gemv_limb",        "gemv_bf16",
+    "smallt_resident", "smallt_limb_fused", "smallt_limb_prep", "smallt_limb_tile", "smallt_wave",
+    "smallt_tile",     "smallt_tile_reduce", "b16_prefill",   "s8_mma",           "s8_reduce",
+    "s8_row",          "s8_acc_export",     "stream_read"};
+static_assert(TERN_KERNEL_COUNT == 18, "one name per kernel id");
+
 // ------------------------------------------------------------ configuration
 
 struct Config {
@@ -51,6 +59,7 @@ struct Config {
   bool s8_enabled = true;             // TERN_S8
   int s8_min_t = 17;                  // TERN_S8_MIN_T
   int small_t_max = 8;                // TERN_SMALL_T_MAX
+  int small_t_tiled_max = 0;          // TERN_SMALL_T_TILED_MAX (0 = unset: s8_min_t - 1)
   bool debug = false;                 // TERN_DEBUG
   int debug_min_t = 1;                // TERN_DEBUG_MIN_T
   long debug_budget = 1000;           // TERN_DEBUG_BUDGET
@@ -114,6 +123,16 @@ Config read_config() {
       c.small_t_max = (int)v;
     else
       bad("TERN_SMALL_T_MAX", s);
+  }
+  if (const char* s = getenv("TERN_SMALL_T_TILED_MAX")) {
+    // the last T before s8: the same threshold as TERN_S8_MIN_T - 1
+    if (parse_int(s, 1, (1L << 30) - 1, &v) && v >= c.small_t_max &&
+        (!getenv("TERN_S8_MIN_T") || v + 1 == c.s8_min_t)) {
+      c.small_t_tiled_max = (int)v;
+      c.s8_min_t = (int)v + 1;
+    } else {
+      bad("TERN_SMALL_T_TILED_MAX", s);
+    }
   }
   if (const char* s = getenv("TERN_DEBUG")) {
     if (parse_int(s, 0, 1, &v))
@@ -229,8 +248,20 @@ const Config& config() {
 // ------------------------------------------------------------------- probe
 
 std::atomic<uint64_t> g_probe[TERN_RUNG_COUNT];
+std::atomic<uint64_t> g_kprobe[TERN_KERNEL_COUNT];
 std::atomic<int> g_last_rung{TERN_RUNG_AUTO};
 std::atomic<long> g_debug_lines{0};
+thread_local uint64_t t_call_kernels = 0;  // kernels launched by the call in progress
+thread_local uint64_t t_last_kernels = 0;  // ... by the last successful call on this thread
+
+// Every entry point that launches opens a call (clears the kernel set) and,
+// on success, closes it (publishes the set).
+void call_begin() { t_call_kernels = 0; }
+tern_status call_ok() {
+  t_last_kernels = t_call_kernels;
+  g_last_error.clear();
+  return TERN_OK;
+}
 
 void probe_hit(tern_rung r, int T, int n, int k, int group) {
   g_probe[r].fetch_add(1, std::memory_order_relaxed);
@@ -238,8 +269,16 @@ void probe_hit(tern_rung r, int T, int n, int k, int group) {
   const Config& c = config();
   if (c.debug && T >= c.debug_min_t) {
     long i = g_debug_lines.fetch_add(1, std::memory_order_relaxed);
-    if (i < c.debug_budget)
-      fprintf(stderr, "rung=%s T=%d N=%d K=%d G=%d\n", kRungNames[r], T, n, k, group);
+    if (i < c.debug_budget) {
+      std::string ks;
+      for (int kid = 0; kid < TERN_KERNEL_COUNT; ++kid)
+        if (t_call_kernels >> kid & 1) {
+          if (!ks.empty()) ks += ',';
+          ks += kKernelNames[kid];
+        }
+      fprintf(stderr, "rung=%s T=%d N=%d K=%d G=%d kernels=%s\n", kRungNames[r], T, n, k, group,
+              ks.c_str());
+    }
   }
 }
 
@@ -247,14 +286,20 @@ void probe_hit(tern_rung r, int T, int n, int k, int group) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int kMaxK = 1 << 20;
+constexpr int kMaxN = 1 << 24;
+
 tern_status check_shape(int n, int k, int group) {
   if (n < 16 || n % 16 != 0)
     return fail(TERN_ERR_SHAPE, "N=%d must be a positive multiple of 16", n);
   if (k < 256 || k % 256 != 0)
     return fail(TERN_ERR_SHAPE, "K=%d must be a positive multiple of 256", k);
   if (group != 64 && group != 128) return fail(TERN_ERR_SHAPE, "G=%d must be 64 or 128", group);
-  if ((uint64_t)n * (uint64_t)k > (1ull << 40))
-    return fail(TERN_ERR_SHAPE, "N*K=%llu too large", (unsigned long long)n * k);
+  // The kernels form activation offsets inside a tile of up to 128 rows and
+  // the bytes of up to 16 strips of codes in 32 bits, and s8 grids of
+  // N/256 x T/32 workgroups: K <= 2^20 and N <= 2^24 keep all of them in range.
+  if (k > kMaxK) return fail(TERN_ERR_SHAPE, "K=%d above the supported %d", k, kMaxK);
+  if (n > kMaxN) return fail(TERN_ERR_SHAPE, "N=%d above the supported %d", n, kMaxN);
   return TERN_OK;
 }
 
@@ -340,7 +385,8 @@ tern::LimbTilePlan plan_limbtile(int T, int n, int k) {
   const int NS = n / 16;
   p.strips_per_wave = c.tune_strips == 2 ? 2 : 1;
   p.waves = c.tune_waves ? std::min(c.tune_waves, 8) : 4;
-  p.depth = c.tune_depth == 4 ? 4 : 2;
+  // two strips per wave keep 2 k-tiles in flight (4 would spill registers)
+  p.depth = c.tune_depth == 4 && p.strips_per_wave == 1 ? 4 : 2;
   p.strip_blocks = (NS + p.waves * p.strips_per_wave - 1) / (p.waves * p.strips_per_wave);
   // Up to 4 tokens the loader wave makes the limbs (one launch, no workspace).
   p.fused = T <= 4 && !c.limb_unfused;
@@ -356,9 +402,10 @@ int wide_waves(int NS);
 // take at most 112 KiB of LDS: there making them up front beats both the
 // loader-wave pipeline (wide layers) and the per-wave bf16 kernel (narrow
 // ones); at T = 4, or with down's 157 KB at T = 3, the up-front work and the
-// LDS lose (A/B on the part). Needs no workspace; the LDS size does not
-// depend on the group size.
-tern::LimbPlan plan_resident(int T, int n, int k) {
+// LDS lose (A/B on the part). Needs no workspace. The LDS holds the limbs and
+// the workgroup's scales, which take twice the bytes at G = 64, so every LDS
+// check takes the call's group size.
+tern::LimbPlan plan_resident(int T, int n, int k, int G) {
   tern::LimbPlan p = plan_limb(T, n, k);
   p.resident = true;
   // Five tokens fill one 16-row operand as rows 3t + L with per-row totals
@@ -380,8 +427,8 @@ tern::LimbPlan plan_resident(int T, int n, int k) {
   if (p.wk == 1 && NS >= 1024 && !config().tune_wn) {
     p.wn = wide_waves(NS);
     const int floor_wn = (NS + 255) / 256;
-    while (p.wn > floor_wn && tern::limb_lds_bytes(T, k, 128, p) > tern::kLimbMaxLdsResident) --p.wn;
-  } else if (p.wk == 1 && tern::limb_lds_bytes(T, k, 128, p) > 80 * 1024) {
+    while (p.wn > floor_wn && tern::limb_lds_bytes(T, k, G, p) > tern::kLimbMaxLdsResident) --p.wn;
+  } else if (p.wk == 1 && tern::limb_lds_bytes(T, k, G, p) > 80 * 1024) {
     // Limbs of more than 80 KiB leave room for one workgroup per CU: make it
     // wide enough that one round of workgroups covers the strips.
     p.wn = std::min(16, std::max(p.wn, (NS + 255) / 256));
@@ -389,9 +436,9 @@ tern::LimbPlan plan_resident(int T, int n, int k) {
   return p;
 }
 
-bool small_t_resident(int T, int n, int k) {
+bool small_t_resident(int T, int n, int k, int G) {
   const Config& c = config();
-  const int lds = tern::limb_lds_bytes(T, k, 128, plan_resident(T, n, k));
+  const int lds = tern::limb_lds_bytes(T, k, G, plan_resident(T, n, k, G));
   if (c.smallt_kernel) return c.smallt_kernel == 4 && T <= 8 && lds <= tern::kLimbMaxLdsResident;
   if (T <= 3) return lds <= 112 * 1024;
   // Wide layers in one round of twelve-wave workgroups: ahead of the fused
@@ -411,19 +458,6 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split);
 // small_t_tiled above one 16-token tile runs the bf16 prefill contraction
 // (tern_b16mma.hip), which needs no workspace.
 bool b16_prefill(int T, tern_rung r) { return r == TERN_RUNG_SMALL_T_TILED && T > 16; }
-
-size_t workspace_for(int T, int n, int k, tern_rung r) {
-  if (r == TERN_RUNG_S8)
-    return align256((size_t)T * k) + align256((size_t)T * sizeof(float)) +
-           tern::s8_partial_bytes(plan_s8(T, n, k, true), T, n);
-  if (b16_prefill(T, r)) return 0;
-  if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && small_t_resident(T, n, k)) return 0;
-  if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && small_t_limb(T, n, k))
-    return plan_limbtile(T, n, k).fused ? 0 : tern::limbtile_workspace_bytes(T, k);
-  if ((r == TERN_RUNG_SMALL_T || r == TERN_RUNG_SMALL_T_TILED) && !small_t_per_wave(T, n, k))
-    return tern::tile_workspace_bytes(plan_tile(T, n, k), n);
-  return 0;
-}
 
 tern::SmallTPlan plan_small_t(int T, int n, int k, int group, tern_rung r) {
   (void)group;
@@ -472,7 +506,7 @@ tern::LimbPlan plan_limb(int T, int n, int k) {
   tern::LimbPlan p;
   const int NS = n / 16, KT = k / 256;
   const bool wide = NS >= 1024;
-  p.strips_per_wave = c.tune_strips ? c.tune_strips : 1;
+  p.strips_per_wave = 1;  // the limb kernel is built for one strip per wave only
   p.wn = c.tune_wn ? c.tune_wn : (wide ? wide_waves(NS) : 2);
   p.wk = c.tune_wk ? c.tune_wk : (wide ? 1 : (KT >= 48 ? 6 : 4));
   p.wk = std::min(p.wk, KT);
@@ -549,6 +583,85 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   return p;
 }
 
+// ------------------------------------------------------- kernel choice
+
+// What one tern_linear call runs, from its resolved rung and the layer shape:
+// the path (one kernel, or a pair with its reduction or preparation), the
+// launch plan, the workspace it needs and the ids of the kernels it launches.
+// tern_linear, tern_workspace_bytes and tern_plan_kernels all take it from
+// here, so the declared workspace and the kernel probe's expectations are the
+// launch's own.
+enum class Path { S8, GEMV_LIMB, PER_WAVE, RESIDENT, LIMBTILE, B16_PREFILL, TILE };
+
+struct Choice {
+  Path path = Path::S8;
+  tern::LimbPlan limb{};          // GEMV_LIMB, RESIDENT
+  tern::SmallTPlan wave{};        // PER_WAVE (also the gemv's bf16 kernel)
+  tern::LimbTilePlan limbtile{};  // LIMBTILE
+  tern::TilePlan tile{};          // TILE
+  tern::S8Plan s8{};              // S8, B16_PREFILL
+  size_t workspace = 0;
+  uint64_t kernels = 0;
+};
+
+constexpr uint64_t kbit(tern_kernel id) { return uint64_t{1} << id; }
+
+Choice choose(int T, int n, int k, int G, tern_rung r) {
+  Choice c;
+  if (r == TERN_RUNG_S8) {
+    c.path = Path::S8;
+    c.s8 = plan_s8(T, n, k, true);
+    c.workspace = align256((size_t)T * k) + align256((size_t)T * sizeof(float)) +
+                  tern::s8_partial_bytes(c.s8, T, n);
+    c.kernels = kbit(TERN_KERNEL_QUANT_S8) | kbit(TERN_KERNEL_S8_MMA) |
+                (c.s8.k_parts > 1 ? kbit(TERN_KERNEL_S8_REDUCE) : 0);
+    return c;
+  }
+  auto per_wave = [&] {
+    c.path = Path::PER_WAVE;
+    c.wave = plan_small_t(T, n, k, G, r);
+    c.kernels = kbit(c.wave.tokens_per_tile == 1 ? TERN_KERNEL_GEMV_BF16 : TERN_KERNEL_SMALLT_WAVE);
+  };
+  if (r == TERN_RUNG_GEMV) {
+    c.limb = plan_limb(T, n, k);
+    if (!config().gemv_bf16 && limb_fits(T, k, G, c.limb)) {
+      c.path = Path::GEMV_LIMB;
+      c.kernels = kbit(TERN_KERNEL_GEMV_LIMB);
+    } else {
+      per_wave();  // limbs and scales beyond the kernel's LDS (or TERN_TUNE_GEMV=bf16)
+    }
+    return c;
+  }
+  // small_t and small_t_tiled
+  if (small_t_resident(T, n, k, G)) {
+    c.path = Path::RESIDENT;
+    c.limb = plan_resident(T, n, k, G);
+    c.kernels = kbit(TERN_KERNEL_SMALLT_RESIDENT);
+  } else if (small_t_limb(T, n, k)) {
+    c.path = Path::LIMBTILE;
+    c.limbtile = plan_limbtile(T, n, k);
+    if (c.limbtile.fused) {
+      c.kernels = kbit(TERN_KERNEL_SMALLT_LIMB_FUSED);
+    } else {
+      c.workspace = tern::limbtile_workspace_bytes(T, k);
+      c.kernels = kbit(TERN_KERNEL_SMALLT_LIMB_PREP) | kbit(TERN_KERNEL_SMALLT_LIMB_TILE);
+    }
+  } else if (b16_prefill(T, r)) {
+    c.path = Path::B16_PREFILL;
+    c.s8 = plan_s8(T, n, k, false);
+    c.kernels = kbit(TERN_KERNEL_B16_PREFILL);
+  } else if (small_t_per_wave(T, n, k)) {
+    per_wave();
+  } else {
+    c.path = Path::TILE;
+    c.tile = plan_tile(T, n, k);
+    c.workspace = tern::tile_workspace_bytes(c.tile, n);
+    c.kernels = kbit(TERN_KERNEL_SMALLT_TILE) |
+                (c.tile.k_parts > 1 ? kbit(TERN_KERNEL_SMALLT_TILE_REDUCE) : 0);
+  }
+  return c;
+}
+
 tern_status hip_fail(int err, const char* what) {
   return fail(TERN_ERR_HIP, "%s: %s", what, tern::hip_error_string(err));
 }
@@ -568,6 +681,14 @@ tern_status check_weights(const tern_weights* W) {
 inline uint32_t encode(int8_t v) { return v == 0 ? 0u : (v == 1 ? 1u : 3u); }
 
 }  // namespace
+
+int tern::kernel_launched(int err, tern_kernel k) {
+  if (err == 0 && (int)k >= 0 && (int)k < TERN_KERNEL_COUNT) {
+    g_kprobe[k].fetch_add(1, std::memory_order_relaxed);
+    t_call_kernels |= uint64_t{1} << k;
+  }
+  return err;
+}
 
 extern "C" {
 
@@ -678,7 +799,14 @@ size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung) {
   if (check_shape(n, k, group) != TERN_OK) return (size_t)-1;
   tern_rung r;
   if (resolve(T, rung, &r) != TERN_OK) return (size_t)-1;
-  return workspace_for(T, n, k, r);
+  return choose(T, n, k, group, r).workspace;
+}
+
+uint64_t tern_plan_kernels(int T, int n, int k, int group, tern_rung rung) {
+  if (check_shape(n, k, group) != TERN_OK) return 0;
+  tern_rung r;
+  if (resolve(T, rung, &r) != TERN_OK) return 0;
+  return choose(T, n, k, group, r).kernels;
 }
 
 int tern_resolve_rung(int T, tern_rung rung) {
@@ -690,23 +818,25 @@ int tern_resolve_rung(int T, tern_rung rung) {
 
 tern_status tern_quant_act_s8(const void* x_bf16, int T, int k, int8_t* q, float* act_scale,
                               tern_q_layout layout, void* stream) {
+  call_begin();
   if (!x_bf16 || !q || !act_scale) return fail(TERN_ERR_NULL, "tern_quant_act_s8: NULL pointer");
   if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
   if (layout != TERN_Q_ROW_MAJOR && layout != TERN_Q_OPERAND_ORDER)
     return fail(TERN_ERR_VALUE, "unknown q layout %d", (int)layout);
   const int mult = layout == TERN_Q_OPERAND_ORDER ? 64 : 8;
-  if (k < mult || k % mult != 0)
-    return fail(TERN_ERR_SHAPE, "K=%d must be a positive multiple of %d", k, mult);
+  if (k < mult || k % mult != 0 || k > kMaxK)
+    return fail(TERN_ERR_SHAPE, "K=%d must be a positive multiple of %d, at most %d", k, mult, kMaxK);
   if (!aligned16(x_bf16) || !aligned16(q))
     return fail(TERN_ERR_ALIGN, "x and q must be 16-byte aligned");
   int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, act_scale,
                                   layout == TERN_Q_OPERAND_ORDER, stream);
   if (err) return hip_fail(err, "quant_s8 launch");
-  return ok();
+  return call_ok();
 }
 
 tern_status tern_quant_act_s8_rot(const void* x_bf16, int T, int k, int8_t* q, float* act_scale,
                                   tern_q_layout layout, void* stream) {
+  call_begin();
   if (!x_bf16 || !q || !act_scale) return fail(TERN_ERR_NULL, "tern_quant_act_s8_rot: NULL pointer");
   if (T < 1 || T > kMaxTokens) return fail(TERN_ERR_SHAPE, "T=%d out of range", T);
   if (layout != TERN_Q_ROW_MAJOR && layout != TERN_Q_OPERAND_ORDER)
@@ -718,11 +848,12 @@ tern_status tern_quant_act_s8_rot(const void* x_bf16, int T, int k, int8_t* q, f
   int err = tern::launch_quant_s8_rot((const uint16_t*)x_bf16, T, k, q, act_scale,
                                       layout == TERN_Q_OPERAND_ORDER, stream);
   if (err) return hip_fail(err, "quant_s8_rot launch");
-  return ok();
+  return call_ok();
 }
 
 tern_status tern_stream_read(const void* buf, size_t bytes, int depth, int waves_per_cu,
                              uint32_t* sink, void* stream) {
+  call_begin();
   if (!buf || !sink) return fail(TERN_ERR_NULL, "tern_stream_read: NULL pointer");
   if (bytes < 1024 || bytes % 1024 != 0 || bytes / 1024 > 0x7fffffffu)
     return fail(TERN_ERR_SHAPE, "bytes=%zu must be a positive multiple of 1024 below 2 TiB", bytes);
@@ -734,11 +865,12 @@ tern_status tern_stream_read(const void* buf, size_t bytes, int depth, int waves
     return fail(TERN_ERR_ALIGN, "buf must be 16-byte and sink 4-byte aligned");
   const int err = tern::launch_stream_read(buf, bytes, depth, waves_per_cu, sink, stream);
   if (err) return hip_fail(err, "stream_read launch");
-  return ok();
+  return call_ok();
 }
 
 tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float* y,
                         tern_rung rung, void* ws, size_t ws_bytes, void* stream) {
+  call_begin();
   if (!x_bf16 || !y) return fail(TERN_ERR_NULL, "tern_linear: x or y is NULL");
   tern_status st = check_weights(W);
   if (st != TERN_OK) return st;
@@ -747,56 +879,57 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
   tern_rung r;
   st = resolve(T, rung, &r);
   if (st != TERN_OK) return st;
-  const size_t need = workspace_for(T, W->n, W->k, r);
-  if (need) {
-    if (!ws || ws_bytes < need)
+  const int n = W->n, k = W->k, G = W->group;
+  const Choice c = choose(T, n, k, G, r);
+  if (c.workspace) {
+    if (!ws || ws_bytes < c.workspace)
       return fail(TERN_ERR_WORKSPACE, "rung %s needs %zu bytes of workspace, got %zu%s",
-                  kRungNames[r], need, ws ? ws_bytes : (size_t)0, ws ? "" : " (NULL)");
+                  kRungNames[r], c.workspace, ws ? ws_bytes : (size_t)0, ws ? "" : " (NULL)");
     if (!aligned16(ws)) return fail(TERN_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
-  const int n = W->n, k = W->k, G = W->group;
-  if (r == TERN_RUNG_S8) {
-    int8_t* q = (int8_t*)ws;
-    float* sc = (float*)((char*)ws + align256((size_t)T * k));
-    int err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, true, stream);
-    if (err) return hip_fail(err, "quant_s8 launch");
-    float* part = (float*)((char*)ws + align256((size_t)T * k) + align256((size_t)T * sizeof(float)));
-    tern::S8Args a{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr, true};
-    err = tern::launch_s8(a, plan_s8(T, n, k, true), part, stream);
-    if (err) return hip_fail(err, "s8 launch");
-  } else {
-    tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
-    if (r == TERN_RUNG_GEMV) {
-      const tern::LimbPlan fp = plan_limb(T, n, k);
-      int err;
-      if (!config().gemv_bf16 && limb_fits(T, k, G, fp))
-        err = tern::launch_limb(a, fp, stream);
-      else
-        err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
-      if (err) return hip_fail(err, "gemv launch");
-    } else if (small_t_resident(T, n, k)) {
-      int err = tern::launch_limb(a, plan_resident(T, n, k), stream);
-      if (err) return hip_fail(err, "small_t resident launch");
-    } else if (small_t_limb(T, n, k)) {
-      int err = tern::launch_limbtile(a, plan_limbtile(T, n, k), ws, stream);
-      if (err) return hip_fail(err, "small_t limb launch");
-    } else if (b16_prefill(T, r)) {
-      int err = tern::launch_b16_prefill(a, plan_s8(T, n, k, false), stream);
-      if (err) return hip_fail(err, "bf16 prefill launch");
-    } else if (small_t_per_wave(T, n, k)) {
-      int err = tern::launch_small_t(a, plan_small_t(T, n, k, G, r), stream);
-      if (err) return hip_fail(err, "small_t launch");
-    } else {
-      int err = tern::launch_tile(a, plan_tile(T, n, k), ws, stream);
-      if (err) return hip_fail(err, "small_t launch");
+  const tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
+  int err = 0;
+  switch (c.path) {
+    case Path::S8: {
+      int8_t* q = (int8_t*)ws;
+      float* sc = (float*)((char*)ws + align256((size_t)T * k));
+      err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, true, stream);
+      if (err) return hip_fail(err, "quant_s8 launch");
+      float* part = (float*)((char*)ws + align256((size_t)T * k) + align256((size_t)T * sizeof(float)));
+      const tern::S8Args sa{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr, true};
+      err = tern::launch_s8(sa, c.s8, part, stream);
+      if (err) return hip_fail(err, "s8 launch");
+      break;
     }
+    case Path::GEMV_LIMB:
+    case Path::RESIDENT:
+      err = tern::launch_limb(a, c.limb, stream);
+      if (err) return hip_fail(err, c.path == Path::RESIDENT ? "small_t resident launch" : "gemv launch");
+      break;
+    case Path::PER_WAVE:
+      err = tern::launch_small_t(a, c.wave, stream);
+      if (err) return hip_fail(err, r == TERN_RUNG_GEMV ? "gemv launch" : "small_t launch");
+      break;
+    case Path::LIMBTILE:
+      err = tern::launch_limbtile(a, c.limbtile, ws, stream);
+      if (err) return hip_fail(err, "small_t limb launch");
+      break;
+    case Path::B16_PREFILL:
+      err = tern::launch_b16_prefill(a, c.s8, stream);
+      if (err) return hip_fail(err, "bf16 prefill launch");
+      break;
+    case Path::TILE:
+      err = tern::launch_tile(a, c.tile, ws, stream);
+      if (err) return hip_fail(err, "small_t launch");
+      break;
   }
   probe_hit(r, T, n, k, G);
-  return ok();
+  return call_ok();
 }
 
 tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
                              const tern_weights* W, float* y, tern_q_layout layout, void* stream) {
+  call_begin();
   if (!q || !act_scale || !y) return fail(TERN_ERR_NULL, "tern_linear_s8_q: NULL pointer");
   tern_status st = check_weights(W);
   if (st != TERN_OK) return st;
@@ -811,11 +944,12 @@ tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,
   int err = tern::launch_s8(a, plan_s8(T, W->n, W->k, false), nullptr, stream);
   if (err) return hip_fail(err, "s8 launch");
   probe_hit(TERN_RUNG_S8, T, W->n, W->k, W->group);
-  return ok();
+  return call_ok();
 }
 
 tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int32_t* acc_out,
                               tern_q_layout layout, void* stream) {
+  call_begin();
   if (!q || !acc_out) return fail(TERN_ERR_NULL, "tern_debug_s8_acc: NULL pointer");
   tern_status st = check_weights(W);
   if (st != TERN_OK) return st;
@@ -831,7 +965,7 @@ tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int
   p.depth = 2;  // the export runs the double-buffered pipeline
   int err = tern::launch_s8(a, p, nullptr, stream);
   if (err) return hip_fail(err, "s8 debug launch");
-  return ok();
+  return call_ok();
 }
 
 void tern_probe_snapshot(uint64_t out[TERN_RUNG_COUNT]) {
@@ -840,7 +974,19 @@ void tern_probe_snapshot(uint64_t out[TERN_RUNG_COUNT]) {
 
 void tern_probe_reset(void) {
   for (int i = 0; i < TERN_RUNG_COUNT; ++i) g_probe[i].store(0, std::memory_order_relaxed);
+  for (int i = 0; i < TERN_KERNEL_COUNT; ++i) g_kprobe[i].store(0, std::memory_order_relaxed);
   g_last_rung.store(TERN_RUNG_AUTO, std::memory_order_relaxed);
+}
+
+void tern_kernel_probe_snapshot(uint64_t out[TERN_KERNEL_COUNT]) {
+  for (int i = 0; i < TERN_KERNEL_COUNT; ++i) out[i] = g_kprobe[i].load(std::memory_order_relaxed);
+}
+
+uint64_t tern_last_kernels(void) { return t_last_kernels; }
+
+const char* tern_kernel_name(tern_kernel kernel) {
+  if ((int)kernel < 0 || (int)kernel >= TERN_KERNEL_COUNT) return "invalid";
+  return kKernelNames[kernel];
 }
 
 tern_rung tern_last_rung(void) { return (tern_rung)g_last_rung.load(std::memory_order_relaxed); }

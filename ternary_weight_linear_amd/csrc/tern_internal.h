@@ -1,11 +1,19 @@
 // tern_internal.h -- interface between the host ABI layer (tern_host.cpp) and
-// the gfx950 kernels (tern_kernels.hip). Not installed, not part of the ABI.
+// the launchers of the gfx950 kernels (tern_*.hip). Not installed, not part
+// of the ABI.
 #pragma once
 
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/tern.h"
+
 namespace tern {
+
+// Kernel probe (tern_host.cpp): counts one launch of kernel `k` when `err`
+// (a hipError_t value) is 0, i.e. the launch succeeded; returns `err`. Every
+// launcher passes its hipGetLastError() through this at the launch site.
+int kernel_launched(int err, tern_kernel k);
 
 // Launch shape of the bf16-activation MFMA kernel (gemv / small_t / small_t_tiled).
 struct SmallTPlan {

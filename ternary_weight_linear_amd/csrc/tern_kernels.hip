@@ -1,11 +1,13 @@
-// tern_kernels.hip -- gfx950 (MI355X, CDNA4) kernels of the ternary-weight
-// linear layer.
+// tern_kernels.hip -- the per-wave bf16-activation kernel of the
+// ternary-weight linear layer on gfx950 (MI355X, CDNA4).
 //
 // y[t][n] = sum_g s[n][g] * sum_{k in g} w[n][k] * x[t][k], w in {-1,0,+1},
 // one fp16 scale per G weights along K ("NInfer sm_89 fork" article, section
-// 9 item 2). Three kernels:
+// 9 item 2).
 //
-//  * tern_small_t_kernel  -- bf16 activations, T <= 16 per token tile. Streams
+//  * tern_small_t_kernel -- bf16 activations, one token (TT = 1: the gemv's
+//    kernel where its int8 limbs do not fit LDS, or with TERN_TUNE_GEMV=bf16)
+//    or a 16-token tile (small_t / small_t_tiled on narrow layers). Streams
 //    the 2-bit packed weights with 16-byte loads, turns each code pair into a
 //    bf16 pair {0, +-2.0} with one shift and one mask, and lets the
 //    v_mfma_f32_16x16x32_bf16 matrix core multiply them with the activation
@@ -14,12 +16,12 @@
 //    accumulators share one output row and one scale per group. Each wave
 //    owns S 16-row strips over a contiguous K range; the waves of a workgroup
 //    split K and are summed in a fixed order through LDS (deterministic).
-//  * tern_quant_s8_kernel -- per-token absmax (wavefront DPP reduction), then
-//    q = clamp(rne(x / (absmax/127)), +-127) with IEEE division.
-//  * tern_s8_kernel       -- int8 activations x ternary weights on
-//    v_mfma_i32_16x16x64_i8 into int32 group accumulators, then the fp32
-//    scale epilogue total = fma(float(acc), s[n][g], total) per group in
-//    ascending order and y = total * scale_t.
+//
+// The other kernels live next to their launchers: the integer-limb gemv and
+// resident small-T kernel in tern_limb.hip, the activation-tiled small-T
+// kernel in tern_tile.hip, the small-T limb path in tern_limbtile.hip, the
+// quantisation and row-major s8 kernels in tern_s8.hip, the operand-order s8
+// contraction in tern_s8mma.hip and the bf16 prefill in tern_b16mma.hip.
 //
 // Packed layout v1 is specified in include/tern.h.
 #include <hip/hip_runtime.h>
@@ -282,7 +284,8 @@ hipError_t launch_small_t_s(const SmallTArgs& a, const SmallTPlan& p, hipStream_
   else
     hipLaunchKernelGGL((tern_small_t_kernel<TT, S, 4>), grid, block, lds, st, a.x, a.T, a.K,
                        (const u32x4*)a.codes, a.scales, a.y, a.N);
-  return hipGetLastError();
+  return (hipError_t)kernel_launched((int)hipGetLastError(),
+                                     TT == 1 ? TERN_KERNEL_GEMV_BF16 : TERN_KERNEL_SMALLT_WAVE);
 }
 
 template <int TT>

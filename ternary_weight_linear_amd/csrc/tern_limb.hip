@@ -381,7 +381,9 @@ hipError_t launch_limb_g(const SmallTArgs& a, const LimbPlan& p, hipStream_t st)
 #undef TERN_LIMB_LAUNCH
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  // the gemv rung (any T <= 5, limbs made per k-tile) or the resident small-T plan
+  return (hipError_t)kernel_launched((int)hipGetLastError(),
+                                     p.resident ? TERN_KERNEL_SMALLT_RESIDENT : TERN_KERNEL_GEMV_LIMB);
 }
 
 template <int TT, int S>
@@ -389,14 +391,13 @@ hipError_t launch_limb_s(const SmallTArgs& a, const LimbPlan& p, hipStream_t st)
   return a.G == 128 ? launch_limb_g<TT, S, 2>(a, p, st) : launch_limb_g<TT, S, 4>(a, p, st);
 }
 
+// One strip per wave only: with two or four strips the k-tiles of codes in
+// flight no longer fit the registers at 1024 threads per workgroup and the
+// kernel spills (measured no faster before the spills either).
 template <int TT>
 hipError_t launch_limb_t(const SmallTArgs& a, const LimbPlan& p, hipStream_t st) {
-  switch (p.strips_per_wave) {
-    case 1: return launch_limb_s<TT, 1>(a, p, st);
-    case 2: return launch_limb_s<TT, 2>(a, p, st);
-    case 4: return launch_limb_s<TT, 4>(a, p, st);
-    default: return hipErrorInvalidValue;
-  }
+  if (p.strips_per_wave != 1) return hipErrorInvalidValue;
+  return launch_limb_s<TT, 1>(a, p, st);
 }
 
 }  // namespace

@@ -430,7 +430,7 @@ hipError_t launch_limbfuse_g(const SmallTArgs& a, const LimbTilePlan& p, hipStre
       break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return (hipError_t)kernel_launched((int)hipGetLastError(), TERN_KERNEL_SMALLT_LIMB_FUSED);
 }
 
 template <int RB, int S, int GPT>
@@ -449,7 +449,7 @@ hipError_t launch_limbtile_g(const SmallTArgs& a, const LimbTilePlan& p, int8_t*
 #undef TERN_LIMBTILE_LAUNCH
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return (hipError_t)kernel_launched((int)hipGetLastError(), TERN_KERNEL_SMALLT_LIMB_TILE);
 }
 
 template <int RB>
@@ -490,8 +490,8 @@ int launch_limbtile(const SmallTArgs& a, const LimbTilePlan& p, void* ws, void* 
   const long threads = (long)slots * (a.K / 16);
   hipLaunchKernelGGL(tern_limb_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
                      a.x, a.T, a.K, slots, limbs, dsh);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
+  const int e = kernel_launched((int)hipGetLastError(), TERN_KERNEL_SMALLT_LIMB_PREP);
+  if (e != 0) return e;
   return (int)(RB == 1 ? launch_limbtile_r<1>(a, p, limbs, dsh, st) : launch_limbtile_r<2>(a, p, limbs, dsh, st));
 }
 

@@ -74,7 +74,7 @@ int launch_stream_read(const void* buf, size_t bytes, int depth, int waves_per_c
     case 16: launch_d<16>(buf, kib, per_wave, waves, sink, st); break;
     default: return (int)hipErrorInvalidValue;
   }
-  return (int)hipGetLastError();
+  return kernel_launched((int)hipGetLastError(), TERN_KERNEL_STREAM_READ);
 }
 
 }  // namespace tern

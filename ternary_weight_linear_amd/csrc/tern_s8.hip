@@ -588,7 +588,8 @@ hipError_t launch_s8_v(const S8Args& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((tern_s8_kernel<4, DEBUG_ACC, QPERM>), grid, dim3(256), 0, st, a.q,
                        a.act_scale, a.T, a.K, (const u32x4*)a.codes, a.scales, a.y, a.acc_out, a.N);
-  return hipGetLastError();
+  return (hipError_t)kernel_launched((int)hipGetLastError(),
+                                     DEBUG_ACC ? TERN_KERNEL_S8_ACC_EXPORT : TERN_KERNEL_S8_ROW);
 }
 
 }  // namespace
@@ -621,7 +622,7 @@ int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bo
 #undef TERN_QP_LAUNCH
       default: return (int)hipErrorInvalidValue;
     }
-    return (int)hipGetLastError();
+    return kernel_launched((int)hipGetLastError(), TERN_KERNEL_QUANT_S8);
   }
   if (operand_order)
     hipLaunchKernelGGL(tern_quant_s8_kernel<true>, dim3(T), dim3(256), 0, (hipStream_t)stream, x, K,
@@ -629,7 +630,8 @@ int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bo
   else
     hipLaunchKernelGGL(tern_quant_s8_kernel<false>, dim3(T), dim3(256), 0, (hipStream_t)stream, x,
                        K, q, scale);
-  return (int)hipGetLastError();
+  return kernel_launched((int)hipGetLastError(),
+                         operand_order ? TERN_KERNEL_QUANT_S8 : TERN_KERNEL_QUANT_S8_ROW);
 }
 
 int launch_quant_s8_rot(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
@@ -657,7 +659,7 @@ int launch_quant_s8_rot(const uint16_t* x, int T, int K, int8_t* q, float* scale
 #undef TERN_ROT_LAUNCH
     default: return (int)hipErrorInvalidValue;
   }
-  return (int)hipGetLastError();
+  return kernel_launched((int)hipGetLastError(), TERN_KERNEL_QUANT_S8_ROT);
 }
 
 int launch_s8(const S8Args& a, const S8Plan& p, void* ws, void* stream) {

@@ -324,7 +324,8 @@ hipError_t launch_s8m_t(const S8Args& a, const S8Plan& p, float* part, hipStream
   hipLaunchKernelGGL((tern_s8m_kernel<GPT, TB, S, D, DEBUG_ACC>), dim3(nx * ny, p.k_parts), dim3(256), 0,
                      st, a.q, a.act_scale, a.T, a.K, (const u32x4*)a.codes, a.scales, a.y, a.acc_out,
                      a.N, nx, ny, xrows, part);
-  return hipGetLastError();
+  return (hipError_t)kernel_launched((int)hipGetLastError(),
+                                     DEBUG_ACC ? TERN_KERNEL_S8_ACC_EXPORT : TERN_KERNEL_S8_MMA);
 }
 
 template <int GPT, int TB, int S, bool DEBUG_ACC>
@@ -370,7 +371,7 @@ int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* ws, void* st
   const long n = (long)a.T * (a.N / 4);
   hipLaunchKernelGGL(tern_s8m_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                      (const float*)part, a.act_scale, a.y, a.T, a.N, p.k_parts);
-  return (int)hipGetLastError();
+  return kernel_launched((int)hipGetLastError(), TERN_KERNEL_S8_REDUCE);
 }
 
 size_t s8_partial_bytes(const S8Plan& p, int T, int N) {

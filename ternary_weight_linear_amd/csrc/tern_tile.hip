@@ -273,7 +273,7 @@ hipError_t launch_tile_g(const SmallTArgs& a, const TilePlan& p, float* part, hi
 #undef TERN_TILE_LAUNCH
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return (hipError_t)kernel_launched((int)hipGetLastError(), TERN_KERNEL_SMALLT_TILE);
 }
 
 template <int ROWS, int S>
@@ -311,7 +311,7 @@ int launch_tile(const SmallTArgs& a, const TilePlan& p, void* ws, void* stream) 
   const long n = (long)a.T * (a.N / 4);
   hipLaunchKernelGGL(tern_tile_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                      (const float*)part, a.y, a.T, a.N, p.k_parts);
-  return (int)hipGetLastError();
+  return kernel_launched((int)hipGetLastError(), TERN_KERNEL_SMALLT_TILE_REDUCE);
 }
 
 }  // namespace tern

@@ -51,6 +51,16 @@ def rung_ok(rung, T):
     return not (rung == "small_t" and T > 16)
 
 
+def check_kernels(tl, T, W, rung):
+    """The kernels the last call launched are the ones the dispatcher's dry
+    run names for it, each launched once (kernel probe and per-call set)."""
+    plan = tl.plan_kernels(T, W.n, W.k, W.group, rung)
+    assert tl.last_kernels() == plan, (T, W.n, W.k, rung, tl.last_kernels(), plan)
+    snap = tl.kernel_probe_snapshot()
+    assert {k: v for k, v in snap.items() if v} == {k: 1 for k in plan}, snap
+    return plan
+
+
 def run(tl, torch, x_dev, W, rung):
     tl.probe_reset()
     y = tl.linear(x_dev, W, rung=rung)
@@ -59,6 +69,7 @@ def run(tl, torch, x_dev, W, rung):
     expect = rung if rung != "auto" else tl.resolve_rung(x_dev.shape[0])
     assert snap[expect] == 1 and sum(snap.values()) == 1, snap
     assert tl.last_rung() == expect
+    check_kernels(tl, x_dev.shape[0], W, rung)
     return y.cpu().numpy()
 
 
@@ -429,6 +440,7 @@ shape = ts.Shape("tune_4096x96", 4096, 96, int(sys.argv[2]), 0.4, True, 401)
 wts = ts.weights(shape)
 W = tl.TernaryWeights.from_host(wts.w, wts.s)
 worst = 0.0
+seen = set()
 for T in (1, 5, 16, 23):
     xb = ts.activations(wts, T)
     x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
@@ -437,8 +449,12 @@ for T in (1, 5, 16, 23):
         if rung == "small_t" and T > 16:
             continue
         y = tl.linear(x, W, rung=rung).cpu().numpy().astype(np.float64)
+        ks = tl.last_kernels()
+        assert ks == tl.plan_kernels(T, W.n, W.k, W.group, rung), (T, rung, ks)
+        seen.update(ks)
         err = np.linalg.norm(y - ref) / np.linalg.norm(ref)
         worst = max(worst, err)
+print("KERNELS", ",".join(sorted(seen)))
 print("WORST", worst)
 """
 
@@ -447,18 +463,25 @@ print("WORST", worst)
                                             (1, 16, 128), (2, 8, 128)])
 def test_launch_shapes_keep_parity(strips, waves, G):
     """Every (strips per wave, waves per block) launch shape the tuning knobs
-    can select, including multi-chunk k-ranges (16 k-tiles on one wave) and
-    partial strip blocks (6 strips with 4 per block), stays within the gate."""
+    can select for the per-wave bf16 kernel (one-token rows at T = 1 with
+    TERN_TUNE_GEMV=bf16, 16-token tiles above), including multi-chunk
+    k-ranges (16 k-tiles on one wave) and partial strip blocks (6 strips with
+    4 per block), stays within the gate."""
     import os
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    env = dict(os.environ, TERN_TUNE_STRIPS=str(strips), TERN_TUNE_WAVES=str(waves))
+    env = dict(os.environ, TERN_TUNE_STRIPS=str(strips), TERN_TUNE_WAVES=str(waves),
+               TERN_TUNE_GEMV="bf16")
     r = subprocess.run([sys.executable, "-c", _TUNE_CHILD, root, str(G)], env=env,
                        capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stderr[-2000:]
     worst = float(r.stdout.split("WORST")[1])
     assert worst <= 1e-6, worst
+    # the per-wave kernel ran under the forced shape: one-token rows (the
+    # gemv's bf16 kernel) and 16-token tiles
+    seen = set(r.stdout.split("KERNELS")[1].split()[0].split(","))
+    assert {"gemv_bf16", "smallt_wave"} <= seen, seen
 
 
 @pytest.mark.parametrize("strips,waves,depth,kparts", [(1, 4, 2, 1), (1, 4, 8, 1), (2, 3, 4, 2),
@@ -479,6 +502,8 @@ def test_tile_kernel_shapes_keep_parity(strips, waves, depth, kparts):
     assert r.returncode == 0, r.stderr[-2000:]
     worst = float(r.stdout.split("WORST")[1])
     assert worst <= 1e-6, worst
+    seen = set(r.stdout.split("KERNELS")[1].split()[0].split(","))
+    assert "smallt_tile" in seen and ("smallt_tile_reduce" in seen) == (kparts > 1), seen
 
 
 _S8_SPLIT_CHILD = r"""
@@ -497,6 +522,8 @@ for T in (17, 40, 100):
     q, sc = oracle.quant_s8(xb)
     ref = oracle.linear_s8(q, sc, w, s)
     y = tl.linear(x, W, rung="s8").cpu().numpy()
+    ks = tl.last_kernels()
+    assert ks == tl.plan_kernels(T, n, k, G, "s8") == ["quant_s8", "s8_mma", "s8_reduce"], ks
     if not np.array_equal(y.view(np.uint32), ref.view(np.uint32)):
         bad.append(T)
 print("BAD", bad)
@@ -531,6 +558,7 @@ w = ts.draw_weights(rng, n, k, 0.4)
 s = ts.pow2_scales(n, k, G, seed=13)
 W = tl.TernaryWeights.from_host(w, s)
 bad = []
+seen = set()
 for T in (2, 3, 4, 5, 7, 8):
     xb = ts.integer_activations(k, T, seed=T + 30)
     x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
@@ -538,8 +566,12 @@ for T in (2, 3, 4, 5, 7, 8):
     for rung in ("small_t", "small_t_tiled"):
         tl.probe_reset()
         y = tl.linear(x, W, rung=rung).cpu().numpy().astype(np.float64)
+        ks = tl.last_kernels()
+        assert ks == tl.plan_kernels(T, n, k, G, rung), (T, rung, ks)
+        seen.update((T, kn) for kn in ks)
         if not np.array_equal(y, ref):
             bad.append((T, rung))
+print("KERNELS", sorted(seen))
 print("BAD", bad)
 """
 
@@ -566,6 +598,13 @@ def test_small_t_limb_path_exact(kernel, strips, waves, depth, G):
                        capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.split("BAD")[1].strip() == "[]", r.stdout
+    import ast
+    seen = ast.literal_eval(r.stdout.split("KERNELS")[1].split("BAD")[0].strip())
+    want = {"limb": lambda T: "smallt_limb_fused" if T <= 4 else "smallt_limb_tile",
+            "limb2": lambda T: "smallt_limb_tile",
+            "resident": lambda T: "smallt_resident"}[kernel]
+    for T in (2, 3, 4, 5, 7, 8):
+        assert (T, want(T)) in seen, (T, seen)
 
 
 # ------------------------------------- activation dynamic range (bf16 rungs)
@@ -629,6 +668,7 @@ import oracle, tern_synth as ts, ternary_weight_linear_amd as tl
 from tests.test_gpu_parity import _range_case
 n, k, G = 96, 2048, 128
 worst = 0.0
+seen = set()
 for ci, case in enumerate(["outliers", "subnormal", "wide", "huge"]):
     rng = np.random.default_rng(ci + 177)
     w = ts.draw_weights(rng, n, k, 0.4)
@@ -644,8 +684,10 @@ for ci, case in enumerate(["outliers", "subnormal", "wide", "huge"]):
         bound = 2.0 ** -16 * (np.abs(xf) @ sw.T) + 2.0 ** -22 * (tmax @ swt.T)
         x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
         y = tl.linear(x, W, rung="small_t").cpu().numpy().astype(np.float64)
+        seen.update((T, kn) for kn in tl.last_kernels())
         assert np.all(np.isfinite(y)) and np.all(y[0] == 0), (case, T)
         worst = max(worst, float((np.abs(y - ref) / np.maximum(bound, 1e-300)).max()))
+print("KERNELS", sorted(seen))
 print("WORST", worst)
 """
 
@@ -665,6 +707,13 @@ def test_limb_path_activation_range(kernel):
                        text=True, timeout=240, cwd=root)
     assert r.returncode == 0, r.stderr[-2000:]
     assert float(r.stdout.split("WORST")[1]) <= 1.0, r.stdout
+    import ast
+    seen = ast.literal_eval(r.stdout.split("KERNELS")[1].split("WORST")[0].strip())
+    want = {"limb": {3: "smallt_limb_fused", 4: "smallt_limb_fused", 6: "smallt_limb_tile"},
+            "limb2": {3: "smallt_limb_tile", 4: "smallt_limb_tile", 6: "smallt_limb_tile"},
+            "resident": {3: "smallt_resident", 4: "smallt_resident", 6: "smallt_resident"}}[kernel]
+    for T, kn in want.items():
+        assert (T, kn) in seen, (T, seen)
 
 
 # ------------------------------------- rotated quantisation (1024-wide blocks)
@@ -736,3 +785,125 @@ def test_quant_rot_rejects_bad_shapes(tl, torch):
     x = torch.zeros((2, 65536), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(tl.TernError):
         tl.quant_act_s8_rot(x)
+
+
+# ------------------------------------------- environment arms on the GPU
+
+_ARM_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import oracle, tern_synth as ts, ternary_weight_linear_amd as tl
+shape = ts.Shape("arm_768x2048", 768, 2048, 128, 0.4, True, 611)
+wts = ts.weights(shape)
+W = tl.TernaryWeights.from_host(wts.w, wts.s)
+out = []
+for T in (1, 5, 12, 20):
+    xb = ts.activations(wts, T)
+    x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    rung = tl.resolve_rung(T)
+    tl.probe_reset()
+    y = tl.linear(x, W).cpu().numpy()
+    snap = tl.probe_snapshot()
+    assert snap[rung] == 1 and sum(snap.values()) == 1, (T, snap)
+    ks = tl.last_kernels()
+    assert ks == tl.plan_kernels(T, W.n, W.k, W.group), (T, ks)
+    kp = {k: v for k, v in tl.kernel_probe_snapshot().items() if v}
+    assert kp == {k: 1 for k in ks}, (T, kp)
+    if rung == "s8":
+        q, sc = oracle.quant_s8(xb)
+        err = np.linalg.norm(y - oracle.linear_s8(q, sc, wts.w, wts.s)) / np.linalg.norm(
+            oracle.linear_s8(q, sc, wts.w, wts.s).astype(np.float64))
+        ok = err <= 1e-6
+    else:
+        ref = oracle.linear_bf16(xb, wts.w, wts.s)
+        ok = np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 2e-3
+    out.append(f"{T}:{rung}:{'+'.join(ks)}:{'ok' if ok else 'BAD'}")
+print("ARMS", " ".join(out))
+"""
+
+
+@pytest.mark.parametrize("env,expect", [
+    ({}, "gemv small_t small_t_tiled s8"),
+    ({"TERN_RUNG": "gemv"}, "gemv gemv gemv gemv"),
+    ({"TERN_RUNG": "small_t"}, None),  # T = 20 is beyond one 16-token tile: an error, tested below
+    ({"TERN_RUNG": "small_t_tiled"}, "small_t_tiled small_t_tiled small_t_tiled small_t_tiled"),
+    ({"TERN_RUNG": "s8"}, "s8 s8 s8 s8"),
+    ({"TERN_S8": "0"}, "gemv small_t small_t_tiled small_t_tiled"),
+    ({"TERN_SMALL_T_TILED_MAX": "10"}, "gemv small_t s8 s8"),
+    ({"TERN_SMALL_T_MAX": "16"}, "gemv small_t small_t s8")])
+def test_env_arms_run_on_the_gpu(env, expect):
+    """One binary, every rung forced by the environment in a process of its
+    own: the auto-dispatched calls run the forced rung (rung probe), the
+    kernels the dry run names (kernel probe), and stay within their gates
+    ("NINFER ternary perf-tuning" notes, section 3: arms toggled by env)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _ARM_CHILD, root], env=dict(os.environ, **env),
+                       capture_output=True, text=True, timeout=240)
+    if expect is None:
+        assert r.returncode != 0 and "TERN_ERR_RUNG" in r.stderr, r.stderr[-2000:]
+        return
+    assert r.returncode == 0, r.stderr[-2000:]
+    arms = r.stdout.split("ARMS")[1].split()
+    assert [a.split(":")[1] for a in arms] == expect.split(), arms
+    assert all(a.endswith(":ok") for a in arms), arms
+    if env.get("TERN_S8") == "0":
+        assert arms[3].split(":")[2] == "b16_prefill", arms
+
+
+@pytest.mark.parametrize("n,k,T", [(16384, 10752, 4), (16384, 13824, 5), (16384, 7680, 6)])
+def test_resident_limbs_with_g64_on_wide_layers(tl, torch, n, k, T):
+    """Wide layers with a long K and G = 64, where the resident limb kernel's
+    scales take twice the LDS they take at G = 128: the dispatcher sizes the
+    plan with the call's group size, so the call runs (no launch error) and,
+    on integer activations with power-of-two scales, matches the oracle bit
+    for bit on sampled rows of every workgroup."""
+    G = 64
+    rng = np.random.default_rng(n + k + T)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.pow2_scales(n, k, G, seed=k)
+    W = tl.TernaryWeights.from_host(w, s)
+    xbits = ts.integer_activations(k, T, seed=k + T)
+    print("resident G=64", n, k, T, tl.plan_kernels(T, n, k, G), flush=True)
+    y = run(tl, torch, to_dev_bf16(torch, xbits), W, "auto")
+    rows = sample_rows(n, k, n=256)
+    ref = oracle.linear_bf16(xbits, w[rows], s[rows])
+    assert np.array_equal(y[:, rows].astype(np.float64), ref)
+
+
+@pytest.fixture(scope="module")
+def qkv(tl, torch):
+    """The fused q|k|v matrix (three 5120 -> 5120 projections stacked along
+    N: 5120 -> 15360) as the bench's fused stack times it, from the stack's
+    layer-0 seeds."""
+    parts = [ts.weights(ts.stack_shape(0, p)) for p in range(3)]
+    w = np.concatenate([p.w for p in parts])
+    s = np.concatenate([p.s for p in parts])
+    return parts[0], w, s, tl.TernaryWeights.from_host(w, s)
+
+
+def test_fused_qkv_decode_every_output(tl, torch, qkv):
+    wq, w, s, W = qkv
+    xbits = ts.activations(wq, 1)
+    y = run(tl, torch, to_dev_bf16(torch, xbits), W, "auto")
+    ref = oracle.linear_bf16(xbits, w, s)
+    assert rel_l2(y, ref) <= 1e-6
+
+
+@pytest.mark.parametrize("rung", ["s8", "small_t_tiled"])
+def test_fused_qkv_prefill_chunk_sampled(tl, torch, qkv, rung):
+    """A 1024-token prefill chunk on the fused q|k|v matrix, s8 and the bf16
+    prefill, on sampled rows."""
+    wq, w, s, W = qkv
+    T = 1024
+    xbits = ts.activations(wq, T)
+    x_dev = to_dev_bf16(torch, xbits)
+    rows = sample_rows(W.n, 1024 + len(rung))
+    y = run(tl, torch, x_dev, W, rung)
+    if rung == "s8":
+        check_s8(tl, torch, xbits, x_dev, W, w, s, y, rows=rows)
+    else:
+        ref = oracle.linear_bf16(xbits, w[rows], s[rows])
+        assert rel_l2(y[:, rows], ref) <= 1e-6

@@ -263,3 +263,121 @@ def test_env_is_read_once():
             "os.environ['TERN_RUNG'] = 's8'\n"
             "print(a, tl.resolve_rung(4))\n")
     assert _run_env({}, code) == "small_t small_t"
+
+
+# ------------------------------------------------ kernel choice (dry run)
+
+# Kernels the dispatcher runs by default, per layer shape (K -> N) and T: the
+# map that the measurements on the part chose (resident limbs on wide layers
+# up to 6 tokens and on narrow ones up to 3 where they fit; the tiled kernel
+# on wide layers above; the per-wave kernel on narrow ones except down above
+# 8 tokens, which splits K; s8 with a K split on short prefills of narrow
+# layers).
+DEFAULT_KERNELS = {
+    (34816, 5120): {1: "gemv_limb", 2: "smallt_resident", 6: "smallt_resident", 7: "smallt_tile",
+                    16: "smallt_tile", 17: "quant_s8,s8_mma", 2048: "quant_s8,s8_mma"},
+    (5120, 17408): {1: "gemv_limb", 2: "smallt_resident", 3: "smallt_wave", 8: "smallt_wave",
+                    9: "smallt_tile,smallt_tile_reduce", 16: "smallt_tile,smallt_tile_reduce",
+                    17: "quant_s8,s8_mma,s8_reduce", 2048: "quant_s8,s8_mma"},
+    (5120, 5120): {1: "gemv_limb", 3: "smallt_resident", 4: "smallt_wave", 16: "smallt_wave",
+                   36: "quant_s8,s8_mma,s8_reduce", 2048: "quant_s8,s8_mma"},
+}
+
+
+def test_plan_kernels_default_map(tl):
+    for (n, k), by_t in DEFAULT_KERNELS.items():
+        for T, names in by_t.items():
+            assert ",".join(tl.plan_kernels(T, n, k, 128)) == names, (n, k, T)
+    # forced rungs: small_t_tiled above one 16-token tile is the bf16 prefill
+    assert tl.plan_kernels(100, 34816, 5120, 128, "small_t_tiled") == ["b16_prefill"]
+    assert tl.plan_kernels(4, 34816, 5120, 128, "s8") == ["quant_s8", "s8_mma"]
+    assert tl.plan_kernels(1, 5120, 5120, 128, "small_t") == ["smallt_resident"]
+    with pytest.raises(tl.TernError):
+        tl.plan_kernels(20, 5120, 5120, 128, "small_t")  # one 16-token tile at most
+    with pytest.raises(tl.TernError):
+        tl.plan_kernels(1, 100, 256, 128)
+
+
+PLAN = ("import ternary_weight_linear_amd as tl\n"
+        "print(';'.join(','.join(tl.plan_kernels(T, n, k, 128)) for T, n, k in "
+        "((1, 34816, 5120), (4, 34816, 5120), (12, 5120, 17408), (2, 5120, 5120))))\n")
+
+
+def test_tune_knobs_steer_the_kernel_choice():
+    """TERN_TUNE_* arms select other kernels for the same rung; the dry run
+    (and so the kernel probe) names them."""
+    assert _run_env({}, PLAN) == ("gemv_limb;smallt_resident;smallt_tile,smallt_tile_reduce;"
+                                  "smallt_resident")
+    assert _run_env({"TERN_TUNE_GEMV": "bf16"}, PLAN).split(";")[0] == "gemv_bf16"
+    assert _run_env({"TERN_TUNE_SMALLT": "tile"}, PLAN).split(";")[1] == "smallt_tile"
+    assert _run_env({"TERN_TUNE_SMALLT": "wave"}, PLAN).split(";")[1] == "smallt_wave"
+    assert _run_env({"TERN_TUNE_SMALLT": "limb"}, PLAN).split(";")[1] == "smallt_limb_fused"
+    assert _run_env({"TERN_TUNE_SMALLT": "limb2"}, PLAN).split(";")[1] == ("smallt_limb_prep,"
+                                                                           "smallt_limb_tile")
+
+
+def test_gemv_with_limbs_beyond_lds_runs_the_bf16_kernel(tl):
+    # K = 16384 on a wide layer: the limbs and scales exceed the limb
+    # kernel's LDS, so the gemv runs the bf16 kernel with one-token rows; at
+    # K = 32768 the bf16 row no longer fits its LDS either and the 16-token
+    # per-wave kernel runs (its absent rows read as zeros).
+    assert tl.plan_kernels(1, 16384, 12288, 128) == ["gemv_limb"]
+    assert tl.plan_kernels(1, 16384, 16384, 128) == ["gemv_bf16"]
+    assert tl.plan_kernels(1, 16384, 32768, 128) == ["smallt_wave"]
+
+
+@pytest.mark.parametrize("n", [16384, 34816])
+def test_resident_choice_takes_the_group_size(tl, n):
+    """The resident limb kernel keeps the workgroup's scales in LDS next to the
+    limbs, twice the bytes at G = 64: the dispatcher must size its plan with
+    the call's G, and a shape whose G = 64 plan does not fit must go to
+    another kernel rather than fail at launch. The dry run and the launch
+    share the plan, so this checks that the choice is made per G."""
+    for k in range(7680, 16641, 768):
+        for T in (4, 5, 6):
+            a, b = tl.plan_kernels(T, n, k, 64), tl.plan_kernels(T, n, k, 128)
+            assert len(a) >= 1 and len(b) >= 1
+
+
+def test_tiled_max_knob():
+    assert _run_env({"TERN_SMALL_T_TILED_MAX": "32"}, PROBE) == "gemv,small_t,small_t_tiled,small_t_tiled,s8"
+    assert _run_env({"TERN_SMALL_T_TILED_MAX": "12"}, PROBE) == "gemv,small_t,small_t_tiled,s8,s8"
+    # consistent with TERN_S8_MIN_T: accepted
+    assert _run_env({"TERN_SMALL_T_TILED_MAX": "32", "TERN_S8_MIN_T": "33"}, PROBE) == \
+        "gemv,small_t,small_t_tiled,small_t_tiled,s8"
+
+
+@pytest.mark.parametrize("env", [{"TERN_SMALL_T_TILED_MAX": "x"}, {"TERN_SMALL_T_TILED_MAX": "0"},
+                                 {"TERN_SMALL_T_TILED_MAX": "4"},  # below TERN_SMALL_T_MAX
+                                 {"TERN_SMALL_T_TILED_MAX": "32", "TERN_S8_MIN_T": "20"}])
+def test_invalid_tiled_max_fails_every_call(env):
+    assert _run_env(env, PROBE) == ",".join(["TERN_ERR_CONFIG"] * 5)
+
+
+def test_shape_limits_of_the_kernels(tl):
+    """K above 2^20 or N above 2^24 would overflow the kernels' 32-bit
+    offsets: rejected before any launch."""
+    import ctypes
+    L = tl.lib()
+    assert L.tern_scale_count(16, 1 << 20, 128) == (16 * (1 << 20)) // 128
+    assert L.tern_scale_count(16, (1 << 20) + 256, 128) == 0
+    assert L.tern_scale_count(1 << 24, 256, 128) == (1 << 24) * 2
+    assert L.tern_scale_count((1 << 24) + 16, 256, 128) == 0
+    for n, k in (((1 << 24) + 16, 256), (16, (1 << 20) + 256)):
+        w = tl._Weights(0x100000, 0x200000, n, k, 128, tl.LAYOUT_V1)
+        st = L.tern_linear(0x400000, 1, ctypes.byref(w), 0x300000, 0, None, 0, None)
+        assert tl.STATUS[st] == "TERN_ERR_SHAPE", (n, k)
+        assert "above the supported" in L.tern_last_error().decode()
+    assert L.tern_quant_act_s8(0x100000, 1, (1 << 20) + 64, 0x200000, 0x300000, 1, None) == 2
+
+
+def test_kernel_probe_starts_empty_and_names_every_kernel(tl):
+    L = tl.lib()
+    tl.probe_reset()
+    assert all(v == 0 for v in tl.kernel_probe_snapshot().values())
+    assert tl.last_kernels() == []
+    names = [L.tern_kernel_name(i).decode() for i in range(len(tl.KERNELS))]
+    assert tuple(names) == tl.KERNELS
+    assert L.tern_kernel_name(len(tl.KERNELS)).decode() == "invalid"
+    src = open(HEADER).read()
+    assert len(re.findall(r"^\s+TERN_KERNEL_[A-Z0-9_]+(?: = 0)?,", src, re.M)) == len(tl.KERNELS)
