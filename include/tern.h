@@ -228,6 +228,32 @@ size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung);
 tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float* y,
                         tern_rung rung, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the static device scratch behind tern_linear_noalloc (64 MiB). */
+#define TERN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * tern_linear without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same rungs, kernels and results as
+ * tern_linear, with the workspace taken from a static device scratch of
+ * TERN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends. The call allocates nothing; it needs no
+ * initialisation of the scratch (every kernel writes what it later reads).
+ *  - A call whose tern_workspace_bytes() exceeds TERN_NOALLOC_SCRATCH_BYTES
+ *    fails with TERN_ERR_WORKSPACE before any HIP call (e.g. the s8 rung
+ *    from about 3,800 tokens at K = 17408).
+ *  - The first call on each device resolves the scratch's device address
+ *    (a HIP symbol lookup, no allocation): make it outside graph capture.
+ *  - All calls on one GPU share its scratch, which keeps the last call's
+ *    contents: calls that can overlap on one GPU (other streams, other
+ *    threads) race on it. Serialise them, or use tern_linear with a
+ *    workspace per stream.
+ * Arguments and errors as tern_linear (TERN_ERR_HIP also if the symbol
+ * lookup fails).
+ */
+tern_status tern_linear_noalloc(const void* x_bf16, int T, const tern_weights* W, float* y,
+                                tern_rung rung, void* stream);
+
 /*
  * The s8 rung's contraction on activations already quantised by
  * tern_quant_act_s8 (device, async): y[t][n] = scale_t * sum_g s[n][g] *

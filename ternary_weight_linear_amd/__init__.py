@@ -54,7 +54,7 @@ EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpa
            "tern_probe_snapshot", "tern_probe_reset", "tern_last_rung", "tern_resolve_rung",
            "tern_rung_name", "tern_last_error", "tern_abi_version",
            "tern_kernel_probe_snapshot", "tern_last_kernels", "tern_kernel_name",
-           "tern_plan_kernels")
+           "tern_plan_kernels", "tern_linear_noalloc")
 
 
 class TernError(RuntimeError):
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
         "tern_last_kernels": (ctypes.c_uint64, []),
         "tern_kernel_name": (ctypes.c_char_p, [i]),
         "tern_plan_kernels": (ctypes.c_uint64, [i, i, i, i, i]),
+        "tern_linear_noalloc": (st, [p, i, ctypes.POINTER(_Weights), p, i, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -381,6 +382,24 @@ def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=Non
     _check(lib().tern_linear(x.data_ptr(), T, W.ref(), y.data_ptr(), r, ws_ptr, ws_bytes,
                              _stream(stream)))
     _keep_for(stream, y if new_y else None, workspace if new_ws else None)
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def linear_noalloc(x, W: TernaryWeights, y, rung="auto", stream=None):
+    """y = ternary_linear(x) into the caller's y with no workspace and no
+    allocation (tern_linear_noalloc: the library's static device scratch of
+    NOALLOC_SCRATCH_BYTES per GPU; calls that overlap on one GPU race)."""
+    torch = _torch()
+    _dev(x, torch.bfloat16, "x")
+    _dev(y, torch.float32, "y")
+    T, K = x.shape
+    if K != W.k or tuple(y.shape) != (T, W.n):
+        raise ValueError(f"x {tuple(x.shape)} / y {tuple(y.shape)} do not match the weights")
+    _check(lib().tern_linear_noalloc(x.data_ptr(), T, W.ref(), y.data_ptr(), _rung(rung),
+                                     _stream(stream)))
     return y
 
 

@@ -680,6 +680,75 @@ tern_status check_weights(const tern_weights* W) {
 
 inline uint32_t encode(int8_t v) { return v == 0 ? 0u : (v == 1 ? 1u : 3u); }
 
+// tern_linear and tern_linear_noalloc: validate everything on the host, then
+// (noalloc: with the device's static scratch as the workspace) launch.
+tern_status linear_call(const void* x_bf16, int T, const tern_weights* W, float* y, tern_rung rung,
+                        void* ws, size_t ws_bytes, void* stream, bool noalloc) {
+  if (!x_bf16 || !y) return fail(TERN_ERR_NULL, "tern_linear: x or y is NULL");
+  tern_status st = check_weights(W);
+  if (st != TERN_OK) return st;
+  if (!aligned16(x_bf16) || !aligned16(y))
+    return fail(TERN_ERR_ALIGN, "x and y must be 16-byte aligned");
+  tern_rung r;
+  st = resolve(T, rung, &r);
+  if (st != TERN_OK) return st;
+  const int n = W->n, k = W->k, G = W->group;
+  const Choice c = choose(T, n, k, G, r);
+  if (noalloc && c.workspace > ws_bytes)
+    return fail(TERN_ERR_WORKSPACE,
+                "rung %s needs %zu bytes of workspace, more than the %zu of the static scratch",
+                kRungNames[r], c.workspace, ws_bytes);
+  if (noalloc && c.workspace) {
+    const int err = tern::noalloc_scratch(&ws);  // the device address of this GPU's copy
+    if (err) return hip_fail(err, "static scratch lookup");
+  }
+  if (c.workspace) {
+    if (!ws || ws_bytes < c.workspace)
+      return fail(TERN_ERR_WORKSPACE, "rung %s needs %zu bytes of workspace, got %zu%s",
+                  kRungNames[r], c.workspace, ws ? ws_bytes : (size_t)0, ws ? "" : " (NULL)");
+    if (!aligned16(ws)) return fail(TERN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  const tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
+  int err = 0;
+  switch (c.path) {
+    case Path::S8: {
+      int8_t* q = (int8_t*)ws;
+      float* sc = (float*)((char*)ws + align256((size_t)T * k));
+      err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, true, stream);
+      if (err) return hip_fail(err, "quant_s8 launch");
+      float* part = (float*)((char*)ws + align256((size_t)T * k) + align256((size_t)T * sizeof(float)));
+      const tern::S8Args sa{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr, true};
+      err = tern::launch_s8(sa, c.s8, part, stream);
+      if (err) return hip_fail(err, "s8 launch");
+      break;
+    }
+    case Path::GEMV_LIMB:
+    case Path::RESIDENT:
+      err = tern::launch_limb(a, c.limb, stream);
+      if (err) return hip_fail(err, c.path == Path::RESIDENT ? "small_t resident launch" : "gemv launch");
+      break;
+    case Path::PER_WAVE:
+      err = tern::launch_small_t(a, c.wave, stream);
+      if (err) return hip_fail(err, r == TERN_RUNG_GEMV ? "gemv launch" : "small_t launch");
+      break;
+    case Path::LIMBTILE:
+      err = tern::launch_limbtile(a, c.limbtile, ws, stream);
+      if (err) return hip_fail(err, "small_t limb launch");
+      break;
+    case Path::B16_PREFILL:
+      err = tern::launch_b16_prefill(a, c.s8, stream);
+      if (err) return hip_fail(err, "bf16 prefill launch");
+      break;
+    case Path::TILE:
+      err = tern::launch_tile(a, c.tile, ws, stream);
+      if (err) return hip_fail(err, "small_t launch");
+      break;
+  }
+  probe_hit(r, T, n, k, G);
+  return call_ok();
+}
+
+
 }  // namespace
 
 int tern::kernel_launched(int err, tern_kernel k) {
@@ -871,60 +940,13 @@ tern_status tern_stream_read(const void* buf, size_t bytes, int depth, int waves
 tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float* y,
                         tern_rung rung, void* ws, size_t ws_bytes, void* stream) {
   call_begin();
-  if (!x_bf16 || !y) return fail(TERN_ERR_NULL, "tern_linear: x or y is NULL");
-  tern_status st = check_weights(W);
-  if (st != TERN_OK) return st;
-  if (!aligned16(x_bf16) || !aligned16(y))
-    return fail(TERN_ERR_ALIGN, "x and y must be 16-byte aligned");
-  tern_rung r;
-  st = resolve(T, rung, &r);
-  if (st != TERN_OK) return st;
-  const int n = W->n, k = W->k, G = W->group;
-  const Choice c = choose(T, n, k, G, r);
-  if (c.workspace) {
-    if (!ws || ws_bytes < c.workspace)
-      return fail(TERN_ERR_WORKSPACE, "rung %s needs %zu bytes of workspace, got %zu%s",
-                  kRungNames[r], c.workspace, ws ? ws_bytes : (size_t)0, ws ? "" : " (NULL)");
-    if (!aligned16(ws)) return fail(TERN_ERR_ALIGN, "workspace must be 16-byte aligned");
-  }
-  const tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
-  int err = 0;
-  switch (c.path) {
-    case Path::S8: {
-      int8_t* q = (int8_t*)ws;
-      float* sc = (float*)((char*)ws + align256((size_t)T * k));
-      err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, true, stream);
-      if (err) return hip_fail(err, "quant_s8 launch");
-      float* part = (float*)((char*)ws + align256((size_t)T * k) + align256((size_t)T * sizeof(float)));
-      const tern::S8Args sa{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr, true};
-      err = tern::launch_s8(sa, c.s8, part, stream);
-      if (err) return hip_fail(err, "s8 launch");
-      break;
-    }
-    case Path::GEMV_LIMB:
-    case Path::RESIDENT:
-      err = tern::launch_limb(a, c.limb, stream);
-      if (err) return hip_fail(err, c.path == Path::RESIDENT ? "small_t resident launch" : "gemv launch");
-      break;
-    case Path::PER_WAVE:
-      err = tern::launch_small_t(a, c.wave, stream);
-      if (err) return hip_fail(err, r == TERN_RUNG_GEMV ? "gemv launch" : "small_t launch");
-      break;
-    case Path::LIMBTILE:
-      err = tern::launch_limbtile(a, c.limbtile, ws, stream);
-      if (err) return hip_fail(err, "small_t limb launch");
-      break;
-    case Path::B16_PREFILL:
-      err = tern::launch_b16_prefill(a, c.s8, stream);
-      if (err) return hip_fail(err, "bf16 prefill launch");
-      break;
-    case Path::TILE:
-      err = tern::launch_tile(a, c.tile, ws, stream);
-      if (err) return hip_fail(err, "small_t launch");
-      break;
-  }
-  probe_hit(r, T, n, k, G);
-  return call_ok();
+  return linear_call(x_bf16, T, W, y, rung, ws, ws_bytes, stream, false);
+}
+
+tern_status tern_linear_noalloc(const void* x_bf16, int T, const tern_weights* W, float* y,
+                                tern_rung rung, void* stream) {
+  call_begin();
+  return linear_call(x_bf16, T, W, y, rung, nullptr, tern::kNoallocScratchBytes, stream, true);
 }
 
 tern_status tern_linear_s8_q(const int8_t* q, const float* act_scale, int T,

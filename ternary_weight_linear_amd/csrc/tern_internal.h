@@ -128,4 +128,10 @@ int launch_stream_read(const void* buf, size_t bytes, int depth, int waves_per_c
                        void* stream);
 const char* hip_error_string(int err);
 
+// Static device scratch of tern_linear_noalloc (tern_noalloc.hip): its size,
+// and the device address of the current device's copy (resolved with
+// hipGetSymbolAddress on the first call per device). Returns a hipError_t value.
+constexpr size_t kNoallocScratchBytes = (size_t)TERN_NOALLOC_SCRATCH_BYTES;
+int noalloc_scratch(void** out);
+
 }  // namespace tern
