@@ -387,7 +387,7 @@ int oracle_linear_s8(const int8_t* q, const float* scale, int64_t T, int64_t K,
         int64_t ms;
         int es;
         half_to_int_pow2(s[n * NG + g], &ms, &es);
-        S += ((__int128)ms * (__int128)acc) << (es + 24);
+        S += ((__int128)ms * (__int128)acc) * ((__int128)1 << (es + 24));  /* es + 24 >= 0 */
       }
       __int128 P = S * (__int128)mt; /* |P| < 2^97 */
       int negative = P < 0;
