@@ -197,6 +197,85 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
     }
   };
 
+  // The same k-tile as a software pipeline (not DEBUG_ACC). Unit u = (group
+  // gi, strip c) runs its KBPG * TB MFMAs while the vector ALU folds the
+  // previous unit's accumulators into the totals and decodes the next unit's
+  // weight operands: independent instructions, which the matrix core and the
+  // vector ALU execute side by side when they are interleaved (measured on
+  // the part: 8 i8 MFMAs with 16 independent VALU instructions in between
+  // take about the time of the MFMAs alone; done one after the other, the
+  // sum of both). The previous unit of a k-tile's first unit is the last of
+  // the k-tile before (strip S - 1, across the barrier); pend starts as zeros
+  // with a zero scale, whose fold adds +0 to a +0 total. Per strip the folds
+  // still run in ascending group order, so the totals are those of compute.
+  i32x4 pend[TB];
+  float pend_s = 0.f;
+#pragma unroll
+  for (int a = 0; a < TB; ++a) pend[a] = i32x4{0, 0, 0, 0};
+  constexpr int kValuPerMfma = (8 * TB + 7 * KBPG + 2 + KBPG * TB - 1) / (KBPG * TB);
+  auto compute_p = [&](int kt, int buf, const S8mStage<GPT, S>& b) {
+    (void)kt;
+    i32x4 bq[KBPG];
+#pragma unroll
+    for (int kk = 0; kk < KBPG; ++kk) bq[kk] = weights_operand_i8(b.code[0][kk]);
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      i32x4 af[KBPG][TB];
+#pragma unroll
+      for (int kk = 0; kk < KBPG; ++kk)
+#pragma unroll
+        for (int a = 0; a < TB; ++a) {
+          const int chunk = (4 * (gi * KBPG + kk) + g) ^ r;  // row & 15 == r
+          af[kk][a] = *(const i32x4*)&As[buf][(a * 16 + r) * 256 + chunk * 16];
+        }
+#pragma unroll
+      for (int c = 0; c < S; ++c) {
+        i32x4 acc[TB];
+#pragma unroll
+        for (int kk = 0; kk < KBPG; ++kk)
+#pragma unroll
+          for (int a = 0; a < TB; ++a)
+            acc[a] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[kk][a], bq[kk],
+                                                           kk == 0 ? i32x4{0, 0, 0, 0} : acc[a], 0, 0, 0);
+        // the next unit's weight operands, inside this k-tile
+        const int cn = c + 1 < S ? c + 1 : 0;
+        const int gn = c + 1 < S ? gi : gi + 1;
+        if (gn < GPT) {
+#pragma unroll
+          for (int kk = 0; kk < KBPG; ++kk) bq[kk] = weights_operand_i8(b.code[cn][gn * KBPG + kk]);
+        }
+        // the previous unit's epilogue
+        const int cp = c == 0 ? S - 1 : c - 1;
+#pragma unroll
+        for (int a = 0; a < TB; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tot[a][cp][e] = __builtin_fmaf((float)pend[a][e], pend_s, tot[a][cp][e]);
+        const uint32_t sp = b.sw[c][gi >> 1];
+        pend_s = half_bits_to_float((uint16_t)((gi & 1) ? (sp >> 16) : (sp & 0xffffu)));
+#pragma unroll
+        for (int a = 0; a < TB; ++a) pend[a] = acc[a];
+#pragma unroll
+        for (int m = 0; m < KBPG * TB; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // then vector ALU work
+        }
+      }
+    }
+  };
+  // Folds the last pending unit (strip S - 1) after the final k-tile.
+  auto flush = [&]() {
+#pragma unroll
+    for (int a = 0; a < TB; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tot[a][S - 1][e] = __builtin_fmaf((float)pend[a][e], pend_s, tot[a][S - 1][e]);
+  };
+  auto run = [&](int kt, int buf, const S8mStage<GPT, S>& b) {
+    if constexpr (DEBUG_ACC)
+      compute(kt, buf, b);
+    else
+      compute_p(kt, buf, b);
+  };
+
   if constexpr (D == 2) {
     // Pipeline, one barrier per k-tile: the activation tile and the codes of
     // k-tile kt+1 are requested before the MFMAs of k-tile kt; then each wave
@@ -217,18 +296,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
       stage_a(kt + 1, 1);
       load_w(kt + 1, wB);
       __builtin_amdgcn_sched_barrier(0);
-      compute(kt, 0, wA);
+      run(kt, 0, wA);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       const int k2 = min(kt + 2, klast);
       stage_a(k2, 0);
       load_w(k2, wA);
       __builtin_amdgcn_sched_barrier(0);
-      compute(kt + 1, 1, wB);
+      run(kt + 1, 1, wB);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    if (kt <= klast) compute(kt, 0, wA);
+    if (kt <= klast) run(kt, 0, wA);
   } else {
     // Ring of D buffers: k-tile i sits in activation buffer i % D and code
     // stage i % D (i counted from kt0). Iteration i requests k-tile i + D - 1
@@ -253,7 +332,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
         stage_a(kn, (j + D - 1) % D);
         load_w(kn, ring[(j + D - 1) % D]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(kt0 + i + j, j, ring[j]);
+        run(kt0 + i + j, j, ring[j]);
         s8m_handoff<(D - 2) * L>();
       }
     }
@@ -263,10 +342,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
     for (int j = 0; j < D - 1; ++j) {
       if (i + j < nkt) {  // uniform over the workgroup
         if (j > 0) s8m_handoff<0>();
-        compute(kt0 + i + j, j, ring[j]);
+        run(kt0 + i + j, j, ring[j]);
       }
     }
   }
+  if constexpr (!DEBUG_ACC) flush();
 
   if (!DEBUG_ACC && Pk > 1) {
     // Partial totals of this K part, 2^-6 taken out; the reduce kernel adds
