@@ -60,6 +60,7 @@ def _load():
             "oracle_linear_s8": [p, p, i64, i64, p, p, i64, i64, p],
             "oracle_linear_s8_fp32_ordered": [p, p, i64, i64, p, p, i64, i64, p],
             "oracle_unpack_layout_v1": [p, p, i64, i64, i64, p, p],
+            "oracle_unpack_layout_t5": [p, p, i64, i64, i64, p, p],
             "oracle_rotate_f32": [p, i64, i64, p],
             "oracle_quant_s8_rot": [p, i64, i64, p, p],
         }.items():
@@ -198,4 +199,17 @@ def unpack_layout_v1(codes: np.ndarray, scales_packed: np.ndarray, N: int, K: in
     s = np.empty((N, K // G), np.uint16)
     _check(_load().oracle_unpack_layout_v1(_ptr(codes), _ptr(scales_packed), N, K, G, _ptr(w),
                                            _ptr(s)), "unpack_layout_v1")
+    return w, s
+
+
+def unpack_layout_t5(codes: np.ndarray, scales_packed: np.ndarray, N: int, K: int, G: int):
+    """Independent reader of the base-3 layout t5 (five weights per byte):
+    returns (w int8 [N, K], s uint16 [N, K//G])."""
+    codes = _c(codes, np.uint8).reshape(-1)
+    scales_packed = _c(scales_packed, np.uint16).reshape(-1)
+    assert codes.size == N * (K // 1024) * 208 and scales_packed.size == N * (K // G)
+    w = np.empty((N, K), np.int8)
+    s = np.empty((N, K // G), np.uint16)
+    _check(_load().oracle_unpack_layout_t5(_ptr(codes), _ptr(scales_packed), N, K, G, _ptr(w),
+                                           _ptr(s)), "unpack_layout_t5")
     return w, s

@@ -490,3 +490,73 @@ int oracle_unpack_layout_v1(const uint8_t* codes, const uint16_t* scales_packed,
   }
   return ORACLE_OK;
 }
+
+/* ------------------------------------------- packed layout t5 (reader) */
+
+/*
+ * Independent reader of the base-3 packed weight layout "t5": five weights
+ * per byte, the format of the "NInfer sm_89 fork" article, section 9 item 2
+ * ("t5" ternary: 5 trits per byte, one fp16 scale per 128 weights), laid out
+ * by this library for the integer matrix core. Restated from the public
+ * header's prose, sharing no code with the library:
+ *
+ *  - needs N % 16 == 0, K % 1024 == 0, G in {64, 128};
+ *  - a weight w in {-1, 0, +1} is the trit t = w + 1 in {0, 1, 2};
+ *  - strip s = rows [16s, 16s+16); k-quad Q = columns [1024Q, 1024Q+1024),
+ *    four k-tiles j = 0..3 of 256 columns; block (s, Q) is 3328 bytes at
+ *    byte offset (s*KQ + Q)*3328, KQ = K/1024;
+ *  - inside a block, k-tile j's main part is bytes [768j, 768j+768): lane
+ *    L in [0,64) owns bytes [768j + 12L, +12), three 4-byte words W0..W2;
+ *    bytes [3072, 3328) are the tails: byte 3072 + 4L + j is lane L's tail
+ *    byte for k-tile j;
+ *  - weight (row 16s + r, column 1024Q + 256j + kk): with kk = 64q + u,
+ *    u in [0,64), hi = u >= 32, u' = u - 32*hi, g = u' / 8, p = u' % 8,
+ *    i = p / 2, e = hi ? (p odd ? 2 : 0) : (p odd ? 3 : 1): lane L = 16g + r,
+ *    register R = 4q + i, byte e of the register;
+ *  - R < 15: byte e of word W[R / 5] holds five trits t_0..t_4 (t_0 most
+ *    significant) as the value v = sum_d t_d 3^(4-d) stored as the byte
+ *    b = ceil(256 v / 243); the weight is digit d = R % 5. Here v is
+ *    recovered as floor(243 b / 256) and split into base-3 digits;
+ *  - R == 15: the tail byte holds the trit in bits [2e+1 : 2e] (value 3 is
+ *    invalid);
+ *  - scales as in layout v1: [s][kt][r][gi], kt = 4Q + j.
+ *
+ * Outputs w int8 [N][K] and s fp16 bits [N][K/G]. ORACLE_ERR_WEIGHT for a
+ * byte that is not ceil(256 v / 243) of any v (never written) or a tail trit
+ * of 3.
+ */
+int oracle_unpack_layout_t5(const uint8_t* codes, const uint16_t* scales_packed, int64_t N,
+                            int64_t K, int64_t G, int8_t* w, uint16_t* s) {
+  if (N <= 0 || K <= 0 || N % 16 != 0 || K % 1024 != 0 || (G != 64 && G != 128))
+    return ORACLE_ERR_ARGS;
+  const int64_t KQ = K / 1024, KT = K / 256, NG = K / G, GPT = 256 / G;
+  static const int pow3[5] = {81, 27, 9, 3, 1};
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t st = n / 16, r = n % 16;
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t Q = k / 1024, j = (k / 256) % 4, kk = k % 256;
+      const int64_t q = kk / 64, u = kk % 64;
+      const int64_t hi = u >= 32, up = u - 32 * hi;
+      const int64_t g = up / 8, pp = up % 8, i = pp / 2, odd = pp % 2;
+      const int64_t e = hi ? (odd ? 2 : 0) : (odd ? 3 : 1);
+      const int64_t lane = 16 * g + r, R = 4 * q + i;
+      const uint8_t* blk = codes + (st * KQ + Q) * 3328;
+      int t;
+      if (R < 15) {
+        const int b = blk[768 * j + 12 * lane + 4 * (R / 5) + e];
+        const int v = (243 * b) >> 8;
+        if ((256 * v + 242) / 243 != b) return ORACLE_ERR_WEIGHT; /* not ceil(256 v / 243) */
+        t = (v / pow3[R % 5]) % 3;
+      } else {
+        t = (blk[3072 + 4 * lane + j] >> (2 * e)) & 3;
+        if (t == 3) return ORACLE_ERR_WEIGHT;
+      }
+      w[n * K + k] = (int8_t)(t - 1);
+    }
+    for (int64_t g = 0; g < NG; ++g) {
+      const int64_t kt = g / GPT, gi = g % GPT;
+      s[n * NG + g] = scales_packed[((st * KT + kt) * 16 + r) * GPT + gi];
+    }
+  }
+  return ORACLE_OK;
+}

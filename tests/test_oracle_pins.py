@@ -84,6 +84,59 @@ def test_hand_layout_reader(hand):
         assert np.argwhere(s != 0).tolist() == [[sc["n"], sc["g"]]], sc["derivation"]
 
 
+def _t5_zero(N, K):
+    """An all-zero t5 matrix: main bytes 0x80 (five trits 1), tails 0x55."""
+    codes = np.full(N * (K // 1024) * 208, 0x80, np.uint8)
+    blocks = codes.reshape(-1, 3328)
+    blocks[:, 3072:] = 0x55
+    return codes
+
+
+def test_hand_layout_t5_reader(hand):
+    c = hand["layout_t5"]
+    N, K, G = c["N"], c["K"], c["G"]
+    sp = np.zeros(N * (K // G), np.uint16)
+    assert c["zero_main"] == "0x80" and c["zero_tail"] == "0x55"
+    w, _ = oracle.unpack_layout_t5(_t5_zero(N, K), sp, N, K, G)
+    assert not w.any()
+    for case in c["cases"]:
+        codes = _t5_zero(N, K)
+        codes[case["byte"]] = int(case["value"], 16)
+        w, _ = oracle.unpack_layout_t5(codes, sp, N, K, G)
+        assert np.argwhere(w != 0).tolist() == [[case["n"], case["k"]]], case["derivation"]
+        assert w[case["n"], case["k"]] == case["w"], case["derivation"]
+
+
+def test_layout_t5_every_byte_value():
+    """Every canonical main byte ceil(256 v / 243), v = 0..242, decodes to the
+    five base-3 digits of v (most significant first) minus one, at the
+    weights of register 0..4 of lane 0, byte 0 (k = 32, 34, 36, 38 of k-block
+    0 and 32 of k-block 1); every other byte value is rejected."""
+    N, K, G = 16, 1024, 128
+    sp = np.zeros(N * (K // G), np.uint16)
+    canonical = {-(-256 * v // 243): v for v in range(243)}
+    for b in range(256):
+        codes = _t5_zero(N, K)
+        codes[0] = b
+        if b not in canonical:
+            with pytest.raises(ValueError):
+                oracle.unpack_layout_t5(codes, sp, N, K, G)
+            continue
+        v = canonical[b]
+        digits = [(v // 3 ** (4 - d)) % 3 for d in range(5)]
+        w, _ = oracle.unpack_layout_t5(codes, sp, N, K, G)
+        assert w[0, [32, 34, 36, 38, 96]].tolist() == [d - 1 for d in digits], b
+        assert np.count_nonzero(w) == sum(d != 1 for d in digits)
+
+
+def test_layout_t5_rejects_tail_trit_3():
+    N, K, G = 16, 1024, 128
+    codes = _t5_zero(N, K)
+    codes[3072] = 0x57  # bits 1:0 = 11
+    with pytest.raises(ValueError):
+        oracle.unpack_layout_t5(codes, np.zeros(N * (K // G), np.uint16), N, K, G)
+
+
 def test_layout_reader_rejects_code_10():
     codes = np.zeros(16 * 256 // 4, np.uint8)
     codes[3] = 0x80  # bits 31:30 of lane 0 word 0 = 10
