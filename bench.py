@@ -366,6 +366,51 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
                             "tokens_per_s": round(2048 / f_pre, 1)}}}
 
 
+def t5_bytes(T, n, k, group):
+    """Base-3 codes (13 bytes per 64 weights) + fp16 scales + bf16 x + fp32 y."""
+    return n * (k // 1024) * 208 + 2 * n * (k // group) + 2 * T * k + 4 * T * n
+
+
+def t5_leg(torch, ts, tl, dev, wts, steps=200, rounds=3):
+    """A/B of the T=1 gemv on the same matrices packed 2-bit (v1) and base-3
+    (t5, five weights per byte): the arms alternate `rounds` times, each a
+    graph of `steps` launches over weight copies rotated past the Infinity
+    Cache; per arm the median of the rounds."""
+    out = {}
+    for w in wts:
+        shape = w.shape
+        x = torch.from_numpy(ts.activations(w, 1).view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((1, shape.n), dtype=torch.float32, device=dev)
+        arms = {}
+        for layout in ("v1", "t5"):
+            b = tl.TernaryWeights.from_host(w.w, w.s, device=dev, layout=layout)
+            nsets = max(2, math.ceil(ROTATE_BYTES / b.nbytes))
+            arms[layout] = [b] + [tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group,
+                                                    layout) for _ in range(nsets - 1)]
+        times = {"v1": [], "t5": []}
+        for _ in range(rounds):
+            for layout in ("v1", "t5"):
+                sets = arms[layout]
+
+                def one(i, sets=sets):
+                    tl.linear(x, sets[i % len(sets)], y=y)
+                times[layout].append(graph_time(torch, one, steps, 10) / steps)
+        e = {}
+        for layout, fb in (("v1", algorithmic_bytes), ("t5", t5_bytes)):
+            t = float(np.median(times[layout]))
+            by = fb(1, shape.n, shape.k, shape.group)
+            e[layout] = {"us": round(t * 1e6, 3), "bytes": by, "GB/s": round(by / t / 1e9, 1),
+                         "us_rounds": [round(v * 1e6, 3) for v in times[layout]]}
+        e["t5_speedup"] = round(e["v1"]["us"] / e["t5"]["us"], 4)
+        out[shape.name] = e
+        log(f"  t5 A/B {shape.name}: v1 {e['v1']['us']:.2f} us, t5 {e['t5']['us']:.2f} us "
+            f"({e['t5_speedup']:.3f}x; t5 bytes {e['t5']['bytes'] / 1e6:.2f} MB)")
+        del arms
+        torch.cuda.empty_cache()
+    return {"workload": "gemv T=1 on gate_up and down, the same weights packed 2-bit (v1) and "
+                        "base-3 (t5: 5 weights per byte + fp16 scale per 128)", "per_shape": out}
+
+
 SMALL_T = (2, 4, 8, 12, 16)
 
 
@@ -475,6 +520,7 @@ def main():
     ap.add_argument("--no-s8", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 64-layer stack passes")
     ap.add_argument("--no-small-t", action="store_true", help="skip the T = 2..16 batches")
+    ap.add_argument("--no-t5", action="store_true", help="skip the 2-bit / base-3 gemv A/B")
     ap.add_argument("--kernels-only", action="store_true",
                     help="plain launches of the two dominant kernels and a 64 MiB copy, for "
                          "rocprofv3 counter runs (no timing, no JSON line)")
@@ -647,6 +693,10 @@ def main():
                          "traffic": stored_traffic(f"bf16_prefill:{dom}"),
                          "kernel": f"tern_b16m_kernel (bf16 prefill) on {dom}, T={T}"}}
 
+    t5 = None
+    if not args.no_t5:
+        t5 = t5_leg(torch, ts, tl, dev, wts)
+
     small = None
     if not args.no_small_t:
         small = small_t_leg(torch, ts, tl, dev)
@@ -674,7 +724,7 @@ def main():
                       "us_per_step_p10_p50_p90": [round(v * 1e6, 3) for v in (d10, d50, d90)],
                       "read_ceiling_us_per_step": round(ceil_step * 1e6, 3),
                       "frac_of_read_ceiling": round(ceil_step / (el / K), 4)},
-           "roofline": roofline, "s8_prefill": s8, "small_t": small, "stack": stack,
+           "roofline": roofline, "s8_prefill": s8, "t5_gemv_ab": t5, "small_t": small, "stack": stack,
            "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 

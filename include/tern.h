@@ -61,6 +61,8 @@ extern "C" {
 
 /* Tag of packed weight layout v1 (stored in tern_weights.layout). */
 #define TERN_LAYOUT_V1 0x54524e31u /* "TRN1" */
+/* Tag of the base-3 layout t5 (five weights per byte; see below). */
+#define TERN_LAYOUT_T5 0x54524e35u /* "TRN5" */
 
 typedef enum {
   TERN_RUNG_AUTO = 0,
@@ -82,7 +84,8 @@ typedef enum {
   TERN_ERR_WORKSPACE = 6, /* workspace missing or smaller than tern_workspace_bytes() */
   TERN_ERR_CONFIG = 7,    /* invalid TERN_* environment value */
   TERN_ERR_HIP = 8,       /* a HIP runtime call failed (launch error) */
-  TERN_ERR_LAYOUT = 9     /* tern_weights.layout is not TERN_LAYOUT_V1 */
+  TERN_ERR_LAYOUT = 9     /* tern_weights.layout is neither TERN_LAYOUT_V1 nor TERN_LAYOUT_T5,
+                             or a t5 matrix on a rung other than gemv */
 } tern_status;
 
 /*
@@ -108,13 +111,39 @@ typedef enum {
  *    ((s*KT + kt)*16 + r)*(256/G) + gi holds scale[16s + r][kt*(256/G) + gi].
  *  - Sizes: N*K/4 bytes of codes, N*(K/G)*2 bytes of scales.
  */
+/*
+ * Base-3 layout t5: five weights per byte, the "t5" ternary format of the
+ * "NInfer sm_89 fork" article, section 9 item 2, laid out here for the
+ * integer matrix core. 13 bytes per 64 weights (1.625 bits per weight, 19 %
+ * fewer code bytes than v1). Only the gemv rung (T = 1) reads it.
+ *
+ *  - N % 16 == 0, K % 1024 == 0, G in {64, 128}; a weight w is the trit
+ *    t = w + 1 in {0, 1, 2}.
+ *  - Strip s = rows [16s, 16s+16); k-quad Q = columns [1024Q, 1024Q+1024),
+ *    four k-tiles j = 0..3. Block (s, Q) is 3328 bytes at byte offset
+ *    (s*KQ + Q)*3328, KQ = K/1024.
+ *  - In a block, k-tile j's main part is bytes [768j, 768j+768): lane
+ *    L in [0, 64) owns bytes [768j + 12L, +12), little-endian words W0..W2.
+ *    Bytes [3072, 3328) are tails: byte 3072 + 4L + j is lane L's tail byte
+ *    of k-tile j.
+ *  - Weight (row 16s + r, column 1024Q + 256j + kk), kk = 64q + u: with
+ *    hi = (u >= 32), u' = u - 32 hi, g = u' / 8, p = u' % 8, i = p / 2 and
+ *    e = hi ? (p odd ? 2 : 0) : (p odd ? 3 : 1), it is byte e of register
+ *    R = 4q + i of lane L = 16g + r (the order of TERN_Q_OPERAND_ORDER).
+ *  - R < 15: byte e of word W[R / 5] holds five trits t_0..t_4 of
+ *    registers 5(R/5) .. 5(R/5)+4 (digit d = R % 5, t_0 most significant)
+ *    as v = sum_d t_d 3^(4-d), stored as the byte ceil(256 v / 243).
+ *  - R == 15: bits [2e+1 : 2e] of the tail byte hold the trit.
+ *  - Scales as in layout v1. Sizes: N*(K/1024)*208 code bytes.
+ */
+
 typedef struct {
-  const void* codes;      /* device, N*K/4 bytes, layout v1, 16-byte aligned */
+  const void* codes;      /* device, N*K/4 bytes (v1) or N*(K/1024)*208 (t5), 16-byte aligned */
   const uint16_t* scales; /* device, N*(K/G) fp16 in the re-laid order, 16-byte aligned */
   int32_t n;              /* output features N */
   int32_t k;              /* input features K */
   int32_t group;          /* G: 64 or 128 */
-  uint32_t layout;        /* must be TERN_LAYOUT_V1 */
+  uint32_t layout;        /* TERN_LAYOUT_V1 or TERN_LAYOUT_T5 */
 } tern_weights;
 
 /* Bytes of packed codes for an N x K matrix (N*K/4), 0 if the shape is invalid. */
@@ -136,6 +165,20 @@ tern_status tern_pack(const int8_t* w, const uint16_t* scales_f16, int n, int k,
  * NULL to skip the scales. TERN_ERR_VALUE if a code 10 is found. */
 tern_status tern_unpack(const void* codes, const uint16_t* scales_packed, int n, int k,
                         int group, int8_t* w_out, uint16_t* scales_out);
+
+/* Bytes of t5 codes for an N x K matrix (N*(K/1024)*208), 0 if the shape is
+ * invalid for t5 (N % 16, K % 1024). */
+size_t tern_packed_code_bytes_t5(int n, int k);
+/* tern_pack into the base-3 layout t5 (host, synchronous): the same inputs,
+ * tern_packed_code_bytes_t5(n, k) bytes of codes, scales re-laid as for v1.
+ * Errors: TERN_ERR_NULL, TERN_ERR_SHAPE (K % 1024 too), TERN_ERR_VALUE. */
+tern_status tern_pack_t5(const int8_t* w, const uint16_t* scales_f16, int n, int k, int group,
+                         void* codes_out, uint16_t* scales_out);
+/* Inverse of tern_pack_t5 (host, synchronous); TERN_ERR_VALUE for a byte that
+ * tern_pack_t5 never writes (not ceil(256 v / 243) for v <= 242) or a tail
+ * trit of 3. scales_packed and scales_out may both be NULL. */
+tern_status tern_unpack_t5(const void* codes, const uint16_t* scales_packed, int n, int k,
+                           int group, int8_t* w_out, uint16_t* scales_out);
 
 /* Layouts of int8 activations q [T][K]. */
 typedef enum {
@@ -333,6 +376,7 @@ typedef enum {
   TERN_KERNEL_S8_ROW,             /* s8 contraction on row-major q (tern_linear_s8_q) */
   TERN_KERNEL_S8_ACC_EXPORT,      /* tern_debug_s8_acc */
   TERN_KERNEL_STREAM_READ,        /* tern_stream_read */
+  TERN_KERNEL_GEMV_T5,            /* gemv on base-3 (t5) weights: limbs of x on the i8 matrix cores */
   TERN_KERNEL_COUNT
 } tern_kernel;
 
@@ -344,10 +388,11 @@ void tern_kernel_probe_snapshot(uint64_t out[TERN_KERNEL_COUNT]);
  * any). With TERN_DEBUG=1 the rung line of tern_linear names them too. */
 uint64_t tern_last_kernels(void);
 /* Host-only dry run of the dispatcher (no HIP call): the kernel-id bit mask
- * (as tern_last_kernels) that tern_linear(T, N, K, G, rung) would launch
+ * (as tern_last_kernels) that tern_linear(T, N, K, G, rung) on weights of
+ * `layout` would launch
  * under the frozen configuration, 0 if the shape, rung or configuration is
  * invalid (tern_last_error says why). */
-uint64_t tern_plan_kernels(int T, int n, int k, int group, tern_rung rung);
+uint64_t tern_plan_kernels(int T, int n, int k, int group, uint32_t layout, tern_rung rung);
 /* Name of a kernel id ("gemv_limb", "smallt_tile", ...; "invalid" if out of range). */
 const char* tern_kernel_name(tern_kernel kernel);
 /* Rung of the most recent successful tern_linear call on any thread

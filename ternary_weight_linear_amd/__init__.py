@@ -36,6 +36,8 @@ LIB_PATH = os.path.join(_HERE, "libtern.so")
 RUNGS = ("auto", "gemv", "small_t", "small_t_tiled", "s8")
 RUNG_ID = {name: i for i, name in enumerate(RUNGS)}
 LAYOUT_V1 = 0x54524E31
+LAYOUT_T5 = 0x54524E35
+LAYOUTS = {"v1": LAYOUT_V1, "t5": LAYOUT_T5}
 
 STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_ALIGN",
           4: "TERN_ERR_VALUE", 5: "TERN_ERR_RUNG", 6: "TERN_ERR_WORKSPACE", 7: "TERN_ERR_CONFIG",
@@ -45,7 +47,7 @@ STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_AL
 KERNELS = ("quant_s8", "quant_s8_row", "quant_s8_rot", "gemv_limb", "gemv_bf16",
            "smallt_resident", "smallt_limb_fused", "smallt_limb_prep", "smallt_limb_tile",
            "smallt_wave", "smallt_tile", "smallt_tile_reduce", "b16_prefill", "s8_mma",
-           "s8_reduce", "s8_row", "s8_acc_export", "stream_read")
+           "s8_reduce", "s8_row", "s8_acc_export", "stream_read", "gemv_t5")
 
 # Symbols declared in include/tern.h (checked by the host tests).
 EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpack",
@@ -54,7 +56,8 @@ EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpa
            "tern_probe_snapshot", "tern_probe_reset", "tern_last_rung", "tern_resolve_rung",
            "tern_rung_name", "tern_last_error", "tern_abi_version",
            "tern_kernel_probe_snapshot", "tern_last_kernels", "tern_kernel_name",
-           "tern_plan_kernels", "tern_linear_noalloc")
+           "tern_plan_kernels", "tern_linear_noalloc", "tern_packed_code_bytes_t5", "tern_pack_t5",
+           "tern_unpack_t5")
 
 
 class TernError(RuntimeError):
@@ -104,7 +107,10 @@ def lib() -> ctypes.CDLL:
         "tern_kernel_probe_snapshot": (None, [p]),
         "tern_last_kernels": (ctypes.c_uint64, []),
         "tern_kernel_name": (ctypes.c_char_p, [i]),
-        "tern_plan_kernels": (ctypes.c_uint64, [i, i, i, i, i]),
+        "tern_plan_kernels": (ctypes.c_uint64, [i, i, i, i, ctypes.c_uint32, i]),
+        "tern_packed_code_bytes_t5": (sz, [i, i]),
+        "tern_pack_t5": (st, [p, p, i, i, i, p, p]),
+        "tern_unpack_t5": (st, [p, p, i, i, i, p, p]),
         "tern_linear_noalloc": (st, [p, i, ctypes.POINTER(_Weights), p, i, p]),
     }
     for name, (res, args) in sig.items():
@@ -131,9 +137,10 @@ def _rung(r) -> int:
 # ------------------------------------------------------------------- host
 
 
-def pack(w: np.ndarray, scales: np.ndarray):
+def pack(w: np.ndarray, scales: np.ndarray, layout: str = "v1"):
     """Relayout int8 weights [N, K] and fp16 scales [N, K/G] (uint16 bits or
-    float16) to packed layout v1. Returns (codes uint8 [N*K/4], scales uint16 [N*K/G])."""
+    float16) to packed layout v1 (2 bits per weight) or t5 (base-3, five per
+    byte). Returns (codes uint8, scales uint16 [N*K/G])."""
     w = np.ascontiguousarray(w, dtype=np.int8)
     scales = np.ascontiguousarray(scales)
     if scales.dtype == np.float16:
@@ -144,24 +151,25 @@ def pack(w: np.ndarray, scales: np.ndarray):
     if scales.ndim != 2 or scales.shape[0] != n or scales.shape[1] == 0 or k % scales.shape[1]:
         raise ValueError(f"scales shape {scales.shape} does not match w {w.shape}")
     group = k // scales.shape[1]
-    nbytes = lib().tern_packed_code_bytes(n, k)
+    t5 = {"v1": False, "t5": True}[layout]
+    nbytes = (lib().tern_packed_code_bytes_t5 if t5 else lib().tern_packed_code_bytes)(n, k)
     codes = np.empty(max(nbytes, 1), np.uint8)
     sp = np.empty(scales.size, np.uint16)
-    _check(lib().tern_pack(w.ctypes.data, scales.ctypes.data, n, k, group, codes.ctypes.data,
-                           sp.ctypes.data))
+    _check((lib().tern_pack_t5 if t5 else lib().tern_pack)(
+        w.ctypes.data, scales.ctypes.data, n, k, group, codes.ctypes.data, sp.ctypes.data))
     return codes[:nbytes], sp
 
 
-def unpack(codes: np.ndarray, scales_packed, n: int, k: int, group: int):
+def unpack(codes: np.ndarray, scales_packed, n: int, k: int, group: int, layout: str = "v1"):
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    fn = {"v1": lib().tern_unpack, "t5": lib().tern_unpack_t5}[layout]
     w = np.empty((n, k), np.int8)
     if scales_packed is None:
-        _check(lib().tern_unpack(codes.ctypes.data, None, n, k, group, w.ctypes.data, None))
+        _check(fn(codes.ctypes.data, None, n, k, group, w.ctypes.data, None))
         return w, None
     sp = np.ascontiguousarray(scales_packed, dtype=np.uint16)
     s = np.empty((n, k // group), np.uint16)
-    _check(lib().tern_unpack(codes.ctypes.data, sp.ctypes.data, n, k, group, w.ctypes.data,
-                             s.ctypes.data))
+    _check(fn(codes.ctypes.data, sp.ctypes.data, n, k, group, w.ctypes.data, s.ctypes.data))
     return w, s
 
 
@@ -209,10 +217,10 @@ def last_kernels() -> list:
     return _names(lib().tern_last_kernels())
 
 
-def plan_kernels(T: int, n: int, k: int, group: int, rung="auto") -> list:
-    """Names of the kernels linear() would launch for this call (host-only
-    dry run of the dispatcher)."""
-    m = lib().tern_plan_kernels(T, n, k, group, _rung(rung))
+def plan_kernels(T: int, n: int, k: int, group: int, rung="auto", layout="v1") -> list:
+    """Names of the kernels linear() would launch for this call on weights of
+    `layout` ("v1" or "t5"): a host-only dry run of the dispatcher."""
+    m = lib().tern_plan_kernels(T, n, k, group, LAYOUTS[layout], _rung(rung))
     if m == 0:
         raise TernError(5, lib().tern_last_error().decode())
     return _names(m)
@@ -268,24 +276,25 @@ def _dev(t, dtype, name):
 
 
 class TernaryWeights:
-    """Packed ternary weights resident on the GPU (layout v1)."""
+    """Packed ternary weights resident on the GPU (layout "v1" or "t5")."""
 
-    def __init__(self, codes, scales, n: int, k: int, group: int):
+    def __init__(self, codes, scales, n: int, k: int, group: int, layout: str = "v1"):
         torch = _torch()
         self.codes = _dev(codes, torch.uint8, "codes")
         self.scales = _dev(scales, torch.int16, "scales")
         self.n, self.k, self.group = int(n), int(k), int(group)
+        self.layout = layout
         self._struct = _Weights(self.codes.data_ptr(), self.scales.data_ptr(), self.n, self.k,
-                                self.group, LAYOUT_V1)
+                                self.group, LAYOUTS[layout])
 
     @classmethod
-    def from_host(cls, w: np.ndarray, scales: np.ndarray, device="cuda"):
+    def from_host(cls, w: np.ndarray, scales: np.ndarray, device="cuda", layout: str = "v1"):
         torch = _torch()
-        codes, sp = pack(w, scales)
+        codes, sp = pack(w, scales, layout)
         n, k = w.shape
         group = k // scales.shape[1]
         return cls(torch.from_numpy(codes).to(device), torch.from_numpy(sp.view(np.int16)).to(device),
-                   n, k, group)
+                   n, k, group, layout)
 
     @property
     def nbytes(self) -> int:

@@ -47,8 +47,8 @@ const char* const kKernelNames[TERN_KERNEL_COUNT] = {
     "quant_s8",        "quant_s8_row",      "quant_s8_rot",   "gemv_limb",        "gemv_bf16",
     "smallt_resident", "smallt_limb_fused", "smallt_limb_prep", "smallt_limb_tile", "smallt_wave",
     "smallt_tile",     "smallt_tile_reduce", "b16_prefill",   "s8_mma",           "s8_reduce",
-    "s8_row",          "s8_acc_export",     "stream_read"};
-static_assert(TERN_KERNEL_COUNT == 18, "one name per kernel id");
+    "s8_row",          "s8_acc_export",     "stream_read",    "gemv_t5"};
+static_assert(TERN_KERNEL_COUNT == 19, "one name per kernel id");
 
 // ------------------------------------------------------------ configuration
 
@@ -662,6 +662,25 @@ Choice choose(int T, int n, int k, int G, tern_rung r) {
   return c;
 }
 
+// The same for base-3 (t5) weights: the gemv rung only, on the limb kernel,
+// with the plan of the 2-bit layout; an error for any other rung (a forced
+// rung never falls back) or a K whose limbs do not fit the kernel's LDS.
+tern_status choose_t5(int T, int n, int k, int G, tern_rung r, Choice* out) {
+  if (r != TERN_RUNG_GEMV)
+    return fail(TERN_ERR_LAYOUT, "layout t5 runs on the gemv rung only (T = %d resolves to %s)", T,
+                kRungNames[r]);
+  if (T != 1) return fail(TERN_ERR_LAYOUT, "layout t5 takes one token, T = %d", T);
+  Choice c;
+  c.path = Path::GEMV_LIMB;
+  c.limb = plan_limb(T, n, k);
+  c.limb.t5 = true;
+  if (tern::limb_lds_bytes(T, k, G, c.limb) > tern::kLimbMaxLds)
+    return fail(TERN_ERR_SHAPE, "layout t5: K=%d needs more LDS than the gemv kernel has", k);
+  c.kernels = kbit(TERN_KERNEL_GEMV_T5);
+  *out = c;
+  return TERN_OK;
+}
+
 tern_status hip_fail(int err, const char* what) {
   return fail(TERN_ERR_HIP, "%s: %s", what, tern::hip_error_string(err));
 }
@@ -669,10 +688,12 @@ tern_status hip_fail(int err, const char* what) {
 tern_status check_weights(const tern_weights* W) {
   if (!W) return fail(TERN_ERR_NULL, "W is NULL");
   if (!W->codes || !W->scales) return fail(TERN_ERR_NULL, "W->codes or W->scales is NULL");
-  if (W->layout != TERN_LAYOUT_V1)
-    return fail(TERN_ERR_LAYOUT, "W->layout=0x%08x is not TERN_LAYOUT_V1", W->layout);
+  if (W->layout != TERN_LAYOUT_V1 && W->layout != TERN_LAYOUT_T5)
+    return fail(TERN_ERR_LAYOUT, "W->layout=0x%08x is neither TERN_LAYOUT_V1 nor TERN_LAYOUT_T5", W->layout);
   tern_status st = check_shape(W->n, W->k, W->group);
   if (st != TERN_OK) return st;
+  if (W->layout == TERN_LAYOUT_T5 && W->k % 1024 != 0)
+    return fail(TERN_ERR_SHAPE, "layout t5: K=%d must be a multiple of 1024", W->k);
   if (!aligned16(W->codes) || !aligned16(W->scales))
     return fail(TERN_ERR_ALIGN, "W->codes / W->scales must be 16-byte aligned");
   return TERN_OK;
@@ -693,7 +714,13 @@ tern_status linear_call(const void* x_bf16, int T, const tern_weights* W, float*
   st = resolve(T, rung, &r);
   if (st != TERN_OK) return st;
   const int n = W->n, k = W->k, G = W->group;
-  const Choice c = choose(T, n, k, G, r);
+  Choice c;
+  if (W->layout == TERN_LAYOUT_T5) {
+    st = choose_t5(T, n, k, G, r, &c);
+    if (st != TERN_OK) return st;
+  } else {
+    c = choose(T, n, k, G, r);
+  }
   if (noalloc && c.workspace > ws_bytes)
     return fail(TERN_ERR_WORKSPACE,
                 "rung %s needs %zu bytes of workspace, more than the %zu of the static scratch",
@@ -864,6 +891,110 @@ tern_status tern_unpack(const void* codes, const uint16_t* scales_packed, int n,
   return ok();
 }
 
+size_t tern_packed_code_bytes_t5(int n, int k) {
+  if (n < 16 || n % 16 || k < 1024 || k % 1024 || k > kMaxK || n > kMaxN) return 0;
+  return (size_t)n * (size_t)(k / 1024) * 208;
+}
+
+tern_status tern_pack_t5(const int8_t* w, const uint16_t* scales_f16, int n, int k, int group,
+                         void* codes_out, uint16_t* scales_out) {
+  if (!w || !scales_f16 || !codes_out || !scales_out)
+    return fail(TERN_ERR_NULL, "tern_pack_t5: NULL pointer");
+  tern_status st = check_shape(n, k, group);
+  if (st != TERN_OK) return st;
+  if (k % 1024 != 0) return fail(TERN_ERR_SHAPE, "layout t5: K=%d must be a multiple of 1024", k);
+  const size_t NS = (size_t)n / 16, KQ = (size_t)k / 1024, KT = (size_t)k / 256;
+  const size_t GPT = 256 / (size_t)group, NG = (size_t)k / group;
+  for (size_t i = 0; i < (size_t)n * k; ++i)
+    if (w[i] < -1 || w[i] > 1)
+      return fail(TERN_ERR_VALUE, "tern_pack_t5: w[%zu][%zu]=%d not in {-1,0,1}", i / k, i % k, (int)w[i]);
+  uint8_t* out = (uint8_t*)codes_out;
+  // column of byte e of register R (R = 4q + i) of lane group g, in a k-tile
+  auto col = [](int R, int e, int g) {
+    const int q = R >> 2, i = R & 3;
+    const int m = e == 0 ? 32 + 2 * i : e == 1 ? 2 * i : e == 2 ? 33 + 2 * i : 2 * i + 1;
+    return 64 * q + 8 * g + m;
+  };
+  for (size_t s = 0; s < NS; ++s)
+    for (size_t Q = 0; Q < KQ; ++Q) {
+      uint8_t* blk = out + (s * KQ + Q) * 3328;
+      for (int j = 0; j < 4; ++j)
+        for (int L = 0; L < 64; ++L) {
+          const int r = L & 15, g = L >> 4;
+          const int8_t* wrow = w + (s * 16 + r) * (size_t)k + (Q * 4 + j) * 256;
+          for (int word = 0; word < 3; ++word)
+            for (int e = 0; e < 4; ++e) {
+              int v = 0;  // trits t_0..t_4 of registers 5 word .. 5 word + 4, t_0 most significant
+              for (int d = 0; d < 5; ++d) v = 3 * v + (wrow[col(5 * word + d, e, g)] + 1);
+              blk[768 * j + 12 * L + 4 * word + e] = (uint8_t)((256 * v + 242) / 243);
+            }
+          int tail = 0;
+          for (int e = 0; e < 4; ++e) tail |= (wrow[col(15, e, g)] + 1) << (2 * e);
+          blk[3072 + 4 * L + j] = (uint8_t)tail;
+        }
+    }
+  for (size_t s = 0; s < NS; ++s)
+    for (size_t kt = 0; kt < KT; ++kt)
+      for (int r = 0; r < 16; ++r)
+        for (size_t gi = 0; gi < GPT; ++gi)
+          scales_out[((s * KT + kt) * 16 + r) * GPT + gi] = scales_f16[(s * 16 + r) * NG + kt * GPT + gi];
+  return ok();
+}
+
+tern_status tern_unpack_t5(const void* codes, const uint16_t* scales_packed, int n, int k, int group,
+                           int8_t* w_out, uint16_t* scales_out) {
+  if (!codes || !w_out) return fail(TERN_ERR_NULL, "tern_unpack_t5: NULL pointer");
+  if ((scales_packed == nullptr) != (scales_out == nullptr))
+    return fail(TERN_ERR_NULL, "tern_unpack_t5: give both scale pointers or neither");
+  tern_status st = check_shape(n, k, group);
+  if (st != TERN_OK) return st;
+  if (k % 1024 != 0) return fail(TERN_ERR_SHAPE, "layout t5: K=%d must be a multiple of 1024", k);
+  const size_t NS = (size_t)n / 16, KQ = (size_t)k / 1024, KT = (size_t)k / 256;
+  const size_t GPT = 256 / (size_t)group, NG = (size_t)k / group;
+  const uint8_t* in = (const uint8_t*)codes;
+  auto col = [](int R, int e, int g) {
+    const int q = R >> 2, i = R & 3;
+    const int m = e == 0 ? 32 + 2 * i : e == 1 ? 2 * i : e == 2 ? 33 + 2 * i : 2 * i + 1;
+    return 64 * q + 8 * g + m;
+  };
+  for (size_t s = 0; s < NS; ++s)
+    for (size_t Q = 0; Q < KQ; ++Q) {
+      const uint8_t* blk = in + (s * KQ + Q) * 3328;
+      for (int j = 0; j < 4; ++j)
+        for (int L = 0; L < 64; ++L) {
+          const int r = L & 15, g = L >> 4;
+          int8_t* wrow = w_out + (s * 16 + r) * (size_t)k + (Q * 4 + j) * 256;
+          for (int word = 0; word < 3; ++word)
+            for (int e = 0; e < 4; ++e) {
+              const int b = blk[768 * j + 12 * L + 4 * word + e];
+              int q = b;  // the kernel's decode: five times q = 3q, trit = q >> 8, q &= 255
+              int v = 0;
+              for (int d = 0; d < 5; ++d) {
+                const int q3 = 3 * q;
+                wrow[col(5 * word + d, e, g)] = (int8_t)((q3 >> 8) - 1);
+                v = 3 * v + (q3 >> 8);
+                q = q3 & 255;
+              }
+              if ((256 * v + 242) / 243 != b)
+                return fail(TERN_ERR_VALUE, "tern_unpack_t5: byte 0x%02x is not a packed value", b);
+            }
+          const int tail = blk[3072 + 4 * L + j];
+          for (int e = 0; e < 4; ++e) {
+            const int t = (tail >> (2 * e)) & 3;
+            if (t == 3) return fail(TERN_ERR_VALUE, "tern_unpack_t5: tail trit 3");
+            wrow[col(15, e, g)] = (int8_t)(t - 1);
+          }
+        }
+    }
+  if (scales_out)
+    for (size_t s = 0; s < NS; ++s)
+      for (size_t kt = 0; kt < KT; ++kt)
+        for (int r = 0; r < 16; ++r)
+          for (size_t gi = 0; gi < GPT; ++gi)
+            scales_out[(s * 16 + r) * NG + kt * GPT + gi] = scales_packed[((s * KT + kt) * 16 + r) * GPT + gi];
+  return ok();
+}
+
 size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung) {
   if (check_shape(n, k, group) != TERN_OK) return (size_t)-1;
   tern_rung r;
@@ -871,10 +1002,22 @@ size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung) {
   return choose(T, n, k, group, r).workspace;
 }
 
-uint64_t tern_plan_kernels(int T, int n, int k, int group, tern_rung rung) {
+uint64_t tern_plan_kernels(int T, int n, int k, int group, uint32_t layout, tern_rung rung) {
   if (check_shape(n, k, group) != TERN_OK) return 0;
+  if (layout != TERN_LAYOUT_V1 && layout != TERN_LAYOUT_T5) {
+    fail(TERN_ERR_LAYOUT, "layout=0x%08x is neither TERN_LAYOUT_V1 nor TERN_LAYOUT_T5", layout);
+    return 0;
+  }
+  if (layout == TERN_LAYOUT_T5 && k % 1024 != 0) {
+    fail(TERN_ERR_SHAPE, "layout t5: K=%d must be a multiple of 1024", k);
+    return 0;
+  }
   tern_rung r;
   if (resolve(T, rung, &r) != TERN_OK) return 0;
+  if (layout == TERN_LAYOUT_T5) {
+    Choice c;
+    return choose_t5(T, n, k, group, r, &c) == TERN_OK ? c.kernels : 0;
+  }
   return choose(T, n, k, group, r).kernels;
 }
 

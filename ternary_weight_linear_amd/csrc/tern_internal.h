@@ -74,6 +74,7 @@ struct LimbPlan {
   int depth;            // k-tiles of codes in flight per wave: 2, 4 or 8
   bool token_lanes = false;  // T <= 4: lane group u holds token u (single-token epilogue)
   bool resident = false;     // limbs of the whole K in up to kLimbMaxLdsResident of LDS (one workgroup per CU)
+  bool t5 = false;           // base-3 weights (layout t5): T = 1, one strip per wave, K % 1024 == 0
 };
 constexpr int kLimbMaxLds = 65536;
 constexpr int kLimbMaxLdsResident = 160 * 1024;  // the resident small-T mode: all of a CU's LDS

@@ -41,6 +41,19 @@
 // of packed layout v1. Lane 16g + r then reads its 16-byte A operand for
 // k-block b at row r, offset 64b + 16g.
 //
+// Base-3 weights (layout t5, include/tern.h; L5 = true, T = 1 only). Five
+// weights per byte ("NInfer sm_89 fork" article, section 9 item 2): a lane's
+// 64 weights of a k-tile are three words of five-trit bytes (60 weights) and
+// a tail byte of four 2-bit trits. A word splits into its even and odd bytes
+// in 16-bit lanes; five times "multiply by 3" moves the next trit (t = w + 1)
+// of every byte into bits 8-9 of its lane, and one byte permute gathers the
+// four trits into an int8 operand register (about 5 VALU instructions per 4
+// weights, against 7 per 16 for the 2-bit layout). The MFMA then sums
+// t * limb = w * limb + limb; each scale group's accumulators start from
+// minus the group's limb sums (made once per workgroup in the prep, kept in
+// LDS), so the accumulators are exactly those of the 2-bit path without its
+// 64x factor.
+//
 // Work split. A workgroup owns Wn*S strips of 16 outputs over the whole K; its
 // Wn*Wk waves take S strips each over a 1/Wk share of the k-tiles (wide layers
 // use Wk = 1, narrow ones split K so that enough waves stream). Each wave keeps
@@ -73,12 +86,41 @@ struct LimbStage {
 // exponents d [T][K/256] (int), then the workgroup's scales in their packed
 // order [strip][k-tile][row][group]; all of it is reused for the final
 // reduction.
-template <int TT, int S, int GPT, int D>
+// Trits t = w + 1 of a t5 k-tile as four int8 operand quads (registers
+// R = 4q + i for MFMA q): R = 5w + d from word w, digit d; R = 15 from the
+// tail byte j of P.w.
+__device__ __forceinline__ void t5_operands(const u32x4& P, int j, i32x4 (&op)[4]) {
+  uint32_t reg[16];
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    uint32_t E = __builtin_amdgcn_perm(P[w], P[w], 0x0c020c00u);  // bytes 0, 2 in 16-bit lanes
+    uint32_t O = __builtin_amdgcn_perm(P[w], P[w], 0x0c030c01u);  // bytes 1, 3
+#pragma unroll
+    for (int d = 0; d < 5; ++d) {
+      const uint32_t E3 = E * 3u, O3 = O * 3u;  // no carry out of a lane: 3 * 255 < 2^16
+      reg[5 * w + d] = __builtin_amdgcn_perm(O3, E3, 0x07030501u);  // [E3.1, O3.1, E3.3, O3.3]
+      if (d < 4) {
+        E = E3 & 0x00ff00ffu;
+        O = O3 & 0x00ff00ffu;
+      }
+    }
+  }
+  const uint32_t tb = (P[3] >> (8 * j)) & 0xffu;
+  uint32_t x = (tb << 6) | tb;
+  x = (x << 12) | x;  // bits 2e..2e+1 of tb at bits 8e..8e+1
+  reg[15] = x & 0x03030303u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    op[q] = i32x4{(int)reg[4 * q], (int)reg[4 * q + 1], (int)reg[4 * q + 2], (int)reg[4 * q + 3]};
+}
+
+template <int TT, int S, int GPT, int D, bool L5>
 __global__ void __launch_bounds__(1024) tern_limb_kernel(
     const uint16_t* __restrict__ x, int T, int K, const u32x4* __restrict__ codes,
     const uint16_t* __restrict__ scales, float* __restrict__ y, int N, int Wn, int Wk) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   static_assert(GPT == 2 || GPT == 4, "G must be 128 or 64");
+  static_assert(!L5 || (TT == 1 && S == 1), "layout t5: one token, one strip per wave");
   constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,6 +141,8 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
   const int nsb = min(SB, NS - wstrip0);      // of which exist
   int* dexp = (int*)(smem + (size_t)NR * rs);  // [T][KT]
   char* lsc = smem + (size_t)NR * rs + (size_t)T * KT * 4;  // [SB][KT][16][GPT] fp16
+  // t5: per scale group {-S0, -S1, -S2, 0}, S_L the sum of limb L over the group
+  int* gbias = (int*)(lsc + (size_t)SB * KT * 16 * GPT * 2);  // [KT * GPT][4]
 
   const rsrc_t xr = make_rsrc(x, (uint32_t)T * K * 2);
   // The workgroup's scales, 16-byte chunks (2*GPT per strip and k-tile).
@@ -130,15 +174,27 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
   // 2. Weight prefetch ring: the first D - 1 k-tiles of this wave's strips.
   //    (The codes are read once: non-temporal.)
   const int sclamp = max(min(strip0, NS - 1), 0);
-  const rsrc_t crs = make_rsrc(codes + (size_t)sclamp * KT * 64, (uint32_t)max(nstrips, 0) * KT * 1024);
+  constexpr int kStripTileBytes = L5 ? 832 : 1024;  // code bytes per strip and k-tile
+  const rsrc_t crs = make_rsrc((const char*)codes + (size_t)sclamp * KT * kStripTileBytes,
+                               (uint32_t)max(nstrips, 0) * KT * kStripTileBytes);
   auto load = [&](LimbStage<S>& b, int i) {
     const int kt = __builtin_amdgcn_readfirstlane(min(kt0 + i, KT - 1));
-    const int cv = i < nkt ? lane * 16 : kOffPastEnd;
+    if constexpr (L5) {
+      // block of 4 k-tiles: 4 x 768 bytes of main words, then 256 bytes of tails
+      const int blk = (kt >> 2) * 3328;
+      const int cm = i < nkt ? lane * 12 : kOffPastEnd;
+      const int ct = i < nkt ? 3072 + lane * 4 : kOffPastEnd;
+      const auto m = __builtin_amdgcn_raw_buffer_load_b96(crs, cm, blk + 768 * (kt & 3), kAuxNontemporal);
+      const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(crs, ct, blk, 0);  // shared by 4 k-tiles
+      b.P[0] = u32x4{m[0], m[1], m[2], t};
+    } else {
+      const int cv = i < nkt ? lane * 16 : kOffPastEnd;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int se = max(min(s, nstrips - 1), 0);
-      b.P[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             crs, cv, (se * KT + kt) * 1024, kAuxNontemporal));
+      for (int s = 0; s < S; ++s) {
+        const int se = max(min(s, nstrips - 1), 0);
+        b.P[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               crs, cv, (se * KT + kt) * 1024, kAuxNontemporal));
+      }
     }
   };
   LimbStage<S> ring[D];
@@ -166,6 +222,26 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
       const int t = c / KC16, j = c - t * KC16;
       u32x4 out0, out1, out2;
       limb_chunk(lo, hi, d, out0, out1, out2);
+      if constexpr (L5) {
+        // limb sums of the chunk, then of its scale group (8 or 4 chunks,
+        // consecutive lanes of the DPP row): S_L = sum of limb L over the group
+        int sl[3] = {0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sl[0] = __builtin_amdgcn_sdot4((int)out0[e], 0x01010101, sl[0], false);
+          sl[1] = __builtin_amdgcn_sdot4((int)out1[e], 0x01010101, sl[1], false);
+          sl[2] = __builtin_amdgcn_sdot4((int)out2[e], 0x01010101, sl[2], false);
+        }
+#pragma unroll
+        for (int L = 0; L < 3; ++L) {
+          sl[L] += __builtin_amdgcn_update_dpp(0, sl[L], 0xb1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+          sl[L] += __builtin_amdgcn_update_dpp(0, sl[L], 0x4e, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+          if (GPT == 2) sl[L] += __builtin_amdgcn_update_dpp(0, sl[L], 0x141, 0xf, 0xf, false);  // row_half_mirror
+        }
+        constexpr int kChunksPerGroup = 16 / GPT;
+        if ((j & (kChunksPerGroup - 1)) == 0)
+          *(i32x4*)(gbias + 4 * (j / kChunksPerGroup)) = i32x4{-sl[0], -sl[1], -sl[2], 0};
+      }
       char* row = smem + (size_t)(3 * t) * rs + 16 * j;
       *(u32x4*)row = out0;
       *(u32x4*)(row + rs) = out1;
@@ -216,7 +292,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
     // L = row mod 3) so that every partial sum carries its true magnitude.
     int dsh[4];
     if (TT == 1) {
-      dsh[0] = dexp[kt] - 6;
+      dsh[0] = dexp[kt] - (L5 ? 0 : 6);  // the 2-bit operands carry 64 w
     } else if (TL) {
       dsh[0] = dexp[min(g, T - 1) * KT + kt] - 6;
       if (RB == 2) dsh[1] = dexp[min(g + 4, T - 1) * KT + kt] - 6;
@@ -224,6 +300,8 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) dsh[e] = dexp[tok[e] * KT + kt] - 6 + 8 * ((4 * g + e) % 3);
     }
+    i32x4 op5[4];
+    if constexpr (L5) t5_operands(b.P[0], kt & 3, op5);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const u32x4 P = b.P[s];
@@ -240,10 +318,11 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
         i32x4 acc = i32x4{0, 0, 0, 0}, acc1 = acc;
+        if constexpr (L5) acc = *(const i32x4*)(gbias + 4 * (kt * GPT + gi));  // minus the limb sums
 #pragma unroll
         for (int kk = 0; kk < KBPG; ++kk) {
           const int q = gi * KBPG + kk;
-          const i32x4 bq = weights_operand_i8(P[q]);
+          const i32x4 bq = L5 ? op5[q] : weights_operand_i8(P[q]);
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[q], bq, acc, 0, 0, 0);
           if (RB == 2) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[q], bq, acc1, 0, 0, 0);
         }
@@ -363,7 +442,7 @@ __global__ void __launch_bounds__(1024) tern_limb_kernel(
   }
 }
 
-template <int TT, int S, int GPT>
+template <int TT, int S, int GPT, bool L5 = false>
 hipError_t launch_limb_g(const SmallTArgs& a, const LimbPlan& p, hipStream_t st) {
   const int NS = a.N / 16;
   dim3 grid((NS + p.wn * S - 1) / (p.wn * S));
@@ -372,7 +451,7 @@ hipError_t launch_limb_g(const SmallTArgs& a, const LimbPlan& p, hipStream_t st)
   switch (p.depth) {
 #define TERN_LIMB_LAUNCH(D)                                                                        \
   case D:                                                                                          \
-    hipLaunchKernelGGL((tern_limb_kernel<TT, S, GPT, D>), grid, block, lds, st, a.x, a.T, a.K,     \
+    hipLaunchKernelGGL((tern_limb_kernel<TT, S, GPT, D, L5>), grid, block, lds, st, a.x, a.T, a.K, \
                        (const u32x4*)a.codes, a.scales, a.y, a.N, p.wn, p.wk);                     \
     break;
     TERN_LIMB_LAUNCH(2)
@@ -383,7 +462,8 @@ hipError_t launch_limb_g(const SmallTArgs& a, const LimbPlan& p, hipStream_t st)
   }
   // the gemv rung (any T <= 5, limbs made per k-tile) or the resident small-T plan
   return (hipError_t)kernel_launched((int)hipGetLastError(),
-                                     p.resident ? TERN_KERNEL_SMALLT_RESIDENT : TERN_KERNEL_GEMV_LIMB);
+                                     L5 ? TERN_KERNEL_GEMV_T5
+                                        : p.resident ? TERN_KERNEL_SMALLT_RESIDENT : TERN_KERNEL_GEMV_LIMB);
 }
 
 template <int TT, int S>
@@ -404,7 +484,8 @@ hipError_t launch_limb_t(const SmallTArgs& a, const LimbPlan& p, hipStream_t st)
 
 int limb_lds_bytes(int T, int K, int G, const LimbPlan& p) {
   const size_t SB = (size_t)p.wn * p.strips_per_wave;
-  const size_t main = (size_t)3 * T * (K + 64) + (size_t)T * (K / 256) * 4 + SB * (K / 256) * 16 * (256 / G) * 2;
+  const size_t main = (size_t)3 * T * (K + 64) + (size_t)T * (K / 256) * 4 + SB * (K / 256) * 16 * (256 / G) * 2 +
+                      (p.t5 ? (size_t)(K / G) * 16 : 0);
   const size_t red = (size_t)p.wk * SB * 256 * 4;
   return (int)std::max(main, red);
 }
@@ -412,6 +493,12 @@ int limb_lds_bytes(int T, int K, int G, const LimbPlan& p) {
 int launch_limb(const SmallTArgs& a, const LimbPlan& p, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int W = p.wn * p.wk;
+  if (p.t5) {  // base-3 weights: the single-token gemv, one strip per wave
+    if (a.T != 1 || p.strips_per_wave != 1 || p.token_lanes || p.resident || a.K % 1024 != 0 || p.wn < 1 ||
+        p.wk < 1 || W > 16 || limb_lds_bytes(1, a.K, a.G, p) > kLimbMaxLds)
+      return (int)hipErrorInvalidValue;
+    return (int)(a.G == 128 ? launch_limb_g<1, 1, 2, true>(a, p, st) : launch_limb_g<1, 1, 4, true>(a, p, st));
+  }
   if (a.T < 1 || a.T > (p.token_lanes ? 8 : 5) || p.wn < 1 || p.wk < 1 || W > 16) return (int)hipErrorInvalidValue;
   if (limb_lds_bytes(a.T, a.K, a.G, p) > (p.token_lanes || p.resident ? kLimbMaxLdsResident : kLimbMaxLds))
     return (int)hipErrorInvalidValue;

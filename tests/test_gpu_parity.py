@@ -54,7 +54,7 @@ def rung_ok(rung, T):
 def check_kernels(tl, T, W, rung):
     """The kernels the last call launched are the ones the dispatcher's dry
     run names for it, each launched once (kernel probe and per-call set)."""
-    plan = tl.plan_kernels(T, W.n, W.k, W.group, rung)
+    plan = tl.plan_kernels(T, W.n, W.k, W.group, rung, layout=W.layout)
     assert tl.last_kernels() == plan, (T, W.n, W.k, rung, tl.last_kernels(), plan)
     snap = tl.kernel_probe_snapshot()
     assert {k: v for k, v in snap.items() if v} == {k: 1 for k in plan}, snap
@@ -907,3 +907,63 @@ def test_fused_qkv_prefill_chunk_sampled(tl, torch, qkv, rung):
     else:
         ref = oracle.linear_bf16(xbits, w[rows], s[rows])
         assert rel_l2(y[:, rows], ref) <= 1e-6
+
+
+# ------------------------------------------------------ base-3 layout t5
+
+
+@pytest.mark.parametrize("n,k,G", [(64, 1024, 128), (128, 2048, 64), (16 * 1100, 1024, 128),
+                                   (16 * 2176, 5120, 128), (5120, 17408, 128)])
+def test_t5_gemv_exact(tl, torch, n, k, G):
+    """The gemv on base-3 weights: integer activations and power-of-two
+    scales make every step exact, so y must equal the oracle bit for bit;
+    narrow (K split over waves) and wide plans, a ragged last workgroup,
+    both group sizes. Rows sampled on the two large shapes."""
+    rng = np.random.default_rng(n + k + G)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.pow2_scales(n, k, G, seed=n + 3)
+    W = tl.TernaryWeights.from_host(w, s, layout="t5")
+    xbits = ts.integer_activations(k, 1, seed=k + 9)
+    print("t5 gemv", n, k, G, flush=True)
+    y = run(tl, torch, to_dev_bf16(torch, xbits), W, "auto")
+    assert tl.last_kernels() == ["gemv_t5"]
+    rows = np.arange(n) if n * k <= 64 * 2**20 else sample_rows(n, n, n=256)
+    ref = oracle.linear_bf16(xbits, w[rows], s[rows])
+    assert np.array_equal(y[:, rows].astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("shape", [ts.GATE_UP, ts.DOWN])
+def test_t5_gemv_decode_full_rows(tl, torch, big, shape):
+    """Decode at T = 1 from t5 weights on the 27B-class shapes: every output
+    within the gate (and within 1e-6 of the fp64 oracle, as the 2-bit gemv)."""
+    wts, _ = big(shape)
+    W = tl.TernaryWeights.from_host(wts.w, wts.s, layout="t5")
+    xbits = ts.activations(wts, 1)
+    y = run(tl, torch, to_dev_bf16(torch, xbits), W, "gemv")
+    ref = oracle.linear_bf16(xbits, wts.w, wts.s)
+    assert rel_l2(y, ref) <= 1e-6
+    del W
+
+
+@pytest.mark.parametrize("case", ["outliers", "subnormal", "wide", "huge"])
+def test_t5_gemv_activation_range(tl, torch, case):
+    """The per-element bound of test_bf16_rungs_activation_range for the t5
+    gemv (the same 22-bit fixed point per k-tile)."""
+    n, k, G, T = 256, 2048, 128, 1
+    rng = np.random.default_rng(["outliers", "subnormal", "wide", "huge"].index(case) + 91)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.draw_scales(rng, n, k, G)
+    xb = _range_case(case, 2, k, rng)[1:2].copy()
+    W = tl.TernaryWeights.from_host(w, s, layout="t5")
+    ref = oracle.linear_bf16(xb, w, s)
+    xf = ts.bf16_bits_to_f32(xb).astype(np.float64)
+    sw = np.abs(w.astype(np.float64) * np.repeat(ts.f16_bits_to_f32(s).astype(np.float64), G, axis=1))
+    tmax = np.abs(xf).reshape(T, k // 256, 256).max(axis=2)
+    swt = sw.reshape(n, k // 256, 256).sum(axis=2)
+    bound = 2.0 ** -16 * (np.abs(xf) @ sw.T) + 2.0 ** -22 * (tmax @ swt.T)
+    y = run(tl, torch, to_dev_bf16(torch, xb), W, "gemv").astype(np.float64)
+    assert np.all(np.isfinite(y))
+    assert np.all(np.abs(y - ref) <= bound), float((np.abs(y - ref) / np.maximum(bound, 1e-300)).max())
+    # an all-zero row gives zeros
+    z = run(tl, torch, to_dev_bf16(torch, np.zeros((1, k), np.uint16)), W, "gemv")
+    assert np.all(z == 0)

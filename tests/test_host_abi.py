@@ -381,3 +381,81 @@ def test_kernel_probe_starts_empty_and_names_every_kernel(tl):
     assert L.tern_kernel_name(len(tl.KERNELS)).decode() == "invalid"
     src = open(HEADER).read()
     assert len(re.findall(r"^\s+TERN_KERNEL_[A-Z0-9_]+(?: = 0)?,", src, re.M)) == len(tl.KERNELS)
+
+
+# ------------------------------------------------------ base-3 layout t5
+
+
+@pytest.mark.parametrize("n,k,G", [(16, 1024, 128), (32, 2048, 64), (48, 3072, 128)])
+def test_pack_t5_roundtrip_and_independent_reader(tl, n, k, G):
+    rng = np.random.default_rng(n * 7 + k)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.draw_scales(rng, n, k, G)
+    codes, sp = tl.pack(w, s, layout="t5")
+    assert codes.size == n * (k // 1024) * 208 == tl.lib().tern_packed_code_bytes_t5(n, k)
+    assert codes.size * 64 == n * k * 13 // 4 * 4  # 13 bytes per 64 weights
+    w2, s2 = tl.unpack(codes, sp, n, k, G, layout="t5")
+    assert np.array_equal(w2, w) and np.array_equal(s2, s)
+    w3, s3 = oracle.unpack_layout_t5(codes, sp, n, k, G)
+    assert np.array_equal(w3, w) and np.array_equal(s3, s)
+    # the scales are re-laid exactly as for v1
+    assert np.array_equal(sp, tl.pack(w, s)[1])
+
+
+def test_pack_t5_hand_bytes(tl):
+    """tern_pack_t5 writes the hand-worked bytes of the golden file."""
+    with open(os.path.join(ROOT, "tests", "golden", "hand_cases.json")) as f:
+        c = json.load(f)["layout_t5"]
+    N, K, G = c["N"], c["K"], c["G"]
+    s = np.zeros((N, K // G), np.uint16)
+    zero, _ = tl.pack(np.zeros((N, K), np.int8), s, layout="t5")
+    blocks = zero.reshape(-1, 3328)
+    assert np.all(blocks[:, :3072] == int(c["zero_main"], 16)) and np.all(blocks[:, 3072:] == int(c["zero_tail"], 16))
+    for case in c["cases"]:
+        w = np.zeros((N, K), np.int8)
+        w[case["n"], case["k"]] = case["w"]
+        codes, _ = tl.pack(w, s, layout="t5")
+        diff = np.flatnonzero(codes != zero)
+        assert diff.tolist() == [case["byte"]], case["derivation"]
+        assert codes[case["byte"]] == int(case["value"], 16), case["derivation"]
+
+
+def test_t5_rejects_bad_input(tl):
+    L = tl.lib()
+    s = np.zeros((16, 8), np.uint16)
+    with pytest.raises(tl.TernError):  # K not a multiple of 1024
+        tl.pack(np.zeros((16, 512), np.int8), np.zeros((16, 4), np.uint16), layout="t5")
+    w = np.zeros((16, 1024), np.int8)
+    w[3, 5] = 2
+    with pytest.raises(tl.TernError):
+        tl.pack(w, s, layout="t5")
+    codes, sp = tl.pack(np.zeros((16, 1024), np.int8), s, layout="t5")
+    bad = codes.copy()
+    bad[7] = 1  # not ceil(256 v / 243) of any v
+    with pytest.raises(tl.TernError):
+        tl.unpack(bad, sp, 16, 1024, 128, layout="t5")
+    bad = codes.copy()
+    bad[3072] = 0x57  # tail trit 3
+    with pytest.raises(tl.TernError):
+        tl.unpack(bad, sp, 16, 1024, 128, layout="t5")
+    assert L.tern_packed_code_bytes_t5(16, 1536) == 0
+
+
+def test_t5_dispatch(tl):
+    """t5 weights run the gemv rung only; any other rung is an error, never a
+    fallback."""
+    import ctypes
+    assert tl.plan_kernels(1, 34816, 5120, 128, layout="t5") == ["gemv_t5"]
+    assert tl.plan_kernels(1, 5120, 17408, 128, "gemv", layout="t5") == ["gemv_t5"]
+    for T, rung in ((4, "auto"), (1, "small_t"), (20, "auto"), (1, "s8")):
+        with pytest.raises(tl.TernError) as e:
+            tl.plan_kernels(T, 34816, 5120, 128, rung, layout="t5")
+        assert "layout t5" in str(e.value)
+    with pytest.raises(tl.TernError):
+        tl.plan_kernels(1, 5120, 5376, 128, layout="t5")  # K % 1024
+    W = tl._Weights(0x100000, 0x200000, 5120, 5120, 128, tl.LAYOUT_T5)
+    st = tl.lib().tern_linear(0x400000, 4, ctypes.byref(W), 0x300000, 0, None, 0, None)
+    assert tl.STATUS[st] == "TERN_ERR_LAYOUT"
+    W = tl._Weights(0x100000, 0x200000, 5120, 5376, 128, tl.LAYOUT_T5)
+    st = tl.lib().tern_linear(0x400000, 1, ctypes.byref(W), 0x300000, 0, None, 0, None)
+    assert tl.STATUS[st] == "TERN_ERR_SHAPE"
