@@ -109,6 +109,26 @@ def graph_time(torch, fn, steps, warmup):
     return start.elapsed_time(end) * 1e-3
 
 
+def event_time(torch, fn, reps, warmup=2):
+    """Seconds per call of fn() (one launch each), timed between events on
+    the current stream over `reps` calls after `warmup` untimed ones."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) * 1e-3 / reps
+
+
+def dec_bytes_of(layers):
+    return sum(algorithmic_bytes(1, b.n, b.k, b.group) for L in layers for b in L)
+
+
 def graph_batches(torch, fn, warmup, per=50, batches=20):
     """The spread of per-step times: a graph of `per` steps captured once and
     replayed `batches` times, each replay between its own events (so each
@@ -304,6 +324,34 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
 
     t_dec = graph_time(torch, decode_pass, decode_reps, 1) / decode_reps
     ops = sum(2 * 2048 * b.n * b.k for L in layers for b in L)
+
+    # The same decode pass as one persistent launch (tern_linear_chain). As
+    # the stack is defined here every projection reads its own synthetic x, so
+    # the chain needs no waits; a second chain adds the waits a layer would
+    # have if outputs were chained (q, k, v after the previous layer's down,
+    # o after v, gate and up after o, down after up): each is a device-wide
+    # drain.
+    def chain_items(Ls, xs, ys, deps):
+        items = []
+        for L in Ls:
+            base = len(items)
+            for j, b in enumerate(L):
+                d = deps[j]
+                after = -1 if d is None else (base + d if d >= 0 else (base - 1 if base > 0 else -1))
+                items.append((b, xs[j], ys[j], None, after))
+        return items
+
+    # offsets within a layer (-1: the previous layer's last item; None: no wait)
+    ch = tl.Chain(chain_items(layers, xs1, y1, [None] * 7), device=dev)
+    t_chain = event_time(torch, ch.run, decode_reps)
+    assert not ch.failed()
+    del ch
+    ch = tl.Chain(chain_items(layers, xs1, y1, [-1, -1, -1, 2, 3, 3, 5]), device=dev)
+    t_chain_w = event_time(torch, ch.run, decode_reps)
+    assert not ch.failed()
+    del ch
+    log(f"stack decode pass as one chain launch: {t_chain * 1e3:.3f} ms ({dec_bytes_of(layers) / t_chain / 1e9:.0f} GB/s); "
+        f"with the layer's 4 waits: {t_chain_w * 1e3:.3f} ms ({dec_bytes_of(layers) / t_chain_w / 1e9:.0f} GB/s)")
     t_pre = graph_time(torch, prefill_pass, prefill_reps, 1) / prefill_reps
     dec_bytes = sum(algorithmic_bytes(1, b.n, b.k, b.group) for L in layers for b in L)
     log(f"stack decode pass {t_dec * 1e3:.3f} ms ({dec_bytes / t_dec / 1e9:.0f} GB/s), "
@@ -346,15 +394,28 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
                     tl.linear(fxp[j][1024 * c:1024 * (c + 1)], b, y=fyp[j], workspace=fwsp)
 
     f_dec = graph_time(torch, fdecode_pass, decode_reps, 1) / decode_reps
+    fch = tl.Chain(chain_items(flayers, fx1, fy1, [None] * 4), device=dev)
+    f_chain = event_time(torch, fch.run, decode_reps)
+    assert not fch.failed()
+    del fch
     f_pre = graph_time(torch, fprefill_pass, prefill_reps, 1) / prefill_reps
     f_bytes = sum(algorithmic_bytes(1, b.n, b.k, b.group) for L in flayers for b in L)
     log(f"stack, fused q|k|v and gate|up: decode pass {f_dec * 1e3:.3f} ms "
-        f"({f_bytes / f_dec / 1e9:.0f} GB/s), prefill pass {f_pre * 1e3:.2f} ms ({ops / f_pre / 1e12:.0f} TOPS)")
+        f"({f_bytes / f_dec / 1e9:.0f} GB/s; one chain launch {f_chain * 1e3:.3f} ms, "
+        f"{f_bytes / f_chain / 1e9:.0f} GB/s), prefill pass {f_pre * 1e3:.2f} ms ({ops / f_pre / 1e12:.0f} TOPS)")
     return {"workload": "64-layer stack, 448 projections (6.33 GB packed); decode T=1 pass; "
                         "2048-token prefill in two 1024-token chunks (s8)",
             "decode": {"ms_per_pass": round(t_dec * 1e3, 4), "GB/s": round(dec_bytes / t_dec / 1e9, 1),
                        "frac_of_hbm_peak": round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4),
                        "launches": ts.STACK_LAYERS * len(base)},
+            "decode_chain": {"ms_per_pass": round(t_chain * 1e3, 4), "GB/s": round(dec_bytes / t_chain / 1e9, 1),
+                             "frac_of_hbm_peak": round(dec_bytes / t_chain / 1e9 / HBM_PEAK_GBS, 4),
+                             "launches": 1,
+                             "kernel": "tern_chain_kernel: the 448 projections in one persistent launch"},
+            "decode_chain_with_layer_waits": {
+                "ms_per_pass": round(t_chain_w * 1e3, 4), "GB/s": round(dec_bytes / t_chain_w / 1e9, 1),
+                "waits": 4 * ts.STACK_LAYERS,
+                "note": "q, k, v after the previous layer's down; o after v; gate, up after o; down after up"},
             "prefill": {"ms_per_pass": round(t_pre * 1e3, 3), "TOPS": round(ops / t_pre / 1e12, 1),
                         "frac_of_i8_peak": round(ops / t_pre / 1e12 / I8_PEAK_TOPS, 4),
                         "tokens_per_s": round(2048 / t_pre, 1)},
@@ -362,6 +423,9 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
                 "launches_per_pass": ts.STACK_LAYERS * len(groups),
                 "decode": {"ms_per_pass": round(f_dec * 1e3, 4), "GB/s": round(f_bytes / f_dec / 1e9, 1),
                            "frac_of_hbm_peak": round(f_bytes / f_dec / 1e9 / HBM_PEAK_GBS, 4)},
+                "decode_chain": {"ms_per_pass": round(f_chain * 1e3, 4), "GB/s": round(f_bytes / f_chain / 1e9, 1),
+                                 "frac_of_hbm_peak": round(f_bytes / f_chain / 1e9 / HBM_PEAK_GBS, 4),
+                                 "launches": 1},
                 "prefill": {"ms_per_pass": round(f_pre * 1e3, 3), "TOPS": round(ops / f_pre / 1e12, 1),
                             "tokens_per_s": round(2048 / f_pre, 1)}}}
 

@@ -298,6 +298,68 @@ tern_status tern_linear_noalloc(const void* x_bf16, int T, const tern_weights* W
                                 tern_rung rung, void* stream);
 
 /*
+ * A whole decode pass in one launch: a chain of T = 1 projections (the gemv
+ * rung's arithmetic, bit-identical results) run by one persistent,
+ * cooperatively launched kernel, so the next projection's codes stream
+ * while the previous one drains, instead of each launch paying its own ramp
+ * and tail ("NINFER ternary perf-tuning" notes, section 6: a decode round is
+ * one graph of about 1224 kernels; "NInfer sm_89 fork" article, section 9
+ * item 5: each decode round replayed as one graph).
+ *
+ * Dependencies: item i with after = j (j < i) reads its x only once items
+ * 0..j have all finished (their y and y_bf16 stores visible), e.g. x of item
+ * i = y_bf16 of item j; after = -1 reads x at any time. Completion goes
+ * through device-scope counters in caller memory (release / acquire); every
+ * wait polls at most spin_limit times (each poll sleeps about 0.05 us plus
+ * a memory round trip), then sets *error_flag = 1 and the rest of the chain
+ * is skipped: the kernel always exits, and the results are then undefined.
+ */
+typedef struct {
+  tern_weights W;   /* layout v1; every item of a chain has the same group size */
+  const void* x;    /* device bf16 [K], 16-byte aligned */
+  float* y;         /* device fp32 [N], 16-byte aligned; fully overwritten */
+  uint16_t* y_bf16; /* device bf16 [N] or NULL: y rounded to nearest even (finite y) */
+  int32_t after;    /* -1, or j < the item's index: x is read once items 0..j are done */
+} tern_chain_item;
+
+/* Host-side summary of a built chain, filled by tern_chain_build. */
+typedef struct {
+  int32_t count;      /* items */
+  int32_t group;      /* their group size */
+  int32_t workgroups; /* cooperative workgroups of the launch (one per CU) */
+  int32_t lds_bytes;  /* dynamic LDS per workgroup */
+} tern_chain_plan;
+
+/* Device bytes of the chain table for these items (their plans and work
+ * lists), 0 if the chain is invalid (tern_last_error says why). */
+size_t tern_chain_table_bytes(const tern_chain_item* items, int count);
+/* Device bytes of the completion counters of `count` items (count + 1 ints). */
+size_t tern_chain_counter_bytes(int count);
+/*
+ * Validates the chain (host), plans every item as the gemv rung plans it,
+ * gives one workgroup per CU of the current device a list of work units,
+ * balanced between the waits, and writes the table (device memory,
+ * tern_chain_table_bytes(items, count), 16-byte aligned) with one
+ * synchronous host-to-device copy. Build once per set of
+ * buffers; the table holds the pointers of items[]. Errors: TERN_ERR_NULL,
+ * TERN_ERR_SHAPE (count < 1, shapes, mixed group sizes, LDS), TERN_ERR_VALUE
+ * (after out of range), TERN_ERR_LAYOUT, TERN_ERR_ALIGN, TERN_ERR_WORKSPACE
+ * (table too small), TERN_ERR_HIP (device query or copy).
+ */
+tern_status tern_chain_build(const tern_chain_item* items, int count, void* table, size_t table_bytes,
+                             tern_chain_plan* plan);
+/*
+ * Runs a built chain (device, async, one cooperative launch). counters:
+ * device, tern_chain_counter_bytes(count), zeroed before the first call and
+ * left zeroed by every call (the last workgroup out clears them); calls that
+ * share counters must not overlap. error_flag: device int32, set to 1 if a
+ * wait gave up (the caller zeroes it). spin_limit >= 1. TERN_ERR_HIP if the
+ * cooperative launch is refused.
+ */
+tern_status tern_linear_chain(const tern_chain_plan* plan, const void* table, void* counters,
+                              size_t counter_bytes, int32_t* error_flag, int spin_limit, void* stream);
+
+/*
  * The s8 rung's contraction on activations already quantised by
  * tern_quant_act_s8 (device, async): y[t][n] = scale_t * sum_g s[n][g] *
  * acc[t][n][g] in fp32, groups ascending -- the same kernel and numerics as
@@ -377,6 +439,7 @@ typedef enum {
   TERN_KERNEL_S8_ACC_EXPORT,      /* tern_debug_s8_acc */
   TERN_KERNEL_STREAM_READ,        /* tern_stream_read */
   TERN_KERNEL_GEMV_T5,            /* gemv on base-3 (t5) weights: limbs of x on the i8 matrix cores */
+  TERN_KERNEL_CHAIN,              /* tern_linear_chain: a chain of T = 1 projections in one launch */
   TERN_KERNEL_COUNT
 } tern_kernel;
 

@@ -47,7 +47,7 @@ STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_AL
 KERNELS = ("quant_s8", "quant_s8_row", "quant_s8_rot", "gemv_limb", "gemv_bf16",
            "smallt_resident", "smallt_limb_fused", "smallt_limb_prep", "smallt_limb_tile",
            "smallt_wave", "smallt_tile", "smallt_tile_reduce", "b16_prefill", "s8_mma",
-           "s8_reduce", "s8_row", "s8_acc_export", "stream_read", "gemv_t5")
+           "s8_reduce", "s8_row", "s8_acc_export", "stream_read", "gemv_t5", "chain")
 
 # Symbols declared in include/tern.h (checked by the host tests).
 EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpack",
@@ -57,7 +57,8 @@ EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpa
            "tern_rung_name", "tern_last_error", "tern_abi_version",
            "tern_kernel_probe_snapshot", "tern_last_kernels", "tern_kernel_name",
            "tern_plan_kernels", "tern_linear_noalloc", "tern_packed_code_bytes_t5", "tern_pack_t5",
-           "tern_unpack_t5")
+           "tern_unpack_t5", "tern_chain_table_bytes", "tern_chain_counter_bytes", "tern_chain_build",
+           "tern_linear_chain")
 
 
 class TernError(RuntimeError):
@@ -70,6 +71,16 @@ class TernError(RuntimeError):
 class _Weights(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("n", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("group", ctypes.c_int32), ("layout", ctypes.c_uint32)]
+
+
+class _ChainItem(ctypes.Structure):
+    _fields_ = [("W", _Weights), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("y_bf16", ctypes.c_void_p), ("after", ctypes.c_int32)]
+
+
+class _ChainPlan(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("group", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32)]
 
 
 _lib = None
@@ -112,6 +123,10 @@ def lib() -> ctypes.CDLL:
         "tern_pack_t5": (st, [p, p, i, i, i, p, p]),
         "tern_unpack_t5": (st, [p, p, i, i, i, p, p]),
         "tern_linear_noalloc": (st, [p, i, ctypes.POINTER(_Weights), p, i, p]),
+        "tern_chain_table_bytes": (sz, [ctypes.POINTER(_ChainItem), i]),
+        "tern_chain_counter_bytes": (sz, [i]),
+        "tern_chain_build": (st, [ctypes.POINTER(_ChainItem), i, p, sz, ctypes.POINTER(_ChainPlan)]),
+        "tern_linear_chain": (st, [ctypes.POINTER(_ChainPlan), p, p, sz, p, i, p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -445,3 +460,49 @@ def debug_s8_acc(q, W: TernaryWeights, acc=None, stream=None, layout="row_major"
                                    _stream(stream)))
     _keep_for(stream, acc if new_acc else None)
     return acc
+
+
+class Chain:
+    """A chain of T = 1 projections run by one persistent launch
+    (tern_linear_chain). items: (W, x, y, y_bf16 or None, after) tuples of
+    device tensors (x bf16 [1, K] or [K], y float32 [1, N], y_bf16 bf16 [1, N]);
+    after = -1 or the index j of an earlier item: x is read once items 0..j are
+    done. The table is built once; run() enqueues the whole chain."""
+
+    def __init__(self, items, device="cuda"):
+        torch = _torch()
+        self._keep = []
+        arr = (_ChainItem * len(items))()
+        for i, (W, x, y, yb, after) in enumerate(items):
+            _dev(x, torch.bfloat16, "x")
+            _dev(y, torch.float32, "y")
+            if yb is not None:
+                _dev(yb, torch.bfloat16, "y_bf16")
+            arr[i].W = W._struct
+            arr[i].x = x.data_ptr()
+            arr[i].y = y.data_ptr()
+            arr[i].y_bf16 = yb.data_ptr() if yb is not None else None
+            arr[i].after = int(after)
+            self._keep += [W, x, y, yb]
+        n = len(items)
+        self.count = n
+        tb = lib().tern_chain_table_bytes(arr, n)
+        if tb == 0:
+            raise TernError(2, lib().tern_last_error().decode())
+        self.table = torch.empty((tb,), dtype=torch.uint8, device=device)
+        cb = lib().tern_chain_counter_bytes(n)
+        self.counters = torch.zeros((cb // 4,), dtype=torch.int32, device=device)
+        self.error_flag = torch.zeros((1,), dtype=torch.int32, device=device)
+        self.plan = _ChainPlan()
+        torch.cuda.synchronize()
+        _check(lib().tern_chain_build(arr, n, self.table.data_ptr(), self.table.numel(),
+                                      ctypes.byref(self.plan)))
+
+    def run(self, spin_limit: int = 1 << 20, stream=None):
+        _check(lib().tern_linear_chain(ctypes.byref(self.plan), self.table.data_ptr(),
+                                       self.counters.data_ptr(), self.counters.numel() * 4,
+                                       self.error_flag.data_ptr(), int(spin_limit), _stream(stream)))
+
+    def failed(self) -> bool:
+        """True if a wait gave up (synchronises on the flag)."""
+        return bool(self.error_flag.item())

@@ -16,8 +16,11 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <mutex>
+#include <queue>
 #include <string>
+#include <vector>
 
 #include "../../include/tern.h"
 #include "tern_internal.h"
@@ -47,8 +50,8 @@ const char* const kKernelNames[TERN_KERNEL_COUNT] = {
     "quant_s8",        "quant_s8_row",      "quant_s8_rot",   "gemv_limb",        "gemv_bf16",
     "smallt_resident", "smallt_limb_fused", "smallt_limb_prep", "smallt_limb_tile", "smallt_wave",
     "smallt_tile",     "smallt_tile_reduce", "b16_prefill",   "s8_mma",           "s8_reduce",
-    "s8_row",          "s8_acc_export",     "stream_read",    "gemv_t5"};
-static_assert(TERN_KERNEL_COUNT == 19, "one name per kernel id");
+    "s8_row",          "s8_acc_export",     "stream_read",    "gemv_t5",          "chain"};
+static_assert(TERN_KERNEL_COUNT == 20, "one name per kernel id");
 
 // ------------------------------------------------------------ configuration
 
@@ -993,6 +996,162 @@ tern_status tern_unpack_t5(const void* codes, const uint16_t* scales_packed, int
           for (size_t gi = 0; gi < GPT; ++gi)
             scales_out[(s * 16 + r) * NG + kt * GPT + gi] = scales_packed[((s * KT + kt) * 16 + r) * GPT + gi];
   return ok();
+}
+
+size_t tern_chain_counter_bytes(int count) { return count < 1 ? 0 : (size_t)(count + 1) * sizeof(int32_t); }
+
+}  // extern "C"
+
+namespace {
+
+// Plans of a chain's items (the gemv's), validated: the shared part of
+// tern_chain_table_bytes and tern_chain_build.
+tern_status chain_plan_items(const tern_chain_item* items, int count, std::vector<tern::ChainEntry>& t, int* lds_out) {
+  if (!items) return fail(TERN_ERR_NULL, "chain: items is NULL");
+  if (count < 1 || count > (1 << 20)) return fail(TERN_ERR_SHAPE, "chain: count=%d", count);
+  const Config& c = config();
+  if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
+  t.assign((size_t)count, tern::ChainEntry{});
+  const int group = items[0].W.group;
+  int lds = 0;
+  for (int i = 0; i < count; ++i) {
+    const tern_chain_item& it = items[i];
+    tern_status st = check_weights(&it.W);
+    if (st != TERN_OK) return fail(st, "chain item %d: %s", i, g_last_error.c_str());
+    if (it.W.layout != TERN_LAYOUT_V1) return fail(TERN_ERR_LAYOUT, "chain item %d: layout v1 only", i);
+    if (it.W.group != group) return fail(TERN_ERR_SHAPE, "chain item %d: group %d, item 0 has %d", i, it.W.group, group);
+    if (!it.x || !it.y) return fail(TERN_ERR_NULL, "chain item %d: x or y is NULL", i);
+    if (!aligned16(it.x) || !aligned16(it.y) || ((uintptr_t)it.y_bf16 & 3u))
+      return fail(TERN_ERR_ALIGN, "chain item %d: x and y 16-byte, y_bf16 4-byte aligned", i);
+    if (it.after < -1 || it.after >= i) return fail(TERN_ERR_VALUE, "chain item %d: after=%d", i, it.after);
+    tern::LimbPlan p = plan_limb(1, it.W.n, it.W.k);
+    if (p.wn * p.wk > tern::kChainWaves || p.strips_per_wave != 1)
+      return fail(TERN_ERR_CONFIG, "chain item %d: plan of %d x %d waves exceeds %d", i, p.wn, p.wk, tern::kChainWaves);
+    const int l = tern::limb_lds_bytes(1, it.W.k, group, p);
+    if (l > tern::kLimbMaxLds)
+      return fail(TERN_ERR_SHAPE, "chain item %d: K=%d needs %d bytes of LDS (at most %d)", i, it.W.k, l, tern::kLimbMaxLds);
+    lds = std::max(lds, l);
+    tern::ChainEntry& e = t[(size_t)i];
+    e.codes = it.W.codes;
+    e.scales = it.W.scales;
+    e.x = (const uint16_t*)it.x;
+    e.y = it.y;
+    e.y_bf16 = it.y_bf16;
+    e.n = it.W.n;
+    e.k = it.W.k;
+    e.wn = p.wn;
+    e.wk = p.wk;
+    e.units = (it.W.n / 16 + p.wn - 1) / p.wn;
+    e.after = it.after;
+    e.signal = 0;
+  }
+  for (int i = 0; i < count; ++i)
+    if (t[(size_t)i].after >= 0) t[(size_t)t[(size_t)i].after].signal = 1;
+  *lds_out = lds;
+  return TERN_OK;
+}
+
+size_t chain_table_size(const std::vector<tern::ChainEntry>& t) {
+  size_t units = 0;
+  for (const auto& e : t) units += (size_t)e.units;
+  return t.size() * sizeof(tern::ChainEntry) + (tern::kChainMaxWorkgroups + 2) * sizeof(int32_t) +
+         units * 2 * sizeof(int32_t);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tern_chain_table_bytes(const tern_chain_item* items, int count) {
+  std::vector<tern::ChainEntry> t;
+  int lds = 0;
+  if (chain_plan_items(items, count, t, &lds) != TERN_OK) return 0;
+  return chain_table_size(t);
+}
+
+tern_status tern_chain_build(const tern_chain_item* items, int count, void* table, size_t table_bytes,
+                             tern_chain_plan* plan) {
+  if (!table || !plan) return fail(TERN_ERR_NULL, "tern_chain_build: NULL pointer");
+  std::vector<tern::ChainEntry> t;
+  int lds = 0;
+  tern_status st = chain_plan_items(items, count, t, &lds);
+  if (st != TERN_OK) return st;
+  const size_t need = chain_table_size(t);
+  if (table_bytes < need) return fail(TERN_ERR_WORKSPACE, "chain table needs %zu bytes, got %zu", need, table_bytes);
+  if (!aligned16(table)) return fail(TERN_ERR_ALIGN, "chain table must be 16-byte aligned");
+  const int dev_max = tern::chain_max_workgroups(lds);
+  if (dev_max <= 0) return hip_fail(-dev_max, "chain occupancy query");
+  int cus = 0;
+  const int cerr = tern::device_cu_count(&cus);
+  if (cerr) return hip_fail(cerr, "chain CU count");
+  const int P = std::min(std::min(dev_max, cus), tern::kChainMaxWorkgroups);  // one workgroup per CU
+  // Work lists: between two waits every workgroup starts together, so each
+  // unit goes to the least loaded workgroup of its stage (loads reset at a
+  // wait). Cost of a unit: its code bytes at one CU's share of the HBM rate
+  // plus the limb preparation of its K (rounds of 768 16-element chunks).
+  std::vector<std::vector<std::pair<int, int>>> lists((size_t)P);
+  using Slot = std::pair<double, int>;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  auto reset = [&]() {
+    heap = decltype(heap)();
+    for (int w = 0; w < P; ++w) heap.push({0.0, w});
+  };
+  reset();
+  for (int i = 0; i < count; ++i) {
+    const tern::ChainEntry& e = t[(size_t)i];
+    if (e.after >= 0) reset();
+    const int NS = e.n / 16;
+    const double prep = 0.5 + 0.6 * ((e.k / 16 + tern::kChainWaves * 64 - 1) / (tern::kChainWaves * 64));
+    for (int u = 0; u < e.units; ++u) {
+      const int nsb = std::min(e.wn, NS - u * e.wn);
+      const double cost = (double)nsb * 16.0 * e.k / 4.0 / 31.0e3 + prep;  // microseconds
+      Slot sl = heap.top();
+      heap.pop();
+      lists[(size_t)sl.second].push_back({i, u});
+      sl.first += cost;
+      heap.push(sl);
+    }
+  }
+  std::vector<char> blob(need, 0);
+  memcpy(blob.data(), t.data(), t.size() * sizeof(tern::ChainEntry));
+  int32_t* wg_begin = (int32_t*)(blob.data() + t.size() * sizeof(tern::ChainEntry));
+  int32_t* work = wg_begin + tern::kChainMaxWorkgroups + 2;
+  int32_t pos = 0;
+  for (int w = 0; w <= tern::kChainMaxWorkgroups + 1; ++w) {
+    wg_begin[w] = pos;
+    if (w < P)
+      for (const auto& pr : lists[(size_t)w]) {  // already in projection order
+        work[2 * pos] = pr.first;
+        work[2 * pos + 1] = pr.second;
+        ++pos;
+      }
+  }
+  const int err = tern::copy_to_device(table, blob.data(), blob.size());
+  if (err) return hip_fail(err, "chain table copy");
+  plan->count = count;
+  plan->group = items[0].W.group;
+  plan->workgroups = P;
+  plan->lds_bytes = lds;
+  return ok();
+}
+
+tern_status tern_linear_chain(const tern_chain_plan* plan, const void* table, void* counters,
+                              size_t counter_bytes, int32_t* error_flag, int spin_limit, void* stream) {
+  call_begin();
+  if (!plan || !table || !counters || !error_flag) return fail(TERN_ERR_NULL, "tern_linear_chain: NULL pointer");
+  if (plan->count < 1 || plan->workgroups < 1 || (plan->group != 64 && plan->group != 128) ||
+      plan->lds_bytes < 0 || plan->lds_bytes > tern::kLimbMaxLds)
+    return fail(TERN_ERR_VALUE, "tern_linear_chain: plan not from tern_chain_build");
+  if (counter_bytes < tern_chain_counter_bytes(plan->count))
+    return fail(TERN_ERR_WORKSPACE, "chain counters need %zu bytes, got %zu", tern_chain_counter_bytes(plan->count),
+                counter_bytes);
+  if (spin_limit < 1) return fail(TERN_ERR_VALUE, "spin_limit=%d must be at least 1", spin_limit);
+  if (!aligned16(table) || ((uintptr_t)counters & 3u) || ((uintptr_t)error_flag & 3u))
+    return fail(TERN_ERR_ALIGN, "table 16-byte, counters and error_flag 4-byte aligned");
+  const int err = tern::launch_chain((const tern::ChainEntry*)table, plan->count, plan->group, plan->workgroups,
+                                     plan->lds_bytes, (int*)counters, (int*)error_flag, spin_limit, stream);
+  if (err) return hip_fail(err, "chain launch");
+  return call_ok();
 }
 
 size_t tern_workspace_bytes(int T, int n, int k, int group, tern_rung rung) {

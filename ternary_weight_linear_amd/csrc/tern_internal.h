@@ -129,6 +129,36 @@ int launch_stream_read(const void* buf, size_t bytes, int depth, int waves_per_c
                        void* stream);
 const char* hip_error_string(int err);
 
+// One projection of a decode chain (tern_chain.hip) as its kernel reads it:
+// built on the host by tern_chain_build and copied to device memory once.
+struct ChainEntry {
+  const void* codes;       // layout v1
+  const uint16_t* scales;  // re-laid fp16 scales
+  const uint16_t* x;       // bf16 [K]
+  float* y;                // fp32 [N]
+  uint16_t* y_bf16;        // bf16 [N] or nullptr
+  int32_t n, k;
+  int32_t wn, wk;          // the gemv plan: wn strips per unit, wk K shares (wn * wk <= 12 waves)
+  int32_t units;           // ceil(N / 16 / wn)
+  int32_t pad;
+  int32_t after;           // -1, or j: read x once items 0..j have all finished
+  int32_t signal;          // 1: a later item waits on this one (its workgroups count themselves done)
+};
+constexpr int kChainWaves = 12;  // waves per workgroup of the chain kernel (one workgroup per CU)
+constexpr int kChainMaxWorkgroups = 1024;
+// Device table of a chain: count ChainEntry, then kChainMaxWorkgroups + 2
+// ints (workgroup w's units are work[wg_begin[w] .. wg_begin[w + 1])), then
+// the (projection, unit) pairs as int2.
+// Launches the chain kernel: `workgroups` cooperative workgroups of
+// kChainWaves waves, `lds` bytes of dynamic LDS, group size 64 or 128 for
+// every item. counters: count + 1 zeroed ints (left zeroed); error_flag: set
+// to 1 by a wait that gives up after spin_limit polls.
+int launch_chain(const ChainEntry* table, int count, int group, int workgroups, int lds, int* counters,
+                 int* error_flag, int spin_limit, void* stream);
+int chain_max_workgroups(int lds);  // co-resident workgroups of the chain kernel (negative: -hipError_t)
+int device_cu_count(int* cus);      // compute units of the current device; returns a hipError_t value
+int copy_to_device(void* dst, const void* src, size_t bytes);  // synchronous; returns a hipError_t value
+
 // Static device scratch of tern_linear_noalloc (tern_noalloc.hip): its size,
 // and the device address of the current device's copy (resolved with
 // hipGetSymbolAddress on the first call per device). Returns a hipError_t value.

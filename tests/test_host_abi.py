@@ -459,3 +459,42 @@ def test_t5_dispatch(tl):
     W = tl._Weights(0x100000, 0x200000, 5120, 5376, 128, tl.LAYOUT_T5)
     st = tl.lib().tern_linear(0x400000, 1, ctypes.byref(W), 0x300000, 0, None, 0, None)
     assert tl.STATUS[st] == "TERN_ERR_SHAPE"
+
+
+# ------------------------------------------------------ decode chain (host)
+
+
+def _chain(tl, shapes, afters, group=128, layout=None):
+    arr = (tl._ChainItem * len(shapes))()
+    for i, ((n, k), a) in enumerate(zip(shapes, afters)):
+        arr[i].W = tl._Weights(0x100000, 0x200000, n, k, group, layout or tl.LAYOUT_V1)
+        arr[i].x, arr[i].y, arr[i].y_bf16, arr[i].after = 0x300000, 0x400000, None, a
+    return arr
+
+
+def test_chain_table_bytes_and_validation(tl):
+    """The table holds the entries, the workgroup offsets and one (item,
+    unit) pair per unit of the gemv plan; invalid chains are refused before
+    any HIP call."""
+    L = tl.lib()
+    shapes = [(5120, 5120), (34816, 5120), (5120, 17408)]
+    arr = _chain(tl, shapes, [-1, 0, 1])
+    units = 160 + 2176 // 12 + (1 if 2176 % 12 else 0) + 160  # narrow 2 strips; wide 12 strips a unit
+    assert L.tern_chain_table_bytes(arr, 3) == 3 * 72 + (1024 + 2) * 4 + 8 * units
+    assert L.tern_chain_table_bytes(_chain(tl, shapes, [-1, 2, 1]), 3) == 0  # after must be earlier
+    assert "after" in L.tern_last_error().decode()
+    assert L.tern_chain_table_bytes(_chain(tl, shapes, [-1, -1, -1], layout=tl.LAYOUT_T5), 3) == 0
+    mixed = _chain(tl, [(5120, 5120), (256, 256)], [-1, -1])
+    mixed[1].W.group = 64
+    assert L.tern_chain_table_bytes(mixed, 2) == 0 and "group" in L.tern_last_error().decode()
+    bad = _chain(tl, shapes, [-1, -1, -1])
+    bad[1].y = 0x400004
+    assert L.tern_chain_table_bytes(bad, 3) == 0 and "aligned" in L.tern_last_error().decode()
+    assert L.tern_chain_table_bytes(arr, 0) == 0
+    plan = tl._ChainPlan(3, 128, 256, 4096)
+    assert tl.STATUS[L.tern_linear_chain(None, 0x100000, 0x200000, 16, 0x300000, 10, None)] == "TERN_ERR_NULL"
+    import ctypes
+    st = L.tern_linear_chain(ctypes.byref(plan), 0x100000, 0x200000, 8, 0x300000, 10, None)
+    assert tl.STATUS[st] == "TERN_ERR_WORKSPACE"  # 4 counters + done needed
+    st = L.tern_linear_chain(ctypes.byref(plan), 0x100000, 0x200000, 16, 0x300000, 0, None)
+    assert tl.STATUS[st] == "TERN_ERR_VALUE"  # spin limit
