@@ -47,8 +47,8 @@ METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
 # their launch plans: a change to any of them voids the stored counters.
 KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
                for f in ("tern_limb.hip", "tern_s8.hip", "tern_s8mma.hip", "tern_b16mma.hip",
-                         "tern_tile.hip", "tern_limbtile.hip", "tern_device.h", "tern_internal.h",
-                         "tern_host.cpp")]
+                         "tern_tile.hip", "tern_limbtile.hip", "tern_chain.hip", "tern_device.h",
+                         "tern_internal.h", "tern_host.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -532,9 +532,10 @@ def kernels_only(torch, ts, tl, dev, n):
     """For rocprofv3 --pmc runs, all on gate_up with weights rotated over
     > 512 MB: n launches of the gemv kernel (T=1), n/10 of the s8 rung (quant
     + contraction, T=2048), n/10 of the bf16 prefill (T=2048), n of the T=8
-    draft-verify batch, n of the rotated quantisation (T=2048), then plain
-    64 MiB device copies whose byte counters calibrate FETCH_SIZE /
-    WRITE_SIZE."""
+    draft-verify batch, n of the rotated quantisation (T=2048), n of the gemv
+    on base-3 (t5) weights, n of the decode step (gate_up + down) as one
+    chain launch, then plain 64 MiB device copies whose byte counters
+    calibrate FETCH_SIZE / WRITE_SIZE."""
     w = ts.weights(ts.GATE_UP)
     b = tl.TernaryWeights.from_host(w.w, w.s, device=dev)
     sets = [b] + [tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group)
@@ -565,6 +566,29 @@ def kernels_only(torch, ts, tl, dev, n):
     for i in range(n):  # rotated quantisation of the T = 2048 prefill activations
         tl.quant_act_s8_rot(x8, q=qr, scale=sr, layout="operand_order")
     torch.cuda.synchronize()
+    del sets
+    torch.cuda.empty_cache()
+    b5 = tl.TernaryWeights.from_host(w.w, w.s, device=dev, layout="t5")
+    s5 = [b5] + [tl.TernaryWeights(b5.codes.clone(), b5.scales.clone(), b5.n, b5.k, b5.group, "t5")
+                 for _ in range(max(1, math.ceil(ROTATE_BYTES / b5.nbytes)) - 1)]
+    for i in range(n):  # gemv on base-3 (t5) weights
+        tl.linear(x1, s5[i % len(s5)], y=y1)
+    torch.cuda.synchronize()
+    del s5, b5
+    wd = ts.weights(ts.DOWN)
+    bd = tl.TernaryWeights.from_host(wd.w, wd.s, device=dev)
+    xd = torch.from_numpy(ts.activations(wd, 1).view(np.int16)).to(dev).view(torch.bfloat16)
+    yd = torch.empty((1, bd.n), dtype=torch.float32, device=dev)
+    nch = max(2, math.ceil(ROTATE_BYTES / (b.nbytes + bd.nbytes)))
+    chains = []
+    for _ in range(nch):
+        bg = tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group)
+        bdd = tl.TernaryWeights(bd.codes.clone(), bd.scales.clone(), bd.n, bd.k, bd.group)
+        chains.append(tl.Chain([(bg, x1, y1, None, -1), (bdd, xd, yd, None, -1)], device=dev))
+    for i in range(n):  # the decode step (gate_up + down) as one chain launch
+        chains[i % nch].run()
+    torch.cuda.synchronize()
+    del chains
     src = torch.empty(64 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -659,6 +683,16 @@ def main():
         e["frac_of_read_ceiling"] = round(tc * 1e6 / e["us_per_launch"], 4)
         log(f"  {s.name}: read ceiling {tc * 1e6:.2f} us ({e['bytes'] / tc / 1e9:.0f} GB/s); the "
             f"kernel reaches {e['frac_of_read_ceiling']:.0%} of it")
+    # Context: the same step as one persistent launch (tern_linear_chain, the
+    # two projections with their own inputs, no wait between them) over the
+    # same rotated weight sets.
+    chains = [tl.Chain([(sets[i][0], x1[0], y1[0], None, -1), (sets[i][1], x1[1], y1[1], None, -1)], device=dev)
+              for i in range(nsets)]
+    t_ch = event_time(torch, lambda: [c.run() for c in chains], max(1, K // nsets)) / nsets
+    assert not any(c.failed() for c in chains)
+    del chains
+    log(f"decode step as one chain launch: {t_ch * 1e6:.2f} us ({step_bytes / t_ch / 1e9:.1f} GB/s)")
+
     dom = shapes[0].name
     achieved = per_shape[dom]["GB/s"]
     traffic = stored_traffic(f"gemv:{dom}")
@@ -787,7 +821,13 @@ def main():
                       "per_shape": per_shape, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                       "us_per_step_p10_p50_p90": [round(v * 1e6, 3) for v in (d10, d50, d90)],
                       "read_ceiling_us_per_step": round(ceil_step * 1e6, 3),
-                      "frac_of_read_ceiling": round(ceil_step / (el / K), 4)},
+                      "frac_of_read_ceiling": round(ceil_step / (el / K), 4),
+                      "chain_launch": {"us_per_step": round(t_ch * 1e6, 3),
+                                       "GB/s": round(step_bytes / t_ch / 1e9, 1),
+                                       "note": "context, not the value: both projections in one "
+                                               "tern_linear_chain launch with independent inputs "
+                                               "(a decode whose down reads gate_up's output waits "
+                                               "between them)"}},
            "roofline": roofline, "s8_prefill": s8, "t5_gemv_ab": t5, "small_t": small, "stack": stack,
            "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)

@@ -326,8 +326,9 @@ typedef struct {
 typedef struct {
   int32_t count;      /* items */
   int32_t group;      /* their group size */
-  int32_t workgroups; /* cooperative workgroups of the launch (one per CU) */
+  int32_t workgroups; /* workgroups of the launch (one per CU) */
   int32_t lds_bytes;  /* dynamic LDS per workgroup */
+  int32_t waits;      /* 1 if some item waits: the launch is then cooperative */
 } tern_chain_plan;
 
 /* Device bytes of the chain table for these items (their plans and work
@@ -349,12 +350,14 @@ size_t tern_chain_counter_bytes(int count);
 tern_status tern_chain_build(const tern_chain_item* items, int count, void* table, size_t table_bytes,
                              tern_chain_plan* plan);
 /*
- * Runs a built chain (device, async, one cooperative launch). counters:
+ * Runs a built chain (device, async, one launch; cooperative, so that
+ * every workgroup is resident, when some item waits). counters:
  * device, tern_chain_counter_bytes(count), zeroed before the first call and
  * left zeroed by every call (the last workgroup out clears them); calls that
  * share counters must not overlap. error_flag: device int32, set to 1 if a
  * wait gave up (the caller zeroes it). spin_limit >= 1. TERN_ERR_HIP if the
- * cooperative launch is refused.
+ * launch is refused. A cooperative launch has a fixed cost of its own (about
+ * 10-20 us measured per launch): chains pay off for whole passes.
  */
 tern_status tern_linear_chain(const tern_chain_plan* plan, const void* table, void* counters,
                               size_t counter_bytes, int32_t* error_flag, int spin_limit, void* stream);

@@ -80,7 +80,7 @@ class _ChainItem(ctypes.Structure):
 
 class _ChainPlan(ctypes.Structure):
     _fields_ = [("count", ctypes.c_int32), ("group", ctypes.c_int32), ("workgroups", ctypes.c_int32),
-                ("lds_bytes", ctypes.c_int32)]
+                ("lds_bytes", ctypes.c_int32), ("waits", ctypes.c_int32)]
 
 
 _lib = None

@@ -65,6 +65,7 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const ChainEn
   __syncthreads();
   int wp = wg_begin[b];             // this workgroup's work list: (projection, unit) pairs,
   const int wend = wg_begin[b + 1];  // in projection order
+  int prepped = -1;                  // projection whose limbs of x are in LDS
 
   for (int i = 0; i < count && !s_abort; ++i) {
     const ChainEntry e = table[i];
@@ -74,6 +75,7 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const ChainEn
     const int rs = K + 64;
     int* dexp = (int*)(smem + (size_t)3 * rs);
     char* lsc = smem + (size_t)3 * rs + (size_t)KT * 4;  // [Wn][KT][16][GPT] fp16
+    float* red = (float*)(lsc + (size_t)Wn * KT * 16 * GPT * 2);  // [Wk][Wn][16]: after the limbs and scales
     bool waited = e.after < 0;
     for (; wp < wend && work[wp].x == i; ++wp) {
       const int u = work[wp].y;
@@ -117,9 +119,12 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const ChainEn
       __syncthreads();  // the wait, and the previous unit's last reads of the LDS
       if (s_abort) break;
 
-      // 3. limbs of x and the unit's scales into LDS (as the gemv kernel)
+      // 3. limbs of x (unless this workgroup's previous unit was of the same
+      //    projection: they are still in LDS) and the unit's scales into LDS
+      //    (as the gemv kernel)
       const rsrc_t xr = make_rsrc(e.x, (uint32_t)K * 2);
-      const int nchunk = K >> 4;
+      const int nchunk = prepped == i ? 0 : K >> 4;
+      prepped = i;
       for (int c = tid; c < nchunk; c += kChainThreads) {  // rows of 16 lanes are wholly in or out
         const int base = 64 * (c >> 2) + 8 * (c & 3);
         const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, base * 2, 0, 0));
@@ -196,8 +201,7 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const ChainEn
           if (e.y_bf16) e.y_bf16[(size_t)strip * 16 + lane] = f32_to_bf16_rne(total);
         }
       } else {
-        __syncthreads();  // every wave is done with the limbs
-        float* red = (float*)smem;  // [Wk][Wn][16]
+        __syncthreads();  // the previous unit's readers of red are done
         if (wk < Wk && lane < 16) red[(wk * Wn + wn) * 16 + lane] = total;
         __syncthreads();
         if (tid < nsb * 16) {
@@ -222,14 +226,15 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const ChainEn
       }
     }
   }
-  // 7. the last workgroup out zeroes the counters for the next launch
-  __builtin_amdgcn_s_waitcnt(0);
+  // 7. the last workgroup out zeroes the counters for the next launch. No
+  //    data is published here (the kernel's end does that), so no release
+  //    fence (an L2 write-back per workgroup): thread 0 only waits until its
+  //    own counter operations are done before it counts itself out.
   __syncthreads();
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (__hip_atomic_fetch_add(&counters[count], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == P - 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (__hip_atomic_fetch_add(&counters[count], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P - 1) {
       for (int j = 0; j <= count; ++j) __hip_atomic_store(&counters[j], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     }
   }
 }
@@ -258,7 +263,7 @@ int copy_to_device(void* dst, const void* src, size_t bytes) {
 }
 
 int launch_chain(const ChainEntry* table, int count, int group, int workgroups, int lds, int* counters,
-                 int* error_flag, int spin_limit, void* stream) {
+                 int* error_flag, int spin_limit, bool cooperative, void* stream) {
   if (count < 1 || workgroups < 1 || workgroups > kChainMaxWorkgroups || (group != 64 && group != 128))
     return (int)hipErrorInvalidValue;
   const int* wg_begin = (const int*)(table + count);
@@ -266,8 +271,22 @@ int launch_chain(const ChainEntry* table, int count, int group, int workgroups, 
   void* args[] = {(void*)&table, (void*)&count, (void*)&wg_begin, (void*)&work, (void*)&counters,
                   (void*)&error_flag, (void*)&spin_limit};
   const void* fn = group == 128 ? (const void*)tern_chain_kernel<2> : (const void*)tern_chain_kernel<4>;
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(workgroups), dim3(kChainThreads), args, (unsigned)lds,
-                                            (hipStream_t)stream);
+  hipError_t e;
+  if (cooperative) {
+    // a workgroup that waits needs every other one resident: the launch
+    // guarantees it or fails
+    e = hipLaunchCooperativeKernel(fn, dim3(workgroups), dim3(kChainThreads), args, (unsigned)lds,
+                                   (hipStream_t)stream);
+  } else {
+    // no waits: nothing depends on co-residency, an ordinary launch
+    if (group == 128)
+      hipLaunchKernelGGL(tern_chain_kernel<2>, dim3(workgroups), dim3(kChainThreads), (size_t)lds, (hipStream_t)stream,
+                         table, count, wg_begin, work, counters, error_flag, spin_limit);
+    else
+      hipLaunchKernelGGL(tern_chain_kernel<4>, dim3(workgroups), dim3(kChainThreads), (size_t)lds, (hipStream_t)stream,
+                         table, count, wg_begin, work, counters, error_flag, spin_limit);
+    e = hipGetLastError();
+  }
   return kernel_launched((int)e, TERN_KERNEL_CHAIN);
 }
 

@@ -1027,7 +1027,9 @@ tern_status chain_plan_items(const tern_chain_item* items, int count, std::vecto
     tern::LimbPlan p = plan_limb(1, it.W.n, it.W.k);
     if (p.wn * p.wk > tern::kChainWaves || p.strips_per_wave != 1)
       return fail(TERN_ERR_CONFIG, "chain item %d: plan of %d x %d waves exceeds %d", i, p.wn, p.wk, tern::kChainWaves);
-    const int l = tern::limb_lds_bytes(1, it.W.k, group, p);
+    // limbs, exponents and scales, then the K-share sums [wk][wn][16] after them
+    const int l = 3 * (it.W.k + 64) + (it.W.k / 256) * 4 + p.wn * (it.W.k / 256) * 16 * (256 / group) * 2 +
+                  p.wk * p.wn * 16 * 4;
     if (l > tern::kLimbMaxLds)
       return fail(TERN_ERR_SHAPE, "chain item %d: K=%d needs %d bytes of LDS (at most %d)", i, it.W.k, l, tern::kLimbMaxLds);
     lds = std::max(lds, l);
@@ -1132,6 +1134,8 @@ tern_status tern_chain_build(const tern_chain_item* items, int count, void* tabl
   plan->group = items[0].W.group;
   plan->workgroups = P;
   plan->lds_bytes = lds;
+  plan->waits = 0;
+  for (const auto& e : t) plan->waits |= e.after >= 0;
   return ok();
 }
 
@@ -1149,7 +1153,8 @@ tern_status tern_linear_chain(const tern_chain_plan* plan, const void* table, vo
   if (!aligned16(table) || ((uintptr_t)counters & 3u) || ((uintptr_t)error_flag & 3u))
     return fail(TERN_ERR_ALIGN, "table 16-byte, counters and error_flag 4-byte aligned");
   const int err = tern::launch_chain((const tern::ChainEntry*)table, plan->count, plan->group, plan->workgroups,
-                                     plan->lds_bytes, (int*)counters, (int*)error_flag, spin_limit, stream);
+                                     plan->lds_bytes, (int*)counters, (int*)error_flag, spin_limit,
+                                     plan->waits != 0, stream);
   if (err) return hip_fail(err, "chain launch");
   return call_ok();
 }

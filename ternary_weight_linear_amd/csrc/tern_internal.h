@@ -149,12 +149,12 @@ constexpr int kChainMaxWorkgroups = 1024;
 // Device table of a chain: count ChainEntry, then kChainMaxWorkgroups + 2
 // ints (workgroup w's units are work[wg_begin[w] .. wg_begin[w + 1])), then
 // the (projection, unit) pairs as int2.
-// Launches the chain kernel: `workgroups` cooperative workgroups of
-// kChainWaves waves, `lds` bytes of dynamic LDS, group size 64 or 128 for
+// Launches the chain kernel: `workgroups` workgroups of kChainWaves waves
+// (a cooperative launch when some item waits), `lds` bytes of dynamic LDS, group size 64 or 128 for
 // every item. counters: count + 1 zeroed ints (left zeroed); error_flag: set
 // to 1 by a wait that gives up after spin_limit polls.
 int launch_chain(const ChainEntry* table, int count, int group, int workgroups, int lds, int* counters,
-                 int* error_flag, int spin_limit, void* stream);
+                 int* error_flag, int spin_limit, bool cooperative, void* stream);
 int chain_max_workgroups(int lds);  // co-resident workgroups of the chain kernel (negative: -hipError_t)
 int device_cu_count(int* cus);      // compute units of the current device; returns a hipError_t value
 int copy_to_device(void* dst, const void* src, size_t bytes);  // synchronous; returns a hipError_t value

@@ -479,7 +479,7 @@ def test_chain_table_bytes_and_validation(tl):
     L = tl.lib()
     shapes = [(5120, 5120), (34816, 5120), (5120, 17408)]
     arr = _chain(tl, shapes, [-1, 0, 1])
-    units = 160 + 2176 // 12 + (1 if 2176 % 12 else 0) + 160  # narrow 2 strips; wide 12 strips a unit
+    units = 160 + -(-2176 // 12) + 160  # the gemv's units: 2 strips (narrow), 12 strips (wide)
     assert L.tern_chain_table_bytes(arr, 3) == 3 * 72 + (1024 + 2) * 4 + 8 * units
     assert L.tern_chain_table_bytes(_chain(tl, shapes, [-1, 2, 1]), 3) == 0  # after must be earlier
     assert "after" in L.tern_last_error().decode()
@@ -491,7 +491,7 @@ def test_chain_table_bytes_and_validation(tl):
     bad[1].y = 0x400004
     assert L.tern_chain_table_bytes(bad, 3) == 0 and "aligned" in L.tern_last_error().decode()
     assert L.tern_chain_table_bytes(arr, 0) == 0
-    plan = tl._ChainPlan(3, 128, 256, 4096)
+    plan = tl._ChainPlan(3, 128, 256, 4096, 1)
     assert tl.STATUS[L.tern_linear_chain(None, 0x100000, 0x200000, 16, 0x300000, 10, None)] == "TERN_ERR_NULL"
     import ctypes
     st = L.tern_linear_chain(ctypes.byref(plan), 0x100000, 0x200000, 8, 0x300000, 10, None)
