@@ -380,17 +380,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
 }
 
 // y[t][n] = act_scale[t] * sum_{p < Pk} part[p][t][n], parts in ascending
-// order; four outputs per thread.
+// order; four outputs per thread, token t = blockIdx.y. The parts are
+// requested 8 at a time before they are added (each is a memory round trip:
+// they were just written on other XCDs).
 __global__ void __launch_bounds__(256) tern_s8m_reduce_kernel(const float* __restrict__ part,
                                                              const float* __restrict__ act_scale,
                                                              float* __restrict__ y, int T, int N, int Pk) {
   const int n4 = N >> 2;
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long)T * n4) return;
-  const int t = (int)(i / n4);
+  const int c = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int t = (int)blockIdx.y;
+  if (c >= n4) return;
+  const size_t i = (size_t)t * n4 + c;
   const f32x4* src = (const f32x4*)part + i;
-  f32x4 sum = src[0];
-  for (int p = 1; p < Pk; ++p) sum += __builtin_nontemporal_load(src + (size_t)p * T * n4);
+  const size_t stride = (size_t)T * n4;
+  // -0 + v == v for every v (zeros keep their sign): the sum starts as part 0
+  f32x4 sum = f32x4{-0.f, -0.f, -0.f, -0.f};
+  for (int p0 = 0; p0 < Pk; p0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (p0 + j < Pk) v[j] = __builtin_nontemporal_load(src + (size_t)(p0 + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (p0 + j < Pk) sum += v[j];
+  }
   ((f32x4*)y)[i] = sum * act_scale[t];
 }
 
@@ -440,7 +453,7 @@ int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* ws, void* st
   hipStream_t st = (hipStream_t)stream;
   const bool dbg = a.acc_out != nullptr;
   if (p.k_parts < 1 || p.k_parts > a.K / 256 || (p.depth != 2 && p.depth != 4)) return (int)hipErrorInvalidValue;
-  if (p.k_parts > 1 && (dbg || ws == nullptr || a.N % 4 != 0)) return (int)hipErrorInvalidValue;
+  if (p.k_parts > 1 && (dbg || ws == nullptr || a.N % 4 != 0 || a.T > 65535)) return (int)hipErrorInvalidValue;
   float* part = p.k_parts > 1 ? (float*)ws : nullptr;
   hipError_t e;
   if (a.G == 128)
@@ -448,9 +461,8 @@ int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* ws, void* st
   else
     e = dbg ? launch_s8m_g<4, true>(a, p, part, st) : launch_s8m_g<4, false>(a, p, part, st);
   if (e != hipSuccess || p.k_parts == 1) return (int)e;
-  const long n = (long)a.T * (a.N / 4);
-  hipLaunchKernelGGL(tern_s8m_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const float*)part, a.act_scale, a.y, a.T, a.N, p.k_parts);
+  hipLaunchKernelGGL(tern_s8m_reduce_kernel, dim3((unsigned)((a.N / 4 + 255) / 256), (unsigned)a.T), dim3(256), 0,
+                     st, (const float*)part, a.act_scale, a.y, a.T, a.N, p.k_parts);
   return kernel_launched((int)hipGetLastError(), TERN_KERNEL_S8_REDUCE);
 }
 

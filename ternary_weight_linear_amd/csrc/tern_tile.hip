@@ -237,17 +237,27 @@ __global__ void __launch_bounds__(576) tern_tile_kernel(
 }
 
 // y[t][n] = 0.5 * sum_{p < Pk} part[t / 16][p][t % 16][n], parts in ascending
-// order; four outputs per thread.
+// order; four outputs per thread, token t = blockIdx.y. The parts are
+// requested 8 at a time before they are added: they were just written on
+// other XCDs, so each load is a full memory round trip, and a loop that
+// waited for each in turn would pay Pk of them.
 __global__ void __launch_bounds__(256) tern_tile_reduce_kernel(const float* __restrict__ part,
-                                                              float* __restrict__ y, int T, int N,
-                                                              int Pk) {
+                                                              float* __restrict__ y, int N, int Pk) {
   const int n4 = N >> 2;
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long)T * n4) return;
-  const int t = (int)(i / n4), c = (int)(i % n4);
+  const int c = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int t = (int)blockIdx.y;
+  if (c >= n4) return;
   const f32x4* src = (const f32x4*)(part + ((size_t)(t >> 4) * Pk * 16 + (t & 15)) * N) + c;
   f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < Pk; ++p) sum += __builtin_nontemporal_load(src + (size_t)p * 16 * n4);
+  for (int p0 = 0; p0 < Pk; p0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (p0 + j < Pk) v[j] = __builtin_nontemporal_load(src + (size_t)(p0 + j) * 16 * n4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (p0 + j < Pk) sum += v[j];
+  }
   ((f32x4*)(y + (size_t)t * N))[c] = sum * 0.5f;
 }
 
@@ -304,13 +314,13 @@ int launch_tile(const SmallTArgs& a, const TilePlan& p, void* ws, void* stream) 
   if (p.waves < 1 || p.waves > 8 || p.k_parts < 1 || p.token_tiles < 1 || p.strip_blocks < 1)
     return (int)hipErrorInvalidValue;
   if (p.depth != 2 && p.depth != 4 && p.depth != 8) return (int)hipErrorInvalidValue;
+  if (p.k_parts > 1 && a.T > 65535) return (int)hipErrorInvalidValue;  // the reduce's grid.y
   float* part = p.k_parts > 1 ? (float*)ws : nullptr;
   hipError_t e = p.rows == 8 ? launch_tile_r<8>(a, p, part, st)
                : p.rows == 16 ? launch_tile_r<16>(a, p, part, st) : hipErrorInvalidValue;
   if (e != hipSuccess || p.k_parts == 1) return (int)e;
-  const long n = (long)a.T * (a.N / 4);
-  hipLaunchKernelGGL(tern_tile_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     (const float*)part, a.y, a.T, a.N, p.k_parts);
+  hipLaunchKernelGGL(tern_tile_reduce_kernel, dim3((unsigned)((a.N / 4 + 255) / 256), (unsigned)a.T), dim3(256), 0,
+                     st, (const float*)part, a.y, a.N, p.k_parts);
   return kernel_launched((int)hipGetLastError(), TERN_KERNEL_SMALLT_TILE_REDUCE);
 }
 
