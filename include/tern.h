@@ -299,12 +299,13 @@ tern_status tern_linear_noalloc(const void* x_bf16, int T, const tern_weights* W
 
 /*
  * A whole decode pass in one launch: a chain of T = 1 projections (the gemv
- * rung's arithmetic, bit-identical results) run by one persistent,
- * cooperatively launched kernel, so the next projection's codes stream
- * while the previous one drains, instead of each launch paying its own ramp
- * and tail ("NINFER ternary perf-tuning" notes, section 6: a decode round is
- * one graph of about 1224 kernels; "NInfer sm_89 fork" article, section 9
- * item 5: each decode round replayed as one graph).
+ * rung's arithmetic and K split, bit-identical results) run by one
+ * persistent kernel, one workgroup per CU, whose waves stream the codes of
+ * the next projection while they finish the previous one, instead of each
+ * launch paying its own ramp and tail ("NINFER ternary perf-tuning" notes,
+ * section 6: a decode round is one graph of about 1224 kernels; "NInfer
+ * sm_89 fork" article, section 9 item 5: each decode round replayed as one
+ * graph).
  *
  * Dependencies: item i with after = j (j < i) reads its x only once items
  * 0..j have all finished (their y and y_bf16 stores visible), e.g. x of item
@@ -331,21 +332,25 @@ typedef struct {
   int32_t waits;      /* 1 if some item waits: the launch is then cooperative */
 } tern_chain_plan;
 
-/* Device bytes of the chain table for these items (their plans and work
- * lists), 0 if the chain is invalid (tern_last_error says why). */
+/* Device bytes to allocate for the chain table of these items: enough for
+ * any device (up to 1024 workgroups); 0 if the chain is invalid
+ * (tern_last_error says why). */
 size_t tern_chain_table_bytes(const tern_chain_item* items, int count);
 /* Device bytes of the completion counters of `count` items (count + 1 ints). */
 size_t tern_chain_counter_bytes(int count);
 /*
- * Validates the chain (host), plans every item as the gemv rung plans it,
- * gives one workgroup per CU of the current device a list of work units,
- * balanced between the waits, and writes the table (device memory,
- * tern_chain_table_bytes(items, count), 16-byte aligned) with one
- * synchronous host-to-device copy. Build once per set of
- * buffers; the table holds the pointers of items[]. Errors: TERN_ERR_NULL,
- * TERN_ERR_SHAPE (count < 1, shapes, mixed group sizes, LDS), TERN_ERR_VALUE
- * (after out of range), TERN_ERR_LAYOUT, TERN_ERR_ALIGN, TERN_ERR_WORKSPACE
- * (table too small), TERN_ERR_HIP (device query or copy).
+ * Validates the chain (host), splits every item's K as the gemv rung does,
+ * cuts the chain into stages at the items that wait and gives each of one
+ * workgroup per CU of the current device a contiguous run of every stage's
+ * work, balanced by bytes, and writes the table (device memory, at least
+ * tern_chain_table_bytes(items, count) bytes, 16-byte aligned) with one
+ * synchronous host-to-device copy. Build once per set of buffers; the table
+ * holds the pointers of items[]. The limbs of two items' activations share
+ * the LDS, so the largest K is about 26,000. Errors: TERN_ERR_NULL,
+ * TERN_ERR_SHAPE (count < 1, shapes, mixed group sizes, K too large for the
+ * LDS), TERN_ERR_VALUE (after out of range), TERN_ERR_LAYOUT,
+ * TERN_ERR_ALIGN, TERN_ERR_WORKSPACE (table too small), TERN_ERR_HIP
+ * (device query or copy).
  */
 tern_status tern_chain_build(const tern_chain_item* items, int count, void* table, size_t table_bytes,
                              tern_chain_plan* plan);
@@ -355,8 +360,8 @@ tern_status tern_chain_build(const tern_chain_item* items, int count, void* tabl
  * device, tern_chain_counter_bytes(count), zeroed before the first call and
  * left zeroed by every call (the last workgroup out clears them); calls that
  * share counters must not overlap. error_flag: device int32, set to 1 if a
- * wait gave up (the caller zeroes it). spin_limit >= 1. TERN_ERR_HIP if the
- * launch is refused. A cooperative launch has a fixed cost of its own (about
+ * wait gave up or the table does not match the plan (the caller zeroes it).
+ * spin_limit >= 1. TERN_ERR_HIP if the launch is refused. A cooperative launch has a fixed cost of its own (about
  * 10-20 us measured per launch): chains pay off for whole passes.
  */
 tern_status tern_linear_chain(const tern_chain_plan* plan, const void* table, void* counters,

@@ -5,31 +5,47 @@
 // sm_89 fork" article, section 9 item 5), where every launch pays its own
 // ramp and drain.
 //
-// One workgroup of 12 waves per CU, launched cooperatively (all resident or
-// the launch fails). Each projection's 16-row strips are cut into units of
-// wn strips (the gemv's plan, K split over wk waves). The host gives every
-// workgroup a list of units in projection order, balanced between the
-// waits (each unit to the least loaded workgroup, by its bytes of codes and
-// its K); every workgroup walks the projections in order. A projection may depend on earlier ones
-// (after = j: items 0..j all finished): a workgroup requests its unit's
-// first k-tiles of codes, which do not depend on anything, and only then
-// waits, so the weight stream goes on while the previous projection drains.
+// One workgroup of 12 waves per CU. The host cuts the chain into stages at
+// the items that wait, and gives every workgroup one contiguous run of each
+// stage's work, balanced by bytes of codes: its event list holds ranges of
+// work of one item at a time, in item order, and a signal after every item
+// that a later one waits on. Work of an item with its K split over Wk waves
+// (the gemv's plan) comes in units of 12 / Wk strips, each wave one K share
+// of one strip, the shares added through LDS in ascending order; work of an
+// item with Wk = 1 comes as single strips, dealt over the waves in turn.
 //
-// Completion: after its units of a projection that a later one waits on,
-// every workgroup (with or without units) makes its stores visible at
-// device scope (release fence) and adds one to the projection's counter;
-// waiting for items 0..j means waiting for counter j to reach the number of
-// workgroups, then an acquire fence. Each wait polls at most spin_limit
-// times; on giving up it sets *error_flag and the workgroup skips the rest
-// of the chain, so every wave exits. The last workgroup out zeroes the
-// counters for the next launch.
+// Streaming. Each wave walks its own sequence of (strip, k-tile) positions
+// across units, items and stages, and keeps the codes and scales of the
+// next D - 1 positions in flight in registers, so the weight stream does not
+// stop at a unit's or an item's end. The positions are processed in groups
+// of D with the ring slot of every position fixed at compile time (the
+// compiler's memory-counter waits then keep the whole ring in flight); the
+// work between positions (unit ends, item switches, waits, signals) sits in
+// each of the D steps.
 //
-// The arithmetic of a unit is the T = 1 integer-limb gemv of tern_limb.hip
-// (limbs of x in LDS, codes decoded into i8 MFMA operands, per-group fp32
-// epilogue, K shares added in ascending order), so y is bit-identical to
-// tern_linear's gemv rung for the same weights.
+// Limbs of x. The int8 limbs of the current item's activations live in one
+// of two LDS slots; at an item switch the workgroup makes the next item's
+// limbs in the other slot (every wave a share of the chunks, after its last
+// position of the previous item) and passes one barrier, so waves still
+// finishing the previous item keep reading theirs.
+//
+// Dependencies (after = j: items 0..j all finished) go through device-scope
+// counters: at a signal every wave waits for its stores, the workgroup meets
+// at a barrier and one thread issues a release fence and adds one to the
+// item's counter; a waiting workgroup's thread 0 polls counter j until it
+// reaches the number of workgroups (bounded by spin_limit, then it sets
+// *error_flag and the workgroup skips the rest), issues an acquire fence and
+// the workgroup meets at a barrier before it reads x. The last workgroup out
+// zeroes the counters for the next launch.
+//
+// The arithmetic of a strip is the T = 1 integer-limb gemv of tern_limb.hip
+// (limbs of x, codes decoded into i8 MFMA operands, per-group fp32 epilogue,
+// k-tiles added in order, K shares added in ascending order), with the
+// gemv's K split, so y is bit-identical to tern_linear's gemv rung.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "tern_device.h"
 #include "tern_internal.h"
@@ -39,18 +55,75 @@ namespace {
 using namespace dev;
 
 constexpr int kChainThreads = 64 * kChainWaves;
-constexpr int kChainDepth = 4;  // k-tiles of codes in flight per wave
+constexpr int kChainDepth = 4;  // positions of codes and scales in flight per wave (D - 1) plus the one in use
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   const uint32_t u = __float_as_uint(v);
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);  // finite inputs
 }
 
+// Workgroup barrier for LDS hand-offs only: this wave's LDS operations are
+// complete, then s_barrier. Without the workgroup fence of __syncthreads(),
+// which would also wait for the wave's outstanding global loads (the ring)
+// and stores. The "memory" clobber keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Scalar loads of the chain table (read-only for the whole launch, written
+// by the host before it). The compiler would read it with vector loads (it
+// cannot tell that the kernel's stores leave it alone), and waiting for a
+// vector load waits for every code load issued before it: the ring would
+// drain at every unit. The wait is for the scalar counter only.
+typedef int si4 __attribute__((ext_vector_type(4)));
+typedef int si16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
+  const uint64_t a = (uint64_t)p;
+  // readfirstlane returns an int: each half goes through uint32_t, or a low
+  // word with bit 31 set would sign-extend into the high word
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ si4 sload4(const void* p) {
+  si4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ si16 sload16(const void* p) {
+  si16 v;
+  asm volatile("s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_addr(p)) : "memory");
+  return v;
+}
+// Fields of a ChainEntry from its first 64 bytes.
+__device__ __forceinline__ const void* ent_ptr(const si16& v, int i) {
+  return (const void*)(((uint64_t)(uint32_t)v[2 * i + 1] << 32) | (uint32_t)v[2 * i]);
+}
+constexpr int kEntCodes = 0, kEntScales = 1, kEntX = 2, kEntY = 3, kEntYb = 4;  // pointers
+constexpr int kEntN = 10, kEntK = 11, kEntWn = 12, kEntWk = 13, kEntAfter = 15;  // ints
+static_assert(offsetof(ChainEntry, n) == 4 * kEntN && offsetof(ChainEntry, after) == 4 * kEntAfter &&
+                  offsetof(ChainEntry, y_bf16) == 8 * kEntYb && offsetof(ChainEntry, wk) == 4 * kEntWk,
+              "ChainEntry field offsets");
+
+// One wave's walk over its workgroup's event list: ranges of units of one
+// item (Wk > 1: units of 12 / Wk strips, this wave share wk of strip wn;
+// Wk = 1: single strips, strip i of the range to wave (rot + i) mod 12) and
+// signals. The load side and the compute side each run one of these over
+// the same list, the compute side D - 1 positions behind.
+struct Walk {
+  int ev, ev_end;       // next event, end of the list
+  int item;             // item of the current range (-1: none)
+  int u, u0, u1;        // current unit (Wk > 1) or strip (Wk = 1); range
+  int rot;              // Wk = 1: wave that took the first strip of the range
+  int NS, KT, wn_, wk_; // item shape and plan
+  int strip, kt0, nkt;  // current task of this wave (nkt = 0: none)
+};
+
 template <int GPT>
-__global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const ChainEntry* __restrict__ table,
-                                                                   int count, const int* __restrict__ wg_begin,
-                                                                   const int2* __restrict__ work,
-                                                                   int* __restrict__ counters,
+__global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* __restrict__ head, int count,
+                                                                   int lds, int* __restrict__ counters,
                                                                    int* __restrict__ error_flag, int spin_limit) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_abort;
@@ -61,180 +134,326 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const ChainEn
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
+  // The table's own layout against the launch: a table from another build
+  // would put the limbs outside this launch's LDS.
+  const int4 hd = head[0];
+  const int rs = hd.x, slot_bytes = hd.y;
+  if (hd.z != count || hd.w != (int)kChainTableMagic || rs < 64 || slot_bytes < 3 * rs ||
+      2 * slot_bytes + 2 * kChainWaves * 16 * 4 > lds) {
+    if (tid == 0) __hip_atomic_store(error_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const ChainEntry* __restrict__ table = (const ChainEntry*)(head + 1);
+  // global, not flat, atomics: a pending flat operation makes every later
+  // memory-counter wait a wait for zero
+  __attribute__((address_space(1))) int* const gcount = (__attribute__((address_space(1))) int*)counters;
+  __attribute__((address_space(1))) int* const gerror = (__attribute__((address_space(1))) int*)error_flag;
+  const int* __restrict__ wg_begin = (const int*)(table + count);
+  const si4* __restrict__ events = (const si4*)(wg_begin + kChainMaxWorkgroups + 4);
   if (tid == 0) s_abort = 0;
   __syncthreads();
-  int wp = wg_begin[b];             // this workgroup's work list: (projection, unit) pairs,
-  const int wend = wg_begin[b + 1];  // in projection order
-  int prepped = -1;                  // projection whose limbs of x are in LDS
+  float* red = (float*)(smem + 2 * (size_t)slot_bytes);  // [2][12][16]: K-share sums of a unit
+  const int ev0 = wg_begin[b], ev1 = wg_begin[b + 1];
 
-  for (int i = 0; i < count && !s_abort; ++i) {
-    const ChainEntry e = table[i];
-    const int NS = e.n >> 4, K = e.k, KT = K >> 8;
-    const int Wn = e.wn, Wk = e.wk;
-    const int wn = wave % Wn, wk = wave / Wn;
-    const int rs = K + 64;
-    int* dexp = (int*)(smem + (size_t)3 * rs);
-    char* lsc = smem + (size_t)3 * rs + (size_t)KT * 4;  // [Wn][KT][16][GPT] fp16
-    float* red = (float*)(lsc + (size_t)Wn * KT * 16 * GPT * 2);  // [Wk][Wn][16]: after the limbs and scales
-    bool waited = e.after < 0;
-    for (; wp < wend && work[wp].x == i; ++wp) {
-      const int u = work[wp].y;
-      const int strip = u * Wn + wn;
-      const bool has = wk < Wk && strip < NS;
-      const int kt0 = has ? (wk * KT) / Wk : 0;
-      const int nkt = has ? ((wk + 1) * KT) / Wk - kt0 : 0;
-      const rsrc_t crs = make_rsrc((const char*)e.codes + (size_t)(has ? strip : 0) * KT * 1024,
-                                   has ? (uint32_t)KT * 1024 : 0u);
-      auto load = [&](u32x4& P4, int j) {
-        const int kt = __builtin_amdgcn_readfirstlane(min(kt0 + j, KT - 1));
-        const int cv = j < nkt ? lane * 16 : kOffPastEnd;
-        P4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, cv, kt * 1024, kAuxNontemporal));
-      };
-      // 1. the first k-tiles of codes: they depend on nothing
-      u32x4 ring[D];
-#pragma unroll
-      for (int j = 0; j < D - 1; ++j) load(ring[j], j);
-
-      // 2. the dependency, once per projection and workgroup
-      if (!waited) {
-        if (tid == 0) {
-          bool ok = false;
-          for (int it = 0;; ++it) {
-            if (__hip_atomic_load(&counters[e.after], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= P) {
-              ok = true;
-              break;
-            }
-            if (__hip_atomic_load(error_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
-            if (it >= spin_limit) {
-              __hip_atomic_store(error_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-          }
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // later reads of x see the producers' stores
-          if (!ok) s_abort = 1;
-        }
-        waited = true;
-      }
-      __syncthreads();  // the wait, and the previous unit's last reads of the LDS
-      if (s_abort) break;
-
-      // 3. limbs of x (unless this workgroup's previous unit was of the same
-      //    projection: they are still in LDS) and the unit's scales into LDS
-      //    (as the gemv kernel)
-      const rsrc_t xr = make_rsrc(e.x, (uint32_t)K * 2);
-      const int nchunk = prepped == i ? 0 : K >> 4;
-      prepped = i;
-      for (int c = tid; c < nchunk; c += kChainThreads) {  // rows of 16 lanes are wholly in or out
-        const int base = 64 * (c >> 2) + 8 * (c & 3);
-        const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, base * 2, 0, 0));
-        const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (base + 32) * 2, 0, 0));
-        const int d = limb_shift(row16_max_u32(absmax16(lo, hi)));
-        u32x4 o0, o1, o2;
-        limb_chunk(lo, hi, d, o0, o1, o2);
-        char* row = smem + 16 * c;
-        *(u32x4*)row = o0;
-        *(u32x4*)(row + rs) = o1;
-        *(u32x4*)(row + 2 * rs) = o2;
-        if ((c & 15) == 0) dexp[c >> 4] = d;
-      }
-      const int nsb = min(Wn, NS - u * Wn);
-      const int nsc = nsb * KT * 2 * GPT;  // 16-byte chunks of scales
-      const rsrc_t wsr = make_rsrc(e.scales + (size_t)u * Wn * KT * 16 * GPT, (uint32_t)nsc * 16);
-      for (int c = tid; c < nsc; c += kChainThreads)
-        *(u32x4*)(lsc + 16 * c) = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wsr, c * 16, 0, 0));
-      __syncthreads();
-
-      // 4. the contraction over this wave's k-tiles
-      float total = 0.f;
-      const char* abase = smem + (size_t)(r < 3 ? r : 0) * rs + 16 * g;
-      const char* wsc = lsc + ((size_t)wn * KT * 16 + r) * GPT * 2;
-      auto compute = [&](const u32x4& P4, int j) {
-        const int kt = kt0 + j;
-        i32x4 a[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = *(const i32x4*)(abase + 64 * (4 * kt + q));
-        const int dsh = dexp[kt] - 6;
-        uint32_t sw[GPT / 2];
-        const char* sp = wsc + (size_t)kt * 16 * GPT * 2;
-        if (GPT == 2) {
-          sw[0] = *(const uint32_t*)sp;
-        } else {
-          const uint2 v = *(const uint2*)sp;
-          sw[0] = v.x;
-          sw[GPT / 2 - 1] = v.y;
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int gi = 0; gi < GPT; ++gi) {
-          i32x4 acc = i32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int kk = 0; kk < KBPG; ++kk) {
-            const int q = gi * KBPG + kk;
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[q], weights_operand_i8(P4[q]), acc, 0, 0, 0);
-          }
-          const uint32_t spair = sw[gi >> 1];
-          const float sc = half_bits_to_float((uint16_t)((gi & 1) ? (spair >> 16) : (spair & 0xffffu)));
-          const int low = (int)(((uint32_t)acc[1] << 8) + (uint32_t)acc[0]);  // 256 a1 + a0
-          const float v = __builtin_fmaf(65536.0f, (float)acc[2], (float)low);
-          part = gi == 0 ? sc * v : __builtin_fmaf(sc, v, part);
-        }
-        total += __builtin_ldexpf(part, dsh);
-      };
-      int j = 0;
-      for (; j + D <= nkt; j += D) {
-#pragma unroll
-        for (int jj = 0; jj < D; ++jj) {
-          load(ring[(jj + D - 1) % D], j + jj + D - 1);
-          __builtin_amdgcn_sched_barrier(0);
-          compute(ring[jj], j + jj);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < D - 1; ++jj)
-        if (j + jj < nkt) compute(ring[jj], j + jj);
-
-      // 5. y (and its bf16 copy); K shares added through LDS in ascending order
-      if (Wk == 1) {
-        if (has && lane < 16) {
-          e.y[(size_t)strip * 16 + lane] = total;
-          if (e.y_bf16) e.y_bf16[(size_t)strip * 16 + lane] = f32_to_bf16_rne(total);
-        }
-      } else {
-        __syncthreads();  // the previous unit's readers of red are done
-        if (wk < Wk && lane < 16) red[(wk * Wn + wn) * 16 + lane] = total;
-        __syncthreads();
-        if (tid < nsb * 16) {
-          const int ls = tid >> 4, col = tid & 15;
-          float sum = 0.f;
-          for (int w = 0; w < Wk; ++w) sum += red[(w * Wn + ls) * 16 + col];
-          const size_t o = (size_t)(u * Wn + ls) * 16 + col;
-          e.y[o] = sum;
-          if (e.y_bf16) e.y_bf16[o] = f32_to_bf16_rne(sum);
-        }
-      }
+  // ---- the walk (shared by both sides; side effects only on the compute side)
+  // Task of this wave in the current unit / strip of walk w.
+  auto set_task = [&](Walk& w) {
+    if (w.wk_ == 1) {
+      w.strip = w.u;
+      w.kt0 = 0;
+      w.nkt = w.KT;
+    } else {
+      const int wn = wave % w.wn_, wk = wave / w.wn_;
+      w.strip = w.u * w.wn_ + wn;
+      const bool has = wk < w.wk_ && w.strip < w.NS;
+      w.kt0 = has ? (wk * w.KT) / w.wk_ : 0;
+      w.nkt = has ? ((wk + 1) * w.KT) / w.wk_ - w.kt0 : 0;
     }
-    if (s_abort) break;
-    // 6. this workgroup is done with projection i (and, in order, with all
-    //    before it): count it for the projections that wait
-    if (e.signal) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed (reached its L2)
-      __syncthreads();                // ... and every other wave's
-      if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // write them back for every XCD
-        __hip_atomic_fetch_add(&counters[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto enter_range = [&](Walk& w, const si4 e, const si16& c) {
+    w.item = e.x;
+    w.NS = c[kEntN] >> 4;
+    w.KT = c[kEntK] >> 8;
+    w.wn_ = c[kEntWn];
+    w.wk_ = c[kEntWk];
+    w.u0 = e.y;
+    w.u1 = e.z;
+    // the loop's step lands on the first unit, or on this wave's first strip
+    w.u = w.wk_ == 1 ? e.y + (wave - w.rot + kChainWaves) % kChainWaves - kChainWaves : e.y - 1;
+  };
+  auto leave_range = [&](Walk& w) {
+    if (w.wk_ == 1) w.rot = (w.rot + (w.u1 - w.u0)) % kChainWaves;
+    w.item = -1;
+  };
+
+  // ---- load side: the ring
+  Walk L{ev0, ev1, -1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  const void* lcodes = nullptr;  // codes and scales of L's item
+  const void* lscales = nullptr;
+  int lj = 0;                 // next k-tile of L's task
+  bool lend = false;          // L has passed the last task
+  rsrc_t lcr = make_rsrc(table, 0), lsr = lcr;  // codes and scales of L's task (none yet: every load past the end)
+  auto lnext_task = [&]() {   // L to its next task with positions (or to the end)
+    const int kt0_last = L.kt0, nkt_last = L.nkt;
+    for (;;) {
+      if (L.item >= 0) {
+        L.u += L.wk_ == 1 ? kChainWaves : 1;
+        if (L.u < L.u1) {
+          set_task(L);
+          if (L.nkt > 0) break;
+          continue;
+        }
+        leave_range(L);
       }
+      if (L.ev >= L.ev_end) {  // the end: L stays on its last task's last position
+        lend = true;
+        L.kt0 = kt0_last;
+        L.nkt = nkt_last;
+        return;
+      }
+      const si4 e = sload4(events + L.ev++);
+      if (e.w != 0) continue;  // a signal
+      const si16 c = sload16(table + e.x);
+      enter_range(L, e, c);
+      lcodes = ent_ptr(c, kEntCodes);
+      lscales = ent_ptr(c, kEntScales);
+    }
+    lcr = make_rsrc((const char*)lcodes + (size_t)L.strip * L.KT * 1024, (uint32_t)L.KT * 1024);
+    lsr = make_rsrc((const char*)lscales + (size_t)L.strip * L.KT * 32 * GPT, (uint32_t)L.KT * 32 * GPT);
+    lj = 0;
+  };
+  struct Slot {
+    u32x4 P;
+    uint32_t sw[GPT / 2];
+  };
+  // The next position of L into s, then L one on. Past the last task the
+  // last position is read again (a wave without tasks reads zeros: its
+  // resource holds no bytes), so that every load is issued the same way and
+  // the ring's memory-counter waits stay exact.
+  auto lload = [&](Slot& s) {
+    const int kt = __builtin_amdgcn_readfirstlane(L.kt0 + lj);
+    s.P = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lcr, lane * 16, kt * 1024, kAuxNontemporal));
+    if (GPT == 2) {
+      s.sw[0] = __builtin_amdgcn_raw_buffer_load_b32(lsr, r * GPT * 2, kt * 32 * GPT, 0);
+    } else {
+      const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(lsr, r * GPT * 2, kt * 32 * GPT, 0);
+      s.sw[0] = w2[0];
+      s.sw[GPT / 2 - 1] = w2[1];
+    }
+    if (!lend && ++lj == L.nkt) {
+      lnext_task();
+      if (lend) lj = max(L.nkt - 1, 0);
+    }
+  };
+
+  // ---- compute side
+  Walk C{ev0, ev1, -1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  int cj = 0;              // next k-tile of C's task
+  bool cend = false;
+  int lslot = 1;           // LDS slot of the limbs in use (the first item takes slot 0)
+  int limb_item = -1;      // item whose limbs are in slot lslot
+  int units_done = 0;      // Wk > 1 units passed (parity of red)
+  float total = 0.f;
+  rsrc_t ys = make_rsrc(table, 0), ybs = ys;  // y and y_bf16 of C's item (0 bytes: no y_bf16)
+  const char* abase = nullptr;
+  const int* dexp = nullptr;
+
+  // Limbs of item i into the other LDS slot, after its wait (the whole
+  // workgroup passes here together).
+  auto item_switch = [&](int i, const si16& e) {
+    const int after = e[kEntAfter];
+    if (after >= 0) {
+      if (tid == 0) {
+        bool ok = false;
+        for (int it = 0;; ++it) {
+          if (__hip_atomic_load(&gcount[after], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= P) {
+            ok = true;
+            break;
+          }
+          if (__hip_atomic_load(gerror, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+          if (it >= spin_limit) {
+            __hip_atomic_store(gerror, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // later reads of x see the producers' stores
+        if (!ok) s_abort = 1;
+      }
+      lds_barrier();
+      if (s_abort) return;
+    }
+    lslot ^= 1;
+    char* base = smem + (size_t)lslot * slot_bytes;
+    int* dx = (int*)(base + 3 * (size_t)rs);
+    const int K = e[kEntK];
+    const rsrc_t xr = make_rsrc(ent_ptr(e, kEntX), (uint32_t)K * 2);
+    for (int c = tid; c < (K >> 4); c += kChainThreads) {  // rows of 16 lanes are wholly in or out
+      const int off = 64 * (c >> 2) + 8 * (c & 3);
+      const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off * 2, 0, 0));
+      const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (off + 32) * 2, 0, 0));
+      const int d = limb_shift(row16_max_u32(absmax16(lo, hi)));
+      u32x4 o0, o1, o2;
+      limb_chunk(lo, hi, d, o0, o1, o2);
+      char* row = base + 16 * c;
+      *(u32x4*)row = o0;
+      *(u32x4*)(row + rs) = o1;
+      *(u32x4*)(row + 2 * rs) = o2;
+      if ((c & 15) == 0) dx[c >> 4] = d;
+    }
+    lds_barrier();
+    limb_item = i;
+  };
+  // A signal: this workgroup is done with items 0..i.
+  auto signal = [&](int i) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed (reached its L2)
+    lds_barrier();                  // ... and every other wave's
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // write them back for every XCD
+      __hip_atomic_fetch_add(&gcount[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  // Output o of C's item (buffer stores: a flat store would make the
+  // compiler wait for every outstanding load before the next position).
+  auto store_y = [&](size_t o, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ys, (int)o * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), ybs, (int)o * 2, 0, 0);  // dropped without y_bf16
+  };
+  // End of a Wk > 1 unit: the shares meet in LDS, the first threads add them
+  // in ascending order and store.
+  auto unit_end = [&]() {
+    float* rb = red + (units_done & 1) * (kChainWaves * 16);
+    const int wn = wave % C.wn_, wk = wave / C.wn_;
+    if (C.nkt > 0 && lane < 16) rb[(wk * C.wn_ + wn) * 16 + lane] = total;
+    lds_barrier();
+    const int nsb = min(C.wn_, C.NS - C.u * C.wn_);
+    if (tid < nsb * 16) {
+      const int ls = tid >> 4, col = tid & 15;
+      float sum = 0.f;
+      for (int w = 0; w < C.wk_; ++w) sum += rb[(w * C.wn_ + ls) * 16 + col];
+      const size_t o = (size_t)(C.u * C.wn_ + ls) * 16 + col;
+      store_y(o, sum);
+    }
+    ++units_done;
+  };
+  // C to its next task with positions, doing the work between (unit ends
+  // of tasks without positions, item switches, waits, signals).
+  auto cnext_task = [&]() {
+    for (;;) {
+      if (C.item >= 0) {
+        C.u += C.wk_ == 1 ? kChainWaves : 1;
+        if (C.u < C.u1) {
+          set_task(C);
+          if (C.nkt > 0) break;
+          unit_end();  // Wk > 1: a unit where this wave has no share
+          continue;
+        }
+        leave_range(C);
+      }
+      if (C.ev >= C.ev_end) {
+        cend = true;
+        return;
+      }
+      const si4 e = sload4(events + C.ev++);
+      if (e.w != 0) {
+        signal(e.x);
+        continue;
+      }
+      const si16 c = sload16(table + e.x);
+      if (e.x != limb_item) {
+        item_switch(e.x, c);
+        if (s_abort) {
+          cend = true;
+          return;
+        }
+      }
+      enter_range(C, e, c);
+      const int n = c[kEntN];
+      const void* yb = ent_ptr(c, kEntYb);
+      ys = make_rsrc(ent_ptr(c, kEntY), (uint32_t)n * 4);
+      ybs = make_rsrc(yb, yb ? (uint32_t)n * 2 : 0u);
+    }
+    const char* base = smem + (size_t)lslot * slot_bytes;
+    abase = base + (size_t)(r < 3 ? r : 0) * rs + 16 * g;
+    dexp = (const int*)(base + 3 * (size_t)rs);
+    total = 0.f;
+    cj = 0;
+  };
+  // End of C's task: its sum to y, or to the unit's reduction.
+  auto task_end = [&]() {
+    if (C.wk_ == 1) {
+      if (lane < 16) {
+        const size_t o = (size_t)C.strip * 16 + lane;
+        store_y(o, total);
+      }
+    } else {
+      unit_end();
+    }
+  };
+  // One position: the k-tile cj of C's task from ring slot s.
+  auto compute = [&](const Slot& s) {
+    const int kt = C.kt0 + cj;
+    i32x4 a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = *(const i32x4*)(abase + 64 * (4 * kt + q));
+    const int dsh = dexp[kt] - 6;
+    float part = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      i32x4 acc = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KBPG; ++kk) {
+        const int q = gi * KBPG + kk;
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[q], weights_operand_i8(s.P[q]), acc, 0, 0, 0);
+      }
+      const uint32_t spair = s.sw[gi >> 1];
+      const float sc = half_bits_to_float((uint16_t)((gi & 1) ? (spair >> 16) : (spair & 0xffffu)));
+      const int low = (int)(((uint32_t)acc[1] << 8) + (uint32_t)acc[0]);  // 256 a1 + a0
+      const float v = __builtin_fmaf(65536.0f, (float)acc[2], (float)low);
+      part = gi == 0 ? sc * v : __builtin_fmaf(sc, v, part);
+    }
+    total += __builtin_ldexpf(part, dsh);
+  };
+
+  // ---- the stream. Step s of a group requests the position D - 1 ahead
+  // into slot (s + D - 1) mod D and computes the one in slot s. The first
+  // positions are requested before the first item's limbs are made.
+  lnext_task();
+  {
+    Slot ring[D];
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) lload(ring[j]);
+    cnext_task();
+    if (cend) goto stream_done;
+    // one position in ring slot S (S a compile-time constant); true at the end
+    auto step = [&](auto slot) {
+      constexpr int S = decltype(slot)::value;
+      lload(ring[(S + D - 1) % D]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ring[S]);
+      if (++cj == C.nkt) {
+        task_end();
+        cnext_task();
+      }
+      return cend;
+    };
+    static_assert(D == 4, "the group below is written out for four slots");
+    for (;;) {
+      if (step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
+          step(std::integral_constant<int, 2>{}) || step(std::integral_constant<int, 3>{}))
+        break;
     }
   }
-  // 7. the last workgroup out zeroes the counters for the next launch. No
-  //    data is published here (the kernel's end does that), so no release
-  //    fence (an L2 write-back per workgroup): thread 0 only waits until its
-  //    own counter operations are done before it counts itself out.
+stream_done:
+
+  // The last workgroup out zeroes the counters for the next launch. No data
+  // is published here (the kernel's end does that), so no release fence:
+  // thread 0 only waits until its own counter operations are done.
   __syncthreads();
   if (tid == 0) {
     __builtin_amdgcn_s_waitcnt(0);
-    if (__hip_atomic_fetch_add(&counters[count], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P - 1) {
-      for (int j = 0; j <= count; ++j) __hip_atomic_store(&counters[j], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(&gcount[count], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P - 1) {
+      for (int j = 0; j <= count; ++j) __hip_atomic_store(&gcount[j], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -262,14 +481,13 @@ int copy_to_device(void* dst, const void* src, size_t bytes) {
   return (int)hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice);
 }
 
-int launch_chain(const ChainEntry* table, int count, int group, int workgroups, int lds, int* counters,
-                 int* error_flag, int spin_limit, bool cooperative, void* stream) {
+int launch_chain(const void* table, int count, int group, int workgroups, int lds, int* counters, int* error_flag,
+                 int spin_limit, bool cooperative, void* stream) {
   if (count < 1 || workgroups < 1 || workgroups > kChainMaxWorkgroups || (group != 64 && group != 128))
     return (int)hipErrorInvalidValue;
-  const int* wg_begin = (const int*)(table + count);
-  const int2* work = (const int2*)(wg_begin + kChainMaxWorkgroups + 2);
-  void* args[] = {(void*)&table, (void*)&count, (void*)&wg_begin, (void*)&work, (void*)&counters,
-                  (void*)&error_flag, (void*)&spin_limit};
+  const int4* head = (const int4*)table;
+  void* args[] = {(void*)&head, (void*)&count, (void*)&lds, (void*)&counters, (void*)&error_flag,
+                  (void*)&spin_limit};
   const void* fn = group == 128 ? (const void*)tern_chain_kernel<2> : (const void*)tern_chain_kernel<4>;
   hipError_t e;
   if (cooperative) {
@@ -281,10 +499,10 @@ int launch_chain(const ChainEntry* table, int count, int group, int workgroups, 
     // no waits: nothing depends on co-residency, an ordinary launch
     if (group == 128)
       hipLaunchKernelGGL(tern_chain_kernel<2>, dim3(workgroups), dim3(kChainThreads), (size_t)lds, (hipStream_t)stream,
-                         table, count, wg_begin, work, counters, error_flag, spin_limit);
+                         head, count, lds, counters, error_flag, spin_limit);
     else
       hipLaunchKernelGGL(tern_chain_kernel<4>, dim3(workgroups), dim3(kChainThreads), (size_t)lds, (hipStream_t)stream,
-                         table, count, wg_begin, work, counters, error_flag, spin_limit);
+                         head, count, lds, counters, error_flag, spin_limit);
     e = hipGetLastError();
   }
   return kernel_launched((int)e, TERN_KERNEL_CHAIN);

@@ -10,6 +10,7 @@
 // fallback; every scratch counted in the declared workspace) and section 7
 // (one launch signature; decode choices frozen per process).
 #include <algorithm>
+#include <array>
 #include <atomic>
 #include <cerrno>
 #include <cstdarg>
@@ -1004,16 +1005,23 @@ size_t tern_chain_counter_bytes(int count) { return count < 1 ? 0 : (size_t)(cou
 
 namespace {
 
-// Plans of a chain's items (the gemv's), validated: the shared part of
-// tern_chain_table_bytes and tern_chain_build.
-tern_status chain_plan_items(const tern_chain_item* items, int count, std::vector<tern::ChainEntry>& t, int* lds_out) {
+// Plans of a chain's items (the gemv's K split), validated: the shared part
+// of tern_chain_table_bytes and tern_chain_build. The LDS layout of the
+// kernel: two limb slots sized for the largest K, then the K-share sums.
+struct ChainLayout {
+  int rs = 0;          // bytes of one limb row (largest K + 64)
+  int slot_bytes = 0;  // 3 limb rows and the k-tile exponents, 16-byte aligned
+  int lds = 0;
+};
+tern_status chain_plan_items(const tern_chain_item* items, int count, std::vector<tern::ChainEntry>& t,
+                             ChainLayout* lay) {
   if (!items) return fail(TERN_ERR_NULL, "chain: items is NULL");
   if (count < 1 || count > (1 << 20)) return fail(TERN_ERR_SHAPE, "chain: count=%d", count);
   const Config& c = config();
   if (!c.valid) return fail(TERN_ERR_CONFIG, "%s", c.error.c_str());
   t.assign((size_t)count, tern::ChainEntry{});
   const int group = items[0].W.group;
-  int lds = 0;
+  int kmax = 0;
   for (int i = 0; i < count; ++i) {
     const tern_chain_item& it = items[i];
     tern_status st = check_weights(&it.W);
@@ -1024,15 +1032,10 @@ tern_status chain_plan_items(const tern_chain_item* items, int count, std::vecto
     if (!aligned16(it.x) || !aligned16(it.y) || ((uintptr_t)it.y_bf16 & 3u))
       return fail(TERN_ERR_ALIGN, "chain item %d: x and y 16-byte, y_bf16 4-byte aligned", i);
     if (it.after < -1 || it.after >= i) return fail(TERN_ERR_VALUE, "chain item %d: after=%d", i, it.after);
-    tern::LimbPlan p = plan_limb(1, it.W.n, it.W.k);
-    if (p.wn * p.wk > tern::kChainWaves || p.strips_per_wave != 1)
-      return fail(TERN_ERR_CONFIG, "chain item %d: plan of %d x %d waves exceeds %d", i, p.wn, p.wk, tern::kChainWaves);
-    // limbs, exponents and scales, then the K-share sums [wk][wn][16] after them
-    const int l = 3 * (it.W.k + 64) + (it.W.k / 256) * 4 + p.wn * (it.W.k / 256) * 16 * (256 / group) * 2 +
-                  p.wk * p.wn * 16 * 4;
-    if (l > tern::kLimbMaxLds)
-      return fail(TERN_ERR_SHAPE, "chain item %d: K=%d needs %d bytes of LDS (at most %d)", i, it.W.k, l, tern::kLimbMaxLds);
-    lds = std::max(lds, l);
+    const tern::LimbPlan p = plan_limb(1, it.W.n, it.W.k);
+    if (p.wk < 1 || p.wk > tern::kChainWaves)
+      return fail(TERN_ERR_CONFIG, "chain item %d: %d K shares exceed %d waves", i, p.wk, tern::kChainWaves);
+    kmax = std::max(kmax, it.W.k);
     tern::ChainEntry& e = t[(size_t)i];
     e.codes = it.W.codes;
     e.scales = it.W.scales;
@@ -1041,23 +1044,76 @@ tern_status chain_plan_items(const tern_chain_item* items, int count, std::vecto
     e.y_bf16 = it.y_bf16;
     e.n = it.W.n;
     e.k = it.W.k;
-    e.wn = p.wn;
     e.wk = p.wk;
-    e.units = (it.W.n / 16 + p.wn - 1) / p.wn;
+    e.wn = p.wk == 1 ? 1 : tern::kChainWaves / p.wk;
+    e.units = (it.W.n / 16 + e.wn - 1) / e.wn;
     e.after = it.after;
     e.signal = 0;
   }
   for (int i = 0; i < count; ++i)
     if (t[(size_t)i].after >= 0) t[(size_t)t[(size_t)i].after].signal = 1;
-  *lds_out = lds;
+  lay->rs = kmax + 64;
+  lay->slot_bytes = (3 * lay->rs + (kmax / 256) * 4 + 15) & ~15;
+  lay->lds = 2 * lay->slot_bytes + 2 * tern::kChainWaves * 16 * 4;
+  if (lay->lds > tern::kLimbMaxLdsResident)
+    return fail(TERN_ERR_SHAPE, "chain: K=%d needs %d bytes of LDS (at most %d)", kmax, lay->lds,
+                tern::kLimbMaxLdsResident);
   return TERN_OK;
 }
 
-size_t chain_table_size(const std::vector<tern::ChainEntry>& t) {
-  size_t units = 0;
-  for (const auto& e : t) units += (size_t)e.units;
-  return t.size() * sizeof(tern::ChainEntry) + (tern::kChainMaxWorkgroups + 2) * sizeof(int32_t) +
-         units * 2 * sizeof(int32_t);
+// Work of a chain for P workgroups: the items are cut into stages at every
+// item that waits; each stage's units (in item order) are dealt to the
+// workgroups in contiguous runs of about equal cost, so a workgroup switches
+// items (and makes new limbs) a few times per stage at most. Cost of a unit,
+// in k-tiles a wave streams: wk = 1, one strip of KT k-tiles (dealt over the
+// waves); wk > 1, every wave one share, the longest ceil(KT / wk), plus a
+// barrier. Events per workgroup, in item order: its run of each item, and a
+// signal after every item that a later one waits on.
+std::vector<std::vector<std::array<int32_t, 4>>> chain_events(const std::vector<tern::ChainEntry>& t, int P) {
+  std::vector<std::vector<std::array<int32_t, 4>>> ev((size_t)P);
+  const int count = (int)t.size();
+  for (int s0 = 0; s0 < count;) {
+    int s1 = s0 + 1;
+    while (s1 < count && t[(size_t)s1].after < 0) ++s1;
+    auto cost = [&](const tern::ChainEntry& e) {
+      const int KT = e.k / 256;
+      return e.wk == 1 ? (double)KT : (double)tern::kChainWaves * ((KT + e.wk - 1) / e.wk + 1);
+    };
+    double total = 0.0;
+    for (int i = s0; i < s1; ++i) total += cost(t[(size_t)i]) * t[(size_t)i].units;
+    const double per = total / P;
+    double cum = 0.0;
+    for (int i = s0; i < s1; ++i) {
+      const tern::ChainEntry& e = t[(size_t)i];
+      const double c = cost(e);
+      int cur = -1, u0 = 0;
+      for (int u = 0; u <= e.units; ++u) {
+        const int w = u < e.units ? std::min(P - 1, (int)((cum + 0.5 * c) / per)) : -2;
+        if (w != cur) {
+          if (cur >= 0) ev[(size_t)cur].push_back({i, u0, u, 0});
+          cur = w;
+          u0 = u;
+        }
+        if (u < e.units) cum += c;
+      }
+      if (e.signal)
+        for (int w = 0; w < P; ++w) ev[(size_t)w].push_back({i, 0, 0, 1});
+    }
+    s0 = s1;
+  }
+  return ev;
+}
+
+size_t chain_table_size(int count, size_t events) {
+  return sizeof(int32_t) * 4 + (size_t)count * sizeof(tern::ChainEntry) +
+         (tern::kChainMaxWorkgroups + 4) * sizeof(int32_t) + events * 4 * sizeof(int32_t);
+}
+
+// Events of a chain at most: every workgroup a run of every item, and every signal.
+size_t chain_events_bound(const std::vector<tern::ChainEntry>& t, int P) {
+  size_t n = 0;
+  for (const auto& e : t) n += (size_t)std::min(P, e.units + 1) + (e.signal ? (size_t)P : 0);
+  return n;
 }
 
 }  // namespace
@@ -1066,65 +1122,46 @@ extern "C" {
 
 size_t tern_chain_table_bytes(const tern_chain_item* items, int count) {
   std::vector<tern::ChainEntry> t;
-  int lds = 0;
-  if (chain_plan_items(items, count, t, &lds) != TERN_OK) return 0;
-  return chain_table_size(t);
+  ChainLayout lay;
+  if (chain_plan_items(items, count, t, &lay) != TERN_OK) return 0;
+  // the run count depends on the device's workgroups: a bound for the most
+  return chain_table_size(count, chain_events_bound(t, tern::kChainMaxWorkgroups));
 }
 
 tern_status tern_chain_build(const tern_chain_item* items, int count, void* table, size_t table_bytes,
                              tern_chain_plan* plan) {
   if (!table || !plan) return fail(TERN_ERR_NULL, "tern_chain_build: NULL pointer");
   std::vector<tern::ChainEntry> t;
-  int lds = 0;
-  tern_status st = chain_plan_items(items, count, t, &lds);
+  ChainLayout lay;
+  tern_status st = chain_plan_items(items, count, t, &lay);
   if (st != TERN_OK) return st;
-  const size_t need = chain_table_size(t);
-  if (table_bytes < need) return fail(TERN_ERR_WORKSPACE, "chain table needs %zu bytes, got %zu", need, table_bytes);
   if (!aligned16(table)) return fail(TERN_ERR_ALIGN, "chain table must be 16-byte aligned");
-  const int dev_max = tern::chain_max_workgroups(lds);
+  const int dev_max = tern::chain_max_workgroups(lay.lds);
   if (dev_max <= 0) return hip_fail(-dev_max, "chain occupancy query");
   int cus = 0;
   const int cerr = tern::device_cu_count(&cus);
   if (cerr) return hip_fail(cerr, "chain CU count");
   const int P = std::min(std::min(dev_max, cus), tern::kChainMaxWorkgroups);  // one workgroup per CU
-  // Work lists: between two waits every workgroup starts together, so each
-  // unit goes to the least loaded workgroup of its stage (loads reset at a
-  // wait). Cost of a unit: its code bytes at one CU's share of the HBM rate
-  // plus the limb preparation of its K (rounds of 768 16-element chunks).
-  std::vector<std::vector<std::pair<int, int>>> lists((size_t)P);
-  using Slot = std::pair<double, int>;
-  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
-  auto reset = [&]() {
-    heap = decltype(heap)();
-    for (int w = 0; w < P; ++w) heap.push({0.0, w});
-  };
-  reset();
-  for (int i = 0; i < count; ++i) {
-    const tern::ChainEntry& e = t[(size_t)i];
-    if (e.after >= 0) reset();
-    const int NS = e.n / 16;
-    const double prep = 0.5 + 0.6 * ((e.k / 16 + tern::kChainWaves * 64 - 1) / (tern::kChainWaves * 64));
-    for (int u = 0; u < e.units; ++u) {
-      const int nsb = std::min(e.wn, NS - u * e.wn);
-      const double cost = (double)nsb * 16.0 * e.k / 4.0 / 31.0e3 + prep;  // microseconds
-      Slot sl = heap.top();
-      heap.pop();
-      lists[(size_t)sl.second].push_back({i, u});
-      sl.first += cost;
-      heap.push(sl);
-    }
-  }
+  const auto ev = chain_events(t, P);
+  size_t nev = 0;
+  for (const auto& l : ev) nev += l.size();
+  const size_t need = chain_table_size(count, nev);
+  if (table_bytes < need) return fail(TERN_ERR_WORKSPACE, "chain table needs %zu bytes, got %zu", need, table_bytes);
   std::vector<char> blob(need, 0);
-  memcpy(blob.data(), t.data(), t.size() * sizeof(tern::ChainEntry));
-  int32_t* wg_begin = (int32_t*)(blob.data() + t.size() * sizeof(tern::ChainEntry));
-  int32_t* work = wg_begin + tern::kChainMaxWorkgroups + 2;
+  int32_t* head = (int32_t*)blob.data();
+  head[0] = lay.rs;
+  head[1] = lay.slot_bytes;
+  head[2] = count;
+  head[3] = (int32_t)tern::kChainTableMagic;
+  memcpy(blob.data() + 16, t.data(), t.size() * sizeof(tern::ChainEntry));
+  int32_t* wg_begin = (int32_t*)(blob.data() + 16 + t.size() * sizeof(tern::ChainEntry));
+  int32_t* events = wg_begin + tern::kChainMaxWorkgroups + 4;
   int32_t pos = 0;
-  for (int w = 0; w <= tern::kChainMaxWorkgroups + 1; ++w) {
+  for (int w = 0; w < tern::kChainMaxWorkgroups + 4; ++w) {
     wg_begin[w] = pos;
     if (w < P)
-      for (const auto& pr : lists[(size_t)w]) {  // already in projection order
-        work[2 * pos] = pr.first;
-        work[2 * pos + 1] = pr.second;
+      for (const auto& e : ev[(size_t)w]) {
+        memcpy(events + 4 * pos, e.data(), sizeof(int32_t) * 4);
         ++pos;
       }
   }
@@ -1133,7 +1170,7 @@ tern_status tern_chain_build(const tern_chain_item* items, int count, void* tabl
   plan->count = count;
   plan->group = items[0].W.group;
   plan->workgroups = P;
-  plan->lds_bytes = lds;
+  plan->lds_bytes = lay.lds;
   plan->waits = 0;
   for (const auto& e : t) plan->waits |= e.after >= 0;
   return ok();
@@ -1143,8 +1180,8 @@ tern_status tern_linear_chain(const tern_chain_plan* plan, const void* table, vo
                               size_t counter_bytes, int32_t* error_flag, int spin_limit, void* stream) {
   call_begin();
   if (!plan || !table || !counters || !error_flag) return fail(TERN_ERR_NULL, "tern_linear_chain: NULL pointer");
-  if (plan->count < 1 || plan->workgroups < 1 || (plan->group != 64 && plan->group != 128) ||
-      plan->lds_bytes < 0 || plan->lds_bytes > tern::kLimbMaxLds)
+  if (plan->count < 1 || plan->workgroups < 1 || plan->workgroups > tern::kChainMaxWorkgroups ||
+      (plan->group != 64 && plan->group != 128) || plan->lds_bytes < 0 || plan->lds_bytes > tern::kLimbMaxLdsResident)
     return fail(TERN_ERR_VALUE, "tern_linear_chain: plan not from tern_chain_build");
   if (counter_bytes < tern_chain_counter_bytes(plan->count))
     return fail(TERN_ERR_WORKSPACE, "chain counters need %zu bytes, got %zu", tern_chain_counter_bytes(plan->count),
@@ -1152,9 +1189,8 @@ tern_status tern_linear_chain(const tern_chain_plan* plan, const void* table, vo
   if (spin_limit < 1) return fail(TERN_ERR_VALUE, "spin_limit=%d must be at least 1", spin_limit);
   if (!aligned16(table) || ((uintptr_t)counters & 3u) || ((uintptr_t)error_flag & 3u))
     return fail(TERN_ERR_ALIGN, "table 16-byte, counters and error_flag 4-byte aligned");
-  const int err = tern::launch_chain((const tern::ChainEntry*)table, plan->count, plan->group, plan->workgroups,
-                                     plan->lds_bytes, (int*)counters, (int*)error_flag, spin_limit,
-                                     plan->waits != 0, stream);
+  const int err = tern::launch_chain(table, plan->count, plan->group, plan->workgroups, plan->lds_bytes,
+                                     (int*)counters, (int*)error_flag, spin_limit, plan->waits != 0, stream);
   if (err) return hip_fail(err, "chain launch");
   return call_ok();
 }

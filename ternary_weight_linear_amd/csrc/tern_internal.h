@@ -138,23 +138,31 @@ struct ChainEntry {
   float* y;                // fp32 [N]
   uint16_t* y_bf16;        // bf16 [N] or nullptr
   int32_t n, k;
-  int32_t wn, wk;          // the gemv plan: wn strips per unit, wk K shares (wn * wk <= 12 waves)
-  int32_t units;           // ceil(N / 16 / wn)
-  int32_t pad;
+  int32_t wn, wk;          // wk: the gemv's K shares; wn: strips per unit (12 / wk; 1 when wk = 1)
+  int32_t units;           // wk > 1: ceil(N / 16 / wn) units; wk = 1: N / 16 strips
   int32_t after;           // -1, or j: read x once items 0..j have all finished
   int32_t signal;          // 1: a later item waits on this one (its workgroups count themselves done)
+  int32_t pad[3];          // 80 bytes: what follows the entries stays 16-byte aligned
 };
+static_assert(sizeof(ChainEntry) == 80, "chain table layout");
 constexpr int kChainWaves = 12;  // waves per workgroup of the chain kernel (one workgroup per CU)
 constexpr int kChainMaxWorkgroups = 1024;
-// Device table of a chain: count ChainEntry, then kChainMaxWorkgroups + 2
-// ints (workgroup w's units are work[wg_begin[w] .. wg_begin[w + 1])), then
-// the (projection, unit) pairs as int2.
+constexpr unsigned kChainTableMagic = 0x4e484331u;  // "1CHN"
+// Device table of a chain:
+//   int4 header {row bytes of a limb row, bytes of an LDS limb slot, count, kChainTableMagic};
+//   count ChainEntry;
+//   kChainMaxWorkgroups + 4 ints: workgroup w's events are events[wg_begin[w] .. wg_begin[w + 1]);
+//   int4 events {item, u0, u1, kind}: kind 0 = units (or strips) [u0, u1) of the item, kind 1 = a
+//   signal after the item.
+// LDS of the kernel: two limb slots of slot_bytes (3 limb rows, then the
+// k-tile exponents), then 2 x 12 x 16 floats of K-share sums.
 // Launches the chain kernel: `workgroups` workgroups of kChainWaves waves
 // (a cooperative launch when some item waits), `lds` bytes of dynamic LDS, group size 64 or 128 for
 // every item. counters: count + 1 zeroed ints (left zeroed); error_flag: set
-// to 1 by a wait that gives up after spin_limit polls.
-int launch_chain(const ChainEntry* table, int count, int group, int workgroups, int lds, int* counters,
-                 int* error_flag, int spin_limit, bool cooperative, void* stream);
+// to 1 by a wait that gives up after spin_limit polls, or when the table
+// does not fit the launch.
+int launch_chain(const void* table, int count, int group, int workgroups, int lds, int* counters, int* error_flag,
+                 int spin_limit, bool cooperative, void* stream);
 int chain_max_workgroups(int lds);  // co-resident workgroups of the chain kernel (negative: -hipError_t)
 int device_cu_count(int* cus);      // compute units of the current device; returns a hipError_t value
 int copy_to_device(void* dst, const void* src, size_t bytes);  // synchronous; returns a hipError_t value

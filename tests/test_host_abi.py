@@ -473,14 +473,18 @@ def _chain(tl, shapes, afters, group=128, layout=None):
 
 
 def test_chain_table_bytes_and_validation(tl):
-    """The table holds the entries, the workgroup offsets and one (item,
-    unit) pair per unit of the gemv plan; invalid chains are refused before
-    any HIP call."""
+    """The table holds a header, the entries, the workgroup offsets and
+    room for the events of up to 1024 workgroups (a run of each item per
+    workgroup, at most one per unit, and a signal per workgroup after every
+    item that is waited on); invalid chains are refused before any HIP call."""
     L = tl.lib()
     shapes = [(5120, 5120), (34816, 5120), (5120, 17408)]
     arr = _chain(tl, shapes, [-1, 0, 1])
-    units = 160 + -(-2176 // 12) + 160  # the gemv's units: 2 strips (narrow), 12 strips (wide)
-    assert L.tern_chain_table_bytes(arr, 3) == 3 * 72 + (1024 + 2) * 4 + 8 * units
+    # units: 320 strips in threes (K in 4 shares), 2176 single strips (K
+    # whole), 320 strips in twos (K in 6 shares); items 0 and 1 signal
+    runs = min(1024, 107 + 1) + min(1024, 2176 + 1) + min(1024, 160 + 1)
+    events = runs + 2 * 1024
+    assert L.tern_chain_table_bytes(arr, 3) == 16 + 3 * 80 + (1024 + 4) * 4 + 16 * events
     assert L.tern_chain_table_bytes(_chain(tl, shapes, [-1, 2, 1]), 3) == 0  # after must be earlier
     assert "after" in L.tern_last_error().decode()
     assert L.tern_chain_table_bytes(_chain(tl, shapes, [-1, -1, -1], layout=tl.LAYOUT_T5), 3) == 0
