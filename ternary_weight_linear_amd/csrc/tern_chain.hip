@@ -15,13 +15,14 @@
 // item with Wk = 1 comes as single strips, dealt over the waves in turn.
 //
 // Streaming. Each wave walks its own sequence of (strip, k-tile) positions
-// across units, items and stages, and keeps the codes and scales of the
-// next D - 1 positions in flight in registers, so the weight stream does not
+// across units, items and stages, and keeps the codes and scales of its
+// next D positions in flight in registers, so the weight stream does not
 // stop at a unit's or an item's end. The positions are processed in groups
-// of D with the ring slot of every position fixed at compile time (the
-// compiler's memory-counter waits then keep the whole ring in flight); the
-// work between positions (unit ends, item switches, waits, signals) sits in
-// each of the D steps.
+// of D with the ring slot of every position fixed at compile time, each slot
+// reloaded right after its compute (the compiler's memory-counter waits then
+// keep the whole ring in flight at every position); the work between
+// positions (unit ends, item switches, waits, signals) sits in each of the D
+// steps.
 //
 // Limbs of x. The int8 limbs of the current item's activations live in one
 // of two LDS slots; at an item switch the workgroup makes the next item's
@@ -46,6 +47,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "tern_device.h"
 #include "tern_internal.h"
@@ -55,7 +57,7 @@ namespace {
 using namespace dev;
 
 constexpr int kChainThreads = 64 * kChainWaves;
-constexpr int kChainDepth = 4;  // positions of codes and scales in flight per wave (D - 1) plus the one in use
+constexpr int kChainDepth = 8;  // positions of codes and scales in flight per wave
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   const uint32_t u = __float_as_uint(v);
@@ -107,11 +109,17 @@ static_assert(offsetof(ChainEntry, n) == 4 * kEntN && offsetof(ChainEntry, after
                   offsetof(ChainEntry, y_bf16) == 8 * kEntYb && offsetof(ChainEntry, wk) == 4 * kEntWk,
               "ChainEntry field offsets");
 
+// f(0) || f(1) || ... || f(D - 1) with compile-time indices, in order.
+template <typename F, int... I>
+__device__ __forceinline__ bool run_steps(F& f, std::integer_sequence<int, I...>) {
+  return (f(std::integral_constant<int, I>{}) || ...);
+}
+
 // One wave's walk over its workgroup's event list: ranges of units of one
 // item (Wk > 1: units of 12 / Wk strips, this wave share wk of strip wn;
 // Wk = 1: single strips, strip i of the range to wave (rot + i) mod 12) and
 // signals. The load side and the compute side each run one of these over
-// the same list, the compute side D - 1 positions behind.
+// the same list, the compute side D positions behind.
 struct Walk {
   int ev, ev_end;       // next event, end of the list
   int item;             // item of the current range (-1: none)
@@ -415,33 +423,31 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
     total += __builtin_ldexpf(part, dsh);
   };
 
-  // ---- the stream. Step s of a group requests the position D - 1 ahead
-  // into slot (s + D - 1) mod D and computes the one in slot s. The first
-  // positions are requested before the first item's limbs are made.
+  // ---- the stream. The first D positions are requested before the first
+  // item's limbs are made.
   lnext_task();
   {
     Slot ring[D];
 #pragma unroll
-    for (int j = 0; j < D - 1; ++j) lload(ring[j]);
+    for (int j = 0; j < D; ++j) lload(ring[j]);
     cnext_task();
     if (cend) goto stream_done;
-    // one position in ring slot S (S a compile-time constant); true at the end
+    // One position: compute slot S (a compile-time constant), then request
+    // the position D ahead into it. True at the end of the stream. (Each
+    // slot is reloaded right after its own compute, so every wait finds the
+    // same D positions in flight.)
     auto step = [&](auto slot) {
       constexpr int S = decltype(slot)::value;
-      lload(ring[(S + D - 1) % D]);
-      __builtin_amdgcn_sched_barrier(0);
       compute(ring[S]);
+      __builtin_amdgcn_sched_barrier(0);
+      lload(ring[S]);
       if (++cj == C.nkt) {
         task_end();
         cnext_task();
       }
       return cend;
     };
-    static_assert(D == 4, "the group below is written out for four slots");
-    for (;;) {
-      if (step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
-          step(std::integral_constant<int, 2>{}) || step(std::integral_constant<int, 3>{}))
-        break;
+    while (!run_steps(step, std::make_integer_sequence<int, D>{})) {
     }
   }
 stream_done:
