@@ -105,6 +105,12 @@ __device__ __forceinline__ const void* ent_ptr(const si16& v, int i) {
 }
 constexpr int kEntCodes = 0, kEntScales = 1, kEntX = 2, kEntY = 3, kEntYb = 4;  // pointers
 constexpr int kEntN = 10, kEntK = 11, kEntWn = 12, kEntWk = 13, kEntAfter = 15;  // ints
+// Records of a wave's list: {type | item << 4, strip or unit, unit, kt0 | nkt << 16}.
+constexpr int kRecTask = 0;      // a strip's k-tiles [kt0, kt0 + nkt), its sum to y (K not split)
+constexpr int kRecTaskUnit = 1;  // one K share of a strip of unit `unit`, then the unit's reduction
+constexpr int kRecUnit = 2;      // the reduction of unit `y` without a share of this wave
+constexpr int kRecSwitch = 3;    // the workgroup moves to the item (wait, limbs)
+constexpr int kRecSignal = 4;    // the workgroup is done with items 0..item
 static_assert(offsetof(ChainEntry, n) == 4 * kEntN && offsetof(ChainEntry, after) == 4 * kEntAfter &&
                   offsetof(ChainEntry, y_bf16) == 8 * kEntYb && offsetof(ChainEntry, wk) == 4 * kEntWk,
               "ChainEntry field offsets");
@@ -114,20 +120,6 @@ template <typename F, int... I>
 __device__ __forceinline__ bool run_steps(F& f, std::integer_sequence<int, I...>) {
   return (f(std::integral_constant<int, I>{}) || ...);
 }
-
-// One wave's walk over its workgroup's event list: ranges of units of one
-// item (Wk > 1: units of 12 / Wk strips, this wave share wk of strip wn;
-// Wk = 1: single strips, strip i of the range to wave (rot + i) mod 12) and
-// signals. The load side and the compute side each run one of these over
-// the same list, the compute side D positions behind.
-struct Walk {
-  int ev, ev_end;       // next event, end of the list
-  int item;             // item of the current range (-1: none)
-  int u, u0, u1;        // current unit (Wk > 1) or strip (Wk = 1); range
-  int rot;              // Wk = 1: wave that took the first strip of the range
-  int NS, KT, wn_, wk_; // item shape and plan
-  int strip, kt0, nkt;  // current task of this wave (nkt = 0: none)
-};
 
 template <int GPT>
 __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* __restrict__ head, int count,
@@ -156,90 +148,59 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
   // memory-counter wait a wait for zero
   __attribute__((address_space(1))) int* const gcount = (__attribute__((address_space(1))) int*)counters;
   __attribute__((address_space(1))) int* const gerror = (__attribute__((address_space(1))) int*)error_flag;
-  const int* __restrict__ wg_begin = (const int*)(table + count);
-  const si4* __restrict__ events = (const si4*)(wg_begin + kChainMaxWorkgroups + 4);
+  const int* __restrict__ wv_begin = (const int*)(table + count);
+  const si4* __restrict__ recs = (const si4*)(wv_begin + kChainRecordOffsets);
   if (tid == 0) s_abort = 0;
   __syncthreads();
   float* red = (float*)(smem + 2 * (size_t)slot_bytes);  // [2][12][16]: K-share sums of a unit
-  const int ev0 = wg_begin[b], ev1 = wg_begin[b + 1];
+  const int wv = b * kChainWaves + wave;
+  const int rec0 = wv_begin[wv], rec1 = wv_begin[wv + 1];
 
-  // ---- the walk (shared by both sides; side effects only on the compute side)
-  // Task of this wave in the current unit / strip of walk w.
-  auto set_task = [&](Walk& w) {
-    if (w.wk_ == 1) {
-      w.strip = w.u;
-      w.kt0 = 0;
-      w.nkt = w.KT;
-    } else {
-      const int wn = wave % w.wn_, wk = wave / w.wn_;
-      w.strip = w.u * w.wn_ + wn;
-      const bool has = wk < w.wk_ && w.strip < w.NS;
-      w.kt0 = has ? (wk * w.KT) / w.wk_ : 0;
-      w.nkt = has ? ((wk + 1) * w.KT) / w.wk_ - w.kt0 : 0;
-    }
-  };
-  auto enter_range = [&](Walk& w, const si4 e, const si16& c) {
-    w.item = e.x;
-    w.NS = c[kEntN] >> 4;
-    w.KT = c[kEntK] >> 8;
-    w.wn_ = c[kEntWn];
-    w.wk_ = c[kEntWk];
-    w.u0 = e.y;
-    w.u1 = e.z;
-    // the loop's step lands on the first unit, or on this wave's first strip
-    w.u = w.wk_ == 1 ? e.y + (wave - w.rot + kChainWaves) % kChainWaves - kChainWaves : e.y - 1;
-  };
-  auto leave_range = [&](Walk& w) {
-    if (w.wk_ == 1) w.rot = (w.rot + (w.u1 - w.u0)) % kChainWaves;
-    w.item = -1;
-  };
-
-  // ---- load side: the ring
-  Walk L{ev0, ev1, -1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-  const void* lcodes = nullptr;  // codes and scales of L's item
+  // ---- load side: this wave's tasks in record order, D positions ahead
+  int li = rec0;              // next record
+  int litem = -1;             // item whose codes and scales lcodes, lscales point to
+  const void* lcodes = nullptr;
   const void* lscales = nullptr;
-  int lj = 0;                 // next k-tile of L's task
-  bool lend = false;          // L has passed the last task
-  rsrc_t lcr = make_rsrc(table, 0), lsr = lcr;  // codes and scales of L's task (none yet: every load past the end)
-  auto lnext_task = [&]() {   // L to its next task with positions (or to the end)
-    const int kt0_last = L.kt0, nkt_last = L.nkt;
+  int lKT = 0;                // k-tiles of litem
+  int lkt0 = 0, lnkt = 0, lj = 0;  // current task: k-tiles [lkt0, lkt0 + lnkt), next lj
+  bool lend = false;          // past the last task
+  rsrc_t lcr = make_rsrc(table, 0), lsr = lcr;  // codes and scales of the task (none yet: loads read zeros)
+  auto lnext_task = [&]() {   // to the next task record (or to the end)
     for (;;) {
-      if (L.item >= 0) {
-        L.u += L.wk_ == 1 ? kChainWaves : 1;
-        if (L.u < L.u1) {
-          set_task(L);
-          if (L.nkt > 0) break;
-          continue;
-        }
-        leave_range(L);
-      }
-      if (L.ev >= L.ev_end) {  // the end: L stays on its last task's last position
+      if (li >= rec1) {       // the end: stay on the last task's last position
         lend = true;
-        L.kt0 = kt0_last;
-        L.nkt = nkt_last;
+        lj = max(lnkt - 1, 0);
         return;
       }
-      const si4 e = sload4(events + L.ev++);
-      if (e.w != 0) continue;  // a signal
-      const si16 c = sload16(table + e.x);
-      enter_range(L, e, c);
-      lcodes = ent_ptr(c, kEntCodes);
-      lscales = ent_ptr(c, kEntScales);
+      const si4 e = sload4(recs + li++);
+      const int type = e.x & 15;
+      if (type > kRecTaskUnit) continue;  // no positions
+      const int item = e.x >> 4;
+      if (item != litem) {
+        const si16 c = sload16(table + item);
+        lcodes = ent_ptr(c, kEntCodes);
+        lscales = ent_ptr(c, kEntScales);
+        lKT = c[kEntK] >> 8;
+        litem = item;
+      }
+      lkt0 = e.w & 0xffff;
+      lnkt = e.w >> 16;
+      lcr = make_rsrc((const char*)lcodes + (size_t)e.y * lKT * 1024, (uint32_t)lKT * 1024);
+      lsr = make_rsrc((const char*)lscales + (size_t)e.y * lKT * 32 * GPT, (uint32_t)lKT * 32 * GPT);
+      lj = 0;
+      return;
     }
-    lcr = make_rsrc((const char*)lcodes + (size_t)L.strip * L.KT * 1024, (uint32_t)L.KT * 1024);
-    lsr = make_rsrc((const char*)lscales + (size_t)L.strip * L.KT * 32 * GPT, (uint32_t)L.KT * 32 * GPT);
-    lj = 0;
   };
   struct Slot {
     u32x4 P;
     uint32_t sw[GPT / 2];
   };
-  // The next position of L into s, then L one on. Past the last task the
-  // last position is read again (a wave without tasks reads zeros: its
-  // resource holds no bytes), so that every load is issued the same way and
-  // the ring's memory-counter waits stay exact.
+  // The next position into s, then one on. Past the last task the last
+  // position is read again (a wave without tasks reads zeros: its resource
+  // holds no bytes), so that every load is issued the same way and the
+  // ring's memory-counter waits stay exact.
   auto lload = [&](Slot& s) {
-    const int kt = __builtin_amdgcn_readfirstlane(L.kt0 + lj);
+    const int kt = __builtin_amdgcn_readfirstlane(lkt0 + lj);
     s.P = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lcr, lane * 16, kt * 1024, kAuxNontemporal));
     if (GPT == 2) {
       s.sw[0] = __builtin_amdgcn_raw_buffer_load_b32(lsr, r * GPT * 2, kt * 32 * GPT, 0);
@@ -248,27 +209,25 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
       s.sw[0] = w2[0];
       s.sw[GPT / 2 - 1] = w2[1];
     }
-    if (!lend && ++lj == L.nkt) {
-      lnext_task();
-      if (lend) lj = max(L.nkt - 1, 0);
-    }
+    if (!lend && ++lj == lnkt) lnext_task();
   };
 
-  // ---- compute side
-  Walk C{ev0, ev1, -1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-  int cj = 0;              // next k-tile of C's task
+  // ---- compute side: every record of this wave, in order
+  int ci = rec0;             // next record
+  int ckt0 = 0, cnkt = 0, cj = 0;  // current task
+  int cstrip = 0, cunit = 0, ctype = 0;
   bool cend = false;
-  int lslot = 1;           // LDS slot of the limbs in use (the first item takes slot 0)
-  int limb_item = -1;      // item whose limbs are in slot lslot
-  int units_done = 0;      // Wk > 1 units passed (parity of red)
+  int lslot = 1;             // LDS slot of the limbs in use (the first item takes slot 0)
+  int units_done = 0;        // Wk > 1 units passed (parity of red)
+  int cwn = 1, cwk = 1, cNS = 0;  // plan of the current item
   float total = 0.f;
-  rsrc_t ys = make_rsrc(table, 0), ybs = ys;  // y and y_bf16 of C's item (0 bytes: no y_bf16)
+  rsrc_t ys = make_rsrc(table, 0), ybs = ys;  // y and y_bf16 of the current item (0 bytes: no y_bf16)
   const char* abase = nullptr;
   const int* dexp = nullptr;
 
   // Limbs of item i into the other LDS slot, after its wait (the whole
   // workgroup passes here together).
-  auto item_switch = [&](int i, const si16& e) {
+  auto item_switch = [&](const si16& e) {
     const int after = e[kEntAfter];
     if (after >= 0) {
       if (tid == 0) {
@@ -310,7 +269,15 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
       if ((c & 15) == 0) dx[c >> 4] = d;
     }
     lds_barrier();
-    limb_item = i;
+    // the item's plan and outputs
+    cwn = e[kEntWn];
+    cwk = e[kEntWk];
+    cNS = e[kEntN] >> 4;
+    const void* yb = ent_ptr(e, kEntYb);
+    ys = make_rsrc(ent_ptr(e, kEntY), (uint32_t)e[kEntN] * 4);
+    ybs = make_rsrc(yb, yb ? (uint32_t)e[kEntN] * 2 : 0u);
+    abase = base + (size_t)(r < 3 ? r : 0) * rs + 16 * g;
+    dexp = (const int*)(base + 3 * (size_t)rs);
   };
   // A signal: this workgroup is done with items 0..i.
   auto signal = [&](int i) {
@@ -321,86 +288,72 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
       __hip_atomic_fetch_add(&gcount[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
-  // Output o of C's item (buffer stores: a flat store would make the
-  // compiler wait for every outstanding load before the next position).
+  // Output o of the current item (buffer stores: a flat store would make
+  // the compiler wait for every outstanding load before the next position).
   auto store_y = [&](size_t o, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ys, (int)o * 4, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), ybs, (int)o * 2, 0, 0);  // dropped without y_bf16
   };
-  // End of a Wk > 1 unit: the shares meet in LDS, the first threads add them
-  // in ascending order and store.
-  auto unit_end = [&]() {
+  // End of unit u of a Wk > 1 item (with this wave's share, or without):
+  // the shares meet in LDS, the first threads add them in ascending order
+  // and store.
+  auto unit_end = [&](int u, bool share) {
     float* rb = red + (units_done & 1) * (kChainWaves * 16);
-    const int wn = wave % C.wn_, wk = wave / C.wn_;
-    if (C.nkt > 0 && lane < 16) rb[(wk * C.wn_ + wn) * 16 + lane] = total;
+    const int wn = wave % cwn, wk = wave / cwn;
+    if (share && lane < 16) rb[(wk * cwn + wn) * 16 + lane] = total;
     lds_barrier();
-    const int nsb = min(C.wn_, C.NS - C.u * C.wn_);
+    const int nsb = min(cwn, cNS - u * cwn);
     if (tid < nsb * 16) {
       const int ls = tid >> 4, col = tid & 15;
       float sum = 0.f;
-      for (int w = 0; w < C.wk_; ++w) sum += rb[(w * C.wn_ + ls) * 16 + col];
-      const size_t o = (size_t)(C.u * C.wn_ + ls) * 16 + col;
-      store_y(o, sum);
+      for (int w = 0; w < cwk; ++w) sum += rb[(w * cwn + ls) * 16 + col];
+      store_y((size_t)(u * cwn + ls) * 16 + col, sum);
     }
     ++units_done;
   };
-  // C to its next task with positions, doing the work between (unit ends
-  // of tasks without positions, item switches, waits, signals).
+  // To the next task record, doing the work of the records between
+  // (item switches, waits, signals, unit ends without a share).
   auto cnext_task = [&]() {
     for (;;) {
-      if (C.item >= 0) {
-        C.u += C.wk_ == 1 ? kChainWaves : 1;
-        if (C.u < C.u1) {
-          set_task(C);
-          if (C.nkt > 0) break;
-          unit_end();  // Wk > 1: a unit where this wave has no share
-          continue;
-        }
-        leave_range(C);
-      }
-      if (C.ev >= C.ev_end) {
+      if (ci >= rec1) {
         cend = true;
         return;
       }
-      const si4 e = sload4(events + C.ev++);
-      if (e.w != 0) {
-        signal(e.x);
-        continue;
-      }
-      const si16 c = sload16(table + e.x);
-      if (e.x != limb_item) {
-        item_switch(e.x, c);
+      const si4 e = sload4(recs + ci++);
+      const int type = e.x & 15;
+      if (type == kRecSwitch) {
+        item_switch(sload16(table + (e.x >> 4)));
         if (s_abort) {
           cend = true;
           return;
         }
+      } else if (type == kRecSignal) {
+        signal(e.x >> 4);
+      } else if (type == kRecUnit) {
+        unit_end(e.y, false);
+      } else {
+        ctype = type;
+        cstrip = e.y;
+        cunit = e.z;
+        ckt0 = e.w & 0xffff;
+        cnkt = e.w >> 16;
+        total = 0.f;
+        cj = 0;
+        return;
       }
-      enter_range(C, e, c);
-      const int n = c[kEntN];
-      const void* yb = ent_ptr(c, kEntYb);
-      ys = make_rsrc(ent_ptr(c, kEntY), (uint32_t)n * 4);
-      ybs = make_rsrc(yb, yb ? (uint32_t)n * 2 : 0u);
     }
-    const char* base = smem + (size_t)lslot * slot_bytes;
-    abase = base + (size_t)(r < 3 ? r : 0) * rs + 16 * g;
-    dexp = (const int*)(base + 3 * (size_t)rs);
-    total = 0.f;
-    cj = 0;
   };
-  // End of C's task: its sum to y, or to the unit's reduction.
+  // End of the current task: its sum to y, or to its unit's reduction.
   auto task_end = [&]() {
-    if (C.wk_ == 1) {
-      if (lane < 16) {
-        const size_t o = (size_t)C.strip * 16 + lane;
-        store_y(o, total);
-      }
+    if (ctype == kRecTask) {
+      if (lane < 16) store_y((size_t)cstrip * 16 + lane, total);
     } else {
-      unit_end();
+      unit_end(cunit, true);
     }
   };
-  // One position: the k-tile cj of C's task from ring slot s.
+  // One position: the k-tile cj of the current task from ring slot s.
   auto compute = [&](const Slot& s) {
-    const int kt = C.kt0 + cj;
+    const int kt = ckt0 + cj;
     i32x4 a[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = *(const i32x4*)(abase + 64 * (4 * kt + q));
@@ -441,7 +394,7 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
       compute(ring[S]);
       __builtin_amdgcn_sched_barrier(0);
       lload(ring[S]);
-      if (++cj == C.nkt) {
+      if (++cj == cnkt) {
         task_end();
         cnext_task();
       }

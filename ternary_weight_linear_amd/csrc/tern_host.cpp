@@ -1104,16 +1104,67 @@ std::vector<std::vector<std::array<int32_t, 4>>> chain_events(const std::vector<
   return ev;
 }
 
-size_t chain_table_size(int count, size_t events) {
-  return sizeof(int32_t) * 4 + (size_t)count * sizeof(tern::ChainEntry) +
-         (tern::kChainMaxWorkgroups + 4) * sizeof(int32_t) + events * 4 * sizeof(int32_t);
+size_t chain_table_size(int count, size_t records) {
+  return sizeof(int32_t) * 4 + (size_t)count * sizeof(tern::ChainEntry) + tern::kChainRecordOffsets * sizeof(int32_t) +
+         records * 4 * sizeof(int32_t);
 }
 
-// Events of a chain at most: every workgroup a run of every item, and every signal.
-size_t chain_events_bound(const std::vector<tern::ChainEntry>& t, int P) {
+// Records of a chain at most, for any number of workgroups up to
+// kChainMaxWorkgroups: every task, every unit end, every workgroup's switch
+// to every item (a workgroup has at most one run of an item) and every
+// signal, each of the last two for all 12 waves.
+size_t chain_records_bound(const std::vector<tern::ChainEntry>& t) {
+  const size_t P = tern::kChainMaxWorkgroups, W = tern::kChainWaves;
   size_t n = 0;
-  for (const auto& e : t) n += (size_t)std::min(P, e.units + 1) + (e.signal ? (size_t)P : 0);
+  for (const auto& e : t) {
+    n += e.wk == 1 ? (size_t)e.units : (size_t)e.units * W;
+    n += W * std::min(P, (size_t)e.units);
+    if (e.signal) n += W * P;
+  }
   return n;
+}
+
+// The events of each workgroup expanded into the record lists of its 12
+// waves (the layout of tern_chain.hip): every wave gets the same switches,
+// signals and unit ends in the same order; a wk = 1 run's strips go to the
+// waves in turn, continuing from where the workgroup's previous run stopped.
+std::vector<std::vector<std::array<int32_t, 4>>> chain_records(
+    const std::vector<tern::ChainEntry>& t, const std::vector<std::vector<std::array<int32_t, 4>>>& ev) {
+  const int W = tern::kChainWaves;
+  std::vector<std::vector<std::array<int32_t, 4>>> rec(ev.size() * W);
+  for (size_t b = 0; b < ev.size(); ++b) {
+    auto* wr = &rec[b * W];
+    int rot = 0, cur = -1;
+    for (const auto& e : ev[b]) {
+      const int i = e[0];
+      if (e[3] == 1) {
+        for (int w = 0; w < W; ++w) wr[w].push_back({4 | (i << 4), 0, 0, 0});  // signal
+        continue;
+      }
+      const tern::ChainEntry& c = t[(size_t)i];
+      const int KT = c.k / 256, NS = c.n / 16;
+      if (i != cur) {
+        for (int w = 0; w < W; ++w) wr[w].push_back({3 | (i << 4), 0, 0, 0});  // item switch
+        cur = i;
+      }
+      if (c.wk == 1) {
+        for (int u = e[1]; u < e[2]; ++u) wr[(rot + u - e[1]) % W].push_back({0 | (i << 4), u, 0, KT << 16});
+        rot = (rot + e[2] - e[1]) % W;
+      } else {
+        for (int u = e[1]; u < e[2]; ++u)
+          for (int w = 0; w < W; ++w) {
+            const int wn = w % c.wn, wk = w / c.wn, strip = u * c.wn + wn;
+            if (wk < c.wk && strip < NS) {
+              const int kt0 = (wk * KT) / c.wk, nkt = ((wk + 1) * KT) / c.wk - kt0;
+              wr[w].push_back({1 | (i << 4), strip, u, kt0 | (nkt << 16)});
+            } else {
+              wr[w].push_back({2 | (i << 4), u, 0, 0});
+            }
+          }
+      }
+    }
+  }
+  return rec;
 }
 
 }  // namespace
@@ -1124,8 +1175,8 @@ size_t tern_chain_table_bytes(const tern_chain_item* items, int count) {
   std::vector<tern::ChainEntry> t;
   ChainLayout lay;
   if (chain_plan_items(items, count, t, &lay) != TERN_OK) return 0;
-  // the run count depends on the device's workgroups: a bound for the most
-  return chain_table_size(count, chain_events_bound(t, tern::kChainMaxWorkgroups));
+  // the record count depends on the device's workgroups: a bound for the most
+  return chain_table_size(count, chain_records_bound(t));
 }
 
 tern_status tern_chain_build(const tern_chain_item* items, int count, void* table, size_t table_bytes,
@@ -1142,10 +1193,10 @@ tern_status tern_chain_build(const tern_chain_item* items, int count, void* tabl
   const int cerr = tern::device_cu_count(&cus);
   if (cerr) return hip_fail(cerr, "chain CU count");
   const int P = std::min(std::min(dev_max, cus), tern::kChainMaxWorkgroups);  // one workgroup per CU
-  const auto ev = chain_events(t, P);
-  size_t nev = 0;
-  for (const auto& l : ev) nev += l.size();
-  const size_t need = chain_table_size(count, nev);
+  const auto rec = chain_records(t, chain_events(t, P));
+  size_t nrec = 0;
+  for (const auto& l : rec) nrec += l.size();
+  const size_t need = chain_table_size(count, nrec);
   if (table_bytes < need) return fail(TERN_ERR_WORKSPACE, "chain table needs %zu bytes, got %zu", need, table_bytes);
   std::vector<char> blob(need, 0);
   int32_t* head = (int32_t*)blob.data();
@@ -1154,14 +1205,14 @@ tern_status tern_chain_build(const tern_chain_item* items, int count, void* tabl
   head[2] = count;
   head[3] = (int32_t)tern::kChainTableMagic;
   memcpy(blob.data() + 16, t.data(), t.size() * sizeof(tern::ChainEntry));
-  int32_t* wg_begin = (int32_t*)(blob.data() + 16 + t.size() * sizeof(tern::ChainEntry));
-  int32_t* events = wg_begin + tern::kChainMaxWorkgroups + 4;
+  int32_t* wv_begin = (int32_t*)(blob.data() + 16 + t.size() * sizeof(tern::ChainEntry));
+  int32_t* recs = wv_begin + tern::kChainRecordOffsets;
   int32_t pos = 0;
-  for (int w = 0; w < tern::kChainMaxWorkgroups + 4; ++w) {
-    wg_begin[w] = pos;
-    if (w < P)
-      for (const auto& e : ev[(size_t)w]) {
-        memcpy(events + 4 * pos, e.data(), sizeof(int32_t) * 4);
+  for (size_t v = 0; v < (size_t)tern::kChainRecordOffsets; ++v) {
+    wv_begin[v] = pos;
+    if (v < rec.size())
+      for (const auto& e : rec[v]) {
+        memcpy(recs + 4 * (size_t)pos, e.data(), sizeof(int32_t) * 4);
         ++pos;
       }
   }

@@ -146,14 +146,17 @@ struct ChainEntry {
 };
 static_assert(sizeof(ChainEntry) == 80, "chain table layout");
 constexpr int kChainWaves = 12;  // waves per workgroup of the chain kernel (one workgroup per CU)
-constexpr int kChainMaxWorkgroups = 1024;
+constexpr int kChainMaxWorkgroups = 512;
 constexpr unsigned kChainTableMagic = 0x4e484331u;  // "1CHN"
+constexpr int kChainRecordOffsets = kChainMaxWorkgroups * kChainWaves + 4;
 // Device table of a chain:
 //   int4 header {row bytes of a limb row, bytes of an LDS limb slot, count, kChainTableMagic};
 //   count ChainEntry;
-//   kChainMaxWorkgroups + 4 ints: workgroup w's events are events[wg_begin[w] .. wg_begin[w + 1]);
-//   int4 events {item, u0, u1, kind}: kind 0 = units (or strips) [u0, u1) of the item, kind 1 = a
-//   signal after the item.
+//   kChainRecordOffsets ints: wave v = workgroup * kChainWaves + wave reads records
+//   [wv_begin[v], wv_begin[v + 1]);
+//   int4 records {type | item << 4, strip or unit, unit, kt0 | nkt << 16} (tern_chain.hip): every
+//   wave of a workgroup holds the same item switches, signals and unit ends, in the same order, and
+//   its own tasks among them.
 // LDS of the kernel: two limb slots of slot_bytes (3 limb rows, then the
 // k-tile exponents), then 2 x 12 x 16 floats of K-share sums.
 // Launches the chain kernel: `workgroups` workgroups of kChainWaves waves

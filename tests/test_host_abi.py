@@ -473,18 +473,21 @@ def _chain(tl, shapes, afters, group=128, layout=None):
 
 
 def test_chain_table_bytes_and_validation(tl):
-    """The table holds a header, the entries, the workgroup offsets and
-    room for the events of up to 1024 workgroups (a run of each item per
-    workgroup, at most one per unit, and a signal per workgroup after every
-    item that is waited on); invalid chains are refused before any HIP call."""
+    """The table holds a header, the entries, the offsets of the record lists
+    of up to 512 workgroups of 12 waves, and room for their records: every
+    task and unit end, a switch per workgroup run of each item (at most one
+    run per unit) and a signal per workgroup after every item that is
+    waited on, the last two for each wave; invalid chains are refused before
+    any HIP call."""
     L = tl.lib()
     shapes = [(5120, 5120), (34816, 5120), (5120, 17408)]
     arr = _chain(tl, shapes, [-1, 0, 1])
-    # units: 320 strips in threes (K in 4 shares), 2176 single strips (K
-    # whole), 320 strips in twos (K in 6 shares); items 0 and 1 signal
-    runs = min(1024, 107 + 1) + min(1024, 2176 + 1) + min(1024, 160 + 1)
-    events = runs + 2 * 1024
-    assert L.tern_chain_table_bytes(arr, 3) == 16 + 3 * 80 + (1024 + 4) * 4 + 16 * events
+    # units: 320 strips in threes (K in 4 shares: 12 records a unit), 2176
+    # single strips (K whole), 320 strips in twos (K in 6 shares); items 0
+    # and 1 signal
+    P, W = 512, 12
+    records = (107 * W + W * 107 + W * P) + (2176 + W * P + W * P) + (160 * W + W * 160)
+    assert L.tern_chain_table_bytes(arr, 3) == 16 + 3 * 80 + (P * W + 4) * 4 + 16 * records
     assert L.tern_chain_table_bytes(_chain(tl, shapes, [-1, 2, 1]), 3) == 0  # after must be earlier
     assert "after" in L.tern_last_error().decode()
     assert L.tern_chain_table_bytes(_chain(tl, shapes, [-1, -1, -1], layout=tl.LAYOUT_T5), 3) == 0
