@@ -333,16 +333,18 @@ typedef struct {
 } tern_chain_plan;
 
 /* Device bytes to allocate for the chain table of these items: enough for
- * any device (up to 1024 workgroups); 0 if the chain is invalid
+ * any device (up to 512 workgroups); 0 if the chain is invalid
  * (tern_last_error says why). */
 size_t tern_chain_table_bytes(const tern_chain_item* items, int count);
 /* Device bytes of the completion counters of `count` items (count + 1 ints). */
 size_t tern_chain_counter_bytes(int count);
 /*
  * Validates the chain (host), splits every item's K as the gemv rung does,
- * cuts the chain into stages at the items that wait and gives each of one
+ * cuts the chain into stages at the items that wait, gives each of one
  * workgroup per CU of the current device a contiguous run of every stage's
- * work, balanced by bytes, and writes the table (device memory, at least
+ * work, balanced by bytes, expands it into the list of tasks and
+ * synchronisation points each of the workgroup's waves walks, and writes
+ * the table (device memory, at least
  * tern_chain_table_bytes(items, count) bytes, 16-byte aligned) with one
  * synchronous host-to-device copy. Build once per set of buffers; the table
  * holds the pointers of items[]. The limbs of two items' activations share
