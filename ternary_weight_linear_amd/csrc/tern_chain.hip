@@ -6,23 +6,26 @@
 // ramp and drain.
 //
 // One workgroup of 12 waves per CU. The host cuts the chain into stages at
-// the items that wait, and gives every workgroup one contiguous run of each
-// stage's work, balanced by bytes of codes: its event list holds ranges of
-// work of one item at a time, in item order, and a signal after every item
-// that a later one waits on. Work of an item with its K split over Wk waves
-// (the gemv's plan) comes in units of 12 / Wk strips, each wave one K share
-// of one strip, the shares added through LDS in ascending order; work of an
-// item with Wk = 1 comes as single strips, dealt over the waves in turn.
+// the items that depend on an item of the current stage, gives every
+// workgroup one contiguous run of each stage's work (balanced by bytes of
+// codes), and expands it into one record list per wave: its tasks (a strip
+// and a range of k-tiles), and, the same in every wave of the workgroup and
+// in the same order, the item switches, the signals after items that a later
+// one waits on, and the ends of units. Work of an item with its K split over
+// Wk waves (the gemv's plan) comes in units of 12 / Wk strips, each wave one
+// K share of one strip, the shares added through LDS in ascending order;
+// work of an item with Wk = 1 comes as single strips, dealt over the waves
+// in turn.
 //
-// Streaming. Each wave walks its own sequence of (strip, k-tile) positions
-// across units, items and stages, and keeps the codes and scales of its
-// next D positions in flight in registers, so the weight stream does not
-// stop at a unit's or an item's end. The positions are processed in groups
-// of D with the ring slot of every position fixed at compile time, each slot
-// reloaded right after its compute (the compiler's memory-counter waits then
-// keep the whole ring in flight at every position); the work between
-// positions (unit ends, item switches, waits, signals) sits in each of the D
-// steps.
+// Streaming. Each wave walks its record list twice, once to request
+// positions (strip, k-tile) and once to compute them, D positions apart: the
+// codes and scales of its next D positions stay in flight in registers, so
+// the weight stream does not stop at a unit's or an item's end. The
+// positions are processed in groups of D with the ring slot of every
+// position fixed at compile time, each slot reloaded right after its
+// compute (the compiler's memory-counter waits then keep the whole ring in
+// flight at every position); the records between positions (unit ends,
+// item switches, waits, signals) are handled in each of the D steps.
 //
 // Limbs of x. The int8 limbs of the current item's activations live in one
 // of two LDS slots; at an item switch the workgroup makes the next item's
@@ -33,7 +36,8 @@
 // Dependencies (after = j: items 0..j all finished) go through device-scope
 // counters: at a signal every wave waits for its stores, the workgroup meets
 // at a barrier and one thread issues a release fence and adds one to the
-// item's counter; a waiting workgroup's thread 0 polls counter j until it
+// item's counter; at an item switch that needs it (the first of the
+// workgroup's items with that dependency), thread 0 polls counter j until it
 // reaches the number of workgroups (bounded by spin_limit, then it sets
 // *error_flag and the workgroup skips the rest), issues an acquire fence and
 // the workgroup meets at a barrier before it reads x. The last workgroup out
@@ -109,7 +113,7 @@ constexpr int kEntN = 10, kEntK = 11, kEntWn = 12, kEntWk = 13, kEntAfter = 15; 
 constexpr int kRecTask = 0;      // a strip's k-tiles [kt0, kt0 + nkt), its sum to y (K not split)
 constexpr int kRecTaskUnit = 1;  // one K share of a strip of unit `unit`, then the unit's reduction
 constexpr int kRecUnit = 2;      // the reduction of unit `y` without a share of this wave
-constexpr int kRecSwitch = 3;    // the workgroup moves to the item (wait, limbs)
+constexpr int kRecSwitch = 3;    // the workgroup moves to the item (y = 1: wait for its dependency; limbs)
 constexpr int kRecSignal = 4;    // the workgroup is done with items 0..item
 static_assert(offsetof(ChainEntry, n) == 4 * kEntN && offsetof(ChainEntry, after) == 4 * kEntAfter &&
                   offsetof(ChainEntry, y_bf16) == 8 * kEntYb && offsetof(ChainEntry, wk) == 4 * kEntWk,
@@ -227,9 +231,9 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
 
   // Limbs of item i into the other LDS slot, after its wait (the whole
   // workgroup passes here together).
-  auto item_switch = [&](const si16& e) {
+  auto item_switch = [&](const si16& e, bool wait) {
     const int after = e[kEntAfter];
-    if (after >= 0) {
+    if (wait && after >= 0) {
       if (tid == 0) {
         bool ok = false;
         for (int it = 0;; ++it) {
@@ -322,7 +326,7 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
       const si4 e = sload4(recs + ci++);
       const int type = e.x & 15;
       if (type == kRecSwitch) {
-        item_switch(sload16(table + (e.x >> 4)));
+        item_switch(sload16(table + (e.x >> 4)), e.y != 0);
         if (s_abort) {
           cend = true;
           return;

@@ -1062,7 +1062,7 @@ tern_status chain_plan_items(const tern_chain_item* items, int count, std::vecto
 }
 
 // Work of a chain for P workgroups: the items are cut into stages at every
-// item that waits; each stage's units (in item order) are dealt to the
+// item that depends on an item of the current stage; each stage's units (in item order) are dealt to the
 // workgroups in contiguous runs of about equal cost, so a workgroup switches
 // items (and makes new limbs) a few times per stage at most. Cost of a unit,
 // in k-tiles a wave streams: wk = 1, one strip of KT k-tiles (dealt over the
@@ -1073,8 +1073,10 @@ std::vector<std::vector<std::array<int32_t, 4>>> chain_events(const std::vector<
   std::vector<std::vector<std::array<int32_t, 4>>> ev((size_t)P);
   const int count = (int)t.size();
   for (int s0 = 0; s0 < count;) {
+    // a stage runs on until an item depends on one inside it (items whose
+    // dependency lies before the stage, like k and v beside q, join it)
     int s1 = s0 + 1;
-    while (s1 < count && t[(size_t)s1].after < 0) ++s1;
+    while (s1 < count && t[(size_t)s1].after < s0) ++s1;
     auto cost = [&](const tern::ChainEntry& e) {
       const int KT = e.k / 256;
       return e.wk == 1 ? (double)KT : (double)tern::kChainWaves * ((KT + e.wk - 1) / e.wk + 1);
@@ -1134,7 +1136,7 @@ std::vector<std::vector<std::array<int32_t, 4>>> chain_records(
   std::vector<std::vector<std::array<int32_t, 4>>> rec(ev.size() * W);
   for (size_t b = 0; b < ev.size(); ++b) {
     auto* wr = &rec[b * W];
-    int rot = 0, cur = -1;
+    int rot = 0, cur = -1, waited = -1;  // waited: the highest counter this workgroup has waited for
     for (const auto& e : ev[b]) {
       const int i = e[0];
       if (e[3] == 1) {
@@ -1144,7 +1146,11 @@ std::vector<std::vector<std::array<int32_t, 4>>> chain_records(
       const tern::ChainEntry& c = t[(size_t)i];
       const int KT = c.k / 256, NS = c.n / 16;
       if (i != cur) {
-        for (int w = 0; w < W; ++w) wr[w].push_back({3 | (i << 4), 0, 0, 0});  // item switch
+        // item switch; y = 1: wait for counter `after` first (not needed
+        // when the workgroup has already waited for it or a later one)
+        const int wait = c.after > waited ? 1 : 0;
+        if (wait) waited = c.after;
+        for (int w = 0; w < W; ++w) wr[w].push_back({3 | (i << 4), wait, 0, 0});
         cur = i;
       }
       if (c.wk == 1) {

@@ -139,3 +139,30 @@ def test_chain_wait_gives_up_and_exits(tl, torch):
     torch.cuda.synchronize()
     assert not ch.failed()
     assert torch.equal(y1.view(torch.int32), tl.linear(x1, W1).view(torch.int32))
+
+
+def test_chain_fresh_inputs_each_launch(tl, torch):
+    """Chained projections with two items in one stage (both reading the
+    first item's output, like k and v beside q) and a third reading one of
+    them; x0 changes before every launch, so a read of an earlier launch's
+    (stale) values would show: every stage bit-identical to tern_linear on
+    that launch's inputs."""
+    shapes = [ts.stack_shape(2, 3), ts.stack_shape(2, 0), ts.stack_shape(2, 4), ts.stack_shape(2, 6)]
+    ws = [ts.weights(sh) for sh in shapes]
+    Ws = [tl.TernaryWeights.from_host(w.w, w.s) for w in ws]
+    x0 = torch.empty((1, Ws[0].k), dtype=torch.bfloat16, device="cuda")
+    ys = [torch.empty((1, W.n), device="cuda") for W in Ws]
+    ybs = [torch.empty((1, W.n), dtype=torch.bfloat16, device="cuda") for W in Ws]
+    srcs = [x0, ybs[0], ybs[0], ybs[2]]
+    afters = [-1, 0, 0, 2]
+    ch = tl.Chain([(Ws[i], srcs[i], ys[i], ybs[i], afters[i]) for i in range(4)])
+    for rep in range(4):
+        x0.copy_(dev_bf16(torch, ts.activations(ws[0], 1, salt=rep + 7)))
+        ch.run()
+        torch.cuda.synchronize()
+        assert not ch.failed(), rep
+        refs = []
+        for i, W in enumerate(Ws):
+            src = x0 if i == 0 else refs[afters[i]].to(torch.bfloat16)
+            refs.append(tl.linear(src, W))
+            assert torch.equal(ys[i].view(torch.int32), refs[i].view(torch.int32)), (rep, i)
