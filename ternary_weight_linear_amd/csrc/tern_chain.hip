@@ -34,12 +34,15 @@
 // finishing the previous item keep reading theirs.
 //
 // Dependencies (after = j: items 0..j all finished) go through device-scope
-// counters: at a signal every wave waits for its stores, the workgroup meets
-// at a barrier and one thread issues a release fence and adds one to the
-// item's counter; at an item switch that needs it (the first of the
-// workgroup's items with that dependency), thread 0 polls counter j until it
-// reaches the number of workgroups (bounded by spin_limit, then it sets
-// *error_flag and the workgroup skips the rest), issues an acquire fence and
+// counters. Every value that crosses items (y, y_bf16, and x read from them)
+// is stored and loaded with device-scope coherent accesses, the accesses of
+// relaxed device-scope atomics, so no L2 write-back or invalidation is
+// needed (each cost about 2-3 us per stage as fences): at a signal every
+// wave waits for its stores to complete, the workgroup meets at a barrier
+// and one thread adds one to the item's counter; at an item switch that
+// needs it (the first of the workgroup's items with that dependency), thread
+// 0 polls counter j until it reaches the number of workgroups (bounded by
+// spin_limit, then it sets *error_flag and the workgroup skips the rest) and
 // the workgroup meets at a barrier before it reads x. The last workgroup out
 // zeroes the counters for the next launch.
 //
@@ -61,6 +64,11 @@ namespace {
 using namespace dev;
 
 constexpr int kChainThreads = 64 * kChainWaves;
+// Cache policy of the accesses that carry data between items: device
+// (agent) scope, the encoding of a relaxed device-scope atomic access, which
+// is coherent across the XCDs' L2 caches by itself (stores written through,
+// loads not served from a stale line).
+constexpr int kAuxAgent = 16;  // sc1
 constexpr int kChainDepth = 8;  // positions of codes and scales in flight per wave
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
@@ -248,7 +256,6 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
           }
           __builtin_amdgcn_s_sleep(2);
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // later reads of x see the producers' stores
         if (!ok) s_abort = 1;
       }
       lds_barrier();
@@ -261,8 +268,9 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
     const rsrc_t xr = make_rsrc(ent_ptr(e, kEntX), (uint32_t)K * 2);
     for (int c = tid; c < (K >> 4); c += kChainThreads) {  // rows of 16 lanes are wholly in or out
       const int off = 64 * (c >> 2) + 8 * (c & 3);
-      const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off * 2, 0, 0));
-      const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (off + 32) * 2, 0, 0));
+      const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off * 2, 0, kAuxAgent));
+      const u32x4 hi =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (off + 32) * 2, 0, kAuxAgent));
       const int d = limb_shift(row16_max_u32(absmax16(lo, hi)));
       u32x4 o0, o1, o2;
       limb_chunk(lo, hi, d, o0, o1, o2);
@@ -283,20 +291,21 @@ __global__ void __launch_bounds__(kChainThreads) tern_chain_kernel(const int4* _
     abase = base + (size_t)(r < 3 ? r : 0) * rs + 16 * g;
     dexp = (const int*)(base + 3 * (size_t)rs);
   };
-  // A signal: this workgroup is done with items 0..i.
+  // A signal: this workgroup is done with items 0..i. Its outputs went out
+  // as device-coherent stores, so once they have completed (the wait, every
+  // wave, then the barrier) they are visible to every XCD, and no L2
+  // write-back is needed before the count.
   auto signal = [&](int i) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed (reached its L2)
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
     lds_barrier();                  // ... and every other wave's
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // write them back for every XCD
-      __hip_atomic_fetch_add(&gcount[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid == 0) __hip_atomic_fetch_add(&gcount[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  // Output o of the current item (buffer stores: a flat store would make
-  // the compiler wait for every outstanding load before the next position).
+  // Output o of the current item: device-coherent buffer stores (written
+  // through to where every XCD reads them; a flat store would also make the
+  // compiler wait for every outstanding load before the next position).
   auto store_y = [&](size_t o, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ys, (int)o * 4, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), ybs, (int)o * 2, 0, 0);  // dropped without y_bf16
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ys, (int)o * 4, 0, kAuxAgent);
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), ybs, (int)o * 2, 0, kAuxAgent);  // dropped without y_bf16
   };
   // End of unit u of a Wk > 1 item (with this wave's share, or without):
   // the shares meet in LDS, the first threads add them in ascending order
