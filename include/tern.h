@@ -310,7 +310,8 @@ tern_status tern_linear_noalloc(const void* x_bf16, int T, const tern_weights* W
  * Dependencies: item i with after = j (j < i) reads its x only once items
  * 0..j have all finished (their y and y_bf16 stores visible), e.g. x of item
  * i = y_bf16 of item j; after = -1 reads x at any time. Completion goes
- * through device-scope counters in caller memory (release / acquire); every
+ * through device-scope counters in caller memory, and y, y_bf16 and x move
+ * with device-coherent stores and loads; every
  * wait polls at most spin_limit times (each poll sleeps about 0.05 us plus
  * a memory round trip), then sets *error_flag = 1 and the rest of the chain
  * is skipped: the kernel always exits, and the results are then undefined.
