@@ -534,8 +534,9 @@ def kernels_only(torch, ts, tl, dev, n):
     + contraction, T=2048), n/10 of the bf16 prefill (T=2048), n of the T=8
     draft-verify batch, n of the rotated quantisation (T=2048), n of the gemv
     on base-3 (t5) weights, n of the decode step (gate_up + down) as one
-    chain launch, then plain 64 MiB device copies whose byte counters
-    calibrate FETCH_SIZE / WRITE_SIZE."""
+    chain launch, n each of down and o_proj at T = 1, 4 and 16, then plain
+    64 MiB device copies whose byte counters calibrate FETCH_SIZE /
+    WRITE_SIZE."""
     w = ts.weights(ts.GATE_UP)
     b = tl.TernaryWeights.from_host(w.w, w.s, device=dev)
     sets = [b] + [tl.TernaryWeights(b.codes.clone(), b.scales.clone(), b.n, b.k, b.group)
@@ -589,6 +590,22 @@ def kernels_only(torch, ts, tl, dev, n):
         chains[i % nch].run()
     torch.cuda.synchronize()
     del chains
+    # narrow layers (down 17408 -> 5120, o_proj 5120 -> 5120): the gemv (T = 1)
+    # and the draft-verify kernels at T = 4 and T = 16, weights rotated likewise
+    for shape in (ts.DOWN, ts.OUT_PROJ):
+        wn = ts.weights(shape)
+        bn = tl.TernaryWeights.from_host(wn.w, wn.s, device=dev)
+        sn = [bn] + [tl.TernaryWeights(bn.codes.clone(), bn.scales.clone(), bn.n, bn.k, bn.group)
+                     for _ in range(max(1, math.ceil(ROTATE_BYTES / bn.nbytes)) - 1)]
+        for T in (1, 4, 16):
+            xn = torch.from_numpy(ts.activations(wn, T).view(np.int16)).to(dev).view(torch.bfloat16)
+            yn = torch.empty((T, bn.n), dtype=torch.float32, device=dev)
+            wsn = torch.empty((max(1, tl.workspace_bytes(T, bn.n, bn.k, bn.group)),), dtype=torch.uint8, device=dev)
+            for i in range(n):
+                tl.linear(xn, sn[i % len(sn)], y=yn, workspace=wsn)
+            torch.cuda.synchronize()
+        del sn, bn
+        torch.cuda.empty_cache()
     src = torch.empty(64 * 2**20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
