@@ -47,7 +47,7 @@ METRIC = "ternary linear HBM GB/s (% peak) at T=1; int8 TOPS (% peak) at T=2048"
 # their launch plans: a change to any of them voids the stored counters.
 KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
                for f in ("tern_limb.hip", "tern_s8.hip", "tern_s8mma.hip", "tern_b16mma.hip",
-                         "tern_tile.hip", "tern_limbtile.hip", "tern_chain.hip", "tern_device.h",
+                         "tern_tile.hip", "tern_limbtile.hip", "tern_chain.hip", "tern_narrow.hip", "tern_device.h",
                          "tern_internal.h", "tern_host.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -307,7 +307,7 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
     y1 = [torch.empty((1, b.n), dtype=torch.float32, device=dev) for b in base]
     yp = [torch.empty((1024, b.n), dtype=torch.float32, device=dev) for b in base]
     wsz = max(tl.workspace_bytes(1024, b.n, b.k, b.group) for b in base)
-    wsp = torch.empty((wsz,), dtype=torch.uint8, device=dev)
+    wsp = torch.zeros((wsz,), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"stack: {ts.STACK_LAYERS} layers x {len(base)} projections, {nbytes / 1e9:.2f} GB resident")
 
@@ -379,7 +379,7 @@ def stack_leg(torch, ts, tl, dev, decode_reps=10, prefill_reps=2):
     fy1 = [torch.empty((1, b.n), dtype=torch.float32, device=dev) for b in flayers[0]]
     fyp = [torch.empty((1024, b.n), dtype=torch.float32, device=dev) for b in flayers[0]]
     fwsz = max(tl.workspace_bytes(1024, b.n, b.k, b.group) for b in flayers[0])
-    fwsp = torch.empty((fwsz,), dtype=torch.uint8, device=dev)
+    fwsp = torch.zeros((fwsz,), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def fdecode_pass(_):
@@ -498,7 +498,7 @@ def small_t_leg(torch, ts, tl, dev, steps=1000):
             x = torch.from_numpy(ts.activations(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
             y = torch.empty((T, shape.n), dtype=torch.float32, device=dev)
             wsz = tl.workspace_bytes(T, shape.n, shape.k, shape.group)
-            wsp = torch.empty((max(1, wsz),), dtype=torch.uint8, device=dev)
+            wsp = torch.zeros((max(1, wsz),), dtype=torch.uint8, device=dev)
             rung = tl.resolve_rung(T)
 
             def one(i):
@@ -546,7 +546,7 @@ def kernels_only(torch, ts, tl, dev, n):
     T = 2048
     x8 = torch.from_numpy(ts.activations(w, T).view(np.int16)).to(dev).view(torch.bfloat16)
     y8 = torch.empty((T, b.n), dtype=torch.float32, device=dev)
-    ws = torch.empty((tl.workspace_bytes(T, b.n, b.k, b.group),), dtype=torch.uint8, device=dev)
+    ws = torch.zeros((tl.workspace_bytes(T, b.n, b.k, b.group),), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     for i in range(n):
         tl.linear(x1, sets[i % len(sets)], y=y1)
@@ -600,7 +600,7 @@ def kernels_only(torch, ts, tl, dev, n):
         for T in (1, 4, 16):
             xn = torch.from_numpy(ts.activations(wn, T).view(np.int16)).to(dev).view(torch.bfloat16)
             yn = torch.empty((T, bn.n), dtype=torch.float32, device=dev)
-            wsn = torch.empty((max(1, tl.workspace_bytes(T, bn.n, bn.k, bn.group)),), dtype=torch.uint8, device=dev)
+            wsn = torch.zeros((max(1, tl.workspace_bytes(T, bn.n, bn.k, bn.group)),), dtype=torch.uint8, device=dev)
             for i in range(n):
                 tl.linear(xn, sn[i % len(sn)], y=yn, workspace=wsn)
             torch.cuda.synchronize()
@@ -729,7 +729,7 @@ def main():
               for w in wts]
         ys = [torch.empty((T, s.n), dtype=torch.float32, device=dev) for s in shapes]
         wsz = max(tl.workspace_bytes(T, s.n, s.k, s.group) for s in shapes)
-        wsp = torch.empty((wsz,), dtype=torch.uint8, device=dev)
+        wsp = torch.zeros((wsz,), dtype=torch.uint8, device=dev)
         qs = [tl.quant_act_s8(x, layout="operand_order") for x in xs]
         assert tl.resolve_rung(T) == "s8"
         ops = sum(2 * T * s.n * s.k for s in shapes)

@@ -237,8 +237,13 @@ tern_status tern_quant_act_s8_rot(const void* x_bf16, int T, int k, int8_t* q, f
  * int8 limbs of the activations are made inside the contraction kernel and
  * need none; forced with TERN_TUNE_SMALLT=limb2, or at T = 5..8 with
  * TERN_TUNE_SMALLT=limb, a prep kernel keeps them and their per-k-tile
- * exponents here.) The contents need no initialisation and are not
- * preserved. Every scratch buffer of every rung is counted here; a call given less fails with
+ * exponents here.) Whenever this is not 0 it includes a header of 4096
+ * bytes at the start of the workspace, which only the narrow-layer kernel
+ * (TERN_KERNEL_SMALLT_NARROW) uses: arrival counters that must be zero before
+ * the workspace's first use (one hipMemset) and that every call leaves zero,
+ * also when calls of other rungs share the workspace. The rest needs no
+ * initialisation and is not preserved. Every scratch buffer of every rung is
+ * counted here; a call given less fails with
  * TERN_ERR_WORKSPACE ("NINFER ternary perf-tuning" notes, section 5 item 8:
  * the workspace capacity declaration must cover every scratch).
  * rung may be TERN_RUNG_AUTO (resolved the way tern_linear resolves it).
@@ -281,7 +286,9 @@ tern_status tern_linear(const void* x_bf16, int T, const tern_weights* W, float*
  * tern_linear, with the workspace taken from a static device scratch of
  * TERN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
  * until the process ends. The call allocates nothing; it needs no
- * initialisation of the scratch (every kernel writes what it later reads).
+ * initialisation of the scratch (it is zero when the library is loaded, the
+ * counter header of tern_workspace_bytes stays zero after every call, and
+ * every kernel writes the rest before it reads it).
  *  - A call whose tern_workspace_bytes() exceeds TERN_NOALLOC_SCRATCH_BYTES
  *    fails with TERN_ERR_WORKSPACE before any HIP call (e.g. the s8 rung
  *    from about 3,800 tokens at K = 17408).
@@ -451,6 +458,7 @@ typedef enum {
   TERN_KERNEL_STREAM_READ,        /* tern_stream_read */
   TERN_KERNEL_GEMV_T5,            /* gemv on base-3 (t5) weights: limbs of x on the i8 matrix cores */
   TERN_KERNEL_CHAIN,              /* tern_linear_chain: a chain of T = 1 projections in one launch */
+  TERN_KERNEL_SMALLT_NARROW,      /* small_t / small_t_tiled on narrow layers: K split over workgroups, partials added in-launch */
   TERN_KERNEL_COUNT
 } tern_kernel;
 

@@ -47,7 +47,8 @@ STATUS = {0: "TERN_OK", 1: "TERN_ERR_NULL", 2: "TERN_ERR_SHAPE", 3: "TERN_ERR_AL
 KERNELS = ("quant_s8", "quant_s8_row", "quant_s8_rot", "gemv_limb", "gemv_bf16",
            "smallt_resident", "smallt_limb_fused", "smallt_limb_prep", "smallt_limb_tile",
            "smallt_wave", "smallt_tile", "smallt_tile_reduce", "b16_prefill", "s8_mma",
-           "s8_reduce", "s8_row", "s8_acc_export", "stream_read", "gemv_t5", "chain")
+           "s8_reduce", "s8_row", "s8_acc_export", "stream_read", "gemv_t5", "chain",
+           "smallt_narrow")
 
 # Symbols declared in include/tern.h (checked by the host tests).
 EXPORTS = ("tern_packed_code_bytes", "tern_scale_count", "tern_pack", "tern_unpack",
@@ -400,7 +401,8 @@ def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=Non
         raise TernError(5, lib().tern_last_error().decode())
     new_ws = workspace is None and need > 0
     if new_ws:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+        # zeroed: the workspace header holds arrival counters that start at zero
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().tern_linear(x.data_ptr(), T, W.ref(), y.data_ptr(), r, ws_ptr, ws_bytes,

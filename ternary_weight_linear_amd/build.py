@@ -62,6 +62,7 @@ def build(verbose: bool = True) -> str:
     pr_obj = os.path.join(BUILD, "tern_probe.o")
     na_obj = os.path.join(BUILD, "tern_noalloc.o")
     ch_obj = os.path.join(BUILD, "tern_chain.o")
+    nw_obj = os.path.join(BUILD, "tern_narrow.o")
     h_obj = os.path.join(BUILD, "tern_host.o")
     _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_kernels.hip"), "-o", k_obj])
     _run([HIPCC, *HIP_FLAGS, *S8_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_s8.hip"), "-o", s8_obj])
@@ -73,10 +74,11 @@ def build(verbose: bool = True) -> str:
     _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_probe.hip"), "-o", pr_obj])
     _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_noalloc.hip"), "-o", na_obj])
     _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_chain.hip"), "-o", ch_obj])
+    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_narrow.hip"), "-o", nw_obj])
     _run(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_host.cpp"), "-o", h_obj])
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, k_obj, s8_obj, s8m_obj, b16_obj, t_obj, limb_obj, lt_obj,
-          pr_obj, na_obj, ch_obj, h_obj])
+          pr_obj, na_obj, ch_obj, nw_obj, h_obj])
     os.replace(tmp, LIB)
     return LIB
 

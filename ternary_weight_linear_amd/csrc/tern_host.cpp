@@ -13,6 +13,7 @@
 #include <array>
 #include <atomic>
 #include <cerrno>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -51,8 +52,9 @@ const char* const kKernelNames[TERN_KERNEL_COUNT] = {
     "quant_s8",        "quant_s8_row",      "quant_s8_rot",   "gemv_limb",        "gemv_bf16",
     "smallt_resident", "smallt_limb_fused", "smallt_limb_prep", "smallt_limb_tile", "smallt_wave",
     "smallt_tile",     "smallt_tile_reduce", "b16_prefill",   "s8_mma",           "s8_reduce",
-    "s8_row",          "s8_acc_export",     "stream_read",    "gemv_t5",          "chain"};
-static_assert(TERN_KERNEL_COUNT == 20, "one name per kernel id");
+    "s8_row",          "s8_acc_export",     "stream_read",    "gemv_t5",          "chain",
+    "smallt_narrow"};
+static_assert(TERN_KERNEL_COUNT == 21, "one name per kernel id");
 
 // ------------------------------------------------------------ configuration
 
@@ -77,8 +79,9 @@ struct Config {
   int tune_wk = 0;                    // TERN_TUNE_WK (0 = heuristic)
   int tune_depth = 0;                 // TERN_TUNE_DEPTH (0 = heuristic)
   bool gemv_bf16 = false;             // TERN_TUNE_GEMV=bf16: time the bf16-operand gemv kernel (default: limb)
+  bool gemv_narrow = false;           // TERN_TUNE_GEMV=narrow: narrow layers at T = 1 on the narrow-layer kernel
   bool t5_lanes = false;              // TERN_TUNE_T5=lanes: resident limbs at T = 5 in two token-lane row blocks
-  int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave, 3 = limb, 4 = resident
+  int smallt_kernel = 0;              // TERN_TUNE_SMALLT: 0 = by shape, 1 = tile, 2 = wave, 3 = limb, 4 = resident, 5 = narrow
   bool limb_unfused = false;          // TERN_TUNE_SMALLT=limb2: limbs by the separate prep kernel
 };
 
@@ -195,6 +198,8 @@ Config read_config() {
   if (const char* s = getenv("TERN_TUNE_GEMV")) {
     if (strcmp(s, "bf16") == 0)
       c.gemv_bf16 = true;
+    else if (strcmp(s, "narrow") == 0)
+      c.gemv_narrow = true;
     else if (strcmp(s, "limb") != 0)
       bad("TERN_TUNE_GEMV", s);
   }
@@ -216,6 +221,8 @@ Config read_config() {
       c.limb_unfused = true;
     } else if (strcmp(s, "resident") == 0)
       c.smallt_kernel = 4;
+    else if (strcmp(s, "narrow") == 0)
+      c.smallt_kernel = 5;
     else
       bad("TERN_TUNE_SMALLT", s);
   }
@@ -459,6 +466,48 @@ bool small_t_per_wave(int T, int n, int k) {
 
 tern::S8Plan plan_s8(int T, int n, int k, bool allow_split);
 
+// The narrow-layer kernel (tern_narrow.hip): layers of fewer than 1024
+// strips at T <= 16, each workgroup one block of W strips over one of Pk K
+// parts, the parts added in the same launch. Pk makes about one workgroup
+// per CU (256); every part's k-tiles must fit the wave's register ring. A/B
+// on MI355X (graphs of 100 calls, weights rotated past the Infinity Cache):
+// on down (68 k-tiles) 10.2-11.1 us over T = 3..16 against 11.8-13.8 for the
+// per-wave kernel (T <= 8) and the K-split tile kernel with its reduce launch
+// (T > 8); down at T = 2 keeps the resident limbs (9.4 against 10.1). On
+// o_proj (20 k-tiles) the arrival protocol (about 1.7 us: the partials'
+// stores, the count, the last part's loads) outweighs the gain up to
+// T = 12 (per-wave kernel 5.9-7.2 us against 6.7-7.2), and wins above
+// (7.4 against 8.0 at T = 16).
+bool small_t_narrow(int T, int n, int k) {
+  const Config& c = config();
+  if (c.smallt_kernel) return c.smallt_kernel == 5 && T <= 16;
+  if (n / 16 >= 1024 || T > 16) return false;
+  return (k / 256 >= 48 && T >= 3) || T >= 13;
+}
+
+tern::NarrowPlan plan_narrow(int T, int n, int k) {
+  const Config& c = config();
+  tern::NarrowPlan p;
+  const int NS = n / 16, KT = k / 256;
+  p.rows = T <= 4 ? 4 : T <= 8 ? 8 : 16;
+  p.waves = c.tune_waves == 16 ? 16 : 8;
+  p.strip_blocks = (NS + p.waves - 1) / p.waves;
+  int Pk = c.tune_kparts ? c.tune_kparts : (int)std::lround(256.0 / p.strip_blocks);
+  Pk = std::max(1, std::min(Pk, KT));
+  const int kcap = p.waves == 16 ? 12 : 16;  // registers: 16 waves leave each 128 VGPRs
+  while ((KT + Pk - 1) / Pk > kcap) ++Pk;
+  if (p.strip_blocks > 1024) Pk = 1;  // one counter per strip block in the workspace header
+  const int per = (KT + Pk - 1) / Pk;
+  p.kmax = per <= 4 ? 4 : per <= 8 ? 8 : per <= 12 ? 12 : 16;
+  p.k_parts = Pk;
+  // 4 k-tiles in flight per wave, against all of them requested up front:
+  // down 10.1-11.1 against 11.5-12.6 us (a wave's k-tiles then arrive
+  // spread out, so its arithmetic overlaps the stream); the same where a
+  // part has at most 4 k-tiles (o_proj). TERN_TUNE_DEPTH=2/8 asks for all up front.
+  p.depth = c.tune_depth && c.tune_depth != 4 ? 0 : 4;
+  return p;
+}
+
 // small_t_tiled above one 16-token tile runs the bf16 prefill contraction
 // (tern_b16mma.hip), which needs no workspace.
 bool b16_prefill(int T, tern_rung r) { return r == TERN_RUNG_SMALL_T_TILED && T > 16; }
@@ -595,7 +644,7 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
 // tern_linear, tern_workspace_bytes and tern_plan_kernels all take it from
 // here, so the declared workspace and the kernel probe's expectations are the
 // launch's own.
-enum class Path { S8, GEMV_LIMB, PER_WAVE, RESIDENT, LIMBTILE, B16_PREFILL, TILE };
+enum class Path { S8, GEMV_LIMB, PER_WAVE, RESIDENT, LIMBTILE, B16_PREFILL, TILE, NARROW };
 
 struct Choice {
   Path path = Path::S8;
@@ -603,6 +652,7 @@ struct Choice {
   tern::SmallTPlan wave{};        // PER_WAVE (also the gemv's bf16 kernel)
   tern::LimbTilePlan limbtile{};  // LIMBTILE
   tern::TilePlan tile{};          // TILE
+  tern::NarrowPlan narrow{};      // NARROW
   tern::S8Plan s8{};              // S8, B16_PREFILL
   size_t workspace = 0;
   uint64_t kernels = 0;
@@ -610,7 +660,7 @@ struct Choice {
 
 constexpr uint64_t kbit(tern_kernel id) { return uint64_t{1} << id; }
 
-Choice choose(int T, int n, int k, int G, tern_rung r) {
+Choice choose_path(int T, int n, int k, int G, tern_rung r) {
   Choice c;
   if (r == TERN_RUNG_S8) {
     c.path = Path::S8;
@@ -626,7 +676,17 @@ Choice choose(int T, int n, int k, int G, tern_rung r) {
     c.wave = plan_small_t(T, n, k, G, r);
     c.kernels = kbit(c.wave.tokens_per_tile == 1 ? TERN_KERNEL_GEMV_BF16 : TERN_KERNEL_SMALLT_WAVE);
   };
+  auto narrow = [&] {
+    c.path = Path::NARROW;
+    c.narrow = plan_narrow(T, n, k);
+    c.workspace = tern::narrow_partial_bytes(c.narrow, T, n);
+    c.kernels = kbit(TERN_KERNEL_SMALLT_NARROW);
+  };
   if (r == TERN_RUNG_GEMV) {
+    if (config().gemv_narrow && n / 16 < 1024) {
+      narrow();
+      return c;
+    }
     c.limb = plan_limb(T, n, k);
     if (!config().gemv_bf16 && limb_fits(T, k, G, c.limb)) {
       c.path = Path::GEMV_LIMB;
@@ -637,7 +697,9 @@ Choice choose(int T, int n, int k, int G, tern_rung r) {
     return c;
   }
   // small_t and small_t_tiled
-  if (small_t_resident(T, n, k, G)) {
+  if (small_t_narrow(T, n, k)) {
+    narrow();
+  } else if (small_t_resident(T, n, k, G)) {
     c.path = Path::RESIDENT;
     c.limb = plan_resident(T, n, k, G);
     c.kernels = kbit(TERN_KERNEL_SMALLT_RESIDENT);
@@ -663,6 +725,19 @@ Choice choose(int T, int n, int k, int G, tern_rung r) {
     c.kernels = kbit(TERN_KERNEL_SMALLT_TILE) |
                 (c.tile.k_parts > 1 ? kbit(TERN_KERNEL_SMALLT_TILE_REDUCE) : 0);
   }
+  return c;
+}
+
+// Every workspace starts with a header of kWsHeader bytes that only the
+// narrow-layer kernel uses (its arrival counters, zero on entry and on exit);
+// the other paths' scratch follows it, so a workspace shared by calls of
+// different paths keeps the counters intact.
+constexpr size_t kWsHeader = 4096;
+static_assert(kWsHeader >= 1024 * sizeof(int), "a counter per strip block of a narrow layer (< 1024 strips)");
+
+Choice choose(int T, int n, int k, int G, tern_rung r) {
+  Choice c = choose_path(T, n, k, G, r);
+  if (c.workspace) c.workspace += kWsHeader;
   return c;
 }
 
@@ -740,14 +815,16 @@ tern_status linear_call(const void* x_bf16, int T, const tern_weights* W, float*
     if (!aligned16(ws)) return fail(TERN_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
   const tern::SmallTArgs a{(const uint16_t*)x_bf16, T, k, n, G, W->codes, W->scales, y};
+  // the paths' scratch follows the counter header
+  char* const wsb = c.workspace ? (char*)ws + kWsHeader : nullptr;
   int err = 0;
   switch (c.path) {
     case Path::S8: {
-      int8_t* q = (int8_t*)ws;
-      float* sc = (float*)((char*)ws + align256((size_t)T * k));
+      int8_t* q = (int8_t*)wsb;
+      float* sc = (float*)(wsb + align256((size_t)T * k));
       err = tern::launch_quant_s8((const uint16_t*)x_bf16, T, k, q, sc, true, stream);
       if (err) return hip_fail(err, "quant_s8 launch");
-      float* part = (float*)((char*)ws + align256((size_t)T * k) + align256((size_t)T * sizeof(float)));
+      float* part = (float*)(wsb + align256((size_t)T * k) + align256((size_t)T * sizeof(float)));
       const tern::S8Args sa{q, sc, T, k, n, G, W->codes, W->scales, y, nullptr, true};
       err = tern::launch_s8(sa, c.s8, part, stream);
       if (err) return hip_fail(err, "s8 launch");
@@ -763,7 +840,7 @@ tern_status linear_call(const void* x_bf16, int T, const tern_weights* W, float*
       if (err) return hip_fail(err, r == TERN_RUNG_GEMV ? "gemv launch" : "small_t launch");
       break;
     case Path::LIMBTILE:
-      err = tern::launch_limbtile(a, c.limbtile, ws, stream);
+      err = tern::launch_limbtile(a, c.limbtile, wsb, stream);
       if (err) return hip_fail(err, "small_t limb launch");
       break;
     case Path::B16_PREFILL:
@@ -771,8 +848,12 @@ tern_status linear_call(const void* x_bf16, int T, const tern_weights* W, float*
       if (err) return hip_fail(err, "bf16 prefill launch");
       break;
     case Path::TILE:
-      err = tern::launch_tile(a, c.tile, ws, stream);
+      err = tern::launch_tile(a, c.tile, wsb, stream);
       if (err) return hip_fail(err, "small_t launch");
+      break;
+    case Path::NARROW:
+      err = tern::launch_narrow(a, c.narrow, wsb, c.workspace ? (int*)ws : nullptr, stream);
+      if (err) return hip_fail(err, r == TERN_RUNG_GEMV ? "gemv launch" : "small_t launch");
       break;
   }
   probe_hit(r, T, n, k, G);

@@ -88,6 +88,16 @@ struct LimbTilePlan {
   bool fused;           // T <= 4: the loader wave makes the limbs (one launch, no workspace)
 };
 
+// Launch shape of the narrow-layer small-T kernel (tern_narrow.hip).
+struct NarrowPlan {
+  int rows;          // activation rows staged per k-tile: 4, 8 or 16 (>= T)
+  int waves;         // W: waves per workgroup, one strip each: 8 or 16
+  int kmax;          // k-tiles of codes requested up front per wave: 4, 8, 12 or 16 (>= ceil(KT / Pk))
+  int strip_blocks;  // ceil(NS / W)
+  int k_parts;       // Pk: K split over workgroups, partials added in the same launch
+  int depth;         // k-tiles of codes in flight per wave: 4, or 0 (all kmax requested up front)
+};
+
 // All launchers return 0 on success or a hipError_t value.
 int launch_small_t(const SmallTArgs& a, const SmallTPlan& p, void* stream);
 // ws: tile_workspace_bytes(p, N) bytes of fp32 partials (k_parts > 1, added
@@ -118,6 +128,12 @@ int launch_quant_s8_rot(const uint16_t* x, int T, int K, int8_t* q, float* scale
 int launch_s8(const S8Args& a, const S8Plan& p, void* ws, void* stream);
 size_t s8_partial_bytes(const S8Plan& p, int T, int N);
 int launch_s8_operand_order(const S8Args& a, const S8Plan& p, void* ws, void* stream);
+// part: narrow_partial_bytes(p, T, N) bytes; counters: strip_blocks ints,
+// zero on entry, zero again when the launch completes (both unused when
+// k_parts == 1).
+int launch_narrow(const SmallTArgs& a, const NarrowPlan& p, void* part, int* counters, void* stream);
+size_t narrow_partial_bytes(const NarrowPlan& p, int T, int N);
+int narrow_lds_bytes(const NarrowPlan& p);
 // bf16 prefill contraction (tern_b16mma.hip): the small_t_tiled rung above
 // one 16-token tile; same tile plan as the s8 contraction.
 int launch_b16_prefill(const SmallTArgs& a, const S8Plan& p, void* stream);

@@ -506,6 +506,82 @@ def test_tile_kernel_shapes_keep_parity(strips, waves, depth, kparts):
     assert "smallt_tile" in seen and ("smallt_tile_reduce" in seen) == (kparts > 1), seen
 
 
+_NARROW_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import oracle, tern_synth as ts, ternary_weight_linear_amd as tl
+G = int(sys.argv[2])
+worst, bad, seen = 0.0, [], set()
+# 6 strips over K = 4096 (16 k-tiles) and 25 strips over K = 2816 (11
+# k-tiles): partial strip blocks, waves without a strip, K parts of 1..16
+# k-tiles
+for n, k in ((96, 4096), (400, 2816)):
+    rng = np.random.default_rng(n + k + G)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    shape = ts.Shape(f"narrow_{k}x{n}", k, n, G, 0.4, True, n + k)
+    wts = ts.weights(shape)
+    W = tl.TernaryWeights.from_host(wts.w, wts.s)
+    sp = ts.pow2_scales(n, k, G, seed=n)
+    Wi = tl.TernaryWeights.from_host(w, sp)
+    for T in (1, 2, 3, 4, 5, 8, 9, 13, 16):
+        rung = "gemv" if T == 1 else "small_t"
+        ws = torch.zeros((max(1, tl.workspace_bytes(T, n, k, G, rung)),), dtype=torch.uint8, device="cuda")
+        # two calls on one workspace with fresh activations: the second finds
+        # the arrival counters the first left
+        for salt in (0, 1):
+            xb = ts.activations(wts, T, salt=salt)
+            x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+            y = tl.linear(x, W, rung=rung, workspace=ws).cpu().numpy().astype(np.float64)
+            ks = tl.last_kernels()
+            assert ks == tl.plan_kernels(T, n, k, G, rung) == ["smallt_narrow"], (T, ks)
+            seen.update(ks)
+            ref = oracle.linear_bf16(xb, wts.w, wts.s)
+            worst = max(worst, np.linalg.norm(y - ref) / np.linalg.norm(ref))
+        # integer activations and power-of-two scales: every partial sum is
+        # exact, so y must equal the oracle bit for bit
+        xi = ts.integer_activations(k, T, seed=T)
+        x = torch.from_numpy(xi.view(np.int16)).cuda().view(torch.bfloat16)
+        yi = tl.linear(x, Wi, rung=rung, workspace=ws).cpu().numpy()
+        refi = oracle.linear_bf16(xi, w, sp).astype(np.float32)
+        if not np.array_equal(yi.view(np.uint32), refi.view(np.uint32)):
+            bad.append((n, k, T))
+        # the counters are zero again after the calls
+        if ws.numel() >= 4096:
+            assert int(ws[:4096].view(torch.int32).abs().sum()) == 0, (n, k, T)
+print("KERNELS", ",".join(sorted(seen)))
+print("BAD", bad)
+print("WORST", worst)
+"""
+
+
+@pytest.mark.parametrize("waves,kparts,depth,G", [(8, 0, 8, 128), (8, 1, 8, 64), (8, 3, 4, 128),
+                                                  (16, 5, 8, 64), (8, 16, 0, 128), (16, 0, 4, 128),
+                                                  (8, 1, 0, 128)])
+def test_narrow_kernel_shapes_keep_parity(waves, kparts, depth, G):
+    """The narrow-layer kernel forced (TERN_TUNE_SMALLT=narrow, and
+    TERN_TUNE_GEMV=narrow for T = 1) at T = 1..16 with 4-, 8- and 16-row
+    activation tiles, 8- and 16-wave workgroups and K split over 1 to 11
+    workgroups (register rings of 4, 8, 12 and 16 k-tiles, requested 4 ahead
+    of the one in use, the default, or all up front with TERN_TUNE_DEPTH=8):
+    within the gate
+    of the oracle on random activations, bit-exact on integer ones, two
+    calls per workspace (fresh activations each), and the workspace's
+    arrival counters zero after every call."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, TERN_TUNE_SMALLT="narrow", TERN_TUNE_GEMV="narrow",
+               TERN_TUNE_WAVES=str(waves), TERN_TUNE_KPARTS=str(kparts), TERN_TUNE_DEPTH=str(depth))
+    r = subprocess.run([sys.executable, "-c", _NARROW_CHILD, root, str(G)], env=env,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split("BAD")[1].split("\n")[0].strip() == "[]", r.stdout
+    worst = float(r.stdout.split("WORST")[1])
+    assert worst <= 1e-6, worst
+    assert r.stdout.split("KERNELS")[1].split()[0] == "smallt_narrow", r.stdout
+
+
 _S8_SPLIT_CHILD = r"""
 import sys, numpy as np, torch
 sys.path.insert(0, sys.argv[1])

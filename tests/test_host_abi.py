@@ -131,18 +131,22 @@ def test_workspace_sizes(tl):
     assert tl.workspace_bytes(1, 128, 256, 64) == 0
     assert tl.workspace_bytes(1, 5120, 17408, 128) == 0  # gemv
     assert tl.workspace_bytes(4, 128, 256, 64) == 0  # one k-tile: K is not split
-    # the per-wave small-T kernel (narrow layers: T <= 8, or K <= 8192) and
-    # the activation-tiled kernel of wide layers (no K split) keep no partial sums
-    assert tl.workspace_bytes(16, 5120, 5120, 128) == 0
-    assert tl.workspace_bytes(4, 5120, 17408, 128) == 0
+    # the per-wave small-T kernel (o_proj up to 12 tokens) and the
+    # activation-tiled kernel of wide layers (no K split) keep no partial sums
+    assert tl.workspace_bytes(12, 5120, 5120, 128) == 0
     assert tl.workspace_bytes(8, 34816, 5120, 128) == 0
+    # the narrow-layer kernel: the counter header, then 6 K parts of fp32
+    # partials of T x N
+    assert tl.workspace_bytes(4, 5120, 17408, 128) == 4096 + 6 * 4 * 5120 * 4
+    assert tl.workspace_bytes(16, 5120, 5120, 128) == 4096 + 6 * 16 * 5120 * 4
     # wide layers at T <= 4 run the limb path with the limbs made in the kernel
     assert tl.workspace_bytes(4, 34816, 5120, 128) == 0
     assert tl.workspace_bytes(2, 34816, 5120, 128, "small_t_tiled") == 0
-    # the activation-tiled kernel splits a long K over workgroups: fp32
-    # partials of one 16-token tile per K part
+    # the activation-tiled kernel (forced) splits a long K over workgroups:
+    # fp32 partials of one 16-token tile per K part, after the 4096-byte
+    # header every non-empty workspace starts with
     ws16 = tl.workspace_bytes(16, 5120, 17408, 128)
-    assert ws16 > 0 and ws16 % (16 * 5120 * 4) == 0
+    assert ws16 > 4096 and (ws16 - 4096) % (16 * 5120 * 4) == 0
     # above one 16-token tile small_t_tiled runs the prefill kernel: no K split
     assert tl.workspace_bytes(40, 5120, 17408, 128, "small_t_tiled") == 0
     need = tl.workspace_bytes(17, 5120, 5120, 128)
@@ -210,11 +214,30 @@ def test_linear_validation_happens_before_any_hip_call(tl):
 def test_unfused_limb_path_declares_its_workspace():
     """With the limbs made by the separate prep kernel (TERN_TUNE_SMALLT=limb2)
     the workspace holds one row block of 16 int8 limb rows and the per-token
-    k-tile exponents, each 256-byte aligned; two row blocks above 4 tokens."""
+    k-tile exponents, each 256-byte aligned; two row blocks above 4 tokens
+    (after the 4096-byte header of every non-empty workspace)."""
     out = _run_env({"TERN_TUNE_SMALLT": "limb2"},
                    "import ternary_weight_linear_amd as tl\n"
                    "print(tl.workspace_bytes(4, 34816, 5120, 128), tl.workspace_bytes(8, 34816, 5120, 128))")
-    assert out.split() == [str(16 * 5120 + 512), str(32 * 5120 + 768)]
+    assert out.split() == [str(4096 + 16 * 5120 + 512), str(4096 + 32 * 5120 + 768)]
+
+
+def test_narrow_path_plan_and_workspace():
+    """The narrow-layer kernel (forced with TERN_TUNE_SMALLT=narrow; at T = 1
+    with TERN_TUNE_GEMV=narrow): one kernel, about one workgroup per CU (down:
+    40 blocks of 8 strips, K in 6 parts), and a workspace of the 4096-byte
+    counter header plus Pk fp32 partials of T x N; none without a K split."""
+    out = _run_env({"TERN_TUNE_SMALLT": "narrow", "TERN_TUNE_GEMV": "narrow"},
+                   "import ternary_weight_linear_amd as tl\n"
+                   "print(tl.workspace_bytes(16, 5120, 17408, 128), tl.workspace_bytes(4, 5120, 5120, 128),\n"
+                   "      tl.workspace_bytes(1, 5120, 17408, 128), tl.workspace_bytes(4, 128, 256, 64))\n"
+                   "print(*tl.plan_kernels(4, 5120, 17408, 128, 'small_t'), *tl.plan_kernels(1, 5120, 5120, 128, 'gemv'),\n"
+                   "      *tl.plan_kernels(4, 34816, 5120, 128, 'small_t'))")
+    sizes, kernels = out.split("\n")
+    assert sizes.split() == [str(4096 + 6 * 16 * 5120 * 4), str(4096 + 6 * 4 * 5120 * 4),
+                             str(4096 + 6 * 1 * 5120 * 4), "0"]
+    # forced, it takes wide layers too (272 blocks: one K part, no workspace)
+    assert kernels.split() == ["smallt_narrow"] * 3
 
 
 def _run_env(env_extra: dict, code: str) -> str:
@@ -267,19 +290,21 @@ def test_env_is_read_once():
 
 # ------------------------------------------------ kernel choice (dry run)
 
-# Kernels the dispatcher runs by default, per layer shape (K -> N) and T: the
+# Kernels the dispatcher runs by default, per layer shape (N, K) and T: the
 # map that the measurements on the part chose (resident limbs on wide layers
 # up to 6 tokens and on narrow ones up to 3 where they fit; the tiled kernel
-# on wide layers above; the per-wave kernel on narrow ones except down above
-# 8 tokens, which splits K; s8 with a K split on short prefills of narrow
-# layers).
+# on wide layers above; on narrow ones the narrow-layer kernel with its
+# in-launch K split from 3 tokens on down's long K and above 12 tokens on
+# o_proj, the per-wave kernel between; s8 with a K split on short prefills
+# of narrow layers).
 DEFAULT_KERNELS = {
     (34816, 5120): {1: "gemv_limb", 2: "smallt_resident", 6: "smallt_resident", 7: "smallt_tile",
                     16: "smallt_tile", 17: "quant_s8,s8_mma", 2048: "quant_s8,s8_mma"},
-    (5120, 17408): {1: "gemv_limb", 2: "smallt_resident", 3: "smallt_wave", 8: "smallt_wave",
-                    9: "smallt_tile,smallt_tile_reduce", 16: "smallt_tile,smallt_tile_reduce",
+    (5120, 17408): {1: "gemv_limb", 2: "smallt_resident", 3: "smallt_narrow", 8: "smallt_narrow",
+                    9: "smallt_narrow", 16: "smallt_narrow",
                     17: "quant_s8,s8_mma,s8_reduce", 2048: "quant_s8,s8_mma"},
-    (5120, 5120): {1: "gemv_limb", 3: "smallt_resident", 4: "smallt_wave", 16: "smallt_wave",
+    (5120, 5120): {1: "gemv_limb", 3: "smallt_resident", 4: "smallt_wave", 12: "smallt_wave",
+                   13: "smallt_narrow", 16: "smallt_narrow",
                    36: "quant_s8,s8_mma,s8_reduce", 2048: "quant_s8,s8_mma"},
 }
 
@@ -306,8 +331,7 @@ PLAN = ("import ternary_weight_linear_amd as tl\n"
 def test_tune_knobs_steer_the_kernel_choice():
     """TERN_TUNE_* arms select other kernels for the same rung; the dry run
     (and so the kernel probe) names them."""
-    assert _run_env({}, PLAN) == ("gemv_limb;smallt_resident;smallt_tile,smallt_tile_reduce;"
-                                  "smallt_resident")
+    assert _run_env({}, PLAN) == "gemv_limb;smallt_resident;smallt_narrow;smallt_resident"
     assert _run_env({"TERN_TUNE_GEMV": "bf16"}, PLAN).split(";")[0] == "gemv_bf16"
     assert _run_env({"TERN_TUNE_SMALLT": "tile"}, PLAN).split(";")[1] == "smallt_tile"
     assert _run_env({"TERN_TUNE_SMALLT": "wave"}, PLAN).split(";")[1] == "smallt_wave"

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "ternary_weight_linear_amd")
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
 KERNEL_OBJS = ("tern_kernels", "tern_s8", "tern_s8mma", "tern_b16mma", "tern_tile", "tern_limb",
-               "tern_limbtile", "tern_probe", "tern_noalloc", "tern_chain")
+               "tern_limbtile", "tern_probe", "tern_noalloc", "tern_chain", "tern_narrow")
 
 
 def _runtime(name):
