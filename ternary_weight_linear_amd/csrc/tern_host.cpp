@@ -373,9 +373,9 @@ tern::TilePlan plan_tile(int T, int n, int k) {
 
 // Kernel of the small_t / small_t_tiled rungs, from A/B runs on MI355X over
 // T = 2..16: wide layers (>= 1024 strips) run the activation-tiled kernel;
-// narrow ones give it too few workgroups and run the per-wave kernel (each
-// wave loads its own activation fragments, no barriers), except for T > 8
-// with a long K, where the per-wave activation traffic grows too large.
+// narrow ones give it too few workgroups and run the narrow-layer kernel
+// (small_t_narrow) or, where that loses, the per-wave kernel (each wave loads
+// its own activation fragments, no barriers).
 // The small_t limb path (tern_limbtile.hip) takes T <= 8; by default it runs
 // wide layers (>= 1024 strips) at T <= 4, one row block, where the resident
 // limb kernel (checked first) does not fit its LDS (long K): there it beat

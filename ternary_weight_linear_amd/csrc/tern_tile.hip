@@ -24,13 +24,11 @@
 // does not need yet), and the compute waves only for their codes. One
 // barrier per k-tile hands each tile over.
 //
-// Long K and narrow N (the down projection: 320 strips, 68 k-tiles) need more
-// parallelism than the strips give, so K can also be split across Pk
-// workgroups. Each writes fp32 partial sums to the workspace and a second,
-// small kernel adds the Pk partials in ascending order (deterministic). The
-// kernel boundary orders the two; a ticket-counter handoff inside one kernel
-// would need a device-scope release per workgroup, i.e. an L2 writeback each,
-// which on this part costs far more than the second launch.
+// K can also be split across Pk workgroups (TERN_TUNE_KPARTS; narrow layers
+// now run tern_narrow.hip, which adds its parts inside the launch). Each
+// workgroup writes fp32 partial sums to the workspace and a second, small
+// kernel adds the Pk partials in ascending order (deterministic); the kernel
+// boundary orders the two.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
