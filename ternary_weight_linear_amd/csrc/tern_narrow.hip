@@ -295,6 +295,8 @@ int launch_narrow(const SmallTArgs& a, const NarrowPlan& p, void* part, int* cou
   // every part's k-tiles fit the register ring: ceil(KT / Pk) <= kmax
   if ((KT + p.k_parts - 1) / p.k_parts > p.kmax) return (int)hipErrorInvalidValue;
   if ((long)p.strip_blocks * p.k_parts > 65535L * 64) return (int)hipErrorInvalidValue;
+  // partial offsets are 32-bit byte offsets
+  if ((size_t)p.k_parts * a.T * a.N * sizeof(float) >= (size_t)1 << 31) return (int)hipErrorInvalidValue;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   switch (p.rows) {

@@ -582,6 +582,53 @@ def test_narrow_kernel_shapes_keep_parity(waves, kparts, depth, G):
     assert r.stdout.split("KERNELS")[1].split()[0] == "smallt_narrow", r.stdout
 
 
+def test_narrow_kernel_graph_replays(tl, torch):
+    """The narrow-layer kernel (default above 12 tokens on a short K) captured
+    in a graph of four calls on one workspace, replayed three times with the
+    program's own work and synchronisations between the replays: every replay
+    equals the eager results bit for bit, so the arrival counters start each
+    replay at zero (the calls leave them zero) and no call sees another's
+    partials."""
+    n, k, G = 1024, 4096, 128
+    shape = ts.Shape("narrow_graph_4096x1024", k, n, G, 0.4, True, 77)
+    wts = ts.weights(shape)
+    W = tl.TernaryWeights.from_host(wts.w, wts.s)
+    Ts = (16, 13, 16, 14)
+    assert all(tl.plan_kernels(T, n, k, G) == ["smallt_narrow"] for T in Ts)
+    xs = [to_dev_bf16(torch, ts.activations(wts, T, salt=i)) for i, T in enumerate(Ts)]
+    ws = torch.zeros((max(tl.workspace_bytes(T, n, k, G) for T in Ts),), dtype=torch.uint8, device="cuda")
+    ys = [torch.empty((T, n), dtype=torch.float32, device="cuda") for T in Ts]
+    eager = []
+    for x, y in zip(xs, ys):
+        tl.linear(x, W, y=y, workspace=ws)
+        eager.append(y.clone())
+    torch.cuda.synchronize()
+    for i, (T, e) in enumerate(zip(Ts, eager)):
+        ref = oracle.linear_bf16(ts.activations(wts, T, salt=i), wts.w, wts.s)
+        assert rel_l2(e.cpu().numpy(), ref) <= 1e-6
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for x, y in zip(xs, ys):
+                tl.linear(x, W, y=y, workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y.view(torch.int32), e.view(torch.int32)), rep
+        # eager work between the replays, on the same workspace
+        tl.linear(xs[0], W, y=ys[0], workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0].view(torch.int32), eager[0].view(torch.int32))
+    assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
+
+
 _S8_SPLIT_CHILD = r"""
 import sys, numpy as np, torch
 sys.path.insert(0, sys.argv[1])
