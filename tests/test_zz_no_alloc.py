@@ -37,11 +37,12 @@ def _noalloc(tl, torch, x, W, y, rung):
 
 
 # (layer, rung, first T, second T): the rungs and kernels that use a
-# workspace -- s8 with and without a K split, the tile kernel's K-split
-# partials -- and one that uses none.
+# workspace -- s8 with and without a K split, the narrow-layer kernel's K-split
+# partials and the arrival counters in the scratch's header -- and one that
+# uses none.
 CASES = [
     (ts.OUT_PROJ, "s8", 508, 40),         # unsplit, then split K (partials)
-    (ts.DOWN, "small_t_tiled", 12, 9),    # tile kernel, K split over workgroups
+    (ts.DOWN, "small_t_tiled", 12, 9),    # narrow-layer kernel, K split over workgroups
     (ts.GATE_UP, "s8", 2048, 17),         # 10.5 MB of codes in the scratch, then a short prefill
     (ts.SMALL, "auto", 20, 1),            # s8, then the gemv (no workspace)
 ]
