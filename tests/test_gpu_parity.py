@@ -390,6 +390,28 @@ def test_small_T_batches_sampled(tl, torch, big, shape, T):
         assert rel_l2(y[:, rows], ref) <= BF16_GATE, rung
 
 
+@pytest.mark.parametrize("shape,T", [(ts.DOWN, 3), (ts.DOWN, 8), (ts.DOWN, 16), (ts.OUT_PROJ, 16)],
+                         ids=["down-3", "down-8", "down-16", "o_proj-16"])
+def test_narrow_layers_full_shape(tl, torch, big, shape, T):
+    """The narrow-layer kernel where the dispatcher picks it, at the layers'
+    full size (240 workgroups, K in 6 parts): exact bf16 products summed in
+    fp32, so within 1e-6 of the fp64 oracle on sampled rows; and, on integer
+    activations with power-of-two scales (every partial sum exact), equal to
+    the oracle bit for bit on the same rows."""
+    wts, W = big(shape)
+    assert tl.plan_kernels(T, W.n, W.k, W.group) == ["smallt_narrow"]
+    xbits = ts.activations(wts, T)
+    rows = sample_rows(W.n, T + 101)
+    y = run(tl, torch, to_dev_bf16(torch, xbits), W, "auto")
+    assert rel_l2(y[:, rows], oracle.linear_bf16(xbits, wts.w[rows], wts.s[rows])) <= 1e-6
+    sp = ts.pow2_scales(W.n, W.k, W.group, seed=T)
+    Wi = tl.TernaryWeights.from_host(wts.w, sp)
+    xi = ts.integer_activations(W.k, T, seed=T + 3)
+    yi = run(tl, torch, to_dev_bf16(torch, xi), Wi, "auto")
+    refi = oracle.linear_bf16(xi, wts.w[rows], sp[rows]).astype(np.float32)
+    assert np.array_equal(np.ascontiguousarray(yi[:, rows]).view(np.uint32), refi.view(np.uint32))
+
+
 @pytest.mark.parametrize("shape", [ts.GATE_UP, ts.DOWN])
 @pytest.mark.parametrize("T", [17, 36, 508, 2048])
 def test_prefill_bf16_sampled(tl, torch, big, shape, T):
