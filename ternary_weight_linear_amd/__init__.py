@@ -25,6 +25,7 @@ are done with it.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -271,13 +272,14 @@ def _side_stream(stream):
     return s
 
 
-def _keep_for(stream, *tensors) -> None:
-    """Record the tensors this binding allocated on the launch stream."""
+def _on(stream):
+    """Context for the binding's own allocations: the launch stream when it is
+    not the current one, so that the caching allocator ties each block to the
+    stream that uses it and a zero fill runs before the launch on that stream
+    (an allocation on the current stream could be handed out again, or still
+    be filling, while the launch stream reads it)."""
     s = _side_stream(stream)
-    if s is not None:
-        for t in tensors:
-            if t is not None:
-                t.record_stream(s)
+    return contextlib.nullcontext() if s is None else _torch().cuda.stream(s)
 
 
 def _dev(t, dtype, name):
@@ -329,16 +331,15 @@ def quant_act_s8(x, q=None, scale=None, stream=None, layout="row_major"):
     torch = _torch()
     _dev(x, torch.bfloat16, "x")
     T, K = x.shape
-    new_q, new_scale = q is None, scale is None
-    if new_q:
-        q = torch.empty((T, K), dtype=torch.int8, device=x.device)
-    if new_scale:
-        scale = torch.empty((T,), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((T, K), dtype=torch.int8, device=x.device)
+        if scale is None:
+            scale = torch.empty((T,), dtype=torch.float32, device=x.device)
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
     _check(lib().tern_quant_act_s8(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
                                    Q_LAYOUTS[layout], _stream(stream)))
-    _keep_for(stream, q if new_q else None, scale if new_scale else None)
     return q, scale
 
 
@@ -349,16 +350,15 @@ def quant_act_s8_rot(x, q=None, scale=None, stream=None, layout="row_major"):
     torch = _torch()
     _dev(x, torch.bfloat16, "x")
     T, K = x.shape
-    new_q, new_scale = q is None, scale is None
-    if new_q:
-        q = torch.empty((T, K), dtype=torch.int8, device=x.device)
-    if new_scale:
-        scale = torch.empty((T,), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if q is None:
+            q = torch.empty((T, K), dtype=torch.int8, device=x.device)
+        if scale is None:
+            scale = torch.empty((T,), dtype=torch.float32, device=x.device)
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
     _check(lib().tern_quant_act_s8_rot(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
                                        Q_LAYOUTS[layout], _stream(stream)))
-    _keep_for(stream, q if new_q else None, scale if new_scale else None)
     return q, scale
 
 
@@ -373,14 +373,13 @@ def stream_read(buf, nbytes=None, depth=8, waves_per_cu=8, sink=None, stream=Non
     nbytes = total if nbytes is None else int(nbytes)
     if nbytes > total:
         raise ValueError(f"nbytes={nbytes} exceeds the buffer's {total} bytes")
-    new_sink = sink is None
-    if new_sink:
-        sink = torch.zeros((1,), dtype=torch.int32, device=buf.device)
+    if sink is None:
+        with _on(stream):
+            sink = torch.zeros((1,), dtype=torch.int32, device=buf.device)
     if not sink.is_cuda or sink.numel() * sink.element_size() < 4:
         raise ValueError("sink must be a device tensor of at least 4 bytes")
     _check(lib().tern_stream_read(buf.data_ptr(), nbytes, depth, waves_per_cu, sink.data_ptr(),
                                   _stream(stream)))
-    _keep_for(stream, sink if new_sink else None)
     return sink
 
 
@@ -391,23 +390,22 @@ def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=Non
     T, K = x.shape
     if K != W.k:
         raise ValueError(f"x has K={K}, weights have K={W.k}")
-    new_y = y is None
-    if new_y:
-        y = torch.empty((T, W.n), dtype=torch.float32, device=x.device)
+    if y is None:
+        with _on(stream):
+            y = torch.empty((T, W.n), dtype=torch.float32, device=x.device)
     _dev(y, torch.float32, "y")
     r = _rung(rung)
     need = lib().tern_workspace_bytes(T, W.n, W.k, W.group, r)
     if need == ctypes.c_size_t(-1).value:
         raise TernError(5, lib().tern_last_error().decode())
-    new_ws = workspace is None and need > 0
-    if new_ws:
+    if workspace is None and need > 0:
         # zeroed: the workspace header holds arrival counters that start at zero
-        workspace = torch.zeros((need,), dtype=torch.uint8, device=x.device)
+        with _on(stream):
+            workspace = torch.zeros((need,), dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().tern_linear(x.data_ptr(), T, W.ref(), y.data_ptr(), r, ws_ptr, ws_bytes,
                              _stream(stream)))
-    _keep_for(stream, y if new_y else None, workspace if new_ws else None)
     return y
 
 
@@ -438,13 +436,12 @@ def linear_s8_q(q, scale, W: TernaryWeights, y=None, stream=None, layout="row_ma
     T, K = q.shape
     if K != W.k:
         raise ValueError(f"q has K={K}, weights have K={W.k}")
-    new_y = y is None
-    if new_y:
-        y = torch.empty((T, W.n), dtype=torch.float32, device=q.device)
+    if y is None:
+        with _on(stream):
+            y = torch.empty((T, W.n), dtype=torch.float32, device=q.device)
     _dev(y, torch.float32, "y")
     _check(lib().tern_linear_s8_q(q.data_ptr(), scale.data_ptr(), T, W.ref(), y.data_ptr(),
                                   Q_LAYOUTS[layout], _stream(stream)))
-    _keep_for(stream, y if new_y else None)
     return y
 
 
@@ -454,13 +451,12 @@ def debug_s8_acc(q, W: TernaryWeights, acc=None, stream=None, layout="row_major"
     torch = _torch()
     _dev(q, torch.int8, "q")
     T = q.shape[0]
-    new_acc = acc is None
-    if new_acc:
-        acc = torch.empty((T, W.n, W.k // W.group), dtype=torch.int32, device=q.device)
+    if acc is None:
+        with _on(stream):
+            acc = torch.empty((T, W.n, W.k // W.group), dtype=torch.int32, device=q.device)
     _dev(acc, torch.int32, "acc")
     _check(lib().tern_debug_s8_acc(q.data_ptr(), T, W.ref(), acc.data_ptr(), Q_LAYOUTS[layout],
                                    _stream(stream)))
-    _keep_for(stream, acc if new_acc else None)
     return acc
 
 
