@@ -399,6 +399,7 @@ __global__ void __launch_bounds__(256) tern_s8_kernel(const int8_t* __restrict__
                                                       float* __restrict__ y,
                                                       int32_t* __restrict__ acc_out, int N) {
   __shared__ __attribute__((aligned(1024))) int8_t As[2][kS8BM * 256];
+  __shared__ float sas[kS8BM];
   constexpr int KBPG = 4 / GPT;  // 64-wide k-blocks per scale group
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -541,6 +542,9 @@ __global__ void __launch_bounds__(256) tern_s8_kernel(const int8_t* __restrict__
   }
   load_w(0, wA);
   if (!QPERM) store_a_regs(0, av);
+  // the tile's token scales in LDS for the epilogue (a load per output row
+  // there would wait for every store issued before it)
+  if (!DEBUG_ACC && tid < kS8BM) sas[tid] = act_scale[t0 + min(tid, nt - 1)];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < KT; kt += 2) {
@@ -570,7 +574,7 @@ __global__ void __launch_bounds__(256) tern_s8_kernel(const int8_t* __restrict__
       for (int i = 0; i < 4; ++i) {
         const int tl = a * 16 + 4 * g + i;
         if (tl >= nt) continue;
-        const float as = act_scale[t0 + tl];
+        const float as = sas[tl];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           if (c < nst) y[(size_t)(t0 + tl) * N + (st0 + c) * 16 + r] = tot[a][c][i] * as;

@@ -105,6 +105,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
   const int st0 = tx * kS8WgStrips + wave * S;  // first strip of this wave
   const int nst = max(0, min(S, NS - st0));     // of which exist
 
+  // The tile's token scales, read once here and kept in LDS for the
+  // epilogue: a load per output row at the end would wait for every store
+  // issued before it (the vector memory counter covers both), one memory
+  // round trip per row.
+  __shared__ float sas[BM];
+  const bool stage_scales = !DEBUG_ACC && Pk == 1;
+  float as_ld = 0.f;
+  if (stage_scales && tid < BM) as_ld = act_scale[t0 + min(tid, nt - 1)];
+
   const rsrc_t qr = make_rsrc(q + (size_t)t0 * K, (uint32_t)nt * K);
   const rsrc_t cr = make_rsrc(codes + (size_t)min(st0, NS) * KT * 64, (uint32_t)nst * KT * 1024);
   const rsrc_t sr = make_rsrc(scales + (size_t)min(st0, NS) * KT * 16 * GPT,
@@ -289,6 +298,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
     S8mStage<GPT, S> wA, wB;
     stage_a(kt0, 0);
     load_w(kt0, wA);
+    if (stage_scales && tid < BM) sas[tid] = as_ld;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int kt = kt0;
@@ -323,6 +333,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
       stage_a(kn, j);
       load_w(kn, ring[j]);
     }
+    if (stage_scales && tid < BM) sas[tid] = as_ld;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS writes done (lgkmcnt 0; vmcnt, expcnt free)
     s8m_handoff<(D - 2) * L>();
     int i = 0;
     for (; i + D <= nkt; i += D) {
@@ -371,7 +383,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) t
       for (int e = 0; e < 4; ++e) {
         const int tl = a * 16 + 4 * g + e;
         if (tl >= nt) continue;
-        const float as = act_scale[t0 + tl];
+        const float as = sas[tl];
 #pragma unroll
         for (int c = 0; c < S; ++c)
           if (c < nst) y[(size_t)(t0 + tl) * N + (st0 + c) * 16 + r] = (tot[a][c][e] * 0.015625f) * as;
