@@ -49,36 +49,51 @@ def _run(cmd):
 S8_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
+# (source, extra flags) of every translation unit; the host ABI layer is
+# plain C++ and builds with g++.
+UNITS = [
+    ("tern_kernels.hip", []),
+    ("tern_s8.hip", S8_FLAGS),
+    ("tern_s8mma.hip", S8_FLAGS),
+    ("tern_b16mma.hip", []),
+    ("tern_tile.hip", []),
+    ("tern_limb.hip", []),
+    ("tern_limbtile.hip", S8_FLAGS),
+    ("tern_probe.hip", []),
+    ("tern_noalloc.hip", []),
+    ("tern_chain.hip", []),
+    ("tern_narrow.hip", []),
+]
+
+
+def _jobs() -> int:
+    try:
+        n = int(os.environ.get("MAX_JOBS", "0"))
+    except ValueError:
+        n = 0
+    return max(1, min(n or (os.cpu_count() or 1), 16))
+
+
 def build(verbose: bool = True) -> str:
+    """Compile every unit (in parallel, up to MAX_JOBS or the CPU count, at
+    most 16 at once) and link libtern.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include")]
-    k_obj = os.path.join(BUILD, "tern_kernels.o")
-    s8_obj = os.path.join(BUILD, "tern_s8.o")
-    t_obj = os.path.join(BUILD, "tern_tile.o")
-    limb_obj = os.path.join(BUILD, "tern_limb.o")
-    s8m_obj = os.path.join(BUILD, "tern_s8mma.o")
-    b16_obj = os.path.join(BUILD, "tern_b16mma.o")
-    lt_obj = os.path.join(BUILD, "tern_limbtile.o")
-    pr_obj = os.path.join(BUILD, "tern_probe.o")
-    na_obj = os.path.join(BUILD, "tern_noalloc.o")
-    ch_obj = os.path.join(BUILD, "tern_chain.o")
-    nw_obj = os.path.join(BUILD, "tern_narrow.o")
+    cmds, objs = [], []
+    for src, extra in UNITS:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        cmds.append([HIPCC, *HIP_FLAGS, *extra, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
     h_obj = os.path.join(BUILD, "tern_host.o")
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_kernels.hip"), "-o", k_obj])
-    _run([HIPCC, *HIP_FLAGS, *S8_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_s8.hip"), "-o", s8_obj])
-    _run([HIPCC, *HIP_FLAGS, *S8_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_s8mma.hip"), "-o", s8m_obj])
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_b16mma.hip"), "-o", b16_obj])
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_tile.hip"), "-o", t_obj])
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_limb.hip"), "-o", limb_obj])
-    _run([HIPCC, *HIP_FLAGS, *S8_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_limbtile.hip"), "-o", lt_obj])
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_probe.hip"), "-o", pr_obj])
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_noalloc.hip"), "-o", na_obj])
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_chain.hip"), "-o", ch_obj])
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_narrow.hip"), "-o", nw_obj])
-    _run(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_host.cpp"), "-o", h_obj])
+    cmds.append(["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "tern_host.cpp"), "-o", h_obj])
+    objs.append(h_obj)
+    with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+        for f in [ex.submit(_run, c) for c in cmds]:
+            f.result()  # re-raises the first failure
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, k_obj, s8_obj, s8m_obj, b16_obj, t_obj, limb_obj, lt_obj,
-          pr_obj, na_obj, ch_obj, nw_obj, h_obj])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     return LIB
 
