@@ -214,7 +214,6 @@ hipError_t launch_b16m_g(const SmallTArgs& a, int tb, int s, bool x, hipStream_t
     case 2 * 16 + 2: return launch_b16m_t<GPT, 2, 2>(a, x, st);
     case 2 * 16 + 4: return launch_b16m_t<GPT, 2, 4>(a, x, st);
     case 4 * 16 + 2: return launch_b16m_t<GPT, 4, 2>(a, x, st);
-    case 4 * 16 + 4: return launch_b16m_t<GPT, 4, 4>(a, x, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -224,10 +223,14 @@ hipError_t launch_b16m_g(const SmallTArgs& a, int tb, int s, bool x, hipStream_t
 int launch_b16_prefill(const SmallTArgs& a, const S8Plan& p, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (a.T < 1) return (int)hipErrorInvalidValue;
-  // 8 blocks would not fit the registers; 3 (the s8 plan's 48-token tile) runs as 4
+  // 8 blocks would not fit the registers; 3 (the s8 plan's 48-token tile) runs as 4.
+  // The s8 plan's 64 x 64 wave tile runs as 64 x 32 here: its bf16 A fragments
+  // take twice the s8 ones' registers, and at 64 x 64 the kernel spilled (the
+  // two ran gate_up at T = 2048 in the same time on MI355X, 702 against 704 us).
   const int tb = p.token_blocks > 2 ? 4 : p.token_blocks;
-  return (int)(a.G == 128 ? launch_b16m_g<2>(a, tb, p.strips, p.xcd_order, st)
-                          : launch_b16m_g<4>(a, tb, p.strips, p.xcd_order, st));
+  const int s = tb == 4 && p.strips > 2 ? 2 : p.strips;
+  return (int)(a.G == 128 ? launch_b16m_g<2>(a, tb, s, p.xcd_order, st)
+                          : launch_b16m_g<4>(a, tb, s, p.xcd_order, st));
 }
 
 }  // namespace tern

@@ -227,7 +227,7 @@ Config read_config() {
       bad("TERN_TUNE_SMALLT", s);
   }
   if (const char* s = getenv("TERN_TUNE_S8_BM")) {
-    if (parse_int(s, 0, 128, &v) && (v == 0 || v == 32 || v == 48 || v == 64 || v == 128))  // tokens per wave tile
+    if (parse_int(s, 0, 64, &v) && (v == 0 || v == 32 || v == 48 || v == 64))  // tokens per wave tile
       c.tune_s8_bm = (int)v;
     else
       bad("TERN_TUNE_S8_BM", s);
@@ -586,12 +586,11 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   // do not waste the matrix cores, and one strip per wave up to T = 64, where the kernel is
   // bound by load latency and wants as many waves streaming as it can get.
   // (128-token tiles cost registers, and occupancy, without paying back on
-  // either 27B-class shape.)
+  // either 27B-class shape; they spilled and are not built.)
   const int tb = c.tune_s8_bm ? c.tune_s8_bm / 16 : (T > 48 ? 4 : T > 32 ? 3 : 2);
   const long tiles4 = (long)((n / 16 + 15) / 16) * ((T + 16 * tb - 1) / (16 * tb));
   int strips = T <= 64 ? 1 : (tiles4 >= 1024 ? 4 : 2);
   if (c.tune_s8_strips) strips = c.tune_s8_strips;
-  if (tb == 8) strips = 2;  // the one 128-token shape
   p.token_blocks = tb;
   p.strips = strips;
   p.xcd_order = c.tune_s8_raster != 1;
@@ -608,9 +607,9 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   };
   auto parts_for = [&](long tiles) {
     int pk = 1;
-    if (allow_split && tb != 8 && tiles < 256)
+    if (allow_split && tiles < 256)
       pk = (int)std::min<long>(512 / tiles, 16);
-    else if (allow_split && tb != 8 && tiles < 512 && KT >= 32)
+    else if (allow_split && tiles < 512 && KT >= 32)
       pk = (int)std::min<long>((512 + tiles - 1) / tiles, 16);
     return std::max(1, std::min(pk, KT / 6));  // parts of at least 6 k-tiles (o_proj: 3 parts beat 5 by 6-17 %)
   };
@@ -630,9 +629,10 @@ tern::S8Plan plan_s8(int T, int n, int k, bool allow_split) {
   }
   if (c.tune_kparts && allow_split) pk = std::max(1, std::min(c.tune_kparts, KT));
   p.k_parts = pk;
-  p.depth = (tb != 8 && (T <= 64 || pk > 1)) ? 4 : 2;
-  if (c.tune_depth == 2 || (c.tune_depth == 4 && tb != 8)) p.depth = c.tune_depth;
-  if (tb * strips >= 16) p.depth = 2;  // the 64 x 64 wave tile runs double-buffered only
+  p.depth = (T <= 64 || pk > 1) ? 4 : 2;
+  if (c.tune_depth == 2 || c.tune_depth == 4) p.depth = c.tune_depth;
+  // the 64 x 64 and 32 x 64 wave tiles run double-buffered only (registers)
+  if (tb * strips >= 16 || (tb == 2 && strips == 4)) p.depth = 2;
   return p;
 }
 
@@ -1466,6 +1466,7 @@ tern_status tern_debug_s8_acc(const int8_t* q, int T, const tern_weights* W, int
                  nullptr, acc_out, layout == TERN_Q_OPERAND_ORDER};
   tern::S8Plan p = plan_s8(T, W->n, W->k, false);
   p.depth = 2;  // the export runs the double-buffered pipeline
+  if (p.token_blocks * p.strips >= 16) p.strips = 2;  // and the 64 x 64 tile as 64 x 32 (registers)
   int err = tern::launch_s8(a, p, nullptr, stream);
   if (err) return hip_fail(err, "s8 debug launch");
   return call_ok();

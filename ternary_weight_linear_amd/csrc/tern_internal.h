@@ -34,7 +34,8 @@ struct SmallTArgs {
 // Launch shape of the s8 integer MFMA kernel for operand-order activations
 // (tern_s8mma.hip), also used by the bf16 prefill kernel (tern_b16mma.hip):
 // a wave tile of token_blocks x 16 tokens by strips x 16 outputs, (tb, s) in
-// {(2,1), (2,2), (2,4), (4,1), (4,2), (4,4), (8,2)} ((8,2): s8 only). The kernel for row-major activations
+// {(2,1), (3,1), (2,2), (2,4), (4,1), (4,2), (4,4)} (the bf16 prefill runs
+// (4,4) as (4,2) and 3 blocks as 4). The kernel for row-major activations
 // (tern_s8.hip) has one fixed shape.
 struct S8Plan {
   int token_blocks;

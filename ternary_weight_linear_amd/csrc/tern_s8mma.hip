@@ -435,8 +435,13 @@ hipError_t launch_s8m_t(const S8Args& a, const S8Plan& p, float* part, hipStream
 
 template <int GPT, int TB, int S, bool DEBUG_ACC>
 hipError_t launch_s8m_d(const S8Args& a, const S8Plan& p, float* part, hipStream_t st) {
-  if constexpr (DEBUG_ACC || TB * S >= 16) {
-    // (the 64 x 64 wave tile has no registers left for two more code stages)
+  if constexpr (DEBUG_ACC && TB * S >= 16) {
+    // the accumulator export at 64 x 64 would spill: tern_debug_s8_acc runs
+    // that tile as 64 x 32
+    return hipErrorInvalidValue;
+  } else if constexpr (DEBUG_ACC || TB * S >= 16 || (TB == 2 && S == 4)) {
+    // (the 64 x 64 and 32 x 64 wave tiles have no registers left for two more
+    // code stages)
     return launch_s8m_t<GPT, TB, S, 2, DEBUG_ACC>(a, p, part, st);
   } else {
     return p.depth == 4 ? launch_s8m_t<GPT, TB, S, 4, false>(a, p, part, st)
@@ -454,7 +459,6 @@ hipError_t launch_s8m_g(const S8Args& a, const S8Plan& p, float* part, hipStream
     case 2 * 16 + 4: return launch_s8m_d<GPT, 2, 4, DEBUG_ACC>(a, p, part, st);
     case 4 * 16 + 2: return launch_s8m_d<GPT, 4, 2, DEBUG_ACC>(a, p, part, st);
     case 4 * 16 + 4: return launch_s8m_d<GPT, 4, 4, DEBUG_ACC>(a, p, part, st);
-    case 8 * 16 + 2: return launch_s8m_t<GPT, 8, 2, 2, DEBUG_ACC>(a, p, part, st);  // LDS: double buffer only
     default: return hipErrorInvalidValue;
   }
 }
