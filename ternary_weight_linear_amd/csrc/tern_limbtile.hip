@@ -445,7 +445,16 @@ hipError_t launch_limbtile_g(const SmallTArgs& a, const LimbTilePlan& p, int8_t*
                        (const u32x4*)a.codes, a.scales, a.y, a.N);                                       \
     break;
     TERN_LIMBTILE_LAUNCH(2)
-    TERN_LIMBTILE_LAUNCH(4)
+    case 4:
+      // four k-tiles in flight with two strips per wave would spill; the plan
+      // takes depth 4 with one strip only
+      if constexpr (S == 1) {
+        hipLaunchKernelGGL((tern_limbtile_kernel<RB, S, GPT, 4>), grid, block, lds, st, limbs, dsh, a.T, a.K,
+                           (const u32x4*)a.codes, a.scales, a.y, a.N);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
 #undef TERN_LIMBTILE_LAUNCH
     default: return hipErrorInvalidValue;
   }
