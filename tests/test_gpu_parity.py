@@ -120,7 +120,9 @@ def check_s8(tl, torch, xbits, x_dev, W, w, s, y, rows=None):
     y2cols = y2 if rows is None else y2[:, rows]
     assert np.array_equal(y2cols.view(np.uint32), ordered.view(np.uint32))
     if split:
-        assert rel_l2(y, y2) <= S8_GATE
+        # both are held to the gate against the exact oracle above and below;
+        # two results within it of the same value differ by at most twice it
+        assert rel_l2(y, y2) <= 2 * S8_GATE
         y = y2  # the unsplit result, for the layout comparison below
     if q_ref.shape[1] % 64 == 0:
         qo, sco = tl.quant_act_s8(x_dev, layout="operand_order")
@@ -239,6 +241,62 @@ def test_single_nonzero_weight(tl, torch, rung):
 
 
 # ------------------------------------------------------------ edge cases
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("T", [1, 2, 5, 13, 16, 17, 64, 65])
+def test_minimal_shape_every_rung(tl, torch, G, T):
+    """The smallest layer the boundary accepts, N = 16 (one strip) by K = 256
+    (one k-tile), on every rung that takes T: integer activations and
+    power-of-two scales, so the bf16 rungs match the oracle bit for bit and
+    the s8 rung is checked as everywhere else."""
+    n, k = 16, 256
+    rng = np.random.default_rng(10 * T + G)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.pow2_scales(n, k, G, seed=T + G)
+    xbits = ts.integer_activations(k, T, seed=T)
+    W = tl.TernaryWeights.from_host(w, s)
+    x_dev = to_dev_bf16(torch, xbits)
+    ref = oracle.linear_bf16(xbits, w, s)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    for rung in RUNGS + ("auto",):
+        if not rung_ok(rung, T):
+            continue
+        print("minimal shape G", G, "T", T, "rung", rung, flush=True)
+        y = run(tl, torch, x_dev, W, rung)
+        effective = rung if rung != "auto" else tl.resolve_rung(T)
+        if effective == "s8":
+            check_s8(tl, torch, xbits, x_dev, W, w, s, y)
+        else:
+            assert np.array_equal(y.astype(np.float64), ref), rung
+
+
+@pytest.mark.parametrize("T", [1, 4, 17])
+def test_longest_k_every_rung(tl, torch, T):
+    """The longest K the boundary accepts (2^20, 4096 k-tiles) on one strip:
+    the gemv's bf16 fallback, the narrow-layer kernel's widest K split, the
+    two-pass quantisation (K above 32768) and the s8 K split."""
+    n, k, G = 16, 1 << 20, 128
+    rng = np.random.default_rng(77 + T)
+    w = ts.draw_weights(rng, n, k, 0.4)
+    s = ts.draw_scales(rng, n, k, G)
+    xbits = ts.f32_to_bf16_bits(rng.standard_normal((T, k)).astype(np.float32))
+    W = tl.TernaryWeights.from_host(w, s)
+    x_dev = to_dev_bf16(torch, xbits)
+    ref = oracle.linear_bf16(xbits, w, s)
+    for rung in RUNGS + ("auto",):
+        if not rung_ok(rung, T):
+            continue
+        print("longest K, T", T, "rung", rung, flush=True)
+        y = run(tl, torch, x_dev, W, rung)
+        effective = rung if rung != "auto" else tl.resolve_rung(T)
+        if effective == "s8":
+            check_s8(tl, torch, xbits, x_dev, W, w, s, y)
+        else:
+            assert rel_l2(y, ref) <= BF16_GATE, rung
+            assert rel_l2(y, ref) <= 1e-5, rung  # fp32 sums of exact products over 2^20 terms
+
+
 
 
 @pytest.fixture(scope="module")
