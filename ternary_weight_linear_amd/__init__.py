@@ -282,7 +282,10 @@ def _on(stream):
     return contextlib.nullcontext() if s is None else _torch().cuda.stream(s)
 
 
-def _dev(t, dtype, name):
+def _dev(t, dtype, name, shape=None, device=None):
+    """Checks a device tensor argument: HIP, dtype, contiguous, and (when
+    given) its exact shape and device. The library takes raw pointers, so a
+    buffer smaller than the call needs would be read or written past its end."""
     torch = _torch()
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
@@ -290,6 +293,10 @@ def _dev(t, dtype, name):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     return t
 
 
@@ -336,8 +343,8 @@ def quant_act_s8(x, q=None, scale=None, stream=None, layout="row_major"):
             q = torch.empty((T, K), dtype=torch.int8, device=x.device)
         if scale is None:
             scale = torch.empty((T,), dtype=torch.float32, device=x.device)
-    _dev(q, torch.int8, "q")
-    _dev(scale, torch.float32, "scale")
+    _dev(q, torch.int8, "q", (T, K), x.device)
+    _dev(scale, torch.float32, "scale", (T,), x.device)
     _check(lib().tern_quant_act_s8(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
                                    Q_LAYOUTS[layout], _stream(stream)))
     return q, scale
@@ -355,8 +362,8 @@ def quant_act_s8_rot(x, q=None, scale=None, stream=None, layout="row_major"):
             q = torch.empty((T, K), dtype=torch.int8, device=x.device)
         if scale is None:
             scale = torch.empty((T,), dtype=torch.float32, device=x.device)
-    _dev(q, torch.int8, "q")
-    _dev(scale, torch.float32, "scale")
+    _dev(q, torch.int8, "q", (T, K), x.device)
+    _dev(scale, torch.float32, "scale", (T,), x.device)
     _check(lib().tern_quant_act_s8_rot(x.data_ptr(), T, K, q.data_ptr(), scale.data_ptr(),
                                        Q_LAYOUTS[layout], _stream(stream)))
     return q, scale
@@ -393,7 +400,9 @@ def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=Non
     if y is None:
         with _on(stream):
             y = torch.empty((T, W.n), dtype=torch.float32, device=x.device)
-    _dev(y, torch.float32, "y")
+    if W.codes.device != x.device:
+        raise ValueError(f"x is on {x.device}, the weights on {W.codes.device}")
+    _dev(y, torch.float32, "y", (T, W.n), x.device)
     r = _rung(rung)
     need = lib().tern_workspace_bytes(T, W.n, W.k, W.group, r)
     if need == ctypes.c_size_t(-1).value:
@@ -402,6 +411,9 @@ def linear(x, W: TernaryWeights, rung="auto", y=None, workspace=None, stream=Non
         # zeroed: the workspace header holds arrival counters that start at zero
         with _on(stream):
             workspace = torch.zeros((need,), dtype=torch.uint8, device=x.device)
+    if workspace is not None and (not workspace.is_cuda or workspace.device != x.device
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the device of x")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().tern_linear(x.data_ptr(), T, W.ref(), y.data_ptr(), r, ws_ptr, ws_bytes,
@@ -418,10 +430,10 @@ def linear_noalloc(x, W: TernaryWeights, y, rung="auto", stream=None):
     NOALLOC_SCRATCH_BYTES per GPU; calls that overlap on one GPU race)."""
     torch = _torch()
     _dev(x, torch.bfloat16, "x")
-    _dev(y, torch.float32, "y")
     T, K = x.shape
-    if K != W.k or tuple(y.shape) != (T, W.n):
-        raise ValueError(f"x {tuple(x.shape)} / y {tuple(y.shape)} do not match the weights")
+    if K != W.k:
+        raise ValueError(f"x {tuple(x.shape)} does not match the weights' K={W.k}")
+    _dev(y, torch.float32, "y", (T, W.n), x.device)
     _check(lib().tern_linear_noalloc(x.data_ptr(), T, W.ref(), y.data_ptr(), _rung(rung),
                                      _stream(stream)))
     return y
@@ -432,14 +444,14 @@ def linear_s8_q(q, scale, W: TernaryWeights, y=None, stream=None, layout="row_ma
     scale float32 [T])."""
     torch = _torch()
     _dev(q, torch.int8, "q")
-    _dev(scale, torch.float32, "scale")
     T, K = q.shape
     if K != W.k:
         raise ValueError(f"q has K={K}, weights have K={W.k}")
+    _dev(scale, torch.float32, "scale", (T,), q.device)
     if y is None:
         with _on(stream):
             y = torch.empty((T, W.n), dtype=torch.float32, device=q.device)
-    _dev(y, torch.float32, "y")
+    _dev(y, torch.float32, "y", (T, W.n), q.device)
     _check(lib().tern_linear_s8_q(q.data_ptr(), scale.data_ptr(), T, W.ref(), y.data_ptr(),
                                   Q_LAYOUTS[layout], _stream(stream)))
     return y
@@ -454,7 +466,9 @@ def debug_s8_acc(q, W: TernaryWeights, acc=None, stream=None, layout="row_major"
     if acc is None:
         with _on(stream):
             acc = torch.empty((T, W.n, W.k // W.group), dtype=torch.int32, device=q.device)
-    _dev(acc, torch.int32, "acc")
+    if q.shape[1] != W.k:
+        raise ValueError(f"q has K={q.shape[1]}, weights have K={W.k}")
+    _dev(acc, torch.int32, "acc", (T, W.n, W.k // W.group), q.device)
     _check(lib().tern_debug_s8_acc(q.data_ptr(), T, W.ref(), acc.data_ptr(), Q_LAYOUTS[layout],
                                    _stream(stream)))
     return acc
@@ -474,8 +488,13 @@ class Chain:
         for i, (W, x, y, yb, after) in enumerate(items):
             _dev(x, torch.bfloat16, "x")
             _dev(y, torch.float32, "y")
+            if x.numel() != W.k or y.numel() != W.n:
+                raise ValueError(f"chain item {i}: x has {x.numel()} elements and y {y.numel()}, "
+                                 f"the weights take {W.k} and give {W.n}")
             if yb is not None:
                 _dev(yb, torch.bfloat16, "y_bf16")
+                if yb.numel() != W.n:
+                    raise ValueError(f"chain item {i}: y_bf16 has {yb.numel()} elements, not {W.n}")
             arr[i].W = W._struct
             arr[i].x = x.data_ptr()
             arr[i].y = y.data_ptr()

@@ -1170,3 +1170,26 @@ def test_t5_gemv_activation_range(tl, torch, case):
     # an all-zero row gives zeros
     z = run(tl, torch, to_dev_bf16(torch, np.zeros((1, k), np.uint16)), W, "gemv")
     assert np.all(z == 0)
+
+
+def test_binding_rejects_mismatched_buffers(tl, torch, small):
+    """The library takes raw pointers; the binding checks every buffer's
+    shape and device before a call, so none is read or written past its end."""
+    wts, W = small
+    x = to_dev_bf16(torch, ts.activations(wts, 4))
+    with pytest.raises(ValueError):
+        tl.linear(x, W, y=torch.empty((3, W.n), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        tl.linear(x, W, y=torch.empty((4, W.n - 16), dtype=torch.float32, device="cuda"))
+    with pytest.raises((ValueError, TypeError)):
+        tl.linear(x, W, workspace=torch.zeros((1 << 20,), dtype=torch.uint8))  # host memory
+    with pytest.raises(ValueError):
+        tl.quant_act_s8(x, q=torch.empty((4, W.k - 64), dtype=torch.int8, device="cuda"))
+    with pytest.raises(ValueError):
+        tl.quant_act_s8(x, scale=torch.empty((3,), dtype=torch.float32, device="cuda"))
+    q, sc = tl.quant_act_s8(x)
+    with pytest.raises(ValueError):
+        tl.linear_s8_q(q, sc[:3], W)
+    with pytest.raises(ValueError):
+        tl.debug_s8_acc(q, W, acc=torch.empty((4, W.n, 1), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
