@@ -454,8 +454,10 @@ bool small_t_resident(int T, int n, int k, int G) {
   if (T <= 3) return lds <= 112 * 1024;
   // Wide layers in one round of twelve-wave workgroups: ahead of the fused
   // limb kernel at T = 4 (10.8 against 14.2 us on gate_up) and, with two row
-  // blocks of tokens, of the bf16 tile kernel at T = 5, 6.
-  return T <= 6 && n / 16 >= 1024 && lds <= tern::kLimbMaxLdsResident;
+  // blocks of tokens, of the bf16 tile kernel at T = 5..8 (gate_up at T = 7:
+  // 16.4-16.5 against 17.2-17.4 us, T = 8: 16.9-17.1 against 17.2-17.4, A/B
+  // in one run on MI355X).
+  return T <= 8 && n / 16 >= 1024 && lds <= tern::kLimbMaxLdsResident;
 }
 
 bool small_t_per_wave(int T, int n, int k) {

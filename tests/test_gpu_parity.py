@@ -180,7 +180,7 @@ def test_wide_limb_plans_exact(tl, torch, ns, k):
     per wave: 7, 8 and 12 waves here, with a ragged last workgroup at 1100 and
     2176 strips. With K = 16384 the limbs and scales outgrow the LDS: the
     gemv falls back to the bf16 kernel, T = 2..4 take the fused limb kernel
-    (the resident limbs would need 128-165 KB) and T = 5, 6 the tile kernel. Integer activations and power-of-two scales make every product
+    (the resident limbs would need 128-165 KB) and T = 5..8 the tile kernel. Integer activations and power-of-two scales make every product
     and sum exact in fp32, so each T must match the oracle bit for bit, rows
     of every workgroup included."""
     n, G = 16 * ns, 128
@@ -188,7 +188,7 @@ def test_wide_limb_plans_exact(tl, torch, ns, k):
     w = ts.draw_weights(rng, n, k, 0.4)
     s = ts.pow2_scales(n, k, G, seed=ns)
     W = tl.TernaryWeights.from_host(w, s)
-    for T in range(1, 7):
+    for T in range(1, 9):
         print("wide plan", ns, "strips, K", k, "T", T, flush=True)
         xbits = ts.integer_activations(k, T, seed=ns + T)
         ref = oracle.linear_bf16(xbits, w, s)

@@ -298,8 +298,8 @@ def test_env_is_read_once():
 # o_proj, the per-wave kernel between; s8 with a K split on short prefills
 # of narrow layers).
 DEFAULT_KERNELS = {
-    (34816, 5120): {1: "gemv_limb", 2: "smallt_resident", 6: "smallt_resident", 7: "smallt_tile",
-                    16: "smallt_tile", 17: "quant_s8,s8_mma", 2048: "quant_s8,s8_mma"},
+    (34816, 5120): {1: "gemv_limb", 2: "smallt_resident", 6: "smallt_resident", 8: "smallt_resident",
+                    9: "smallt_tile", 16: "smallt_tile", 17: "quant_s8,s8_mma", 2048: "quant_s8,s8_mma"},
     (5120, 17408): {1: "gemv_limb", 2: "smallt_resident", 3: "smallt_narrow", 8: "smallt_narrow",
                     9: "smallt_narrow", 16: "smallt_narrow",
                     17: "quant_s8,s8_mma,s8_reduce", 2048: "quant_s8,s8_mma"},
