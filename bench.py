@@ -559,7 +559,7 @@ def kernels_only(torch, ts, tl, dev, n):
     torch.cuda.synchronize()
     x16 = torch.from_numpy(ts.activations(w, 8).view(np.int16)).to(dev).view(torch.bfloat16)
     y16 = torch.empty((8, b.n), dtype=torch.float32, device=dev)
-    for i in range(n):  # draft-verify batch T = 8 (activation-tiled kernel on this wide layer)
+    for i in range(n):  # draft-verify batch T = 8 (resident limb kernel on this wide layer)
         tl.linear(x16, sets[i % len(sets)], y=y16)
     torch.cuda.synchronize()
     qr = torch.empty((T, b.k), dtype=torch.int8, device=dev)
