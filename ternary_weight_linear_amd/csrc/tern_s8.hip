@@ -174,16 +174,29 @@ __global__ void __launch_bounds__(NT) tern_quant_s8_perm_kernel(const uint16_t* 
   for (int w = 1; w < NW; ++w) am = max(am, wmax[w]);
   const float sc = __uint_as_float(am) / 127.0f;  // IEEE single division
   if (threadIdx.x == 0) scale[t] = am == 0 ? 0.0f : sc;
-  // (Codes by division here: the reciprocal shortcut of the rotated kernel
-  // keeps 16 more values live per chunk, which costs this kernel occupancy.)
+  // Codes by the reciprocal (quant_code_rcp); the 8 values of a 16-byte load
+  // are redone by division when one of them lies near a rounding boundary,
+  // from the same packed registers, so no more values stay live.
+  const float r = 1.0f / sc;
+  const bool rcp_ok = sc >= 0x1p-126f;  // a normal scale: r is finite
   u32x4* qr = (u32x4*)(q + (size_t)t * K);
   auto codes8 = [&](const uint4 v, uint32_t& c0, uint32_t& c1) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t b[8];
+    bool near = !rcp_ok;
+    if (rcp_ok) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      b[2 * i] = quant_byte(w[i] << 16, sc);
-      b[2 * i + 1] = quant_byte(w[i] & 0xffff0000u, sc);
+      for (int i = 0; i < 4; ++i) {
+        b[2 * i] = quant_code_rcp(__uint_as_float(w[i] << 16), r, near);
+        b[2 * i + 1] = quant_code_rcp(__uint_as_float(w[i] & 0xffff0000u), r, near);
+      }
+    }
+    if (near) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b[2 * i] = quant_byte(w[i] << 16, sc);
+        b[2 * i + 1] = quant_byte(w[i] & 0xffff0000u, sc);
+      }
     }
     c0 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
     c1 = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
@@ -598,35 +611,45 @@ hipError_t launch_s8_v(const S8Args& a, hipStream_t st) {
 
 }  // namespace
 
+template <int NT, int MAXNU>
+int launch_quant_perm(int nu, const uint16_t* x, int T, int K, int8_t* q, float* scale, hipStream_t st) {
+  switch (nu) {
+#define TERN_QP_LAUNCH(NU)                                                                              \
+  case NU:                                                                                              \
+    if constexpr (NU <= MAXNU)                                                                          \
+      hipLaunchKernelGGL((tern_quant_s8_perm_kernel<NU, NT>), dim3(T), dim3(NT), 0, st, x, K, q, scale); \
+    break;
+    TERN_QP_LAUNCH(1)
+    TERN_QP_LAUNCH(2)
+    TERN_QP_LAUNCH(3)
+    TERN_QP_LAUNCH(4)
+    TERN_QP_LAUNCH(5)
+    TERN_QP_LAUNCH(6)
+    TERN_QP_LAUNCH(7)
+    TERN_QP_LAUNCH(8)
+#undef TERN_QP_LAUNCH
+    default: return (int)hipErrorInvalidValue;
+  }
+  return kernel_launched((int)hipGetLastError(), TERN_KERNEL_QUANT_S8);
+}
+
 int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bool operand_order,
                     void* stream) {
   if (T <= 0) return 0;
   hipStream_t st = (hipStream_t)stream;
-  // Short batches (fewer tokens than CUs): 1024 threads per token, for K up
-  // to 32768 (two chunks per thread); otherwise 256.
+  // Threads per token. Short batches (fewer tokens than CUs): 1024, for K up
+  // to 32768 (two chunks per thread). Long ones: 256 below K = 16384, else
+  // 512. Measured at T = 2048 on MI355X: K = 5120 ran in 8.9 us with 256
+  // threads and 13.5-18 us with 320 to 1024; K = 17408 in 23.1 us with 512
+  // (3 chunks per thread) against 25.1 with 256 (5 chunks, half the
+  // occupancy) and 24.1-26.6 with 320, 384 and 1024.
   const bool wide_wg = T < 256 && K <= 32768;
-  const int nt = wide_wg ? 1024 : 256;
+  const int nt = wide_wg ? 1024 : K < 16384 ? 256 : 512;
   const int nu = (K / 16 + nt - 1) / nt;  // output chunks per thread
-  if (operand_order && nu <= (wide_wg ? 2 : 8)) {
-    switch (nu * 2 + (wide_wg ? 1 : 0)) {
-#define TERN_QP_LAUNCH(NU, NT)                                                                        \
-  case NU * 2 + (NT == 1024 ? 1 : 0):                                                                 \
-    hipLaunchKernelGGL((tern_quant_s8_perm_kernel<NU, NT>), dim3(T), dim3(NT), 0, st, x, K, q, scale); \
-    break;
-      TERN_QP_LAUNCH(1, 256)
-      TERN_QP_LAUNCH(2, 256)
-      TERN_QP_LAUNCH(3, 256)
-      TERN_QP_LAUNCH(4, 256)
-      TERN_QP_LAUNCH(5, 256)
-      TERN_QP_LAUNCH(6, 256)
-      TERN_QP_LAUNCH(7, 256)
-      TERN_QP_LAUNCH(8, 256)
-      TERN_QP_LAUNCH(1, 1024)
-      TERN_QP_LAUNCH(2, 1024)
-#undef TERN_QP_LAUNCH
-      default: return (int)hipErrorInvalidValue;
-    }
-    return kernel_launched((int)hipGetLastError(), TERN_KERNEL_QUANT_S8);
+  if (operand_order && nu <= 8) {
+    if (nt == 1024) return launch_quant_perm<1024, 2>(nu, x, T, K, q, scale, st);
+    if (nt == 512) return launch_quant_perm<512, 8>(nu, x, T, K, q, scale, st);
+    return launch_quant_perm<256, 4>(nu, x, T, K, q, scale, st);
   }
   if (operand_order)
     hipLaunchKernelGGL(tern_quant_s8_kernel<true>, dim3(T), dim3(256), 0, (hipStream_t)stream, x, K,

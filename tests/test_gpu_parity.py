@@ -990,6 +990,51 @@ def test_quant_rot_rejects_bad_shapes(tl, torch):
         tl.quant_act_s8_rot(x)
 
 
+def _boundary_tokens(T, K, seed):
+    """bf16 tokens whose quotients v / scale lie on or near half-integers:
+    even tokens have an absmax of 127 * 2^e (scale 2^e exactly, every value
+    (k + 1/2) 2^e an exact tie), odd ones a random absmax; the other values
+    are the bf16 roundings of (k + 1/2) * scale moved by -2..2 bf16 steps."""
+    rng = np.random.default_rng(seed)
+    x = np.empty((T, K), np.uint16)
+    for t in range(T):
+        e = int(rng.integers(-20, 20))
+        am = 127.0 * 2.0 ** e if t % 2 == 0 else rng.uniform(0.5, 4.0) * 2.0 ** e
+        amb = ts.f32_to_bf16_bits(np.asarray([am], np.float32))[0]
+        amf = ts.bf16_bits_to_f32(np.asarray([amb]))[0]
+        sc = amf / np.float32(127.0)
+        k = rng.integers(-127, 127, K).astype(np.float64)
+        v = ts.f32_to_bf16_bits(((k + 0.5) * np.float64(sc)).astype(np.float32))
+        v = (v.astype(np.int32) + rng.integers(-2, 3, K) * (t % 2)).astype(np.uint16)
+        big = np.abs(ts.bf16_bits_to_f32(v)) > amf
+        v[big] = amb
+        v[int(rng.integers(0, K))] = amb
+        x[t] = v
+    return x
+
+
+@pytest.mark.parametrize("K", [5120, 17408, 65536])
+@pytest.mark.parametrize("layout", ["row_major", "operand_order"])
+def test_quant_codes_at_rounding_boundaries(tl, torch, K, layout):
+    """Quotients on and near half-integers, where a code computed through the
+    reciprocal of the scale could differ from the oracle's rounding of the
+    IEEE quotient: codes and scales bit-exact at 256 tokens (the launch shapes
+    of long batches: 256 threads per token below K = 16384, 512 from there)
+    and at 16 (1024 threads per token up to K = 32768)."""
+    x = _boundary_tokens(256, K, 5 + K)
+    scale = oracle.quant_s8(x)[1].astype(np.float64)
+    quot = ts.bf16_bits_to_f32(x).astype(np.float64) / scale[:, None]
+    off = np.abs(quot - np.floor(quot) - 0.5)
+    assert (off == 0).sum() > 1000 and ((off > 0) & (off < 2.0 ** -15)).sum() > 100
+    for T in (256, 16):
+        q_ref, s_ref = oracle.quant_s8(x[:T])
+        q, sc = tl.quant_act_s8(to_dev_bf16(torch, x[:T]), layout=layout)
+        torch.cuda.synchronize()
+        want = q_ref if layout == "row_major" else operand_order(q_ref)
+        assert np.array_equal(q.cpu().numpy(), want)
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
 # ------------------------------------------- environment arms on the GPU
 
 _ARM_CHILD = r"""
