@@ -207,6 +207,12 @@ __global__ void __launch_bounds__(NT) tern_quant_s8_perm_kernel(const uint16_t* 
     if (j >= nu) break;
     u32x4 out = u32x4{0u, 0u, 0u, 0u};
     if (am != 0) {
+      // An empty asm that takes the chunk's packed words as read and
+      // rewritten here keeps the compiler from unpacking every chunk to fp32
+      // right after the loads (twice the registers: 102 instead of 63 VGPRs
+      // at NU = 5); no instruction is emitted.
+      asm volatile("" : "+v"(lo[u].x), "+v"(lo[u].y), "+v"(lo[u].z), "+v"(lo[u].w), "+v"(hi[u].x), "+v"(hi[u].y),
+                   "+v"(hi[u].z), "+v"(hi[u].w));
       uint32_t L0, L1, H0, H1;
       codes8(lo[u], L0, L1);
       codes8(hi[u], H0, H1);
@@ -639,10 +645,10 @@ int launch_quant_s8(const uint16_t* x, int T, int K, int8_t* q, float* scale, bo
   hipStream_t st = (hipStream_t)stream;
   // Threads per token. Short batches (fewer tokens than CUs): 1024, for K up
   // to 32768 (two chunks per thread). Long ones: 256 below K = 16384, else
-  // 512. Measured at T = 2048 on MI355X: K = 5120 ran in 8.9 us with 256
-  // threads and 13.5-18 us with 320 to 1024; K = 17408 in 23.1 us with 512
-  // (3 chunks per thread) against 25.1 with 256 (5 chunks, half the
-  // occupancy) and 24.1-26.6 with 320, 384 and 1024.
+  // 512. Measured at T = 2048 on MI355X: at K = 5120, 256 threads beat 320
+  // to 1024 (8.9 against 13.5-18 us); at K = 17408, 512 threads (3 chunks
+  // each) ran in 22.1 us against 23.4 with 256 (5 chunks) and 24.1-26.6
+  // with 320, 384 and 1024.
   const bool wide_wg = T < 256 && K <= 32768;
   const int nt = wide_wg ? 1024 : K < 16384 ? 256 : 512;
   const int nu = (K / 16 + nt - 1) / nt;  // output chunks per thread
